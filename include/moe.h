@@ -1,0 +1,289 @@
+/*
+ * moe.h -- C ABI of the int4/int8 group-quantized sparse MoE layer for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * One call computes one sparse Mixture-of-Experts layer of the kind the
+ * Swiftlet pages describe for the Qwen3-Next / Qwen3.5-3.6 hybrid models:
+ * every token is routed to the top-k of E experts (10 of 512 for the
+ * 80B-A3B family, 8 of 256 for the 35B-A3B family) by a resident router, an
+ * always-active shared expert is added, and the routed experts' weights are
+ * MLX-style int4/int8 group-quantized and held as fixed-stride blobs, one
+ * contiguous blob per expert, addressed with 64-bit offsets
+ * (page "Paquets Swiftlet 80B Qwen ..." on xix.ai, 4th and last paragraphs;
+ * page "Swiftlet — Swift + Metal рантайм" on news.bugfactory.tech,
+ * 3rd paragraph; page "Swiftlet: 在 Mac 和 iPhone 上執行 80B 與 35B Qwen 模型"
+ * on agentlenshq.com, section "記憶體管理與權重串流").  On one MI355X the whole
+ * expert pack fits in HBM, so a per-layer slot table maps expert -> slot of a
+ * device-resident slab instead of a host-side pool.
+ *
+ * What one layer computes, per token t with input x_hat[t] (stored values of
+ * the activation dtype):
+ *   l      = Wr x_hat (+ router bias)                       (router, fp32 Wr)
+ *   S, w   = top-k of softmax(l), renormalised over the k selected
+ *            (ordered by logit descending, ties to the lower expert index)
+ *   gamma  = sigmoid(w_sg . x_hat)                           (shared gate)
+ *   y_e    = Wd_e (silu(Wg_e x_hat) * (Wu_e x_hat))          (SwiGLU expert)
+ *   out    = sum_j w_j y_{S_j} + gamma y_shared
+ * with W[r,c] = scale[r, c/64] * q[r,c] + bias[r, c/64], q unsigned
+ * (0..15 int4, 0..255 int8), scale and bias bf16, groups of 64 consecutive
+ * input columns.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Return value: MOE_OK (0) or a negative moe_status.  Arguments are fully
+ *   validated before anything is enqueued; on error nothing is enqueued.
+ * - Memory: every tensor argument is a caller-owned *device* pointer unless
+ *   the parameter documentation says "host".  The library never allocates,
+ *   frees or synchronises; all work is enqueued on the given HIP stream and
+ *   the pointers must stay valid until that work completes.  Device faults
+ *   surface at the caller's next synchronisation.
+ * - Layouts are row-major and dense.  Activations are [n_tokens x hidden] of
+ *   act_dtype (fp32 or bf16).  Device pointers must be 16-byte aligned; the
+ *   expert slab and every blob must be 256-byte aligned.
+ * - Slab addressing is 64-bit: blob of expert e = slab + slot_table[e] *
+ *   expert_stride.  slot_table entries are not range-checked on the device.
+ * - No global mutable state: calls are reentrant; concurrent calls must use
+ *   distinct workspaces.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null pointer, size out of range, k > E ...   */
+  MOE_ERR_UNSUPPORTED = -2, /* bits, group, dtype or shape not implemented  */
+  MOE_ERR_MISALIGNED = -3,  /* pointer or stride alignment violated         */
+  MOE_ERR_NO_DEVICE = -4,   /* no HIP device visible                        */
+  MOE_ERR_LAUNCH = -5       /* a kernel launch returned an error            */
+};
+
+/* activation dtypes */
+enum moe_act_dtype { MOE_ACT_F32 = 0, MOE_ACT_BF16 = 1 };
+
+/* desc.flags */
+enum moe_flags {
+  MOE_FLAG_ROUTER_BIAS = 1u, /* an additive fp32 router bias [E] is given */
+  MOE_FLAG_SHARED = 2u       /* the layer has a sigmoid-gated shared expert */
+};
+
+/* Limits of this implementation (validated). */
+#define MOE_MAX_TOP_K 16
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_HIDDEN 8192
+#define MOE_MAX_INTER 4096
+
+/*
+ * Shape and format of one MoE layer.  Host memory, read at call time only.
+ *   n_tokens      tokens in the call (1 for batch-1 decode)
+ *   hidden        H: multiple of 128 (int4) / 64 (int8), <= MOE_MAX_HIDDEN
+ *   n_experts     E: 1 .. MOE_MAX_EXPERTS routed experts
+ *   top_k         k: 1 .. min(E, MOE_MAX_TOP_K)
+ *   inter         I: routed-expert intermediate size, multiple of 128 (int4)
+ *                 / 64 (int8), 16 <= I <= MOE_MAX_INTER
+ *   shared_inter  Is: shared-expert intermediate size, same rule (ignored
+ *                 without MOE_FLAG_SHARED)
+ *   group         quantisation group along the input axis; must be 64
+ *   bits          4 or 8
+ *   act_dtype     enum moe_act_dtype
+ *   expert_stride bytes between consecutive slab slots; >= the blob size of
+ *                 moe_blob_layout(), multiple of 256
+ *   flags         enum moe_flags
+ *   rms_eps       epsilon of the RMSNorm used by moe_rmsnorm / chains
+ */
+typedef struct moe_layer_desc {
+  int32_t n_tokens;
+  int32_t hidden;
+  int32_t n_experts;
+  int32_t top_k;
+  int32_t inter;
+  int32_t shared_inter;
+  int32_t group;
+  int32_t bits;
+  int32_t act_dtype;
+  int32_t reserved0;
+  int64_t expert_stride;
+  uint32_t flags;
+  float rms_eps;
+} moe_layer_desc;
+
+/*
+ * Physical layout of one expert blob (the fixed-stride unit the pages
+ * describe; the format itself is this library's own).
+ *
+ * Both sections are made of row tiles of `row_tile` (16) consecutive output
+ * rows.  A tile is split along the input axis into k-blocks of
+ * `kblock_cols` columns (128 for int4, 64 for int8: 64 bytes of codes per
+ * row).  Per (tile, k-block) the codes are stored row-major, 64 bytes per row
+ * (16 x 64 B = 1 KiB), followed by the bf16 (scale, bias) pairs of the
+ * block's groups, row-major [row][group][scale, bias].
+ *   gate/up section: unit = gate codes 1 KiB | up codes 1 KiB |
+ *                    gate (scale,bias) | up (scale,bias);
+ *                    tiles over I rows, k-blocks over H columns.
+ *   down section:    unit = down codes 1 KiB | down (scale,bias);
+ *                    tiles over H rows, k-blocks over I columns.
+ * Within a row's 64 bytes, byte i holds columns 2i (low nibble) and 2i+1
+ * (high nibble) for int4, column i for int8 (columns relative to the
+ * k-block).  Units are stored k-block-fastest, then tile.
+ * The shared-expert blob uses the same layout with I = shared_inter and is
+ * followed, at shared_gate_offset, by the shared gate weight w_sg: fp32[H].
+ */
+typedef struct moe_blob_layout_t {
+  int64_t gu_offset;         /* start of the gate/up section            */
+  int64_t gu_unit_bytes;     /* bytes of one (tile, k-block) unit       */
+  int64_t gu_tile_bytes;     /* bytes of one row tile (all k-blocks)    */
+  int64_t down_offset;       /* start of the down section               */
+  int64_t down_unit_bytes;
+  int64_t down_tile_bytes;
+  int64_t blob_bytes;        /* bytes of the blob, multiple of 256      */
+  int64_t shared_gate_offset;/* shared blob: byte offset of w_sg fp32[H]*/
+  int64_t shared_bytes;      /* shared blob incl. w_sg, multiple of 256 */
+  int32_t row_tile;          /* 16                                      */
+  int32_t kblock_cols;       /* 128 (int4) / 64 (int8)                  */
+  int32_t groups_per_kblock; /* 2 (int4) / 1 (int8)                     */
+  int32_t reserved0;
+} moe_blob_layout_t;
+
+/* Library version string, e.g. "moe-gfx950 0.1.0". */
+const char* moe_version(void);
+
+/* Human-readable name of a status code (never NULL). */
+const char* moe_status_string(int status);
+
+/*
+ * Byte layout of one expert blob with intermediate size `inter` (pass
+ * desc->inter for routed experts, desc->shared_inter for the shared blob).
+ * `out` is host memory.  Pure host function; needs no device.
+ */
+int moe_blob_layout(const moe_layer_desc* desc, int32_t inter, moe_blob_layout_t* out);
+
+/*
+ * Host packer (the analogue of the pages' repack tool): writes one blob from
+ * logical arrays, all in host memory.
+ *   q_gate, q_up  [inter x hidden] codes, one code per byte (0..2^bits-1)
+ *   q_down        [hidden x inter] codes, one code per byte
+ *   sb_gate, sb_up  scale then bias planes: 2 x [inter x hidden/64] bf16 bits
+ *                   (uint16), i.e. scale[inter][G] followed by bias[inter][G]
+ *   sb_down         2 x [hidden x inter/64] bf16 bits, scale plane then bias
+ *   shared_gate_w   fp32[hidden] or NULL; when given, written at
+ *                   shared_gate_offset (shared blob)
+ *   blob_out      host buffer of at least blob_bytes (shared_bytes when
+ *                 shared_gate_w is given); padding bytes are zeroed
+ * Codes out of range return MOE_ERR_INVALID_ARG.
+ */
+int moe_pack_expert(const moe_layer_desc* desc, int32_t inter, const uint8_t* q_gate,
+                    const uint8_t* q_up, const uint8_t* q_down, const uint16_t* sb_gate,
+                    const uint16_t* sb_up, const uint16_t* sb_down, const float* shared_gate_w,
+                    void* blob_out);
+
+/*
+ * Device packer: packs n experts from device-resident logical arrays into the
+ * slab.  Arrays are as for moe_pack_expert, stacked over the n experts
+ * (expert i's q_gate at q_gate + i*inter*hidden, its sb_gate at
+ * sb_gate + i*2*inter*(hidden/64), ...).  Expert i is written to
+ * slab + dst_slots[i] * desc->expert_stride; dst_slots is a *host* int64
+ * array of n slots.  Codes must already be in range (not checked).
+ */
+int moe_pack_experts_device(const moe_layer_desc* desc, int32_t inter, int32_t n,
+                            const uint8_t* q_gate, const uint8_t* q_up, const uint8_t* q_down,
+                            const uint16_t* sb_gate, const uint16_t* sb_up,
+                            const uint16_t* sb_down, void* slab, const int64_t* dst_slots,
+                            hipStream_t stream);
+
+/* Workspace bytes needed by the compute entry points for `desc` (host). */
+size_t moe_workspace_bytes(const moe_layer_desc* desc);
+
+/*
+ * Router, softmax, top-k and renormalisation, plus the shared gate.
+ *   x             [T x H] act_dtype, the layer input x_hat
+ *   router_w      [E x H] fp32
+ *   router_bias   [E] fp32 or NULL (required iff MOE_FLAG_ROUTER_BIAS)
+ *   shared_gate_w [H] fp32 or NULL
+ *   topk_idx      out [T x k] int32, by logit descending (ties: lower index)
+ *   topk_w        out [T x k] fp32, sums to 1 per token
+ *   shared_gate   out [T] fp32 sigmoid(w_sg . x), or NULL (needs shared_gate_w)
+ *   ws            workspace of moe_workspace_bytes(desc) bytes
+ */
+int moe_router_topk(const moe_layer_desc* desc, const void* x, const float* router_w,
+                    const float* router_bias, const float* shared_gate_w, int32_t* topk_idx,
+                    float* topk_w, float* shared_gate, void* ws, hipStream_t stream);
+
+/*
+ * The experts with a given routing ("forward with given routing"): steps
+ * after the router.
+ *   x            [T x H] act_dtype
+ *   topk_idx     [T x k] int32 expert ids in [0, E)
+ *   topk_w       [T x k] fp32 routing weights
+ *   shared_gate  [T] fp32 gamma, required iff MOE_FLAG_SHARED
+ *   expert_slab  base of the slab (256-byte aligned)
+ *   slot_table   [E] int32 slab slot of each expert
+ *   shared_blob  shared-expert blob (layout above) iff MOE_FLAG_SHARED
+ *   out          out [T x H] act_dtype
+ */
+int moe_experts_forward(const moe_layer_desc* desc, const void* x, const int32_t* topk_idx,
+                        const float* topk_w, const float* shared_gate, const void* expert_slab,
+                        const int32_t* slot_table, const void* shared_blob, void* out, void* ws,
+                        hipStream_t stream);
+
+/*
+ * One whole MoE layer: router + top-k + shared gate + experts + combine.
+ * The shared gate weight is read from the shared blob.  The routing of the
+ * call stays in the workspace and can be read with moe_workspace_routing().
+ */
+int moe_layer_forward(const moe_layer_desc* desc, const void* x, const float* router_w,
+                      const float* router_bias, const void* expert_slab,
+                      const int32_t* slot_table, const void* shared_blob, void* out, void* ws,
+                      hipStream_t stream);
+
+/*
+ * Device pointers, inside `ws`, of the routing written by the last
+ * moe_layer_forward / moe_chain_forward layer that used `ws`:
+ * topk_idx [T x k] int32, topk_w [T x k] fp32, shared_gate [T] fp32.
+ * Any output pointer may be NULL.  Pure host arithmetic on `ws`.
+ */
+int moe_workspace_routing(const moe_layer_desc* desc, void* ws, int32_t** topk_idx,
+                          float** topk_w, float** shared_gate);
+
+/*
+ * Chain step around a layer: optional residual add, then RMSNorm.
+ *   x        in/out [T x H] act_dtype residual stream.  If `out` is non-NULL,
+ *            x <- act(x + out) first.
+ *   out      [T x H] act_dtype layer output, or NULL
+ *   x_hat    out [T x H] act_dtype: act(x / sqrt(mean(x^2) + rms_eps))
+ *            (unit weight)
+ */
+int moe_rmsnorm(const moe_layer_desc* desc, void* x, const void* out, void* x_hat,
+                hipStream_t stream);
+
+/*
+ * A chain of n_layers distinct layers over one batch:
+ *   for l: x_hat = rmsnorm(x); out = layer_l(x_hat); x <- act(x + out).
+ *   x             in/out [T x H] act_dtype
+ *   router_w      layer l at router_w + l * E * H (fp32)
+ *   router_bias   layer l at router_bias + l * E, or NULL
+ *   expert_slab   one slab for all layers
+ *   slot_tables   layer l at slot_tables + l * E
+ *   shared_blobs  layer l at shared_blobs + l * shared_stride bytes
+ *   shared_stride bytes between shared blobs, multiple of 256
+ *   x_hat, out    [T x H] act_dtype scratch tensors (hold the last layer's)
+ */
+int moe_chain_forward(const moe_layer_desc* desc, int32_t n_layers, void* x,
+                      const float* router_w, const float* router_bias, const void* expert_slab,
+                      const int32_t* slot_tables, const void* shared_blobs,
+                      int64_t shared_stride, void* x_hat, void* out, void* ws,
+                      hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

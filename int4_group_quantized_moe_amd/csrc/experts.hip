@@ -1,0 +1,777 @@
+// Expert kernels of the MoE layer: fused int4/int8 group-dequant gate/up GEMV
+// with SiLU*up, dequant down GEMV with the weighted combine, token->expert
+// bucketing, residual + RMSNorm, and the device packer of expert blobs.
+//
+// Quantisation: MLX-style int4/int8 group quantisation with byte-addressed
+// blobs and 64-bit offsets (page "Paquets Swiftlet 80B Qwen ..." on xix.ai,
+// last paragraph); w = scale * q + bias per group of 64 input columns.
+// Each routed expert is one fixed-stride blob, so one slot index gives one
+// contiguous expert (same page, 4th paragraph).
+//
+// The dot products use the group-affine factoring
+//   sum_c (s q_c + b) x_c = s * sum_c q_c x_c + b * sum_c x_c,
+// so codes are never turned into weights.  With bf16 activations the int
+// codes are widened to fp16 by OR-ing them into the mantissa of 1024.0
+// (0x6400 | q == 1024 + q exactly, and 0x6400 | (q << 4) == 1024 + 16 q), and
+// the products are taken two at a time with v_dot2_f32_f16 against fp16
+// activations prepared once per token; the 1024 * x terms are removed with a
+// per-chunk correction.  fp32 activations keep an exact fp32 path.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c,
+                                false);
+}
+
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const _Float16 l = (_Float16)lo, h = (_Float16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, l) | ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
+}
+
+__device__ __forceinline__ float f16_lo(uint32_t p) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(p & 0xFFFFu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t p) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(p >> 16));
+}
+
+// Columns covered by one lane's 16 code bytes.
+template <int BITS>
+constexpr int chunk_cols() { return BITS == 4 ? 32 : 16; }
+
+// ---------------------------------------------------------------------------
+// Per-token activation staging in LDS.
+//
+// BF16 path: xp holds, per chunk of chunk_cols columns, the fp16 pairs in the
+// order the code unpacking produces them; cs holds per chunk
+// (1024 * sum of the staged fp16 values, sum of the effective x values).
+//   int4, chunk of 32 columns, dword j (columns 8j..8j+7):
+//     [x0, x4], [x1/16, x5/16], [x2, x6], [x3/16, x7/16]
+//   int8, chunk of 16 columns: [x0, x1], [x2, x3], ... (8 dwords)
+// F32 path: xs holds x as fp32; cs.y the chunk sum of x.
+template <int BITS, int ACT>
+struct XStage {
+  static constexpr int kCC = chunk_cols<BITS>();
+  // dwords of staged activations per token
+  static __host__ __device__ constexpr int dwords(int H) {
+    return ACT == MOE_ACT_F32 ? H : H / 2;
+  }
+  static __host__ __device__ constexpr int bytes(int H) {
+    return dwords(H) * 4 + (H / kCC) * 8;
+  }
+};
+
+template <int BITS, int ACT>
+__device__ void stage_token(const void* __restrict__ x, int64_t row, int H, uint32_t* xp,
+                            float2* cs) {
+  constexpr int CC = chunk_cols<BITS>();
+  const int nchunk = H / CC;
+  // one thread per chunk
+  for (int ch = threadIdx.x; ch < nchunk; ch += blockDim.x) {
+    const int64_t base = row * H + (int64_t)ch * CC;
+    float xv[CC];
+#pragma unroll
+    for (int i = 0; i < CC; ++i) xv[i] = load_act<ACT>(x, base + i);
+    if constexpr (ACT == MOE_ACT_F32) {
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < CC; ++i) {
+        xp[ch * CC + i] = __float_as_uint(xv[i]);
+        s += xv[i];
+      }
+      cs[ch] = make_float2(0.f, s);
+    } else if constexpr (BITS == 4) {
+      float c = 0.f, s = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float* v = xv + 8 * j;
+        const uint32_t pa = pack_f16x2(v[0], v[4]);
+        const uint32_t pb = pack_f16x2(v[1] * 0.0625f, v[5] * 0.0625f);
+        const uint32_t pc = pack_f16x2(v[2], v[6]);
+        const uint32_t pf = pack_f16x2(v[3] * 0.0625f, v[7] * 0.0625f);
+        xp[ch * 16 + j * 4 + 0] = pa;
+        xp[ch * 16 + j * 4 + 1] = pb;
+        xp[ch * 16 + j * 4 + 2] = pc;
+        xp[ch * 16 + j * 4 + 3] = pf;
+        c += f16_lo(pa) + f16_hi(pa) + f16_lo(pb) + f16_hi(pb) + f16_lo(pc) + f16_hi(pc) +
+             f16_lo(pf) + f16_hi(pf);
+        s += f16_lo(pa) + f16_hi(pa) + f16_lo(pc) + f16_hi(pc) +
+             16.0f * (f16_lo(pb) + f16_hi(pb) + f16_lo(pf) + f16_hi(pf));
+      }
+      cs[ch] = make_float2(1024.0f * c, s);
+    } else {
+      float c = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t p = pack_f16x2(xv[2 * j], xv[2 * j + 1]);
+        xp[ch * 8 + j] = p;
+        c += f16_lo(p) + f16_hi(p);
+      }
+      cs[ch] = make_float2(1024.0f * c, c);
+    }
+  }
+}
+
+// sum_c q_c * x_c over one lane's 16 code bytes (32 int4 / 16 int8 codes),
+// returned as (dot, correction) so that dot - correction = sum q x.
+template <int BITS, int ACT>
+__device__ __forceinline__ float lane_dot(const uint4 q, const uint32_t* __restrict__ xp, int gc) {
+  const uint32_t d[4] = {q.x, q.y, q.z, q.w};
+  float acc = 0.f;
+  if constexpr (ACT == MOE_ACT_F32) {
+    const float* xs = reinterpret_cast<const float*>(xp) + gc * chunk_cols<BITS>();
+    if constexpr (BITS == 4) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = d[j] & 0x0F0F0F0Fu, hi = (d[j] >> 4) & 0x0F0F0F0Fu;
+        const float* v = xs + 8 * j;
+        acc += (float)(lo & 0xFF) * v[0] + (float)(hi & 0xFF) * v[1] +
+               (float)((lo >> 8) & 0xFF) * v[2] + (float)((hi >> 8) & 0xFF) * v[3] +
+               (float)((lo >> 16) & 0xFF) * v[4] + (float)((hi >> 16) & 0xFF) * v[5] +
+               (float)(lo >> 24) * v[6] + (float)(hi >> 24) * v[7];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float* v = xs + 4 * j;
+        acc += (float)(d[j] & 0xFF) * v[0] + (float)((d[j] >> 8) & 0xFF) * v[1] +
+               (float)((d[j] >> 16) & 0xFF) * v[2] + (float)(d[j] >> 24) * v[3];
+      }
+    }
+  } else if constexpr (BITS == 4) {
+    const uint4* xq = reinterpret_cast<const uint4*>(xp + gc * 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint4 X = xq[j];
+      const uint32_t e = d[j] >> 8;
+      acc = dot2((d[j] & 0x000F000Fu) | 0x64006400u, X.x, acc);
+      acc = dot2((d[j] & 0x00F000F0u) | 0x64006400u, X.y, acc);
+      acc = dot2((e & 0x000F000Fu) | 0x64006400u, X.z, acc);
+      acc = dot2((e & 0x00F000F0u) | 0x64006400u, X.w, acc);
+    }
+  } else {
+    const uint4* xq = reinterpret_cast<const uint4*>(xp + gc * 8);
+    const uint4 X0 = xq[0], X1 = xq[1];
+    const uint32_t xs[8] = {X0.x, X0.y, X0.z, X0.w, X1.x, X1.y, X1.z, X1.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc = dot2(__builtin_amdgcn_perm(0x64646464u, d[j], 0x04010400u), xs[2 * j], acc);
+      acc = dot2(__builtin_amdgcn_perm(0x64646464u, d[j], 0x04030402u), xs[2 * j + 1], acc);
+    }
+  }
+  return acc;
+}
+
+// ---------------------------------------------------------------------------
+// gate/up: one workgroup = one 16-row tile of one work item (a (token, j)
+// pair at small batch, or an expert bucket).  4 waves split the k-blocks;
+// lane l owns row l/4 and chunk l%4 of each k-block.
+
+constexpr int kGuTokens = 4;  // tokens per LDS staging round
+
+struct GuItem {
+  const uint8_t* blob;
+  int n;          // tokens
+  int start;      // bucket start position
+  int tile_limit; // tiles of this blob
+  int kind;       // 0 decode pair, 1 bucket, 2 shared
+  int t;          // decode: token
+  int64_t hrow;   // decode: h row
+};
+
+template <int BITS, int ACT>
+__global__ __launch_bounds__(256) void gateup_kernel(
+    const void* __restrict__ x, const int32_t* __restrict__ topk_idx,
+    const uint8_t* __restrict__ slab, const int32_t* __restrict__ slot_table, int64_t stride,
+    const uint8_t* __restrict__ shared_blob, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ pairs,
+    float* __restrict__ h, int T, int H, int E, int k, int I, int Is, int64_t gu_unit_r,
+    int64_t gu_tile_r, int64_t gu_unit_s, int64_t gu_tile_s, int bucketed, int has_shared) {
+  constexpr int GPK = BITS == 4 ? 2 : 1;
+  constexpr int CC = chunk_cols<BITS>();
+  extern __shared__ uint8_t smem[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tile = blockIdx.x;
+
+  // resolve the work item
+  const int item = blockIdx.y;
+  const uint8_t* blob;
+  int n, start = 0, inter, kind, t_dec = 0;
+  int64_t unit_b, tile_b, hbase;
+  if (!bucketed) {
+    const int t = item / (k + has_shared), j = item % (k + has_shared);
+    t_dec = t;
+    n = 1;
+    if (j < k) {
+      const int e = topk_idx[(int64_t)t * k + j];
+      blob = slab + (int64_t)slot_table[e] * stride;
+      inter = I;
+      unit_b = gu_unit_r;
+      tile_b = gu_tile_r;
+      hbase = ((int64_t)t * k + j) * I;
+      kind = 0;
+    } else {
+      blob = shared_blob;
+      inter = Is;
+      unit_b = gu_unit_s;
+      tile_b = gu_tile_s;
+      hbase = (int64_t)T * k * I + (int64_t)t * Is;
+      kind = 0;
+    }
+  } else if (item < E) {
+    n = counts[item];
+    if (n == 0) return;
+    start = offsets[item];
+    blob = slab + (int64_t)slot_table[item] * stride;
+    inter = I;
+    unit_b = gu_unit_r;
+    tile_b = gu_tile_r;
+    hbase = 0;
+    kind = 1;
+  } else {
+    n = T;
+    blob = shared_blob;
+    inter = Is;
+    unit_b = gu_unit_s;
+    tile_b = gu_tile_s;
+    hbase = (int64_t)T * k * I;
+    kind = 2;
+  }
+  if (tile * kRowTile >= inter) return;
+
+  const int stage_bytes = XStage<BITS, ACT>::bytes(H);
+  const int n_kb = H / (kRowBytes * (8 / BITS));
+  float* red = reinterpret_cast<float*>(smem + kGuTokens * stage_bytes);  // [4][kGuTokens][16][2]
+  const int row = lane >> 2, c4 = lane & 3;
+  const uint8_t* tbase = blob + (int64_t)tile * tile_b;
+  const int sbg_off = 2 * kCodeBlockBytes + (row * GPK + (c4 * CC) / kGroup) * 4;
+  const int sbu_off = sbg_off + kRowTile * GPK * 4;
+
+  for (int t0 = 0; t0 < n; t0 += kGuTokens) {
+    const int nt = min(kGuTokens, n - t0);
+    __syncthreads();
+    for (int tt = 0; tt < nt; ++tt) {
+      int tok;
+      if (kind == 0) tok = t_dec;
+      else if (kind == 1) tok = pairs[start + t0 + tt] / k;
+      else tok = t0 + tt;
+      uint8_t* st = smem + tt * stage_bytes;
+      stage_token<BITS, ACT>(x, tok, H, reinterpret_cast<uint32_t*>(st),
+                             reinterpret_cast<float2*>(st + XStage<BITS, ACT>::dwords(H) * 4));
+    }
+    __syncthreads();
+    float g[kGuTokens], u[kGuTokens];
+#pragma unroll
+    for (int tt = 0; tt < kGuTokens; ++tt) g[tt] = u[tt] = 0.f;
+    for (int kb = wave; kb < n_kb; kb += 4) {
+      const uint8_t* unit = tbase + (int64_t)kb * unit_b;
+      const uint4 qg = *reinterpret_cast<const uint4*>(unit + lane * 16);
+      const uint4 qu = *reinterpret_cast<const uint4*>(unit + kCodeBlockBytes + lane * 16);
+      const uint32_t sbg = *reinterpret_cast<const uint32_t*>(unit + sbg_off);
+      const uint32_t sbu = *reinterpret_cast<const uint32_t*>(unit + sbu_off);
+      const float sg = bf16_bits_to_f32(sbg & 0xFFFFu), bg = bf16_bits_to_f32(sbg >> 16);
+      const float su = bf16_bits_to_f32(sbu & 0xFFFFu), bu = bf16_bits_to_f32(sbu >> 16);
+      const int gc = kb * 4 + c4;
+#pragma unroll
+      for (int tt = 0; tt < kGuTokens; ++tt) {
+        if (tt < nt) {
+          const uint8_t* st = smem + tt * stage_bytes;
+          const uint32_t* xp = reinterpret_cast<const uint32_t*>(st);
+          const float2 cs =
+              reinterpret_cast<const float2*>(st + XStage<BITS, ACT>::dwords(H) * 4)[gc];
+          const float pg = lane_dot<BITS, ACT>(qg, xp, gc) - cs.x;
+          const float pu = lane_dot<BITS, ACT>(qu, xp, gc) - cs.x;
+          g[tt] += sg * pg + bg * cs.y;
+          u[tt] += su * pu + bu * cs.y;
+        }
+      }
+    }
+    // reduce the 4 lanes of a row, then the 4 waves
+#pragma unroll
+    for (int tt = 0; tt < kGuTokens; ++tt) {
+      g[tt] += __shfl_xor(g[tt], 1, 64);
+      g[tt] += __shfl_xor(g[tt], 2, 64);
+      u[tt] += __shfl_xor(u[tt], 1, 64);
+      u[tt] += __shfl_xor(u[tt], 2, 64);
+      if (c4 == 0) {
+        red[((wave * kGuTokens + tt) * kRowTile + row) * 2 + 0] = g[tt];
+        red[((wave * kGuTokens + tt) * kRowTile + row) * 2 + 1] = u[tt];
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < nt * kRowTile) {
+      const int tt = threadIdx.x / kRowTile, r = threadIdx.x % kRowTile;
+      float gs = 0.f, us = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        gs += red[((w * kGuTokens + tt) * kRowTile + r) * 2 + 0];
+        us += red[((w * kGuTokens + tt) * kRowTile + r) * 2 + 1];
+      }
+      int64_t hrow;
+      if (kind == 0) hrow = hbase;
+      else if (kind == 1) hrow = (int64_t)(start + t0 + tt) * inter;
+      else hrow = hbase + (int64_t)(t0 + tt) * inter;
+      h[hrow + tile * kRowTile + r] = silu_f32(gs) * us;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// down + combine at small batch: one workgroup = one 16-row tile of the
+// output of one token; it walks the token's k routed items and the shared
+// item, so the weighted sum is formed in a fixed order without atomics.
+
+template <int BITS>
+__device__ __forceinline__ float lane_dot_h(const uint4 q, const float* __restrict__ hv,
+                                            float& hsum) {
+  const uint32_t d[4] = {q.x, q.y, q.z, q.w};
+  float acc = 0.f;
+  if constexpr (BITS == 4) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 a = *reinterpret_cast<const float4*>(hv + 8 * j);
+      const float4 b = *reinterpret_cast<const float4*>(hv + 8 * j + 4);
+      const uint32_t lo = d[j] & 0x0F0F0F0Fu, hi = (d[j] >> 4) & 0x0F0F0F0Fu;
+      acc += (float)(lo & 0xFF) * a.x + (float)(hi & 0xFF) * a.y +
+             (float)((lo >> 8) & 0xFF) * a.z + (float)((hi >> 8) & 0xFF) * a.w +
+             (float)((lo >> 16) & 0xFF) * b.x + (float)((hi >> 16) & 0xFF) * b.y +
+             (float)(lo >> 24) * b.z + (float)(hi >> 24) * b.w;
+      hsum += (a.x + a.y) + (a.z + a.w) + (b.x + b.y) + (b.z + b.w);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 a = *reinterpret_cast<const float4*>(hv + 4 * j);
+      acc += (float)(d[j] & 0xFF) * a.x + (float)((d[j] >> 8) & 0xFF) * a.y +
+             (float)((d[j] >> 16) & 0xFF) * a.z + (float)(d[j] >> 24) * a.w;
+      hsum += (a.x + a.y) + (a.z + a.w);
+    }
+  }
+  return acc;
+}
+
+template <int BITS, int ACT>
+__global__ __launch_bounds__(256) void down_decode_kernel(
+    const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_w,
+    const float* __restrict__ gamma, const uint8_t* __restrict__ slab,
+    const int32_t* __restrict__ slot_table, int64_t stride, const uint8_t* __restrict__ shared_blob,
+    const float* __restrict__ h, void* __restrict__ out, int T, int H, int k, int I, int Is,
+    int64_t d_off_r, int64_t d_unit_r, int64_t d_tile_r, int64_t d_off_s, int64_t d_unit_s,
+    int64_t d_tile_s, int has_shared) {
+  constexpr int GPK = BITS == 4 ? 2 : 1;
+  constexpr int CC = chunk_cols<BITS>();
+  constexpr int KBC = kRowBytes * (8 / BITS);
+  __shared__ float red[4][kRowTile];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tile = blockIdx.x, t = blockIdx.y;
+  const int row = lane >> 2, c4 = lane & 3;
+  const int sb_off = kCodeBlockBytes + (row * GPK + (c4 * CC) / kGroup) * 4;
+  const int nkb_r = I / KBC, nkb_s = has_shared ? Is / KBC : 0;
+  const int n_units = k * nkb_r + nkb_s;
+  float acc = 0.f;
+  for (int u = wave; u < n_units; u += 4) {
+    const uint8_t* unit;
+    const float* hv;
+    float w;
+    int kb;
+    if (u < k * nkb_r) {
+      const int j = u / nkb_r;
+      kb = u - j * nkb_r;
+      const int e = topk_idx[(int64_t)t * k + j];
+      unit = slab + (int64_t)slot_table[e] * stride + d_off_r + (int64_t)tile * d_tile_r +
+             (int64_t)kb * d_unit_r;
+      hv = h + ((int64_t)t * k + j) * I;
+      w = topk_w[(int64_t)t * k + j];
+    } else {
+      kb = u - k * nkb_r;
+      unit = shared_blob + d_off_s + (int64_t)tile * d_tile_s + (int64_t)kb * d_unit_s;
+      hv = h + (int64_t)T * k * I + (int64_t)t * Is;
+      w = gamma[t];
+    }
+    const uint4 q = *reinterpret_cast<const uint4*>(unit + lane * 16);
+    const uint32_t sb = *reinterpret_cast<const uint32_t*>(unit + sb_off);
+    float hsum = 0.f;
+    const float p = lane_dot_h<BITS>(q, hv + kb * KBC + c4 * CC, hsum);
+    acc += w * (bf16_bits_to_f32(sb & 0xFFFFu) * p + bf16_bits_to_f32(sb >> 16) * hsum);
+  }
+  acc += __shfl_xor(acc, 1, 64);
+  acc += __shfl_xor(acc, 2, 64);
+  if (c4 == 0) red[wave][row] = acc;
+  __syncthreads();
+  if (threadIdx.x < kRowTile) {
+    const float v = (red[0][threadIdx.x] + red[1][threadIdx.x]) +
+                    (red[2][threadIdx.x] + red[3][threadIdx.x]);
+    store_act<ACT>(out, (int64_t)t * H + tile * kRowTile + threadIdx.x, v);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// batched: down per expert bucket, writing weighted per-(token, j) partial
+// rows; a combine kernel then sums each token's k+1 partials in order.
+
+template <int BITS>
+__global__ __launch_bounds__(256) void down_bucket_kernel(
+    const float* __restrict__ topk_w, const float* __restrict__ gamma,
+    const uint8_t* __restrict__ slab, const int32_t* __restrict__ slot_table, int64_t stride,
+    const uint8_t* __restrict__ shared_blob, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ pairs,
+    const float* __restrict__ h, float* __restrict__ partial, int T, int H, int E, int k, int I,
+    int Is, int64_t d_off_r, int64_t d_unit_r, int64_t d_tile_r, int64_t d_off_s,
+    int64_t d_unit_s, int64_t d_tile_s) {
+  constexpr int GPK = BITS == 4 ? 2 : 1;
+  constexpr int CC = chunk_cols<BITS>();
+  constexpr int KBC = kRowBytes * (8 / BITS);
+  constexpr int kTok = 4;
+  __shared__ float red[4][kTok][kRowTile];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tile = blockIdx.x, item = blockIdx.y;
+  const int row = lane >> 2, c4 = lane & 3;
+  const int sb_off = kCodeBlockBytes + (row * GPK + (c4 * CC) / kGroup) * 4;
+  const uint8_t* tbase;
+  int n, start = 0, inter, nkb;
+  int64_t unit_b;
+  const bool shared = item >= E;
+  if (!shared) {
+    n = counts[item];
+    if (n == 0) return;
+    start = offsets[item];
+    inter = I;
+    tbase = slab + (int64_t)slot_table[item] * stride + d_off_r + (int64_t)tile * d_tile_r;
+    unit_b = d_unit_r;
+  } else {
+    n = T;
+    inter = Is;
+    tbase = shared_blob + d_off_s + (int64_t)tile * d_tile_s;
+    unit_b = d_unit_s;
+  }
+  nkb = inter / KBC;
+  for (int t0 = 0; t0 < n; t0 += kTok) {
+    const int nt = min(kTok, n - t0);
+    float acc[kTok];
+#pragma unroll
+    for (int tt = 0; tt < kTok; ++tt) acc[tt] = 0.f;
+    for (int kb = wave; kb < nkb; kb += 4) {
+      const uint8_t* unit = tbase + (int64_t)kb * unit_b;
+      const uint4 q = *reinterpret_cast<const uint4*>(unit + lane * 16);
+      const uint32_t sb = *reinterpret_cast<const uint32_t*>(unit + sb_off);
+      const float s = bf16_bits_to_f32(sb & 0xFFFFu), b = bf16_bits_to_f32(sb >> 16);
+#pragma unroll
+      for (int tt = 0; tt < kTok; ++tt) {
+        if (tt < nt) {
+          const float* hv = shared ? h + (int64_t)T * k * I + (int64_t)(t0 + tt) * Is
+                                   : h + (int64_t)(start + t0 + tt) * I;
+          float hsum = 0.f;
+          const float p = lane_dot_h<BITS>(q, hv + kb * KBC + c4 * CC, hsum);
+          acc[tt] += s * p + b * hsum;
+        }
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < kTok; ++tt) {
+      acc[tt] += __shfl_xor(acc[tt], 1, 64);
+      acc[tt] += __shfl_xor(acc[tt], 2, 64);
+      if (c4 == 0) red[wave][tt][row] = acc[tt];
+    }
+    __syncthreads();
+    if (threadIdx.x < nt * kRowTile) {
+      const int tt = threadIdx.x / kRowTile, r = threadIdx.x % kRowTile;
+      const float v = (red[0][tt][r] + red[1][tt][r]) + (red[2][tt][r] + red[3][tt][r]);
+      int tok, j;
+      float w;
+      if (!shared) {
+        const int p = pairs[start + t0 + tt];
+        tok = p / k;
+        j = p - tok * k;
+        w = topk_w[p];
+      } else {
+        tok = t0 + tt;
+        j = k;
+        w = gamma[tok];
+      }
+      partial[((int64_t)tok * (k + 1) + j) * H + tile * kRowTile + r] = w * v;
+    }
+    __syncthreads();
+  }
+}
+
+template <int ACT>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ partial,
+                                                      void* __restrict__ out, int H, int k,
+                                                      int has_shared) {
+  const int t = blockIdx.x;
+  const int nj = k + has_shared;
+  for (int c = threadIdx.x; c < H; c += blockDim.x) {
+    float v = 0.f;
+    for (int j = 0; j < nj; ++j) v += partial[((int64_t)t * (k + 1) + j) * H + c];
+    store_act<ACT>(out, (int64_t)t * H + c, v);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// token -> expert bucketing: stable by token.  Each 64-token block builds a
+// per-expert 64-bit mask of the tokens that chose the expert; ranks inside a
+// block are popcounts of the mask below the token, so the order is
+// deterministic without sorting.
+
+__global__ __launch_bounds__(64) void bucket_mask_kernel(const int32_t* __restrict__ topk_idx,
+                                                         uint64_t* __restrict__ masks, int T,
+                                                         int E, int k) {
+  __shared__ unsigned long long m[MOE_MAX_EXPERTS];
+  const int b = blockIdx.x, lane = threadIdx.x;
+  for (int e = lane; e < E; e += 64) m[e] = 0ull;
+  __syncthreads();
+  const int t = b * 64 + lane;
+  if (t < T)
+    for (int j = 0; j < k; ++j) atomicOr(&m[topk_idx[(int64_t)t * k + j]], 1ull << lane);
+  __syncthreads();
+  for (int e = lane; e < E; e += 64) masks[(int64_t)b * E + e] = m[e];
+}
+
+__global__ __launch_bounds__(1024) void bucket_scan_kernel(const uint64_t* __restrict__ masks,
+                                                           int32_t* __restrict__ counts,
+                                                           int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ blkoff, int T,
+                                                           int E, int k, int nblk) {
+  __shared__ int wsum[16];
+  const int e = threadIdx.x, lane = e & 63, wave = e >> 6;
+  int c = 0;
+  if (e < E)
+    for (int b = 0; b < nblk; ++b) c += __popcll(masks[(int64_t)b * E + e]);
+  // inclusive scan inside the wave
+  int v = c;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(v, off, 64);
+    if (lane >= off) v += o;
+  }
+  if (lane == 63) wsum[wave] = v;
+  __syncthreads();
+  int wbase = 0;
+  for (int w = 0; w < wave; ++w) wbase += wsum[w];
+  const int excl = wbase + v - c;
+  if (e < E) {
+    counts[e] = c;
+    offsets[e] = excl;
+    int run = excl;
+    for (int b = 0; b < nblk; ++b) {
+      blkoff[(int64_t)b * E + e] = run;
+      run += __popcll(masks[(int64_t)b * E + e]);
+    }
+  }
+  if (e == 0) {
+    counts[E] = T;
+    offsets[E] = T * k;
+  }
+}
+
+__global__ __launch_bounds__(64) void bucket_scatter_kernel(const int32_t* __restrict__ topk_idx,
+                                                            const uint64_t* __restrict__ masks,
+                                                            const int32_t* __restrict__ blkoff,
+                                                            int32_t* __restrict__ pairs, int T,
+                                                            int E, int k) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const int t = b * 64 + lane;
+  if (t >= T) return;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int j = 0; j < k; ++j) {
+    const int e = topk_idx[(int64_t)t * k + j];
+    const uint64_t m = masks[(int64_t)b * E + e];
+    pairs[blkoff[(int64_t)b * E + e] + __popcll(m & below)] = t * k + j;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// residual + RMSNorm (unit weight)
+
+template <int ACT>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(void* __restrict__ x,
+                                                      const void* __restrict__ out,
+                                                      void* __restrict__ x_hat, int H, float eps,
+                                                      int do_norm) {
+  __shared__ float wsum[4];
+  const int t = blockIdx.x;
+  const int64_t base = (int64_t)t * H;
+  float ss = 0.f;
+  for (int c = threadIdx.x; c < H; c += blockDim.x) {
+    float v = load_act<ACT>(x, base + c);
+    if (out != nullptr) {
+      v += load_act<ACT>(out, base + c);
+      store_act<ACT>(x, base + c, v);
+      v = load_act<ACT>(x, base + c);  // the stored value
+    }
+    ss += v * v;
+  }
+  if (!do_norm) return;
+  ss = warp_sum(ss);
+  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+  const float inv = 1.0f / sqrtf(tot / (float)H + eps);
+  for (int c = threadIdx.x; c < H; c += blockDim.x)
+    store_act<ACT>(x_hat, base + c, load_act<ACT>(x, base + c) * inv);
+}
+
+// ---------------------------------------------------------------------------
+// device packer: one workgroup per (tile, k-block) unit of one section.
+
+template <int BITS>
+__device__ __forceinline__ uint4 pack_codes16(const uint8_t* __restrict__ q) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t v = 0;
+    if constexpr (BITS == 4) {
+#pragma unroll
+      for (int b = 0; b < 8; ++b) v |= (uint32_t)(q[8 * i + b] & 15u) << (4 * b);
+    } else {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) v |= (uint32_t)q[4 * i + b] << (8 * b);
+    }
+    w[i] = v;
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+template <int BITS>
+__global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ qa,
+                                                   const uint8_t* __restrict__ qb,
+                                                   const uint16_t* __restrict__ sba,
+                                                   const uint16_t* __restrict__ sbb,
+                                                   uint8_t* __restrict__ dst, int rows, int cols,
+                                                   int64_t unit_bytes, int64_t tile_bytes,
+                                                   int two) {
+  constexpr int GPK = BITS == 4 ? 2 : 1;
+  constexpr int CC = chunk_cols<BITS>();
+  constexpr int KBC = kRowBytes * (8 / BITS);
+  const int nkb = cols / KBC;
+  const int tile = blockIdx.x / nkb, kb = blockIdx.x % nkb;
+  const int G = cols / kGroup;
+  uint8_t* unit = dst + (int64_t)tile * tile_bytes + (int64_t)kb * unit_bytes;
+  const int i = threadIdx.x;
+  const int ncode = two ? 128 : 64;
+  if (i < ncode) {
+    const int which = i >> 6, l = i & 63;
+    const int r = tile * kRowTile + (l >> 2);
+    const int c = kb * KBC + (l & 3) * CC;
+    const uint8_t* q = (which ? qb : qa) + (int64_t)r * cols + c;
+    *reinterpret_cast<uint4*>(unit + which * kCodeBlockBytes + l * 16) = pack_codes16<BITS>(q);
+  } else if (i < ncode + (two ? 2 : 1) * kRowTile * GPK) {
+    const int s = i - ncode;
+    const int which = s / (kRowTile * GPK), idx = s % (kRowTile * GPK);
+    const int rl = idx / GPK, gi = idx % GPK;
+    const int r = tile * kRowTile + rl, g = kb * GPK + gi;
+    const uint16_t* sb = which ? sbb : sba;
+    const uint32_t sc = sb[(int64_t)r * G + g];
+    const uint32_t bi = sb[(int64_t)rows * G + (int64_t)r * G + g];
+    uint8_t* p = unit + (two ? 2 : 1) * kCodeBlockBytes + which * kRowTile * GPK * 4 +
+                 (rl * GPK + gi) * 4;
+    *reinterpret_cast<uint32_t*>(p) = sc | (bi << 16);
+  }
+}
+
+template <int BITS, int ACT>
+hipError_t launch_experts_t(const ExpertArgs& a, hipStream_t s) {
+  const WsPlan& P = a.plan;
+  float* h = reinterpret_cast<float*>(a.ws + P.h);
+  int32_t* counts = reinterpret_cast<int32_t*>(a.ws + P.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(a.ws + P.offsets);
+  int32_t* pairs = reinterpret_cast<int32_t*>(a.ws + P.pairs);
+  const int hs = a.has_shared ? 1 : 0;
+  const int Is = a.has_shared ? a.Ls.inter : 0;
+  const int tiles_gu = max(a.L.n_tiles_gu, a.has_shared ? a.Ls.n_tiles_gu : 0);
+  const size_t lds_gu =
+      (size_t)kGuTokens * XStage<BITS, ACT>::bytes(a.H) + sizeof(float) * 4 * kGuTokens * kRowTile * 2;
+  hipError_t e;
+  if (!P.bucketed) {
+    hipLaunchKernelGGL((gateup_kernel<BITS, ACT>), dim3(tiles_gu, a.T * (a.k + hs)), dim3(256),
+                       lds_gu, s, a.x, a.topk_idx, a.slab, a.slot_table, a.stride, a.shared_blob,
+                       counts, offsets, pairs, h, a.T, a.H, a.E, a.k, a.L.inter, Is, a.L.gu_unit,
+                       a.L.gu_tile, a.Ls.gu_unit, a.Ls.gu_tile, 0, hs);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((down_decode_kernel<BITS, ACT>), dim3(a.L.n_tiles_d, a.T), dim3(256), 0, s,
+                       a.topk_idx, a.topk_w, a.gamma, a.slab, a.slot_table, a.stride,
+                       a.shared_blob, h, a.out, a.T, a.H, a.k, a.L.inter, Is, a.L.d_off,
+                       a.L.d_unit, a.L.d_tile, a.Ls.d_off, a.Ls.d_unit, a.Ls.d_tile, hs);
+    return hipGetLastError();
+  }
+  uint64_t* masks = reinterpret_cast<uint64_t*>(a.ws + P.masks);
+  int32_t* blkoff = reinterpret_cast<int32_t*>(a.ws + P.blkoff);
+  float* partial = reinterpret_cast<float*>(a.ws + P.partial);
+  const int nblk = (a.T + 63) / 64;
+  hipLaunchKernelGGL(bucket_mask_kernel, dim3(nblk), dim3(64), 0, s, a.topk_idx, masks, a.T, a.E,
+                     a.k);
+  hipLaunchKernelGGL(bucket_scan_kernel, dim3(1), dim3(1024), 0, s, masks, counts, offsets, blkoff,
+                     a.T, a.E, a.k, nblk);
+  hipLaunchKernelGGL(bucket_scatter_kernel, dim3(nblk), dim3(64), 0, s, a.topk_idx, masks, blkoff,
+                     pairs, a.T, a.E, a.k);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((gateup_kernel<BITS, ACT>), dim3(tiles_gu, a.E + hs), dim3(256), lds_gu, s,
+                     a.x, a.topk_idx, a.slab, a.slot_table, a.stride, a.shared_blob, counts,
+                     offsets, pairs, h, a.T, a.H, a.E, a.k, a.L.inter, Is, a.L.gu_unit,
+                     a.L.gu_tile, a.Ls.gu_unit, a.Ls.gu_tile, 1, hs);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((down_bucket_kernel<BITS>), dim3(a.L.n_tiles_d, a.E + hs), dim3(256), 0, s,
+                     a.topk_w, a.gamma, a.slab, a.slot_table, a.stride, a.shared_blob, counts,
+                     offsets, pairs, h, partial, a.T, a.H, a.E, a.k, a.L.inter, Is, a.L.d_off,
+                     a.L.d_unit, a.L.d_tile, a.Ls.d_off, a.Ls.d_unit, a.Ls.d_tile);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((combine_kernel<ACT>), dim3(a.T), dim3(256), 0, s, partial, a.out, a.H, a.k,
+                     hs);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_experts(const ExpertArgs& a, hipStream_t s) {
+  if (a.bits == 4)
+    return a.act == MOE_ACT_F32 ? launch_experts_t<4, MOE_ACT_F32>(a, s)
+                                : launch_experts_t<4, MOE_ACT_BF16>(a, s);
+  return a.act == MOE_ACT_F32 ? launch_experts_t<8, MOE_ACT_F32>(a, s)
+                              : launch_experts_t<8, MOE_ACT_BF16>(a, s);
+}
+
+hipError_t launch_rmsnorm(void* x, const void* out, void* x_hat, int T, int H, int act, float eps,
+                          bool do_norm, hipStream_t s) {
+  if (act == MOE_ACT_F32)
+    hipLaunchKernelGGL(rmsnorm_kernel<MOE_ACT_F32>, dim3(T), dim3(256), 0, s, x, out, x_hat, H, eps,
+                       do_norm ? 1 : 0);
+  else
+    hipLaunchKernelGGL(rmsnorm_kernel<MOE_ACT_BF16>, dim3(T), dim3(256), 0, s, x, out, x_hat, H,
+                       eps, do_norm ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_device(const BlobLayout& L, int n, const uint8_t* qg, const uint8_t* qu,
+                              const uint8_t* qd, const uint16_t* sbg, const uint16_t* sbu,
+                              const uint16_t* sbd, uint8_t* slab, int64_t stride,
+                              const int64_t* slots_host, hipStream_t s) {
+  const int64_t H = L.hidden, I = L.inter;
+  for (int i = 0; i < n; ++i) {
+    uint8_t* blob = slab + slots_host[i] * stride;
+    const int64_t qoff = (int64_t)i * I * H;
+    const int64_t sgu = (int64_t)i * 2 * I * (H / kGroup);
+    const int64_t sdd = (int64_t)i * 2 * H * (I / kGroup);
+    const dim3 g_gu(L.n_tiles_gu * L.n_kb_gu), g_d(L.n_tiles_d * L.n_kb_d);
+    if (L.bits == 4) {
+      hipLaunchKernelGGL(pack_kernel<4>, g_gu, dim3(256), 0, s, qg + qoff, qu + qoff, sbg + sgu,
+                         sbu + sgu, blob + L.gu_off, (int)I, (int)H, L.gu_unit, L.gu_tile, 1);
+      hipLaunchKernelGGL(pack_kernel<4>, g_d, dim3(256), 0, s, qd + qoff, nullptr, sbd + sdd,
+                         nullptr, blob + L.d_off, (int)H, (int)I, L.d_unit, L.d_tile, 0);
+    } else {
+      hipLaunchKernelGGL(pack_kernel<8>, g_gu, dim3(256), 0, s, qg + qoff, qu + qoff, sbg + sgu,
+                         sbu + sgu, blob + L.gu_off, (int)I, (int)H, L.gu_unit, L.gu_tile, 1);
+      hipLaunchKernelGGL(pack_kernel<8>, g_d, dim3(256), 0, s, qd + qoff, nullptr, sbd + sdd,
+                         nullptr, blob + L.d_off, (int)H, (int)I, L.d_unit, L.d_tile, 0);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace moe

@@ -1,0 +1,183 @@
+// Internal definitions of the MoE layer library: blob layout arithmetic,
+// workspace plan and device helpers shared by the kernels.  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr int kRowTile = 16;         // rows per tile in both blob sections
+constexpr int kRowBytes = 64;        // code bytes per row per k-block
+constexpr int kCodeBlockBytes = kRowTile * kRowBytes;  // 1 KiB
+constexpr int kGroup = 64;
+constexpr int kDecodeMaxTokens = 8;  // up to this many tokens: per-pair GEMV path
+
+inline int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+// Byte layout of one blob.  Everything is a multiple of 64 bytes; blob sizes
+// are multiples of 256.
+struct BlobLayout {
+  int bits, hidden, inter;
+  int kb_cols;        // columns per k-block (64 bytes of codes per row)
+  int gpk;            // quantisation groups per k-block
+  int n_kb_gu;        // k-blocks along H (gate/up)
+  int n_tiles_gu;     // row tiles along I (gate/up)
+  int n_kb_d;         // k-blocks along I (down)
+  int n_tiles_d;      // row tiles along H (down)
+  int64_t gu_unit, gu_tile, gu_off;
+  int64_t d_unit, d_tile, d_off;
+  int64_t blob, sg_off, shared_bytes;
+};
+
+inline BlobLayout make_layout(int bits, int hidden, int inter) {
+  BlobLayout L{};
+  L.bits = bits;
+  L.hidden = hidden;
+  L.inter = inter;
+  L.kb_cols = kRowBytes * (8 / bits);
+  L.gpk = L.kb_cols / kGroup;
+  L.n_kb_gu = hidden / L.kb_cols;
+  L.n_tiles_gu = inter / kRowTile;
+  L.n_kb_d = inter / L.kb_cols;
+  L.n_tiles_d = hidden / kRowTile;
+  const int64_t sb_block = (int64_t)kRowTile * L.gpk * 4;
+  L.gu_unit = 2 * kCodeBlockBytes + 2 * sb_block;
+  L.gu_tile = L.gu_unit * L.n_kb_gu;
+  L.gu_off = 0;
+  L.d_unit = kCodeBlockBytes + sb_block;
+  L.d_tile = L.d_unit * L.n_kb_d;
+  L.d_off = L.gu_off + L.gu_tile * L.n_tiles_gu;
+  L.blob = align_up(L.d_off + L.d_tile * L.n_tiles_d, 256);
+  L.sg_off = L.blob;
+  L.shared_bytes = align_up(L.sg_off + (int64_t)hidden * 4, 256);
+  return L;
+}
+
+// Workspace plan (byte offsets into the caller's workspace).
+struct WsPlan {
+  size_t logits, idx, w, gamma, h, partial, counts, offsets, pairs, masks, blkoff, xprep;
+  size_t total;
+  bool bucketed;
+};
+
+inline WsPlan make_ws_plan(const moe_layer_desc& d) {
+  WsPlan p{};
+  const int64_t T = d.n_tokens, E = d.n_experts, k = d.top_k, H = d.hidden;
+  const int64_t I = d.inter;
+  const int64_t Is = (d.flags & MOE_FLAG_SHARED) ? d.shared_inter : 0;
+  const int64_t nblk = (T + 63) / 64;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = (size_t)align_up((int64_t)(o + bytes), 256);
+    return at;
+  };
+  p.bucketed = T > kDecodeMaxTokens;
+  p.logits = take(sizeof(float) * T * (E + 1));
+  p.idx = take(sizeof(int32_t) * T * k);
+  p.w = take(sizeof(float) * T * k);
+  p.gamma = take(sizeof(float) * T);
+  p.h = take(sizeof(float) * (T * k * I + T * Is));
+  p.partial = take(p.bucketed ? sizeof(float) * T * (k + 1) * H : 0);
+  p.counts = take(sizeof(int32_t) * (E + 1));
+  p.offsets = take(sizeof(int32_t) * (E + 2));
+  p.pairs = take(sizeof(int32_t) * T * k);
+  p.masks = take(p.bucketed ? sizeof(uint64_t) * nblk * E : 0);
+  p.blkoff = take(p.bucketed ? sizeof(int32_t) * nblk * E : 0);
+  p.xprep = take(0);
+  p.total = o;
+  return p;
+}
+
+// ---------------------------------------------------------------------------
+// device helpers
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <int ACT>
+__device__ __forceinline__ float load_act(const void* p, int64_t i) {
+  if constexpr (ACT == MOE_ACT_F32) {
+    return reinterpret_cast<const float*>(p)[i];
+  } else {
+    return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p)[i]);
+  }
+}
+
+template <int ACT>
+__device__ __forceinline__ void store_act(void* p, int64_t i, float v) {
+  if constexpr (ACT == MOE_ACT_F32) {
+    reinterpret_cast<float*>(p)[i] = v;
+  } else {
+    reinterpret_cast<uint16_t*>(p)[i] = f32_to_bf16_bits(v);
+  }
+}
+
+__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
+
+__device__ __forceinline__ float warp_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+}  // namespace moe
+
+// ---------------------------------------------------------------------------
+// launchers (defined in the .hip files)
+
+namespace moe {
+
+struct RouterArgs {
+  const void* x;
+  const float* router_w;
+  const float* router_bias;
+  const float* shared_gate_w;
+  float* logits;          // [T x (E+1)]
+  int32_t* topk_idx;
+  float* topk_w;
+  float* gamma;           // may be null
+  int T, H, E, k, act;
+};
+hipError_t launch_router_topk(const RouterArgs& a, hipStream_t s);
+
+struct ExpertArgs {
+  const void* x;                 // x_hat [T x H]
+  const int32_t* topk_idx;
+  const float* topk_w;
+  const float* gamma;            // null without shared expert
+  const uint8_t* slab;
+  const int32_t* slot_table;
+  int64_t stride;
+  const uint8_t* shared_blob;    // null without shared expert
+  void* out;
+  uint8_t* ws;
+  WsPlan plan;
+  BlobLayout L;                  // routed experts
+  BlobLayout Ls;                 // shared expert
+  int T, H, E, k, act, bits;
+  bool has_shared;
+};
+hipError_t launch_experts(const ExpertArgs& a, hipStream_t s);
+
+hipError_t launch_rmsnorm(void* x, const void* out, void* x_hat, int T, int H, int act,
+                          float eps, bool do_norm, hipStream_t s);
+
+hipError_t launch_pack_device(const BlobLayout& L, int n, const uint8_t* qg, const uint8_t* qu,
+                              const uint8_t* qd, const uint16_t* sbg, const uint16_t* sbu,
+                              const uint16_t* sbd, uint8_t* slab, int64_t stride,
+                              const int64_t* slots_host, hipStream_t s);
+
+}  // namespace moe

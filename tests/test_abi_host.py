@@ -1,0 +1,210 @@
+"""C ABI checks that need no GPU: exports, blob layout, host packer round
+trip, and argument validation (which returns before anything is enqueued)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import int4_group_quantized_moe_amd as moe
+from int4_group_quantized_moe_amd import _ffi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert len(names) >= 12
+    h = moe.lib()
+    for n in names:
+        assert hasattr(h, n), n
+        assert n in _ffi.exported_symbols(), n
+
+
+def test_version_and_status_strings():
+    assert moe.moe_version().startswith("moe-gfx950")
+    for st in (0, -1, -2, -3, -4, -5):
+        assert moe.moe_status_string(st) != "unknown status"
+    assert moe.moe_status_string(-99) == "unknown status"
+
+
+@pytest.mark.parametrize("bits,H,I,expect", [
+    (4, 2048, 512, 1769472),     # 3 x 524288 code bytes + 3 x 65536 scale/bias bytes
+    (8, 2048, 512, 3342336),
+    (4, 256, 128, 55296),
+])
+def test_blob_sizes(bits, H, I, expect):
+    d = moe.make_desc(1, H, 16, 2, I, I, bits=bits)
+    L = moe.moe_blob_layout(d, I)
+    assert L.blob_bytes == expect
+    assert L.blob_bytes % 256 == 0 and L.shared_bytes % 256 == 0
+    assert L.shared_gate_offset >= L.blob_bytes
+    assert L.shared_bytes >= L.shared_gate_offset + 4 * H
+    assert L.row_tile == 16 and L.kblock_cols == (128 if bits == 4 else 64)
+
+
+def unpack_blob(blob: np.ndarray, bits: int, H: int, I: int, L):
+    """Reads the documented blob layout back into logical arrays."""
+    kbc = L.kblock_cols
+    gpk = L.groups_per_kblock
+
+    def section(off, rows, cols, nmat, unit, tile):
+        qs = [np.zeros((rows, cols), np.uint8) for _ in range(nmat)]
+        sbs = [np.zeros((2, rows, cols // 64), np.uint16) for _ in range(nmat)]
+        for t in range(rows // 16):
+            for kb in range(cols // kbc):
+                u = off + t * tile + kb * unit
+                for m in range(nmat):
+                    codes = blob[u + m * 1024: u + (m + 1) * 1024].reshape(16, 64)
+                    for rl in range(16):
+                        row = codes[rl]
+                        if bits == 4:
+                            vals = np.empty(128, np.uint8)
+                            vals[0::2] = row & 15
+                            vals[1::2] = row >> 4
+                        else:
+                            vals = row
+                        qs[m][t * 16 + rl, kb * kbc:(kb + 1) * kbc] = vals
+                    sb = blob[u + nmat * 1024 + m * 16 * gpk * 4:
+                              u + nmat * 1024 + (m + 1) * 16 * gpk * 4].view(np.uint16)
+                    sb = sb.reshape(16, gpk, 2)
+                    for rl in range(16):
+                        for gi in range(gpk):
+                            sbs[m][0, t * 16 + rl, kb * gpk + gi] = sb[rl, gi, 0]
+                            sbs[m][1, t * 16 + rl, kb * gpk + gi] = sb[rl, gi, 1]
+        return qs, sbs
+
+    (qg, qu), (sg, su) = section(L.gu_offset, I, H, 2, L.gu_unit_bytes, L.gu_tile_bytes)
+    (qd,), (sd,) = section(L.down_offset, H, I, 1, L.down_unit_bytes, L.down_tile_bytes)
+    return qg, qu, qd, sg, su, sd
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_host_packer_round_trip(bits):
+    rng = np.random.default_rng(7)
+    H, I = 256, 128
+    d = moe.make_desc(1, H, 4, 2, I, I, bits=bits)
+    L = moe.moe_blob_layout(d, I)
+    qg = rng.integers(0, 1 << bits, (I, H)).astype(np.uint8)
+    qu = rng.integers(0, 1 << bits, (I, H)).astype(np.uint8)
+    qd = rng.integers(0, 1 << bits, (H, I)).astype(np.uint8)
+    sg = rng.integers(0, 65536, (2, I, H // 64)).astype(np.uint16)
+    su = rng.integers(0, 65536, (2, I, H // 64)).astype(np.uint16)
+    sd = rng.integers(0, 65536, (2, H, I // 64)).astype(np.uint16)
+    wsg = rng.standard_normal(H).astype(np.float32)
+    blob = np.full(L.shared_bytes, 0xAB, np.uint8)
+    moe.moe_pack_expert(d, I, qg, qu, qd, sg, su, sd, wsg, blob)
+    got = unpack_blob(blob, bits, H, I, L)
+    for a, b in zip(got, (qg, qu, qd, sg, su, sd)):
+        assert np.array_equal(a, b)
+    off = L.shared_gate_offset
+    assert np.array_equal(blob[off:off + 4 * H].view(np.float32), wsg)
+    # padding between sections is zero
+    end = L.down_offset + (H // 16) * L.down_tile_bytes
+    assert np.all(blob[end:L.blob_bytes] == 0)
+
+
+def test_host_packer_rejects_out_of_range_codes():
+    H, I = 256, 128
+    d = moe.make_desc(1, H, 4, 2, I, I, bits=4)
+    z = np.zeros((I, H), np.uint8)
+    bad = z.copy()
+    bad[3, 5] = 16
+    sb = np.zeros((2, I, H // 64), np.uint16)
+    sbd = np.zeros((2, H, I // 64), np.uint16)
+    blob = np.zeros(moe.moe_blob_layout(d, I).blob_bytes, np.uint8)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_pack_expert(d, I, bad, z, z.T.copy(), sb, sb, sbd, None, blob)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------------------
+# validation: every one of these returns before any device call
+
+FAKE = 1 << 30          # 256-aligned fake address; never dereferenced
+
+
+def _layer(d, x=FAKE, rw=FAKE, rb=None, slab=FAKE, st=FAKE, sh=FAKE, out=FAKE, ws=FAKE):
+    return moe.lib().moe_layer_forward(ctypes.byref(d), x, rw, rb, slab, st, sh, out, ws, None)
+
+
+@pytest.mark.parametrize("mut,status", [
+    (dict(bits=5), moe.MOE_ERR_UNSUPPORTED),
+    (dict(group=32), moe.MOE_ERR_UNSUPPORTED),
+    (dict(top_k=17), moe.MOE_ERR_INVALID_ARG),
+    (dict(top_k=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(n_experts=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(n_experts=4, top_k=5), moe.MOE_ERR_INVALID_ARG),
+    (dict(hidden=200), moe.MOE_ERR_UNSUPPORTED),
+    (dict(inter=100), moe.MOE_ERR_UNSUPPORTED),
+    (dict(act_dtype=7), moe.MOE_ERR_UNSUPPORTED),
+    (dict(n_tokens=-1), moe.MOE_ERR_INVALID_ARG),
+    (dict(flags=8), moe.MOE_ERR_INVALID_ARG),
+    (dict(expert_stride=1769472 + 100), moe.MOE_ERR_MISALIGNED),
+    (dict(expert_stride=1024), moe.MOE_ERR_MISALIGNED),
+])
+def test_desc_validation(mut, status):
+    d = moe.make_desc(1, 2048, 256, 8, 512, 512)
+    for k, v in mut.items():
+        setattr(d, k, v)
+    assert _layer(d) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), moe.MOE_ERR_INVALID_ARG),
+    (dict(x=FAKE + 2), moe.MOE_ERR_MISALIGNED),
+    (dict(rw=None), moe.MOE_ERR_INVALID_ARG),
+    (dict(slab=FAKE + 64), moe.MOE_ERR_MISALIGNED),
+    (dict(st=None), moe.MOE_ERR_INVALID_ARG),
+    (dict(sh=None), moe.MOE_ERR_INVALID_ARG),
+    (dict(out=None), moe.MOE_ERR_INVALID_ARG),
+    (dict(ws=FAKE + 16), moe.MOE_ERR_MISALIGNED),
+])
+def test_pointer_validation(kw, status):
+    d = moe.make_desc(1, 2048, 256, 8, 512, 512)
+    assert _layer(d, **kw) == status
+
+
+def test_router_bias_required_when_flagged():
+    d = moe.make_desc(64, 2048, 512, 10, 512, 512, router_bias=True)
+    assert _layer(d, rb=None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_zero_tokens_is_a_no_op():
+    d = moe.make_desc(0, 2048, 256, 8, 512, 512)
+    assert _layer(d) == moe.MOE_OK
+
+
+def test_other_entry_points_validate():
+    d = moe.make_desc(1, 2048, 256, 8, 512, 512)
+    h = moe.lib()
+    bad = moe.make_desc(1, 2048, 256, 8, 512, 512)
+    bad.bits = 3
+    assert h.moe_router_topk(ctypes.byref(bad), FAKE, FAKE, None, None, FAKE, FAKE, None, FAKE,
+                             None) == moe.MOE_ERR_UNSUPPORTED
+    assert h.moe_router_topk(ctypes.byref(d), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE,
+                             None) == moe.MOE_ERR_INVALID_ARG   # gamma without w_sg
+    assert h.moe_experts_forward(ctypes.byref(d), FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE,
+                                 FAKE, None) == moe.MOE_ERR_INVALID_ARG  # shared gate missing
+    assert h.moe_rmsnorm(ctypes.byref(d), None, None, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert h.moe_chain_forward(ctypes.byref(d), 0, FAKE, FAKE, None, FAKE, FAKE, FAKE, 1 << 21,
+                               FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert h.moe_chain_forward(ctypes.byref(d), 2, FAKE, FAKE, None, FAKE, FAKE, FAKE, 1000,
+                               FAKE, FAKE, FAKE, None) == moe.MOE_ERR_MISALIGNED
+    assert moe.moe_workspace_bytes(bad) == 0
+    assert moe.moe_workspace_bytes(d) > 0
+
+
+def test_valid_call_without_device_reports_no_device():
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible: fake pointers must not reach a launch")
+    d = moe.make_desc(1, 2048, 256, 8, 512, 512)
+    assert _layer(d) == moe.MOE_ERR_NO_DEVICE

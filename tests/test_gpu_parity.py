@@ -1,0 +1,389 @@
+"""GPU parity of the HIP path against the fp64 oracle, through the C ABI.
+
+Every case prints its name before touching the GPU.  Inputs are seeded
+synthetic workloads (synth); the oracle reads the generator's logical arrays
+on the host, never the packed slab.
+"""
+import gc
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from synth import configs
+from tests.parity import check_out, check_routing, say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import int4_group_quantized_moe_amd as moe
+    from synth import device as sd
+    moe.lib()          # must load: there is no fallback path
+    sd.lib()
+    yield
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def _moe():
+    import int4_group_quantized_moe_amd as moe
+    return moe
+
+
+def _wl():
+    import workload
+    return workload
+
+
+def _free():
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# generator and packer
+
+
+@pytest.mark.parametrize("cfgname,expert", [("tiny", 3), ("decode_80b", 77), ("batched_80b_int8", 5),
+                                            ("decode_35b", synth.SHARED_EXPERT)])
+def test_device_fill_matches_host_generator(cfgname, expert):
+    from synth import device as sd
+    cfg = configs.CONFIGS[cfgname]
+    say(f"[fill] {cfgname} expert {expert}")
+    H, G = cfg.hidden, cfg.group
+    I = cfg.shared_inter if expert == synth.SHARED_EXPERT else cfg.inter
+    qg = torch.empty(1, I, H, dtype=torch.uint8, device="cuda")
+    qu, qd = torch.empty_like(qg), torch.empty(1, H, I, dtype=torch.uint8, device="cuda")
+    sbg = torch.empty(1, 2, I, H // G, dtype=torch.int16, device="cuda")
+    sbu, sbd = torch.empty_like(sbg), torch.empty(1, 2, H, I // G, dtype=torch.int16, device="cuda")
+    sd.fill_experts(cfg, 2, expert, 1, I, qg, qu, qd, sbg, sbu, sbd,
+                    torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    ref = synth.expert_arrays(cfg, 2, expert)
+    assert np.array_equal(qg[0].cpu().numpy(), ref["qg"])
+    assert np.array_equal(qu[0].cpu().numpy(), ref["qu"])
+    assert np.array_equal(qd[0].cpu().numpy(), ref["qd"])
+    for t, (s, b) in ((sbg, ("sg", "bg")), (sbu, ("su", "bu")), (sbd, ("sd", "bd"))):
+        got = t[0].cpu().numpy().view(np.uint16)
+        assert np.array_equal(got[0], ref[s]) and np.array_equal(got[1], ref[b])
+
+
+@pytest.mark.parametrize("cfgname", ["tiny", "decode_80b", "batched_80b_int8"])
+def test_device_packer_matches_host_packer(cfgname):
+    moe, wl = _moe(), _wl()
+    cfg = configs.CONFIGS[cfgname]
+    say(f"[pack] {cfgname}")
+    d = wl.desc_for(cfg)
+    w = wl.Workload(cfg, n_layers=1, batch=8)
+    L = w.layout
+    for e in (0, cfg.n_experts - 1):
+        a = synth.expert_arrays(cfg, 0, e)
+        host = np.zeros(L.blob_bytes, np.uint8)
+        moe.moe_pack_expert(d, cfg.inter, a["qg"], a["qu"], a["qd"],
+                            np.stack([a["sg"], a["bg"]]), np.stack([a["su"], a["bu"]]),
+                            np.stack([a["sd"], a["bd"]]), None, host)
+        slot = int(w.slot_tables_np[0, e])
+        dev = w.slab[slot * w.stride: slot * w.stride + L.blob_bytes].cpu().numpy()
+        assert np.array_equal(dev, host), e
+    a = synth.expert_arrays(cfg, 0, synth.SHARED_EXPERT)
+    host = np.zeros(w.slayout.shared_bytes, np.uint8)
+    moe.moe_pack_expert(d, cfg.shared_inter, a["qg"], a["qu"], a["qd"],
+                        np.stack([a["sg"], a["bg"]]), np.stack([a["su"], a["bu"]]),
+                        np.stack([a["sd"], a["bd"]]), synth.shared_gate_weight(cfg, 0), host)
+    assert np.array_equal(w.shared[0].cpu().numpy(), host)
+    del w
+    _free()
+
+
+# ---------------------------------------------------------------------------
+# router
+
+
+@pytest.mark.parametrize("cfgname", ["tiny", "decode_35b", "decode_80b", "batched_80b",
+                                     "prefill_35b"])
+def test_router_topk_parity(cfgname):
+    moe, wl = _moe(), _wl()
+    cfg = configs.CONFIGS[cfgname]
+    say(f"[router] {cfgname} T={cfg.n_tokens}")
+    d = wl.desc_for(cfg)
+    T, E, k, H = cfg.n_tokens, cfg.n_experts, cfg.top_k, cfg.hidden
+    x_np = synth.activations(cfg)
+    if cfg.act == "bf16":   # router input of a chained layer: a normalised, stored x_hat
+        x_np = oracle.chain_prologue(x_np, cfg.rms_eps, "bf16").astype(np.float32)
+    x = wl.act_tensor(cfg, x_np)
+    Wr = synth.router_weight(cfg, 0)
+    rb = synth.router_bias(cfg, 0)
+    wsg = synth.shared_gate_weight(cfg, 0)
+    Wr_d = torch.from_numpy(Wr).cuda()
+    rb_d = torch.from_numpy(rb).cuda() if rb is not None else None
+    wsg_d = torch.from_numpy(wsg).cuda()
+    idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    gam = torch.empty(T, dtype=torch.float32, device="cuda")
+    ws = torch.empty(moe.moe_workspace_bytes(d), dtype=torch.uint8, device="cuda")
+    moe.moe_router_topk(d, x, Wr_d, rb_d, wsg_d, idx, w, gam, ws)
+    torch.cuda.synchronize()
+    l, ridx, rw, gap = oracle.route(x_np.astype(np.float64), Wr, rb, k)
+    ref = {"logits": l, "idx": ridx, "w": rw, "gap": gap}
+    _, _, n_ties = check_routing(idx.cpu().numpy(), w.cpu().numpy(), ref, k, gam.cpu().numpy(),
+                                 oracle.shared_gate(x_np.astype(np.float64), wsg))
+    say(f"  tokens with gap < 1e-5: {n_ties}")
+
+
+# ---------------------------------------------------------------------------
+# whole layer
+
+
+def run_layer(w, cfg, x, i=0, desc=None):
+    moe = _moe()
+    d = desc or w.desc
+    out = torch.empty_like(x)
+    ws = w.workspace(d)
+    rw, rb, st, sh = w.layer_args(i)
+    moe.moe_layer_forward(d, x, rw, rb, w.slab, st, sh, out, ws)
+    pi, pw, pg = moe.moe_workspace_routing(d, ws)
+    T, k = d.n_tokens, d.top_k
+    idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    wt = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    g = torch.empty(T, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    # copy the routing out of the workspace (device addresses inside ws)
+    base = ws.data_ptr()
+    idx.copy_(ws[pi - base: pi - base + 4 * T * k].view(torch.int32).view(T, k))
+    wt.copy_(ws[pw - base: pw - base + 4 * T * k].view(torch.float32).view(T, k))
+    g.copy_(ws[pg - base: pg - base + 4 * T].view(torch.float32))
+    torch.cuda.synchronize()
+    return out, idx, wt, g
+
+
+def check_layer(cfg, layer, x_hat_np, out, idx, wt, g, what):
+    inp = oracle.LayerInputs(cfg, layer)
+    ref = oracle.oracle_layer(inp, x_hat_np.astype(np.float64))
+    use_idx, use_w, n_ties = check_routing(idx.cpu().numpy(), wt.cpu().numpy(), ref, cfg.top_k,
+                                           g.cpu().numpy(), ref["gamma"])
+    if n_ties:
+        ref = oracle.oracle_layer(inp, x_hat_np.astype(np.float64), routing=(use_idx, use_w))
+    return check_out(out.float().cpu().numpy(), ref["out"], cfg.act, what)
+
+
+def test_tiny_layer_parity():
+    moe, wl = _moe(), _wl()
+    cfg = configs.TINY
+    say("[layer] tiny fp32 T=4")
+    w = wl.Workload(cfg, n_layers=1)
+    x_np = synth.activations(cfg)
+    x = wl.act_tensor(cfg, x_np)
+    out, idx, wt, g = run_layer(w, cfg, x)
+    check_layer(cfg, 0, x_np, out, idx, wt, g, "tiny")
+    # router + experts called separately give the same bits
+    d = w.desc
+    ws = w.workspace()
+    rw, rb, st, sh = w.layer_args(0)
+    idx2 = torch.empty_like(idx)
+    w2 = torch.empty_like(wt)
+    g2 = torch.empty_like(g)
+    wsg = sh[w.slayout.shared_gate_offset: w.slayout.shared_gate_offset + 4 * cfg.hidden].view(torch.float32)
+    moe.moe_router_topk(d, x, rw, rb, wsg, idx2, w2, g2, ws)
+    out2 = torch.empty_like(out)
+    moe.moe_experts_forward(d, x, idx2, w2, g2, w.slab, st, sh, out2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(idx2, idx) and torch.equal(w2, wt) and torch.equal(g2, g)
+    assert torch.equal(out2, out)
+    del w
+    _free()
+
+
+@pytest.mark.parametrize("cfgname,check_layers", [("decode_35b", (0, 1, 19, 39)),
+                                                  ("decode_80b", (0, 1, 30, 47))])
+def test_decode_chain_parity(cfgname, check_layers):
+    """Batch-1 decode through every layer of the chain, teacher-forced:
+    layer l of the oracle takes the GPU's own x_hat_l."""
+    moe, wl = _moe(), _wl()
+    cfg = configs.CONFIGS[cfgname]
+    say(f"[chain] {cfgname}: building {cfg.layers} layers")
+    w = wl.Workload(cfg)
+    d = w.desc
+    x0_np = synth.activations(cfg)
+    x = wl.act_tensor(cfg, x0_np)
+    xh = torch.empty_like(x)
+    out = torch.empty_like(x)
+    ws = w.workspace()
+    for i in range(cfg.layers):
+        checking = i in check_layers
+        if checking:
+            x_before = x.clone()
+            out_prev = out.clone() if i > 0 else None
+        moe.moe_rmsnorm(d, x, out if i > 0 else None, xh)
+        rw, rb, st, sh = w.layer_args(i)
+        if checking:
+            say(f"  layer {i}")
+            torch.cuda.synchronize()
+            xb = wl.to_f64(x_before)
+            if out_prev is not None:
+                x_ref = oracle.chain_epilogue(xb, wl.to_f64(out_prev), cfg.act)
+                assert np.array_equal(wl.to_f64(x), x_ref), "residual"
+            xh_ref = oracle.chain_prologue(wl.to_f64(x), cfg.rms_eps, cfg.act)
+            ulp = np.abs(xh_ref) * 2.0 ** -7
+            assert np.all(np.abs(wl.to_f64(xh) - xh_ref) <= ulp + 1e-30), "rmsnorm"
+            o, idx, wt, g = run_layer(w, cfg, xh, i)
+            out.copy_(o)
+            check_layer(cfg, i, wl.to_f64(xh), o, idx, wt, g, f"{cfgname} layer {i}")
+        else:
+            moe.moe_layer_forward(d, xh, rw, rb, w.slab, st, sh, out, ws)
+    moe.moe_rmsnorm(d, x, out, xh)
+    torch.cuda.synchronize()
+    # the chain entry point runs the same kernels: bit-equal final residual
+    say("  chain entry point")
+    xc = wl.act_tensor(cfg, x0_np)
+    moe.moe_chain_forward(d, cfg.layers, xc, w.router_w, w.router_bias, w.slab, w.slot_tables,
+                          w.shared, w.shared_stride, torch.empty_like(xc), torch.empty_like(xc), ws)
+    torch.cuda.synchronize()
+    assert torch.equal(xc, x)
+    assert torch.isfinite(xc.float()).all()
+    del w
+    _free()
+
+
+@pytest.mark.parametrize("cfgname", ["batched_80b", "batched_80b_int8"])
+def test_batched_parity(cfgname):
+    """64 tokens with a Zipf router bias: token->expert bucketing path."""
+    moe, wl = _moe(), _wl()
+    cfg = configs.CONFIGS[cfgname]
+    say(f"[batched] {cfgname}")
+    w = wl.Workload(cfg, n_layers=2)
+    d = w.desc
+    x = wl.act_tensor(cfg, synth.activations(cfg))
+    xh = torch.empty_like(x)
+    out = None
+    for i in range(2):
+        moe.moe_rmsnorm(d, x, out, xh)
+        o, idx, wt, g = run_layer(w, cfg, xh, i)
+        uniq = len(np.unique(idx.cpu().numpy()))
+        say(f"  layer {i}: {uniq} unique experts")
+        check_layer(cfg, i, wl.to_f64(xh), o, idx, wt, g, f"{cfgname} layer {i}")
+        # token independence: a row of the batch equals the token alone
+        d1 = wl.desc_for(cfg, n_tokens=1)
+        for t in (0, 17, 63):
+            o1, idx1, _, _ = run_layer(w, cfg, xh[t:t + 1].contiguous(), i, desc=d1)
+            assert sorted(idx1[0].tolist()) == sorted(idx[t].tolist())
+            a, b = o1[0].double(), o[t].double()
+            rms = float(torch.sqrt(torch.mean(b * b)))
+            assert float((a - b).abs().max()) <= 2e-2 * rms, t
+        out = o
+    del w
+    _free()
+
+
+def test_prefill_parity():
+    """4096-token chunk, one layer: full routing check, sampled outputs."""
+    moe, wl = _moe(), _wl()
+    cfg = configs.PREFILL_35B
+    say("[prefill] 4096 tokens")
+    w = wl.Workload(cfg, n_layers=1)
+    x_np = oracle.chain_prologue(synth.activations(cfg), cfg.rms_eps, "bf16").astype(np.float32)
+    x = wl.act_tensor(cfg, x_np)
+    out, idx, wt, g = run_layer(w, cfg, x)
+    counts = np.bincount(idx.cpu().numpy().ravel(), minlength=cfg.n_experts)
+    say(f"  tokens per expert: mean {counts.mean():.1f} min {counts.min()} max {counts.max()}")
+    rng = np.random.default_rng(4)
+    tok = np.sort(np.concatenate([[0, cfg.n_tokens - 1], rng.choice(cfg.n_tokens, 6, replace=False)]))
+    check_layer(cfg, 0, x_np[tok], out[tok], idx[tok], wt[tok], g[tok], "prefill sampled tokens")
+    del w
+    _free()
+
+
+def test_slot_permutation_invariance():
+    """Experts moved to other slots (and the slot table with them) give the
+    same bits: the analogue of cache-vs-disk identity."""
+    moe, wl = _moe(), _wl()
+    cfg = configs.DECODE_35B
+    say("[slots] permutation invariance")
+    outs = []
+    for perm in (None, 99):
+        w = wl.Workload(cfg, n_layers=1, permute_seed=perm)
+        x = wl.act_tensor(cfg, synth.activations(cfg, n_tokens=16))
+        r = []
+        for T in (1, 16):
+            d = wl.desc_for(cfg, n_tokens=T)
+            r.append(run_layer(w, cfg, x[:T].contiguous(), 0, desc=d)[0].clone())
+        outs.append(r)
+        del w
+        _free()
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_determinism():
+    moe, wl = _moe(), _wl()
+    cfg = configs.DECODE_35B
+    say("[determinism]")
+    w = wl.Workload(cfg, n_layers=1)
+    x = wl.act_tensor(cfg, synth.activations(cfg, n_tokens=32))
+    for T in (1, 32):
+        d = wl.desc_for(cfg, n_tokens=T)
+        a = run_layer(w, cfg, x[:T].contiguous(), 0, desc=d)[0].clone()
+        b = run_layer(w, cfg, x[:T].contiguous(), 0, desc=d)[0].clone()
+        assert torch.equal(a, b)
+    del w
+    _free()
+
+
+@pytest.mark.parametrize("T,k", [(1, 1), (4, 16), (8, 2), (9, 2), (63, 3), (64, 2), (65, 4),
+                                 (100, 2)])
+def test_edge_cases_tiny(T, k):
+    """Ragged token counts around the small-batch/bucketed boundary and the
+    64-token bucketing blocks, k = 1 and k = E."""
+    wl = _wl()
+    cfg = configs.TINY.with_(n_tokens=T, top_k=k)
+    say(f"[edge] T={T} k={k}")
+    w = wl.Workload(cfg, n_layers=1)
+    x_np = synth.activations(cfg)
+    x = wl.act_tensor(cfg, x_np)
+    out, idx, wt, g = run_layer(w, cfg, x)
+    check_layer(cfg, 0, x_np, out, idx, wt, g, f"T={T} k={k}")
+    if k == cfg.n_experts:
+        assert np.array_equal(np.sort(idx.cpu().numpy(), 1), np.tile(np.arange(k), (T, 1)))
+    del w
+    _free()
+
+
+def test_zero_tokens_no_op():
+    moe, wl = _moe(), _wl()
+    cfg = configs.TINY
+    say("[edge] T=0")
+    w = wl.Workload(cfg, n_layers=1)
+    d0 = wl.desc_for(cfg, n_tokens=0)
+    out = torch.full((1, cfg.hidden), 7.0, device="cuda")
+    rw, rb, st, sh = w.layer_args(0)
+    moe.moe_layer_forward(d0, out, rw, rb, w.slab, st, sh, out, w.workspace())
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
+    del w
+    _free()
+
+
+def test_rmsnorm_parity():
+    moe, wl = _moe(), _wl()
+    say("[rmsnorm]")
+    cfg = configs.DECODE_35B.with_(n_tokens=5)
+    d = wl.desc_for(cfg)
+    rng = np.random.default_rng(3)
+    x_np = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(rng.standard_normal((5, 2048)) * 30))
+    o_np = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(rng.standard_normal((5, 2048)) * 200))
+    x = wl.act_tensor(cfg, x_np)
+    o = wl.act_tensor(cfg, o_np)
+    xh = torch.empty_like(x)
+    moe.moe_rmsnorm(d, x, o, xh)
+    torch.cuda.synchronize()
+    x_ref = oracle.chain_epilogue(x_np, o_np, "bf16")
+    assert np.array_equal(wl.to_f64(x), x_ref)
+    xh_ref = oracle.chain_prologue(x_ref, cfg.rms_eps, "bf16")
+    assert np.all(np.abs(wl.to_f64(xh) - xh_ref) <= np.abs(xh_ref) * 2.0 ** -7)
