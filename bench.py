@@ -1,0 +1,278 @@
+"""Benchmark of the MoE-layer decode hot path on one MI355X.
+
+Default workload: the 35B-A3B-shaped decode chain -- hidden 2048, 256 experts,
+top-8, expert and shared intermediate 512, int4 group-64 weights, bf16
+activations, 1 token through 40 distinct chained layers (pre-RMSNorm, MoE
+layer, residual add).  A step is one token through all 40 layers.  The input
+rotates over 8 seeded vectors so the routed experts change between steps and
+the 18 GB slab cannot be served from the 256 MB Infinity Cache.  Each rotation
+is one captured hipGraph of the whole chain.
+
+Prints ONE JSON line (see the keys below).  ``value`` is the chain throughput
+in tokens/s; the HBM figures use the algorithmic bytes of the step: router
+weights, the routed experts' blobs actually selected, the shared blob and its
+gate vector, and the activations in and out of each layer.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+N_ROTATE = 8
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--config", default="decode_35b",
+                   help="decode_35b (default), decode_80b, batched_80b, batched_80b_int8, "
+                        "prefill_35b, tiny")
+    p.add_argument("--layers", type=int, default=0, help="override the number of layers")
+    p.add_argument("--cpu-layers", type=int, default=8,
+                   help="layers of the oracle's timed sample (0: skip the CPU baseline)")
+    p.add_argument("--no-roofline", action="store_true", help="skip the per-stage event pass")
+    return p.parse_args()
+
+
+def algorithmic_bytes(cfg, wl, unique_per_layer):
+    """Bytes the method must move once per step (no re-reads, no scratch)."""
+    T, E, H = cfg.n_tokens, cfg.n_experts, cfg.hidden
+    act = 4 if cfg.act == "f32" else 2
+    blob = int(wl.layout.blob_bytes)
+    sblob = int(wl.slayout.blob_bytes)
+    per_layer = []
+    for U in unique_per_layer:
+        b = E * H * 4                        # router weights (fp32)
+        b += E * 4 if cfg.zipf_s else 0      # router bias
+        b += U * blob                        # routed experts, each read once
+        b += sblob + H * 4                   # shared expert blob + its gate vector
+        b += 2 * T * H * act                 # x_hat in, out out
+        per_layer.append(b)
+    return per_layer
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              f"(the MoE layer is measured on one MI355X's share of the work)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import int4_group_quantized_moe_amd as moe
+    import synth
+    import workload
+    from synth import configs
+
+    cfg = configs.CONFIGS[args.config]
+    if args.layers:
+        cfg = cfg.with_(layers=args.layers)
+    torch.cuda.set_device(0)
+    moe.lib()
+    t0 = time.time()
+    print(f"# building {cfg.name}: {cfg.layers} layers, T={cfg.n_tokens}", file=sys.stderr,
+          flush=True)
+    wl = workload.Workload(cfg)
+    print(f"# built in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    d = wl.desc
+    L, T = cfg.layers, cfg.n_tokens
+    xs = [workload.act_tensor(cfg, synth.activations(cfg, variant=r)) for r in range(N_ROTATE)]
+    x = torch.empty_like(xs[0])
+    x_hat = torch.empty_like(x)
+    out = torch.empty_like(x)
+    ws = wl.workspace()
+    stream = torch.cuda.Stream()
+
+    def chain(r):
+        x.copy_(xs[r])
+        moe.moe_chain_forward(d, L, x, wl.router_w, wl.router_bias, wl.slab, wl.slot_tables,
+                              wl.shared, wl.shared_stride, x_hat, out, ws)
+
+    # eager run: routing statistics (unique experts per layer) per rotation
+    pi, pw, pg = moe.moe_workspace_routing(d, ws)
+    idx_off = pi - ws.data_ptr()
+    uniq = np.zeros((N_ROTATE, L))
+    for r in range(N_ROTATE):
+        x.copy_(xs[r])
+        for layer in range(L):
+            moe.moe_rmsnorm(d, x, out if layer else None, x_hat)
+            rw, rb, st, sh = wl.layer_args(layer)
+            moe.moe_layer_forward(d, x_hat, rw, rb, wl.slab, st, sh, out, ws)
+            idx = ws[idx_off: idx_off + 4 * T * cfg.top_k].view(torch.int32)
+            uniq[r, layer] = torch.unique(idx).numel()
+    torch.cuda.synchronize()
+    bytes_per_rot = [sum(algorithmic_bytes(cfg, wl, uniq[r])) for r in range(N_ROTATE)]
+
+    # one captured graph per input rotation; eager launches if the chain's
+    # launch cannot be captured
+    graphs = []
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for r in range(N_ROTATE):
+            chain(r)                     # warm the capture stream
+        torch.cuda.synchronize()
+        try:
+            for r in range(N_ROTATE):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    chain(r)
+                graphs.append(g)
+        except Exception as e:          # noqa: BLE001
+            print(f"# graph capture unavailable ({type(e).__name__}); timing eager launches",
+                  file=sys.stderr, flush=True)
+            graphs = []
+    torch.cuda.synchronize()
+    mode = "hipgraph" if graphs else "eager"
+
+    def step(s):
+        if graphs:
+            graphs[s % N_ROTATE].replay()
+        else:
+            chain(s % N_ROTATE)
+
+    # warmup + timed region
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for s in range(args.steps):
+        step(s)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_total = ev0.elapsed_time(ev1)
+    ms_per_step = ms_total / args.steps
+    step_bytes = sum(bytes_per_rot[s % N_ROTATE] for s in range(args.steps)) / args.steps
+    tokens_per_s = T / (ms_per_step / 1e3)
+    gbps = step_bytes / (ms_per_step / 1e3) / 1e9
+
+    # correctness guard of the timed state: finite residual stream
+    assert torch.isfinite(x.float()).all(), "non-finite output"
+
+    roofline = None
+    if not args.no_roofline:
+        roofline = chain_roofline(cfg, chain, bytes_per_rot)
+
+    cpu = None
+    if args.cpu_layers > 0:
+        cpu = cpu_baseline(cfg, min(args.cpu_layers, L))
+
+    line = {
+        "metric": "MoE-layer decode tokens/s and achieved HBM GB/s (% of peak), 1 GPU",
+        "value": round(tokens_per_s, 3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4 weights x bf16 activations, fp32 accumulate" if cfg.act == "bf16"
+                 else "int4 weights x fp32 activations, fp32 accumulate",
+        "data": "synthetic",
+        "config": {
+            "workload": describe(cfg),
+            "tokens_per_step": T,
+            "layers": L,
+            "input_rotations": N_ROTATE,
+            "launch": mode,
+            "unique_experts_per_layer_mean": round(float(uniq.mean()), 2),
+        },
+        "hbm_gbps": round(gbps, 1),
+        "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes_per_step": int(step_bytes),
+        "us_per_layer": round(ms_per_step * 1e3 / L, 3),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    if cfg.name == "decode_35b":
+        line["config"]["bits"] = cfg.bits
+    print(json.dumps(line), flush=True)
+
+
+def describe(cfg):
+    return (f"{cfg.name}: hidden {cfg.hidden}, {cfg.n_experts} experts top-{cfg.top_k}, "
+            f"inter {cfg.inter}, shared {cfg.shared_inter} (sigmoid gate), int{cfg.bits} "
+            f"group {cfg.group}, {cfg.act} activations, {cfg.n_tokens} token(s), "
+            f"{cfg.layers} chained layer(s)")
+
+
+def chain_roofline(cfg, chain, bytes_per_rot, reps=64):
+    """Average duration of one launch of the chain (for batch-1 bf16 int4
+    decode this is the single persistent kernel that streams every layer's
+    weights), timed with HIP events on the launch stream.  The stream is first
+    held by a device-side sleep so that all launches are queued before the
+    first one runs and the intervals contain no host gaps."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(50_000_000)
+    for i in range(reps):
+        evs[i][0].record()
+        chain(i % N_ROTATE)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    durs = [a.elapsed_time(b) * 1e-3 for a, b in evs]
+    avg_s = sum(durs) / len(durs)
+    avg_b = sum(bytes_per_rot[i % N_ROTATE] for i in range(reps)) / reps
+    achieved = avg_b / avg_s / 1e9
+    return {"bound": "hbm",
+            "kernel": "moe_chain_forward: one launch of the whole decode chain "
+                      "(input copy + chain kernel(s))",
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+            "avg_launch_us": round(avg_s * 1e6, 3), "bytes_per_launch": int(avg_b),
+            "launches": reps}
+
+
+def cpu_baseline(cfg, n_layers):
+    """The fp64 oracle, as it is, on a bounded sample: one token through the
+    first n_layers layers of the same chain (inputs generated beforehand and
+    not timed); tokens/s scaled to the full chain."""
+    import numpy as np
+    import threadpoolctl
+
+    import oracle
+    import synth
+    inputs = [oracle.LayerInputs(cfg, l) for l in range(n_layers)]
+    x0 = synth.activations(cfg)
+
+    def run():
+        x = x0.astype(np.float64)
+        for l in range(n_layers):
+            xh = oracle.chain_prologue(x, cfg.rms_eps, cfg.act)
+            r = oracle.oracle_layer(inputs[l], xh)
+            x = oracle.chain_epilogue(x, r["out"], cfg.act)
+        return x
+
+    run()                                  # draws and caches the routed experts' inputs
+    t0 = time.perf_counter()
+    run()
+    dt = time.perf_counter() - t0
+    per_layer = dt / n_layers
+    tokens_per_s = cfg.n_tokens / (per_layer * cfg.layers)
+    threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] + [1])
+    return {"value": round(tokens_per_s, 6), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{cfg.n_tokens} token(s) through layers 0..{n_layers - 1} of {cfg.layers} "
+                      f"(numpy float64; {dt:.1f}s); scaled to the {cfg.layers}-layer chain",
+            "seconds_per_layer": round(per_layer, 4)}
+
+
+if __name__ == "__main__":
+    main()

@@ -81,6 +81,50 @@ int enqueue_router(const moe_layer_desc* d, const void* x, const float* router_w
   return to_status(launch_router_topk(a, s));
 }
 
+bool fast_decode(const moe_layer_desc* d) {
+  const bool sh = (d->flags & MOE_FLAG_SHARED) != 0;
+  return decode_fast_supported(d->n_tokens, d->act_dtype, d->hidden, d->top_k, d->n_experts,
+                               d->bits, d->inter, sh ? d->shared_inter : 0, sh);
+}
+
+int enqueue_decode(const moe_layer_desc* d, const void* x_in, void* x_hat, bool do_norm,
+                   const float* router_w, const float* router_bias, const void* slab,
+                   const int32_t* slot_table, const void* shared_blob, void* out, void* x_res,
+                   uint8_t* ws, hipStream_t s) {
+  const WsPlan P = make_ws_plan(*d);
+  DecodeArgs a{};
+  a.has_shared = (d->flags & MOE_FLAG_SHARED) != 0;
+  a.L = make_layout(d->bits, d->hidden, d->inter);
+  a.Ls = make_layout(d->bits, d->hidden, a.has_shared ? d->shared_inter : d->inter);
+  a.x_in = reinterpret_cast<const uint16_t*>(x_in);
+  a.x_hat = reinterpret_cast<uint16_t*>(x_hat);
+  a.router_w = router_w;
+  a.router_bias = (d->flags & MOE_FLAG_ROUTER_BIAS) ? router_bias : nullptr;
+  a.shared_gate_w =
+      a.has_shared ? reinterpret_cast<const float*>(
+                         reinterpret_cast<const uint8_t*>(shared_blob) + a.Ls.sg_off)
+                   : nullptr;
+  a.logits = reinterpret_cast<float*>(ws + P.logits);
+  a.idx = reinterpret_cast<int32_t*>(ws + P.idx);
+  a.w = reinterpret_cast<float*>(ws + P.w);
+  a.gamma = reinterpret_cast<float*>(ws + P.gamma);
+  a.slots = reinterpret_cast<int32_t*>(ws + P.slots);
+  a.h = reinterpret_cast<float*>(ws + P.h);
+  a.slab = reinterpret_cast<const uint8_t*>(slab);
+  a.slot_table = slot_table;
+  a.stride = d->expert_stride;
+  a.shared_blob = reinterpret_cast<const uint8_t*>(shared_blob);
+  a.out = reinterpret_cast<uint16_t*>(out);
+  a.x_res = reinterpret_cast<uint16_t*>(x_res);
+  a.H = d->hidden;
+  a.E = d->n_experts;
+  a.k = d->top_k;
+  a.bits = d->bits;
+  a.eps = d->rms_eps;
+  a.do_norm = do_norm;
+  return to_status(launch_decode(a, s));
+}
+
 int enqueue_experts(const moe_layer_desc* d, const void* x, const int32_t* idx, const float* w,
                     const float* gamma, const void* slab, const int32_t* slot_table,
                     const void* shared_blob, void* out, uint8_t* ws, hipStream_t s) {
@@ -312,6 +356,9 @@ int moe_layer_forward(const moe_layer_desc* desc, const void* x, const float* ro
   if (shared) MOE_TRY(check_ptr(shared_blob, 256));
   MOE_TRY(device_ok());
   uint8_t* w8 = reinterpret_cast<uint8_t*>(ws);
+  if (fast_decode(desc))
+    return enqueue_decode(desc, x, const_cast<void*>(x), false, router_w, router_bias,
+                          expert_slab, slot_table, shared_blob, out, nullptr, w8, stream);
   const WsPlan P = make_ws_plan(*desc);
   int32_t* idx = reinterpret_cast<int32_t*>(w8 + P.idx);
   float* w = reinterpret_cast<float*>(w8 + P.w);
@@ -366,6 +413,70 @@ int moe_chain_forward(const moe_layer_desc* desc, int32_t n_layers, void* x,
   if (!(desc->rms_eps >= 0.0f)) return MOE_ERR_INVALID_ARG;
   MOE_TRY(device_ok());
   const int64_t EH = (int64_t)desc->n_experts * desc->hidden;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_NO_DEVICE;
+  const int nwg = chain_grid(dev);
+  if (chain_supported(nwg, desc->n_tokens, desc->act_dtype, desc->hidden, desc->n_experts,
+                      desc->top_k, desc->bits, desc->inter, shared ? desc->shared_inter : 0,
+                      shared)) {
+    const WsPlan P = make_ws_plan(*desc);
+    uint8_t* w8 = reinterpret_cast<uint8_t*>(ws);
+    const BlobLayout Lr = make_layout(desc->bits, desc->hidden, desc->inter);
+    const BlobLayout Ls = make_layout(desc->bits, desc->hidden, shared ? desc->shared_inter : desc->inter);
+    ChainParams c{};
+    c.x = reinterpret_cast<uint16_t*>(x);
+    c.x_hat = reinterpret_cast<uint16_t*>(x_hat);
+    c.out = reinterpret_cast<uint16_t*>(out);
+    c.router_w = router_w;
+    c.router_bias = (desc->flags & MOE_FLAG_ROUTER_BIAS) ? router_bias : nullptr;
+    c.slab = reinterpret_cast<const uint8_t*>(expert_slab);
+    c.stride = desc->expert_stride;
+    c.slot_tables = slot_tables;
+    c.shared_blobs = reinterpret_cast<const uint8_t*>(shared_blobs);
+    c.shared_stride = shared_stride;
+    c.L = n_layers;
+    c.H = desc->hidden;
+    c.E = desc->n_experts;
+    c.k = desc->top_k;
+    c.I = desc->inter;
+    c.Is = shared ? desc->shared_inter : 0;
+    c.has_shared = shared ? 1 : 0;
+    c.bits_ = desc->bits;
+    c.eps = desc->rms_eps;
+    c.gu_unit_r = Lr.gu_unit;
+    c.gu_tile_r = Lr.gu_tile;
+    c.d_off_r = Lr.d_off;
+    c.d_unit_r = Lr.d_unit;
+    c.d_tile_r = Lr.d_tile;
+    c.gu_unit_s = Ls.gu_unit;
+    c.gu_tile_s = Ls.gu_tile;
+    c.d_off_s = Ls.d_off;
+    c.d_unit_s = Ls.d_unit;
+    c.d_tile_s = Ls.d_tile;
+    c.sg_off = Ls.sg_off;
+    c.xw = reinterpret_cast<uint64_t*>(w8 + P.xw);
+    c.lw = reinterpret_cast<uint64_t*>(w8 + P.lw);
+    c.hw = reinterpret_cast<uint64_t*>(w8 + P.hw);
+    c.ctr = reinterpret_cast<uint32_t*>(w8 + P.ctr);
+    c.err = c.ctr + 1;
+    c.r_idx = reinterpret_cast<int32_t*>(w8 + P.idx);
+    c.r_w = reinterpret_cast<float*>(w8 + P.w);
+    c.r_gamma = reinterpret_cast<float*>(w8 + P.gamma);
+    return to_status(launch_chain(c, nwg, stream));
+  }
+  if (fast_decode(desc)) {
+    for (int l = 0; l < n_layers; ++l) {
+      const float* rb = (desc->flags & MOE_FLAG_ROUTER_BIAS)
+                            ? router_bias + (int64_t)l * desc->n_experts
+                            : nullptr;
+      const void* sb = shared ? reinterpret_cast<const uint8_t*>(shared_blobs) + l * shared_stride
+                              : nullptr;
+      MOE_TRY(enqueue_decode(desc, x, x_hat, true, router_w + l * EH, rb, expert_slab,
+                             slot_tables + (int64_t)l * desc->n_experts, sb, out, x,
+                             reinterpret_cast<uint8_t*>(ws), stream));
+    }
+    return MOE_OK;
+  }
   for (int l = 0; l < n_layers; ++l) {
     MOE_TRY(to_status(launch_rmsnorm(x, l == 0 ? nullptr : out, x_hat, desc->n_tokens,
                                      desc->hidden, desc->act_dtype, desc->rms_eps, true, stream)));

@@ -1,0 +1,198 @@
+// Device helpers shared by the decode kernels (three-kernel path and the
+// persistent chain kernel): fp16 packing and dot products, DPP wave
+// reductions, exact wave top-k, and the blob tiling constants.
+#pragma once
+
+#include "moe_internal.h"
+
+namespace moe {
+namespace dec {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c,
+                                false);
+}
+
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const _Float16 l = (_Float16)lo, h = (_Float16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, l) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
+}
+__device__ __forceinline__ float f16lo(uint32_t p) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(p & 0xFFFFu));
+}
+__device__ __forceinline__ float f16hi(uint32_t p) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(p >> 16));
+}
+
+// DPP controls (gfx9): row_shr:n = 0x110+n, row_bcast:15 = 0x142, row_bcast:31 = 0x143.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f(float old, float src) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                                               __builtin_bit_cast(int, src), CTRL,
+                                                               ROW_MASK, 0xF, false));
+}
+
+// Sum over the 64 lanes, result returned in every lane.
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_f<0x111, 0xF>(0.0f, v);
+  v += dpp_f<0x112, 0xF>(0.0f, v);
+  v += dpp_f<0x114, 0xF>(0.0f, v);
+  v += dpp_f<0x118, 0xF>(0.0f, v);
+  v += dpp_f<0x142, 0xA>(0.0f, v);
+  v += dpp_f<0x143, 0xC>(0.0f, v);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+__device__ __forceinline__ uint32_t mbcnt(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Monotonic map fp32 -> uint32 (larger value -> larger key); -0 maps as +0.
+__device__ __forceinline__ uint32_t order_key(float v) {
+  const uint32_t b = __float_as_uint(v + 0.0f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+constexpr int kMaxPerLane = MOE_MAX_EXPERTS / 64;
+
+// Exact top-k of one token's E logits by one wave, ties to the lower index,
+// ordered by logit descending; renormalised softmax weights over the k.
+//   1. every lane keeps the max key of its logits; a ballot binary search
+//      finds tau = the k-th largest lane maximum (k lane maxima are >= tau,
+//      so every top-k logit is >= tau);
+//   2. the logits >= tau are compacted into LDS (usually about k of them);
+//   3. each candidate's rank is counted against all candidates.
+// More than 64 candidates (massive ties) take k rounds of wave argmax.
+// Writes sel_idx[0..k), sel_w[0..k) and *gamma (if has_gate) in LDS.
+template <int MPL = kMaxPerLane>
+__device__ __forceinline__ void wave_topk(const float* __restrict__ logits, int E, int k, bool has_gate,
+                          int32_t* sel_idx, float* sel_val, float* sel_w, float* gamma,
+                          uint32_t* cand_key, int32_t* cand_idx, float* cand_val) {
+  const int lane = threadIdx.x & 63;
+  const int per = (E + 63) >> 6;
+  float v[MPL];
+  uint32_t u[MPL];
+  uint32_t M = 0;
+#pragma unroll
+  for (int i = 0; i < MPL; ++i) {
+    const int e = i * 64 + lane;
+    const bool ok = i < per && e < E;
+    v[i] = ok ? logits[e] : -INFINITY;
+    u[i] = ok ? order_key(v[i]) : 0u;
+    M = max(M, u[i]);
+  }
+  float gate_logit = 0.f;
+  if (has_gate) gate_logit = logits[E];
+  // 1. threshold on the lane maxima
+  uint32_t tau = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = tau | (1u << bit);
+    if (__popcll(ballot(M >= c)) >= (unsigned)k) tau = c;
+  }
+  // 2. compact the candidates
+  uint32_t base = 0;
+#pragma unroll
+  for (int i = 0; i < MPL; ++i) {
+    if (i < per) {
+      const bool c = u[i] >= tau && (i * 64 + lane) < E;
+      const uint64_t m = ballot(c);
+      if (c) {
+        const uint32_t pos = base + mbcnt(m);
+        if (pos < 64) {
+          cand_key[pos] = u[i];
+          cand_idx[pos] = i * 64 + lane;
+          cand_val[pos] = v[i];
+        }
+      }
+      base += (uint32_t)__popcll(m);
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_s_waitcnt(0);
+  const int ncand = (int)base;
+  if (ncand <= 64) {
+    // 3. rank among candidates (key descending, index ascending)
+    if (lane < ncand) {
+      const uint32_t K = cand_key[lane];
+      const int I = cand_idx[lane];
+      int rank = 0;
+      for (int j0 = 0; j0 < ncand; j0 += 4) {
+        const uint4 kk = *reinterpret_cast<const uint4*>(cand_key + j0);
+        const int4 ii = *reinterpret_cast<const int4*>(cand_idx + j0);
+        const uint32_t ks[4] = {kk.x, kk.y, kk.z, kk.w};
+        const int is[4] = {ii.x, ii.y, ii.z, ii.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          rank += (j0 + q < ncand && (ks[q] > K || (ks[q] == K && is[q] < I))) ? 1 : 0;
+      }
+      if (rank < k) {
+        sel_idx[rank] = I;
+        sel_val[rank] = cand_val[lane];
+      }
+    }
+  } else {
+    // k rounds of (max key, lowest index) over the whole wave
+    uint32_t taken = 0u;
+    for (int r = 0; r < k; ++r) {
+      uint32_t bk = 0;
+      int bi = 0x7FFFFFFF;
+#pragma unroll
+      for (int i = 0; i < MPL; ++i) {
+        const int e = i * 64 + lane;
+        if (i < per && e < E && !((taken >> i) & 1u)) {
+          if (u[i] > bk || (u[i] == bk && e < bi)) {
+            bk = u[i];
+            bi = e;
+          }
+        }
+      }
+      // wave max of bk, then min index among lanes holding it
+      uint32_t mk = bk;
+      for (int off = 32; off >= 1; off >>= 1) mk = max(mk, (uint32_t)__shfl_xor((int)mk, off, 64));
+      int mi = (bk == mk) ? bi : 0x7FFFFFFF;
+      for (int off = 32; off >= 1; off >>= 1) mi = min(mi, __shfl_xor(mi, off, 64));
+      if ((mi & 63) == lane) {
+        taken |= 1u << (mi >> 6);
+        float sv = 0.f;
+#pragma unroll
+        for (int i = 0; i < MPL; ++i)
+          if (i == (mi >> 6)) sv = v[i];
+        sel_idx[r] = mi;
+        sel_val[r] = sv;
+      }
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_s_waitcnt(0);
+  // renormalised softmax over the selected logits (fixed-order DPP sum)
+  {
+    const float l0 = sel_val[0];
+    const float e = lane < k ? expf(sel_val[lane] - l0) : 0.0f;
+    const float den = wave_sum_dpp(e);
+    if (lane < k) sel_w[lane] = e / den;
+  }
+  if (lane == 0 && has_gate) *gamma = 1.0f / (1.0f + expf(-gate_logit));
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_s_waitcnt(0);
+}
+
+
+template <int BITS>
+struct GuCfg {
+  static constexpr int CC = BITS == 4 ? 32 : 16;  // columns per lane chunk
+  static constexpr int GPK = BITS == 4 ? 2 : 1;
+  static constexpr int KBC = kRowBytes * (8 / BITS);
+  // staged activation dwords per chunk, padded so the 4 chunks a wave reads
+  // at once fall in distinct LDS banks
+  static constexpr int XS = BITS == 4 ? 20 : 8;
+};
+
+constexpr int kMaxKbPerWave = 8;
+
+}  // namespace dec
+}  // namespace moe

@@ -59,7 +59,8 @@ inline BlobLayout make_layout(int bits, int hidden, int inter) {
 
 // Workspace plan (byte offsets into the caller's workspace).
 struct WsPlan {
-  size_t logits, idx, w, gamma, h, partial, counts, offsets, pairs, masks, blkoff, xprep;
+  size_t logits, idx, w, gamma, h, partial, counts, offsets, pairs, slots, masks, blkoff, xprep;
+  size_t xw, lw, hw, ctr;  // persistent-chain exchange words (batch 1)
   size_t total;
   bool bucketed;
 };
@@ -86,9 +87,16 @@ inline WsPlan make_ws_plan(const moe_layer_desc& d) {
   p.counts = take(sizeof(int32_t) * (E + 1));
   p.offsets = take(sizeof(int32_t) * (E + 2));
   p.pairs = take(sizeof(int32_t) * T * k);
+  p.slots = take(sizeof(int32_t) * MOE_MAX_TOP_K);
   p.masks = take(p.bucketed ? sizeof(uint64_t) * nblk * E : 0);
   p.blkoff = take(p.bucketed ? sizeof(int32_t) * nblk * E : 0);
   p.xprep = take(0);
+  if (T == 1) {
+    p.xw = take(sizeof(uint64_t) * (H / 2));
+    p.lw = take(sizeof(uint64_t) * (E + 1));
+    p.hw = take(sizeof(uint64_t) * (k * I + Is));
+    p.ctr = take(sizeof(uint32_t) * 2);
+  }
   p.total = o;
   return p;
 }
@@ -171,6 +179,66 @@ struct ExpertArgs {
   bool has_shared;
 };
 hipError_t launch_experts(const ExpertArgs& a, hipStream_t s);
+
+// Batch-1 bf16 decode fast path: three kernels per layer (router with an
+// optional fused RMSNorm; top-k + gate/up; down + combine with an optional
+// fused residual add).
+struct DecodeArgs {
+  const uint16_t* x_in;          // router input: residual stream (do_norm) or x_hat
+  uint16_t* x_hat;               // [H] normalised input (written when do_norm)
+  const float* router_w;
+  const float* router_bias;
+  const float* shared_gate_w;    // null without shared expert
+  float* logits;                 // ws
+  int32_t* idx;                  // ws routing
+  float* w;
+  float* gamma;
+  int32_t* slots;                // ws: slab slot of each selected expert
+  float* h;                      // ws
+  const uint8_t* slab;
+  const int32_t* slot_table;
+  int64_t stride;
+  const uint8_t* shared_blob;
+  uint16_t* out;                 // [H]
+  uint16_t* x_res;               // residual stream to update, or null
+  BlobLayout L, Ls;
+  int H, E, k, bits;
+  float eps;
+  bool do_norm, has_shared;
+};
+bool decode_fast_supported(int T, int act, int H, int k, int E, int bits, int I, int Is,
+                           bool has_shared);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+
+// Persistent decode chain (one cooperative launch for all layers).
+struct ChainParams {
+  uint16_t* x;                   // [H] residual stream in/out
+  uint16_t* x_hat;               // [H] last layer's normalised input
+  uint16_t* out;                 // [H] last layer's output
+  const float* router_w;         // [L][E][H]
+  const float* router_bias;      // [L][E] or null
+  const uint8_t* slab;
+  int64_t stride;
+  const int32_t* slot_tables;    // [L][E]
+  const uint8_t* shared_blobs;   // layer l at + l * shared_stride
+  int64_t shared_stride;
+  int L, H, E, k, I, Is, has_shared, bits_;
+  float eps;
+  int64_t gu_unit_r, gu_tile_r, d_off_r, d_unit_r, d_tile_r;
+  int64_t gu_unit_s, gu_tile_s, d_off_s, d_unit_s, d_tile_s, sg_off;
+  uint64_t* xw;                  // [H/2] exchange words (epoch | 2 x bf16)
+  uint64_t* lw;                  // [E+1] exchange words (epoch | fp32 logit)
+  uint64_t* hw;                  // [k*I + Is] exchange words (epoch | fp32 h)
+  uint32_t* ctr;                 // last epoch used
+  uint32_t* err;                 // bit 0: an exchange poll expired
+  int32_t* r_idx;                // last layer's routing
+  float* r_w;
+  float* r_gamma;
+};
+int chain_grid(int device);
+bool chain_supported(int nwg, int T, int act, int H, int E, int k, int bits, int I, int Is,
+                     bool has_shared);
+hipError_t launch_chain(const ChainParams& p, int nwg, hipStream_t s);
 
 hipError_t launch_rmsnorm(void* x, const void* out, void* x_hat, int T, int H, int act,
                           float eps, bool do_norm, hipStream_t s);

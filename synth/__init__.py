@@ -121,18 +121,59 @@ def normal_f64(key: int, n: int) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# optional C implementation of the same definition (synth_host.c), used for
+# speed when built; tests check it bit-equal to the numpy definition above.
+
+_clib = None
+
+
+def _host_lib():
+    global _clib
+    if _clib is None:
+        import ctypes
+        import os
+        path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsynth_host.so")
+        if not os.path.exists(path):
+            _clib = False
+        else:
+            h = ctypes.CDLL(path)
+            h.synth_host_codes.argtypes = [ctypes.c_uint64, ctypes.c_int64, ctypes.c_int,
+                                           ctypes.c_void_p]
+            h.synth_host_uniform_bf16.argtypes = [ctypes.c_uint64, ctypes.c_int64, ctypes.c_float,
+                                                  ctypes.c_float, ctypes.c_void_p]
+            _clib = h
+    return _clib or None
+
+
+def codes_c(key: int, n: int, bits: int) -> np.ndarray:
+    out = np.empty(n, np.uint8)
+    _host_lib().synth_host_codes(key, n, bits, out.ctypes.data)
+    return out
+
+
+def uniform_bf16_c(key: int, n: int, lo: float, hi: float) -> np.ndarray:
+    out = np.empty(n, np.uint16)
+    _host_lib().synth_host_uniform_bf16(key, n, lo, hi, out.ctypes.data)
+    return out
+
+
+# ---------------------------------------------------------------------------
 # logical tensors of one configuration
 
 
 def quant_codes(seed: int, tensor: int, layer: int, expert: int, rows: int, cols: int,
                 bits: int) -> np.ndarray:
     key = stream_key(seed, tensor, layer, expert)
+    if _host_lib() is not None:
+        return codes_c(key, rows * cols, bits).reshape(rows, cols)
     return codes_from_draws(draws(key, 0, rows * cols), bits).reshape(rows, cols)
 
 
 def quant_sb(seed: int, tensor: int, layer: int, expert: int, rows: int, groups: int,
              lo: float, hi: float) -> np.ndarray:
     key = stream_key(seed, tensor, layer, expert)
+    if _host_lib() is not None:
+        return uniform_bf16_c(key, rows * groups, lo, hi).reshape(rows, groups)
     return uniform_bf16_from_draws(draws(key, 0, rows * groups), lo, hi).reshape(rows, groups)
 
 

@@ -7,6 +7,18 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(HERE, "libsynth.so")
+HOST_LIB = os.path.join(HERE, "libsynth_host.so")
+
+
+def build_host(verbose: bool = False) -> str:
+    tmp = HOST_LIB + ".tmp"
+    cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared",
+           os.path.join(HERE, "synth_host.c"), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, HOST_LIB)
+    return HOST_LIB
 
 
 def build(verbose: bool = False) -> str:
@@ -19,6 +31,7 @@ def build(verbose: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    build_host(verbose)
     return LIB
 
 

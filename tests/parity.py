@@ -9,7 +9,7 @@
   <= 2e-2 * rms(out) for bf16, rms over the layer's [T x H] output, with
   the error counted beyond the unit roundoff of storing the output in the
   activation dtype (an output element of 20 rms stored in bf16 alone carries
-  up to 20 * 2^-9 = 0.04 rms of rounding error).
+  up to 20 * 2^-8 = 0.08 rms of rounding error).
 """
 from __future__ import annotations
 
@@ -68,14 +68,14 @@ def check_routing(idx_gpu, w_gpu, ref, k, gamma_gpu=None, gamma_ref=None):
 def check_out(got, ref, act, what=""):
     """max|got - ref| <= tol * rms(ref), where the error is measured beyond the
     rounding that storing the output in the activation dtype must add:
-    |got - ref| - u * |ref|  with u = 2^-9 (bf16) or 2^-24 (fp32), the unit
+    |got - ref| - u * |ref|  with u = 2^-8 (bf16, 8 significant bits) or 2^-24 (fp32), the unit
     roundoff of round-to-nearest storage."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, (got.shape, ref.shape)
     assert np.all(np.isfinite(got)), what
     rms = float(np.sqrt(np.mean(ref * ref)))
-    u = 2.0 ** -9 if act == "bf16" else 2.0 ** -24
+    u = 2.0 ** -8 if act == "bf16" else 2.0 ** -24
     raw = np.abs(got - ref)
     err = np.maximum(raw - u * np.abs(ref), 0.0)
     tol = OUT_TOL[act] * rms

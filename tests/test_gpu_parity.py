@@ -204,50 +204,73 @@ def test_tiny_layer_parity():
 @pytest.mark.parametrize("cfgname,check_layers", [("decode_35b", (0, 1, 19, 39)),
                                                   ("decode_80b", (0, 1, 30, 47))])
 def test_decode_chain_parity(cfgname, check_layers):
-    """Batch-1 decode through every layer of the chain, teacher-forced:
-    layer l of the oracle takes the GPU's own x_hat_l."""
+    """Batch-1 decode through every layer of the chain, teacher-forced: the
+    chain entry point is called one layer at a time (the kernels the benchmark
+    runs), and layer l of the oracle takes the GPU's own x_l / x_hat_l."""
     moe, wl = _moe(), _wl()
     cfg = configs.CONFIGS[cfgname]
     say(f"[chain] {cfgname}: building {cfg.layers} layers")
     w = wl.Workload(cfg)
     d = w.desc
+    T, k = 1, cfg.top_k
     x0_np = synth.activations(cfg)
     x = wl.act_tensor(cfg, x0_np)
     xh = torch.empty_like(x)
     out = torch.empty_like(x)
     ws = w.workspace()
+    pi, pw, pg = moe.moe_workspace_routing(d, ws)
+    base = ws.data_ptr()
     for i in range(cfg.layers):
         checking = i in check_layers
-        if checking:
-            x_before = x.clone()
-            out_prev = out.clone() if i > 0 else None
-        moe.moe_rmsnorm(d, x, out if i > 0 else None, xh)
+        x_before = x.clone() if checking else None
         rw, rb, st, sh = w.layer_args(i)
-        if checking:
-            say(f"  layer {i}")
-            torch.cuda.synchronize()
-            xb = wl.to_f64(x_before)
-            if out_prev is not None:
-                x_ref = oracle.chain_epilogue(xb, wl.to_f64(out_prev), cfg.act)
-                assert np.array_equal(wl.to_f64(x), x_ref), "residual"
-            xh_ref = oracle.chain_prologue(wl.to_f64(x), cfg.rms_eps, cfg.act)
-            ulp = np.abs(xh_ref) * 2.0 ** -7
-            assert np.all(np.abs(wl.to_f64(xh) - xh_ref) <= ulp + 1e-30), "rmsnorm"
-            o, idx, wt, g = run_layer(w, cfg, xh, i)
-            out.copy_(o)
-            check_layer(cfg, i, wl.to_f64(xh), o, idx, wt, g, f"{cfgname} layer {i}")
-        else:
-            moe.moe_layer_forward(d, xh, rw, rb, w.slab, st, sh, out, ws)
-    moe.moe_rmsnorm(d, x, out, xh)
+        moe.moe_chain_forward(d, 1, x, rw, rb, w.slab, st, sh, w.shared_stride, xh, out, ws)
+        if not checking:
+            continue
+        say(f"  layer {i}")
+        torch.cuda.synchronize()
+        xb = wl.to_f64(x_before)
+        xh_ref = oracle.chain_prologue(xb, cfg.rms_eps, cfg.act)
+        assert np.all(np.abs(wl.to_f64(xh) - xh_ref) <= np.abs(xh_ref) * 2.0 ** -7), "rmsnorm"
+        idx = ws[pi - base: pi - base + 4 * T * k].view(torch.int32).view(T, k)
+        wt = ws[pw - base: pw - base + 4 * T * k].view(torch.float32).view(T, k)
+        g = ws[pg - base: pg - base + 4 * T].view(torch.float32)
+        check_layer(cfg, i, wl.to_f64(xh), out, idx, wt, g, f"{cfgname} layer {i}")
+        x_ref = oracle.chain_epilogue(xb, wl.to_f64(out), cfg.act)
+        assert np.array_equal(wl.to_f64(x), x_ref), "residual"
     torch.cuda.synchronize()
-    # the chain entry point runs the same kernels: bit-equal final residual
-    say("  chain entry point")
+    # the whole chain in one call runs the same kernels: bit-equal residual
+    say("  chain entry point, all layers")
     xc = wl.act_tensor(cfg, x0_np)
     moe.moe_chain_forward(d, cfg.layers, xc, w.router_w, w.router_bias, w.slab, w.slot_tables,
                           w.shared, w.shared_stride, torch.empty_like(xc), torch.empty_like(xc), ws)
     torch.cuda.synchronize()
     assert torch.equal(xc, x)
     assert torch.isfinite(xc.float()).all()
+    # and a single layer through moe_layer_forward equals the oracle as well
+    rw, rb, st, sh = w.layer_args(0)
+    xh0 = wl.act_tensor(cfg, oracle.chain_prologue(x0_np, cfg.rms_eps, cfg.act).astype(np.float32))
+    o, idx, wt, g = run_layer(w, cfg, xh0, 0)
+    check_layer(cfg, 0, wl.to_f64(xh0), o, idx, wt, g, f"{cfgname} layer_forward")
+    del w
+    _free()
+
+
+def test_decode_massive_ties():
+    """All-zero router: every logit ties, so top-k must take experts 0..k-1
+    with weights 1/k (more ties than the fast candidate path holds)."""
+    moe, wl = _moe(), _wl()
+    cfg = configs.DECODE_35B
+    say("[ties] zero router, E=256")
+    w = wl.Workload(cfg, n_layers=1)
+    w.router_w.zero_()
+    x = wl.act_tensor(cfg, oracle.chain_prologue(synth.activations(cfg), 1e-6, "bf16").astype(np.float32))
+    out, idx, wt, g = run_layer(w, cfg, x)
+    assert idx[0].tolist() == list(range(cfg.top_k))
+    assert torch.allclose(wt[0], torch.full_like(wt[0], 1.0 / cfg.top_k), rtol=1e-6)
+    inp = oracle.LayerInputs(cfg, 0, overrides={"router_w": np.zeros((cfg.n_experts, cfg.hidden), np.float32)})
+    ref = oracle.oracle_layer(inp, wl.to_f64(x))
+    check_out(out.float().cpu().numpy(), ref["out"], cfg.act, "ties")
     del w
     _free()
 

@@ -77,3 +77,17 @@ def test_slot_table_permutation():
     assert np.array_equal(st, 2 * 256 + np.arange(256))
     sp = synth.slot_table(cfg, 2, permute_seed=9)
     assert sorted(sp.tolist()) == st.tolist() and not np.array_equal(sp, st)
+
+
+def test_c_generator_matches_numpy_definition():
+    import pytest
+    if synth._host_lib() is None:
+        pytest.skip("libsynth_host.so not built")
+    for bits in (4, 8):
+        key = synth.stream_key(5, synth.T_QDOWN, 3, 9)
+        ref = synth.codes_from_draws(synth.draws(key, 0, 100003), bits)
+        assert np.array_equal(synth.codes_c(key, 100003, bits), ref)
+    key = synth.stream_key(1, synth.T_BUP, 0, 4)
+    for lo, hi in ((synth.SCALE_LO, synth.SCALE_HI), (synth.BIAS_LO, synth.BIAS_HI)):
+        ref = synth.uniform_bf16_from_draws(synth.draws(key, 0, 70001), lo, hi)
+        assert np.array_equal(synth.uniform_bf16_c(key, 70001, lo, hi), ref)

@@ -104,8 +104,9 @@ class Workload:
         return self.router_w[i], rb, self.slot_tables[i], self.shared[i]
 
     def workspace(self, desc=None):
+        """Zero-filled workspace (the chain's exchange words must start at zero)."""
         n = moe.moe_workspace_bytes(desc or self.desc)
-        return torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
+        return torch.zeros(max(n, 256), dtype=torch.uint8, device=self.device)
 
 
 def act_tensor(cfg, x_np: np.ndarray, device="cuda"):
