@@ -85,6 +85,16 @@ __device__ __forceinline__ void poll_words(const uint64_t* base, int n, int tid,
 
 __device__ __forceinline__ float bf16r(float v) { return bf16_bits_to_f32(f32_to_bf16_bits(v)); }
 
+__device__ __forceinline__ void st_u32(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_u32(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_u64(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int BITS, int NIT>
 __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
   using C = GuCfg<BITS>;
@@ -121,7 +131,6 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
   const int NI = tiles_s + k * tiles_r;
   const int NH = k * I + (hsh ? Is : 0);      // h values per layer
   const int nchh = NH / CC;
-  float* hsum = hs + nchh * CP;
   // phase C: half-tile w (8 output rows)
   const bool has_c = w < H / 8;
   const int ctile = w >> 1, chalf = w & 1;
@@ -156,7 +165,8 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
     }
   };
   // gate/up of one 16-row tile from registers + staged x; h published
-  auto compute_gu = [&](uint64_t* hwl, int64_t hoff, uint32_t ep) {
+  // h exchange: one epoch-tagged word per h value
+  auto compute_gu = [&](int64_t hoff, int item, uint32_t ep) {
     float g = 0.f, u = 0.f;
 #pragma unroll
     for (int i = 0; i < NKW; ++i) {
@@ -208,8 +218,9 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
     if (tid < kRowTile) {
       const float gs = (red[0][tid][0] + red[1][tid][0]) + (red[2][tid][0] + red[3][tid][0]);
       const float us = (red[0][tid][1] + red[1][tid][1]) + (red[2][tid][1] + red[3][tid][1]);
-      st_word(hwl + hoff + tid, ep, __float_as_uint(silu_f32(gs) * us));
+      st_word(p.hw + hoff + tid, ep, __float_as_uint(silu_f32(gs) * us));
     }
+    (void)item;
     __syncthreads();
   };
 
@@ -219,7 +230,6 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
     const float* Wr = p.router_w + (int64_t)l * E * H;
     const uint8_t* sblob = p.shared_blobs + (int64_t)l * p.shared_stride;
     uint64_t* lwl = p.lw;
-    uint64_t* hwl = p.hw;
 
     // ---------------- prefetch (independent of x_l) ----------------
     float4 wr[NIT];
@@ -253,75 +263,75 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
     }
 
     // ---------------- A: input, RMSNorm, router ----------------
-    if (l == 0) {
-      for (int c = tid * 8; c < H; c += 256 * 8) {
-        const uint4 v = *reinterpret_cast<const uint4*>(p.x + c);
-        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+    {
+      // thread tid owns words tid + 256 m (bf16 pairs 2i, 2i+1); its sum of
+      // squares runs over them in a fixed order, so every workgroup gets
+      // the same bits whatever order the words arrive in
+      uint32_t xw4[H / 512];
+      if (l == 0) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          xs[c + 2 * q] = bf16_bits_to_f32(wv[q] & 0xFFFFu);
-          xs[c + 2 * q + 1] = bf16_bits_to_f32(wv[q] >> 16);
-        }
+        for (int m = 0; m < H / 512; ++m)
+          xw4[m] = *reinterpret_cast<const uint32_t*>(p.x + 2 * (tid + 256 * m));
+      } else {
+        poll_words<H / 512>(p.xw, H / 2, tid, 256, ep - 1u, p.err,
+                            [&](int i, uint32_t v) { xw4[(i - tid) >> 8] = v; });
       }
-    } else {
-      poll_words<4>(p.xw, H / 2, tid, 256, ep - 1u, p.err, [&](int i, uint32_t v) {
-        xs[2 * i] = bf16_bits_to_f32(v & 0xFFFFu);
-        xs[2 * i + 1] = bf16_bits_to_f32(v >> 16);
-      });
+      float ss = 0.f;
+#pragma unroll
+      for (int m = 0; m < H / 512; ++m) {
+        const int i = tid + 256 * m;
+        const float a = bf16_bits_to_f32(xw4[m] & 0xFFFFu), b = bf16_bits_to_f32(xw4[m] >> 16);
+        xs[2 * i] = a;
+        xs[2 * i + 1] = b;
+        ss += a * a + b * b;
+      }
+      ss = wave_sum_dpp(ss);
+      if (lane == 0) wsum[wave] = ss;
     }
 #pragma unroll
     for (int m = 0; m < kChainMaxExperts / 256; ++m)
       if (tid + 256 * m < E) slot_l[tid + 256 * m] = slot_r[m];
     __syncthreads();
-    {  // sum of squares in a fixed order (identical in every workgroup)
-      float ss = 0.f;
-      for (int c = tid * 8; c < H; c += 256 * 8) {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) ss += xs[c + q] * xs[c + q];
-      }
-      ss = wave_sum_dpp(ss);
-      if (lane == 0) wsum[wave] = ss;
-    }
-    __syncthreads();
     const float inv = 1.0f / sqrtf(((wsum[0] + wsum[1]) + (wsum[2] + wsum[3])) / (float)H + p.eps);
-    // x_hat: stage for the gate/up dot products; block 0 stores it
-    for (int ch = tid; ch < NCH; ch += 256) {
-      float xv[CC];
+    // x_hat: stage for the gate/up dot products (4 threads per chunk, each
+    // 8 columns for int4 / 4 for int8); block 0 stores it
+    {
+      constexpr int SUB = CC / 4;  // columns per thread
+      for (int t = tid; t < NCH * 4; t += 256) {
+        const int ch = t >> 2, jj = t & 3;
+        const int c0 = ch * CC + jj * SUB;
+        float xv[SUB];
 #pragma unroll
-      for (int q = 0; q < CC; ++q) xv[q] = bf16r(xs[ch * CC + q] * inv);
-      if (w == 0) {
+        for (int q = 0; q < SUB; ++q) xv[q] = bf16r(xs[c0 + q] * inv);
+        if (w == 0) {
 #pragma unroll
-        for (int q = 0; q < CC; q += 2)
-          *reinterpret_cast<uint32_t*>(p.x_hat + ch * CC + q) =
-              (uint32_t)f32_to_bf16_bits(xv[q]) | ((uint32_t)f32_to_bf16_bits(xv[q + 1]) << 16);
-      }
-      if constexpr (BITS == 4) {
-        float c = 0.f, s = 0.f;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const float* vv = xv + 8 * jj;
-          const uint32_t pa = pack_f16x2(vv[0], vv[4]);
-          const uint32_t pb = pack_f16x2(vv[1] * 0.0625f, vv[5] * 0.0625f);
-          const uint32_t pc = pack_f16x2(vv[2], vv[6]);
-          const uint32_t pf = pack_f16x2(vv[3] * 0.0625f, vv[7] * 0.0625f);
+          for (int q = 0; q < SUB; q += 2)
+            *reinterpret_cast<uint32_t*>(p.x_hat + c0 + q) =
+                (uint32_t)f32_to_bf16_bits(xv[q]) | ((uint32_t)f32_to_bf16_bits(xv[q + 1]) << 16);
+        }
+        float c, sx;
+        if constexpr (BITS == 4) {
+          const uint32_t pa = pack_f16x2(xv[0], xv[4]);
+          const uint32_t pb = pack_f16x2(xv[1] * 0.0625f, xv[5] * 0.0625f);
+          const uint32_t pc = pack_f16x2(xv[2], xv[6]);
+          const uint32_t pf = pack_f16x2(xv[3] * 0.0625f, xv[7] * 0.0625f);
           *reinterpret_cast<uint4*>(xp + ch * XS + jj * 4) = make_uint4(pa, pb, pc, pf);
-          c += f16lo(pa) + f16hi(pa) + f16lo(pb) + f16hi(pb) + f16lo(pc) + f16hi(pc) + f16lo(pf) +
-               f16hi(pf);
-          s += f16lo(pa) + f16hi(pa) + f16lo(pc) + f16hi(pc) +
+          c = f16lo(pa) + f16hi(pa) + f16lo(pb) + f16hi(pb) + f16lo(pc) + f16hi(pc) + f16lo(pf) +
+              f16hi(pf);
+          sx = f16lo(pa) + f16hi(pa) + f16lo(pc) + f16hi(pc) +
                16.0f * (f16lo(pb) + f16hi(pb) + f16lo(pf) + f16hi(pf));
+        } else {
+          const uint32_t p0 = pack_f16x2(xv[0], xv[1]), p1 = pack_f16x2(xv[2], xv[3]);
+          *reinterpret_cast<uint2*>(xp + ch * XS + jj * 2) = make_uint2(p0, p1);
+          c = f16lo(p0) + f16hi(p0) + f16lo(p1) + f16hi(p1);
+          sx = c;
         }
-        cs[ch] = make_float2(1024.0f * c, s);
-      } else {
-        float c = 0.f;
-        uint32_t pk[8];
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          pk[jj] = pack_f16x2(xv[2 * jj], xv[2 * jj + 1]);
-          c += f16lo(pk[jj]) + f16hi(pk[jj]);
-        }
-        *reinterpret_cast<uint4*>(xp + ch * XS) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-        *reinterpret_cast<uint4*>(xp + ch * XS + 4) = make_uint4(pk[4], pk[5], pk[6], pk[7]);
-        cs[ch] = make_float2(1024.0f * c, c);
+        // combine the 4 threads of the chunk (adjacent lanes), fixed order
+        c += __shfl_xor(c, 1, 64);
+        c += __shfl_xor(c, 2, 64);
+        sx += __shfl_xor(sx, 1, 64);
+        sx += __shfl_xor(sx, 2, 64);
+        if (jj == 0) cs[ch] = make_float2(1024.0f * c, sx);
       }
     }
     if (has_row) {
@@ -338,7 +348,7 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
     __syncthreads();
 
     // ---------------- B: shared tiles, top-k, routed tiles ----------------
-    if (item0 < tiles_s) compute_gu(hwl, (int64_t)k * I + item0 * kRowTile, ep);
+    if (item0 < tiles_s) compute_gu((int64_t)k * I + item0 * kRowTile, item0, ep);
     if (wave == 0) {
       poll_words<(kChainMaxExperts + 64) / 64>(lwl, E + hsh, lane, 64, ep, p.err,
                                              [&](int i, uint32_t v) { lg[i] = __uint_as_float(v); });
@@ -355,7 +365,22 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
       }
     }
     __syncthreads();
-    if (has_c) {  // routed down units of phase C, issued now
+    // routed gate/up tiles: loads of the first one go out before the down
+    // units of phase C (needed later)
+    int rj[2] = {-1, -1}, rt[2] = {0, 0};
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int item = s2 == 0 ? item0 : item1;
+      if (item >= tiles_s && item < NI) {
+        const int ii = item - tiles_s;
+        rj[s2] = ii / tiles_r;
+        rt[s2] = ii - rj[s2] * tiles_r;
+      }
+    }
+    if (rj[0] >= 0)
+      issue_gu(p.slab + (int64_t)slot_l[sel_idx[rj[0]]] * p.stride, rt[0], p.gu_unit_r,
+               p.gu_tile_r);
+    if (has_c) {  // routed down units of phase C
 #pragma unroll
       for (int i = 0; i < kMaxDownUnits; ++i) {
         const int uidx = hw + 8 * i;
@@ -371,36 +396,21 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
         }
       }
     }
-#pragma unroll 1
-    for (int s = 0; s < 2; ++s) {
-      const int item = s == 0 ? item0 : item1;
-      if (item >= tiles_s && item < NI) {
-        const int ii = item - tiles_s;
-        const int j = ii / tiles_r, tile = ii - j * tiles_r;
-        const uint8_t* blob = p.slab + (int64_t)slot_l[sel_idx[j]] * p.stride;
-        issue_gu(blob, tile, p.gu_unit_r, p.gu_tile_r);
-        compute_gu(hwl, (int64_t)j * I + tile * kRowTile, ep);
-      } else if (s == 1 && item < tiles_s) {
-        issue_gu(sblob, item, p.gu_unit_s, p.gu_tile_s);
-        compute_gu(hwl, (int64_t)k * I + item * kRowTile, ep);
-      }
+    if (rj[0] >= 0) compute_gu((int64_t)rj[0] * I + rt[0] * kRowTile, item0, ep);
+    if (rj[1] >= 0) {
+      issue_gu(p.slab + (int64_t)slot_l[sel_idx[rj[1]]] * p.stride, rt[1], p.gu_unit_r,
+               p.gu_tile_r);
+      compute_gu((int64_t)rj[1] * I + rt[1] * kRowTile, item1, ep);
+    } else if (item1 < tiles_s) {
+      issue_gu(sblob, item1, p.gu_unit_s, p.gu_tile_s);
+      compute_gu((int64_t)k * I + item1 * kRowTile, item1, ep);
     }
 
     // ---------------- C: down + combine + residual ----------------
-    poll_words<24>(hwl, NH, tid, 256, ep, p.err, [&](int i, uint32_t v) {
+    poll_words<24>(p.hw, NH, tid, 256, ep, p.err, [&](int i, uint32_t v) {
       const int ch = i / CC;
       hs[ch * CP + (i - ch * CC)] = __uint_as_float(v);
     });
-    __syncthreads();
-    for (int ch = tid; ch < nchh; ch += 256) {
-      float s = 0.f;
-#pragma unroll
-      for (int q = 0; q < CC; q += 4) {
-        const float4 v = *reinterpret_cast<const float4*>(hs + ch * CP + q);
-        s += (v.x + v.y) + (v.z + v.w);
-      }
-      hsum[ch] = s;
-    }
     __syncthreads();
     if (has_c) {
       float acc = 0.f;
@@ -420,7 +430,7 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
           const int ch = (hb + kb * KBC) / CC + c4;
           const float* hv = hs + ch * CP;
           const uint32_t d[4] = {dq[i].x, dq[i].y, dq[i].z, dq[i].w};
-          float pp = 0.f;
+          float pp = 0.f, hsm = 0.f;
           if constexpr (BITS == 4) {
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
@@ -431,6 +441,7 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
                     (float)((lo >> 8) & 0xFF) * a.z + (float)((hi >> 8) & 0xFF) * a.w +
                     (float)((lo >> 16) & 0xFF) * b.x + (float)((hi >> 16) & 0xFF) * b.y +
                     (float)(lo >> 24) * b.z + (float)(hi >> 24) * b.w;
+              hsm += ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
             }
           } else {
 #pragma unroll
@@ -438,10 +449,11 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
               const float4 a = *reinterpret_cast<const float4*>(hv + 4 * m);
               pp += (float)(d[m] & 0xFF) * a.x + (float)((d[m] >> 8) & 0xFF) * a.y +
                     (float)((d[m] >> 16) & 0xFF) * a.z + (float)(d[m] >> 24) * a.w;
+              hsm += (a.x + a.y) + (a.z + a.w);
             }
           }
           const float sc = bf16_bits_to_f32(dsb[i] & 0xFFFFu), bi = bf16_bits_to_f32(dsb[i] >> 16);
-          acc += dw[i] * (sc * pp + bi * hsum[ch]);
+          acc += dw[i] * (sc * pp + bi * hsm);
         }
       }
       acc += __shfl_xor(acc, 1, 64);
@@ -495,7 +507,7 @@ bool chain_supported(int nwg, int T, int act, int H, int E, int k, int bits, int
   const int kbc = kRowBytes * (8 / bits);
   if (E + (has_shared ? 1 : 0) > 4 * nwg) return false;
   const int NI = (has_shared ? Is / kRowTile : 0) + k * (I / kRowTile);
-  if (NI > 2 * nwg) return false;
+  if (NI > 2 * nwg || NI > 1024) return false;
   if (H / 8 > nwg) return false;
   const int n_units = k * (I / kbc) + (has_shared ? Is / kbc : 0);
   if (n_units > 8 * (bits == 4 ? max_down_units<4>() : max_down_units<8>())) return false;

@@ -46,6 +46,30 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t old, uint32_t src) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)src, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Max over the 64 lanes (idempotent, so lanes without a DPP source keep
+// their own value), result in every lane.
+__device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
+  v = max(v, dpp_u<0x111, 0xF>(v, v));
+  v = max(v, dpp_u<0x112, 0xF>(v, v));
+  v = max(v, dpp_u<0x114, 0xF>(v, v));
+  v = max(v, dpp_u<0x118, 0xF>(v, v));
+  v = max(v, dpp_u<0x142, 0xA>(v, v));
+  v = max(v, dpp_u<0x143, 0xC>(v, v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Waits for this wave's LDS operations only (vmcnt and expcnt left open).
+__device__ __forceinline__ void lds_wave_sync() {
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_wave_barrier();
+}
+
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
 __device__ __forceinline__ uint32_t mbcnt(uint64_t m) {
@@ -62,9 +86,9 @@ constexpr int kMaxPerLane = MOE_MAX_EXPERTS / 64;
 
 // Exact top-k of one token's E logits by one wave, ties to the lower index,
 // ordered by logit descending; renormalised softmax weights over the k.
-//   1. every lane keeps the max key of its logits; a ballot binary search
-//      finds tau = the k-th largest lane maximum (k lane maxima are >= tau,
-//      so every top-k logit is >= tau);
+//   1. every lane keeps the max key of its logits; k rounds of a wave max
+//      (removing the winning lanes) give tau <= the k-th largest lane
+//      maximum, so at least k logits are >= tau and every top-k logit is;
 //   2. the logits >= tau are compacted into LDS (usually about k of them);
 //   3. each candidate's rank is counted against all candidates.
 // More than 64 candidates (massive ties) take k rounds of wave argmax.
@@ -90,9 +114,12 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ logits, int 
   if (has_gate) gate_logit = logits[E];
   // 1. threshold on the lane maxima
   uint32_t tau = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t c = tau | (1u << bit);
-    if (__popcll(ballot(M >= c)) >= (unsigned)k) tau = c;
+  {
+    uint32_t Mr = M;
+    for (int r = 0; r < k; ++r) {
+      tau = wave_max_dpp(Mr);
+      if (Mr == tau) Mr = 0u;
+    }
   }
   // 2. compact the candidates
   uint32_t base = 0;
@@ -112,8 +139,7 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ logits, int 
       base += (uint32_t)__popcll(m);
     }
   }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_s_waitcnt(0);
+  lds_wave_sync();
   const int ncand = (int)base;
   if (ncand <= 64) {
     // 3. rank among candidates (key descending, index ascending)
@@ -167,8 +193,7 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ logits, int 
       }
     }
   }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_s_waitcnt(0);
+  lds_wave_sync();
   // renormalised softmax over the selected logits (fixed-order DPP sum)
   {
     const float l0 = sel_val[0];
@@ -177,8 +202,7 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ logits, int 
     if (lane < k) sel_w[lane] = e / den;
   }
   if (lane == 0 && has_gate) *gamma = 1.0f / (1.0f + expf(-gate_logit));
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_s_waitcnt(0);
+  lds_wave_sync();
 }
 
 
