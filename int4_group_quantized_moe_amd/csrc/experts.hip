@@ -710,6 +710,38 @@ hipError_t launch_experts_t(const ExpertArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(bucket_scatter_kernel, dim3(nblk), dim3(64), 0, s, a.topk_idx, masks, blkoff,
                      pairs, a.T, a.E, a.k);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.mfma) {
+    PrefillArgs pa{};
+    pa.x = reinterpret_cast<const uint16_t*>(a.x);
+    pa.pairs = pairs;
+    pa.counts = counts;
+    pa.offsets = offsets;
+    pa.topk_w = a.topk_w;
+    pa.gamma = a.gamma;
+    pa.slab = a.slab;
+    pa.slot_table = a.slot_table;
+    pa.stride = a.stride;
+    pa.shared_blob = a.shared_blob;
+    pa.h = reinterpret_cast<uint16_t*>(h);
+    pa.partial = partial;
+    pa.xsum = reinterpret_cast<float*>(a.ws + P.xsum);
+    pa.hsum = reinterpret_cast<float*>(a.ws + P.hsum);
+    pa.out = a.out;
+    pa.tiles = reinterpret_cast<int32_t*>(a.ws + P.tiles);
+    pa.ntiles = reinterpret_cast<int32_t*>(a.ws + P.ntiles);
+    pa.max_tiles = P.max_tiles;
+    pa.L = a.L;
+    pa.Ls = a.Ls;
+    pa.T = a.T;
+    pa.H = a.H;
+    pa.E = a.E;
+    pa.k = a.k;
+    pa.I = a.L.inter;
+    pa.Is = Is;
+    pa.bits = a.bits;
+    pa.has_shared = a.has_shared;
+    return launch_prefill(pa, s);
+  }
   hipLaunchKernelGGL((gateup_kernel<BITS, ACT>), dim3(tiles_gu, a.E + hs), dim3(256), lds_gu, s,
                      a.x, a.topk_idx, a.slab, a.slot_table, a.stride, a.shared_blob, counts,
                      offsets, pairs, h, a.T, a.H, a.E, a.k, a.L.inter, Is, a.L.gu_unit,

@@ -14,7 +14,8 @@ constexpr int kRowTile = 16;         // rows per tile in both blob sections
 constexpr int kRowBytes = 64;        // code bytes per row per k-block
 constexpr int kCodeBlockBytes = kRowTile * kRowBytes;  // 1 KiB
 constexpr int kGroup = 64;
-constexpr int kDecodeMaxTokens = 8;  // up to this many tokens: per-pair GEMV path
+constexpr int kDecodeMaxTokens = 8;    // up to this many tokens: per-pair GEMV path
+constexpr int kPrefillMinTokens = 256;  // from this many (bf16): MFMA grouped GEMMs
 
 inline int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
@@ -60,7 +61,10 @@ inline BlobLayout make_layout(int bits, int hidden, int inter) {
 // Workspace plan (byte offsets into the caller's workspace).
 struct WsPlan {
   size_t logits, idx, w, gamma, h, partial, counts, offsets, pairs, slots, masks, blkoff, xprep;
+  size_t xsum, hsum;  // grouped-GEMM path: per-group sums of x_hat and of h
   size_t xw, lw, hw, ctr;  // persistent-chain exchange words (batch 1)
+  size_t tiles, ntiles;    // grouped-GEMM tile list (large batches)
+  int max_tiles;
   size_t total;
   bool bucketed;
 };
@@ -91,6 +95,11 @@ inline WsPlan make_ws_plan(const moe_layer_desc& d) {
   p.masks = take(p.bucketed ? sizeof(uint64_t) * nblk * E : 0);
   p.blkoff = take(p.bucketed ? sizeof(int32_t) * nblk * E : 0);
   p.xprep = take(0);
+  p.xsum = take(p.bucketed ? sizeof(float) * T * (H / kGroup) : 0);
+  p.hsum = take(p.bucketed ? sizeof(float) * (T * k * (I / kGroup) + T * (Is / kGroup)) : 0);
+  p.max_tiles = (int)((T * k + T) / 128 + E + 2);
+  p.tiles = take(p.bucketed ? sizeof(int32_t) * 2 * p.max_tiles : 0);
+  p.ntiles = take(p.bucketed ? sizeof(int32_t) : 0);
   if (T == 1) {
     p.xw = take(sizeof(uint64_t) * (H / 2));
     p.lw = take(sizeof(uint64_t) * (E + 1));
@@ -177,8 +186,36 @@ struct ExpertArgs {
   BlobLayout Ls;                 // shared expert
   int T, H, E, k, act, bits;
   bool has_shared;
+  bool mfma;                     // large batch: grouped GEMMs on MFMA
 };
 hipError_t launch_experts(const ExpertArgs& a, hipStream_t s);
+
+// Grouped-GEMM (MFMA) experts for large batches, after bucketing.
+struct PrefillArgs {
+  const uint16_t* x;
+  const int32_t* pairs;
+  const int32_t* counts;         // [E+1], counts[E] = T (shared)
+  const int32_t* offsets;
+  const float* topk_w;
+  const float* gamma;
+  const uint8_t* slab;
+  const int32_t* slot_table;
+  int64_t stride;
+  const uint8_t* shared_blob;
+  uint16_t* h;                   // per row: I bf16 high parts, then I bf16 low parts
+  float* xsum;                   // [T][H/64] group sums of x
+  float* hsum;                   // [T*k][I/64] then [T][Is/64] group sums of h
+  float* partial;                // fp32 [T*(k+1)*H]
+  void* out;
+  int32_t* tiles;
+  int32_t* ntiles;
+  int max_tiles;
+  BlobLayout L, Ls;
+  int T, H, E, k, I, Is, bits;
+  bool has_shared;
+};
+bool prefill_supported(int T, int act, int H, int I, int Is, bool has_shared);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 
 // Batch-1 bf16 decode fast path: three kernels per layer (router with an
 // optional fused RMSNorm; top-k + gate/up; down + combine with an optional

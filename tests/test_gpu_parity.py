@@ -410,3 +410,38 @@ def test_rmsnorm_parity():
     assert np.array_equal(wl.to_f64(x), x_ref)
     xh_ref = oracle.chain_prologue(x_ref, cfg.rms_eps, "bf16")
     assert np.all(np.abs(wl.to_f64(xh) - xh_ref) <= np.abs(xh_ref) * 2.0 ** -7)
+
+
+@pytest.mark.parametrize("T,k,bits", [(256, 2, 4), (300, 4, 4), (300, 3, 8), (1000, 16, 4)])
+def test_grouped_mfma_path_tiny(T, k, bits):
+    """bf16 batches of >= 256 tokens run the grouped MFMA GEMMs: ragged expert
+    buckets (partial 128-row tiles), int4 and int8, k up to E."""
+    wl = _wl()
+    cfg = configs.TINY.with_(n_tokens=T, top_k=k, bits=bits, act="bf16")
+    say(f"[mfma] tiny bf16 T={T} k={k} int{bits}")
+    w = wl.Workload(cfg, n_layers=1)
+    x_np = synth.activations(cfg)
+    x = wl.act_tensor(cfg, x_np)
+    out, idx, wt, g = run_layer(w, cfg, x)
+    check_layer(cfg, 0, x_np, out, idx, wt, g, f"mfma T={T} k={k} int{bits}")
+    del w
+    _free()
+
+
+@pytest.mark.parametrize("cfgname,T", [("batched_80b", 320), ("batched_80b_int8", 300)])
+def test_grouped_mfma_path_80b(cfgname, T):
+    """80B-shaped layer with a Zipf-skewed router (one bucket holds most tokens)
+    through the grouped MFMA GEMMs; sampled tokens against the oracle."""
+    wl = _wl()
+    cfg = configs.CONFIGS[cfgname].with_(n_tokens=T)
+    say(f"[mfma] {cfgname} T={T}")
+    w = wl.Workload(cfg, n_layers=1)
+    x_np = oracle.chain_prologue(synth.activations(cfg), cfg.rms_eps, "bf16").astype(np.float32)
+    x = wl.act_tensor(cfg, x_np)
+    out, idx, wt, g = run_layer(w, cfg, x)
+    counts = np.bincount(idx.cpu().numpy().ravel(), minlength=cfg.n_experts)
+    say(f"  largest bucket {counts.max()} tokens, {np.count_nonzero(counts)} experts used")
+    tok = np.array([0, 1, 77, 150, T - 2, T - 1])
+    check_layer(cfg, 0, x_np[tok], out[tok], idx[tok], wt[tok], g[tok], f"{cfgname} T={T}")
+    del w
+    _free()
