@@ -191,7 +191,8 @@ __global__ __launch_bounds__(256) void gateup_kernel(
     const uint8_t* __restrict__ shared_blob, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ pairs,
     float* __restrict__ h, int T, int H, int E, int k, int I, int Is, int64_t gu_unit_r,
-    int64_t gu_tile_r, int64_t gu_unit_s, int64_t gu_tile_s, int bucketed, int has_shared) {
+    int64_t gu_tile_r, int64_t gu_unit_s, int64_t gu_tile_s, int bucketed, int has_shared,
+    int min_rows) {
   constexpr int GPK = BITS == 4 ? 2 : 1;
   constexpr int CC = chunk_cols<BITS>();
   extern __shared__ uint8_t smem[];
@@ -225,7 +226,7 @@ __global__ __launch_bounds__(256) void gateup_kernel(
     }
   } else if (item < E) {
     n = counts[item];
-    if (n == 0) return;
+    if (n == 0 || n >= min_rows) return;  // empty, or on the MFMA grouped GEMMs
     start = offsets[item];
     blob = slab + (int64_t)slot_table[item] * stride;
     inter = I;
@@ -235,6 +236,7 @@ __global__ __launch_bounds__(256) void gateup_kernel(
     kind = 1;
   } else {
     n = T;
+    if (n >= min_rows) return;
     blob = shared_blob;
     inter = Is;
     unit_b = gu_unit_s;
@@ -422,7 +424,7 @@ __global__ __launch_bounds__(256) void down_bucket_kernel(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ pairs,
     const float* __restrict__ h, float* __restrict__ partial, int T, int H, int E, int k, int I,
     int Is, int64_t d_off_r, int64_t d_unit_r, int64_t d_tile_r, int64_t d_off_s,
-    int64_t d_unit_s, int64_t d_tile_s) {
+    int64_t d_unit_s, int64_t d_tile_s, int min_rows) {
   constexpr int GPK = BITS == 4 ? 2 : 1;
   constexpr int CC = chunk_cols<BITS>();
   constexpr int KBC = kRowBytes * (8 / BITS);
@@ -438,13 +440,14 @@ __global__ __launch_bounds__(256) void down_bucket_kernel(
   const bool shared = item >= E;
   if (!shared) {
     n = counts[item];
-    if (n == 0) return;
+    if (n == 0 || n >= min_rows) return;  // empty, or on the MFMA grouped GEMMs
     start = offsets[item];
     inter = I;
     tbase = slab + (int64_t)slot_table[item] * stride + d_off_r + (int64_t)tile * d_tile_r;
     unit_b = d_unit_r;
   } else {
     n = T;
+    if (n >= min_rows) return;
     inter = Is;
     tbase = shared_blob + d_off_s + (int64_t)tile * d_tile_s;
     unit_b = d_unit_s;
@@ -505,10 +508,19 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       int has_shared) {
   const int t = blockIdx.x;
   const int nj = k + has_shared;
-  for (int c = threadIdx.x; c < H; c += blockDim.x) {
-    float v = 0.f;
-    for (int j = 0; j < nj; ++j) v += partial[((int64_t)t * (k + 1) + j) * H + c];
-    store_act<ACT>(out, (int64_t)t * H + c, v);
+  for (int c = threadIdx.x * 4; c < H; c += 256 * 4) {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < nj; ++j) {
+      const float4 p = *reinterpret_cast<const float4*>(partial + ((int64_t)t * (k + 1) + j) * H + c);
+      v.x += p.x;
+      v.y += p.y;
+      v.z += p.z;
+      v.w += p.w;
+    }
+    store_act<ACT>(out, (int64_t)t * H + c + 0, v.x);
+    store_act<ACT>(out, (int64_t)t * H + c + 1, v.y);
+    store_act<ACT>(out, (int64_t)t * H + c + 2, v.z);
+    store_act<ACT>(out, (int64_t)t * H + c + 3, v.w);
   }
 }
 
@@ -691,7 +703,7 @@ hipError_t launch_experts_t(const ExpertArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((gateup_kernel<BITS, ACT>), dim3(tiles_gu, a.T * (a.k + hs)), dim3(256),
                        lds_gu, s, a.x, a.topk_idx, a.slab, a.slot_table, a.stride, a.shared_blob,
                        counts, offsets, pairs, h, a.T, a.H, a.E, a.k, a.L.inter, Is, a.L.gu_unit,
-                       a.L.gu_tile, a.Ls.gu_unit, a.Ls.gu_tile, 0, hs);
+                       a.L.gu_tile, a.Ls.gu_unit, a.Ls.gu_tile, 0, hs, 0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((down_decode_kernel<BITS, ACT>), dim3(a.L.n_tiles_d, a.T), dim3(256), 0, s,
                        a.topk_idx, a.topk_w, a.gamma, a.slab, a.slot_table, a.stride,
@@ -740,17 +752,20 @@ hipError_t launch_experts_t(const ExpertArgs& a, hipStream_t s) {
     pa.Is = Is;
     pa.bits = a.bits;
     pa.has_shared = a.has_shared;
-    return launch_prefill(pa, s);
+    pa.min_rows = kMfmaMinRows;
+    if ((e = launch_prefill(pa, s)) != hipSuccess) return e;
   }
+  // buckets below the MFMA threshold (all of them without the MFMA path)
+  const int min_rows = a.mfma ? kMfmaMinRows : 0x7FFFFFFF;
   hipLaunchKernelGGL((gateup_kernel<BITS, ACT>), dim3(tiles_gu, a.E + hs), dim3(256), lds_gu, s,
                      a.x, a.topk_idx, a.slab, a.slot_table, a.stride, a.shared_blob, counts,
                      offsets, pairs, h, a.T, a.H, a.E, a.k, a.L.inter, Is, a.L.gu_unit,
-                     a.L.gu_tile, a.Ls.gu_unit, a.Ls.gu_tile, 1, hs);
+                     a.L.gu_tile, a.Ls.gu_unit, a.Ls.gu_tile, 1, hs, min_rows);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((down_bucket_kernel<BITS>), dim3(a.L.n_tiles_d, a.E + hs), dim3(256), 0, s,
                      a.topk_w, a.gamma, a.slab, a.slot_table, a.stride, a.shared_blob, counts,
                      offsets, pairs, h, partial, a.T, a.H, a.E, a.k, a.L.inter, Is, a.L.d_off,
-                     a.L.d_unit, a.L.d_tile, a.Ls.d_off, a.Ls.d_unit, a.Ls.d_tile);
+                     a.L.d_unit, a.L.d_tile, a.Ls.d_off, a.Ls.d_unit, a.Ls.d_tile, min_rows);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((combine_kernel<ACT>), dim3(a.T), dim3(256), 0, s, partial, a.out, a.H, a.k,
                      hs);

@@ -15,7 +15,7 @@ constexpr int kRowBytes = 64;        // code bytes per row per k-block
 constexpr int kCodeBlockBytes = kRowTile * kRowBytes;  // 1 KiB
 constexpr int kGroup = 64;
 constexpr int kDecodeMaxTokens = 8;    // up to this many tokens: per-pair GEMV path
-constexpr int kPrefillMinTokens = 256;  // from this many (bf16): MFMA grouped GEMMs
+constexpr int kMfmaMinRows = 16;  // bf16 buckets of this many tokens run on the MFMA grouped GEMMs
 
 inline int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
@@ -210,11 +210,12 @@ struct PrefillArgs {
   int32_t* tiles;
   int32_t* ntiles;
   int max_tiles;
+  int min_rows;                  // buckets with fewer tokens are left to the GEMV kernels
   BlobLayout L, Ls;
   int T, H, E, k, I, Is, bits;
   bool has_shared;
 };
-bool prefill_supported(int T, int act, int H, int I, int Is, bool has_shared);
+bool prefill_supported(int act, int H, int I, int Is, bool has_shared);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 
 // Batch-1 bf16 decode fast path: three kernels per layer (router with an

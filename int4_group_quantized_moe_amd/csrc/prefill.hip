@@ -208,13 +208,14 @@ __device__ __forceinline__ TileInfo get_tile(const int32_t* tiles, const int32_t
 }
 
 // ---------------------------------------------------------------------------
-// tile list: every expert bucket (and the shared expert's T tokens as bucket
-// E) cut into tiles of kMT rows.  One workgroup.
+// tile list: every expert bucket of at least min_rows tokens (and the shared
+// expert's T tokens as bucket E) cut into tiles of kMT rows.  One workgroup.
 
 __global__ __launch_bounds__(1024) void tile_list_kernel(const int32_t* __restrict__ counts,
                                                          int32_t* __restrict__ tiles,
                                                          int32_t* __restrict__ ntiles, int E,
-                                                         int has_shared, int max_tiles) {
+                                                         int has_shared, int max_tiles,
+                                                         int min_rows) {
   __shared__ int wsum[16];
   __shared__ int carry_s;
   __shared__ int tbase[MOE_MAX_EXPERTS + 2];
@@ -224,7 +225,8 @@ __global__ __launch_bounds__(1024) void tile_list_kernel(const int32_t* __restri
   // exclusive scan of the per-bucket tile counts, 1024 buckets per pass
   for (int b0 = 0; b0 < n_b; b0 += 1024) {
     const int b = b0 + threadIdx.x;
-    const int c = b < n_b ? (counts[b] + kMT - 1) / kMT : 0;
+    const int nb = b < n_b ? counts[b] : 0;
+    const int c = nb >= min_rows ? (nb + kMT - 1) / kMT : 0;
     int v = c;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -244,7 +246,7 @@ __global__ __launch_bounds__(1024) void tile_list_kernel(const int32_t* __restri
   const int total = min(carry, max_tiles);
   if (threadIdx.x == 0) *ntiles = total;
   for (int b = threadIdx.x; b < n_b; b += 1024) {
-    const int c = (counts[b] + kMT - 1) / kMT;
+    const int c = counts[b] >= min_rows ? (counts[b] + kMT - 1) / kMT : 0;
     for (int i = 0; i < c; ++i) {
       const int t = tbase[b] + i;
       if (t < max_tiles) {
@@ -636,33 +638,11 @@ __global__ __launch_bounds__(256) void prefill_down_kernel(
       }
 }
 
-template <int ACT>
-__global__ __launch_bounds__(256) void combine_rows_kernel(const float* __restrict__ partial,
-                                                           void* __restrict__ out, int H, int k,
-                                                           int has_shared) {
-  const int t = blockIdx.x;
-  const int nj = k + has_shared;
-  for (int c = threadIdx.x * 4; c < H; c += 256 * 4) {
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < nj; ++j) {
-      const float4 p = *reinterpret_cast<const float4*>(partial + ((int64_t)t * (k + 1) + j) * H + c);
-      v.x += p.x;
-      v.y += p.y;
-      v.z += p.z;
-      v.w += p.w;
-    }
-    store_act<ACT>(out, (int64_t)t * H + c + 0, v.x);
-    store_act<ACT>(out, (int64_t)t * H + c + 1, v.y);
-    store_act<ACT>(out, (int64_t)t * H + c + 2, v.z);
-    store_act<ACT>(out, (int64_t)t * H + c + 3, v.w);
-  }
-}
-
 template <int BITS>
 hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s) {
   const int hs = a.has_shared ? 1 : 0;
   hipLaunchKernelGGL(tile_list_kernel, dim3(1), dim3(1024), 0, s, a.counts, a.tiles, a.ntiles,
-                     a.E, hs, a.max_tiles);
+                     a.E, hs, a.max_tiles, a.min_rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int G = a.H / kGroup;
@@ -682,9 +662,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s) {
                      a.E, a.k, a.I, a.Is, a.L.d_off, a.L.d_unit, a.L.d_tile, a.Ls.d_off,
                      a.Ls.d_unit, a.Ls.d_tile);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((combine_rows_kernel<MOE_ACT_BF16>), dim3(a.T), dim3(256), 0, s, a.partial,
-                     a.out, a.H, a.k, hs);
-  return hipGetLastError();
+return hipSuccess;
 }
 
 }  // namespace
@@ -695,8 +673,8 @@ int prefill_max_tiles(int T, int E, int k, bool has_shared) {
   return (int)(rows / kMT + E + (has_shared ? 1 : 0) + 1);
 }
 
-bool prefill_supported(int T, int act, int H, int I, int Is, bool has_shared) {
-  if (act != MOE_ACT_BF16 || T < kPrefillMinTokens) return false;
+bool prefill_supported(int act, int H, int I, int Is, bool has_shared) {
+  if (act != MOE_ACT_BF16) return false;
   if (H % 128 != 0 || I % kGroup != 0 || (has_shared && Is % kGroup != 0)) return false;
   return true;
 }

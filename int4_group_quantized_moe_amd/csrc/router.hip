@@ -13,6 +13,7 @@ namespace {
 constexpr int kRouterWaves = 4;     // rows per workgroup (one per wave)
 constexpr int kRouterMaxTT = 8;     // tokens per LDS chunk
 constexpr int kRouterMaxRegIt = 8;  // row cached in registers when H <= 64*4*8
+constexpr int kRouterMfmaMinTokens = 128;  // GEMM on the matrix cores from this batch size (bf16)
 
 // logits[t][r] = sum_c W[r][c] * x[t][c] (+ bias[r]) for rows r < E, and the
 // shared-gate logit w_sg . x[t] as row E when w_sg is given.
@@ -44,7 +45,9 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const void* __restrict
   }
   const float b = (active && r < E && bias != nullptr) ? bias[r] : 0.0f;
 
-  for (int t0 = 0; t0 < T; t0 += TT) {
+  // token chunks of TT are spread over blockIdx.y (strided when there are
+  // more chunks than workgroup rows)
+  for (int t0 = blockIdx.y * TT; t0 < T; t0 += gridDim.y * TT) {
     const int tt_n = min(TT, T - t0);
     __syncthreads();
     for (int i = threadIdx.x; i < tt_n * H; i += blockDim.x) {
@@ -156,12 +159,157 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   }
 }
 
+// ---------------------------------------------------------------------------
+// Large batches: the router as a GEMM on the matrix cores.  logits[t][e] for
+// e < E over 64-token x 64-expert tiles (4 waves, one 32x32 block each),
+// K staged 64 at a time.  Each fp32 router weight is split exactly into three
+// bf16 parts (8 significant bits each: w = w1 + w2 + w3, by truncation), so
+// that with bf16 activations every product is exact and only the fp32
+// accumulation rounds, as in the fp32 GEMV.
+
+typedef __bf16 rbf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t ru32x4 __attribute__((ext_vector_type(4)));
+typedef float rf32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kRouterTile = 64;
+constexpr int kRouterLdsRow = 72;  // 64 K columns + 8 bf16 padding
+
+__device__ __forceinline__ void split3_pair(float a, float b, uint32_t& p1, uint32_t& p2,
+                                            uint32_t& p3) {
+  const uint32_t ua = __float_as_uint(a) & 0xFFFF0000u, ub = __float_as_uint(b) & 0xFFFF0000u;
+  const float ra = a - __uint_as_float(ua), rb = b - __uint_as_float(ub);
+  const uint32_t va = __float_as_uint(ra) & 0xFFFF0000u, vb = __float_as_uint(rb) & 0xFFFF0000u;
+  const float sa = ra - __uint_as_float(va), sb = rb - __uint_as_float(vb);
+  p1 = (ua >> 16) | ub;
+  p2 = (va >> 16) | vb;
+  p3 = (__float_as_uint(sa) >> 16) | (__float_as_uint(sb) & 0xFFFF0000u);
+}
+
+__global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __restrict__ x,
+                                                          const float* __restrict__ W,
+                                                          const float* __restrict__ bias,
+                                                          float* __restrict__ logits, int T, int H,
+                                                          int E) {
+  __shared__ __align__(16) uint16_t A[2 * kRouterTile * kRouterLdsRow];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, half = lane >> 5;
+  const int t0 = blockIdx.y * kRouterTile, e0 = blockIdx.x * kRouterTile;
+  // staging: token row sr, 16 columns (2 x 16 bytes) per thread
+  const int sr = tid >> 2, sq = tid & 3;
+  const bool srow_ok = t0 + sr < T;
+  const uint16_t* xrow = x + (int64_t)(srow_ok ? t0 + sr : 0) * H + 16 * sq;
+  // B operand: expert row e, this lane's 32 K columns of each stage
+  const int e = e0 + 32 * wn + l32;
+  const bool e_ok = e < E;
+  const float* wrow = W + (int64_t)(e_ok ? e : 0) * H + 32 * half;
+  const int S = H / 64;
+
+  uint4 ra[2];
+  float4 rb[8];
+  auto load_stage = [&](int st) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      ra[q] = srow_ok ? reinterpret_cast<const uint4*>(xrow + st * 64)[q] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      rb[i] = e_ok ? reinterpret_cast<const float4*>(wrow + st * 64)[i]
+                   : make_float4(0.f, 0.f, 0.f, 0.f);
+  };
+  auto store_stage = [&](int buf) {
+    uint16_t* dst = A + buf * kRouterTile * kRouterLdsRow + sr * kRouterLdsRow + 16 * sq;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) *reinterpret_cast<uint4*>(dst + 8 * q) = ra[q];
+  };
+
+  rf32x16 acc = {};
+  load_stage(0);
+  store_stage(0);
+  __syncthreads();
+  for (int st = 0; st < S; ++st) {
+    float4 cb[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) cb[i] = rb[i];
+    if (st + 1 < S) load_stage(st + 1);
+    const uint16_t* As = A + (st & 1) * kRouterTile * kRouterLdsRow;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const ru32x4 a = *reinterpret_cast<const ru32x4*>(
+          As + (32 * wm + l32) * kRouterLdsRow + 32 * half + 8 * ks);
+      const float4 v0 = cb[2 * ks], v1 = cb[2 * ks + 1];
+      uint32_t p1[4], p2[4], p3[4];
+      split3_pair(v0.x, v0.y, p1[0], p2[0], p3[0]);
+      split3_pair(v0.z, v0.w, p1[1], p2[1], p3[1]);
+      split3_pair(v1.x, v1.y, p1[2], p2[2], p3[2]);
+      split3_pair(v1.z, v1.w, p1[3], p2[3], p3[3]);
+      const ru32x4 b1 = {p1[0], p1[1], p1[2], p1[3]};
+      const ru32x4 b2 = {p2[0], p2[1], p2[2], p2[3]};
+      const ru32x4 b3 = {p3[0], p3[1], p3[2], p3[3]};
+      const rbf16x8 av = __builtin_bit_cast(rbf16x8, a);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(rbf16x8, b3), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(rbf16x8, b2), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(rbf16x8, b1), acc, 0, 0, 0);
+    }
+    if (st + 1 < S) store_stage((st + 1) & 1);
+    __syncthreads();
+  }
+  if (!e_ok) return;
+  const float b = bias != nullptr ? bias[e] : 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int t = t0 + 32 * wm + 8 * (r / 4) + 4 * half + (r % 4);
+    if (t < T) logits[(int64_t)t * (E + 1) + e] = acc[r] + b;
+  }
+}
+
+// Shared-gate logit w_sg . x[t] (row E of the logits), one wave per token.
+template <int ACT>
+__global__ __launch_bounds__(256) void gate_logit_kernel(const void* __restrict__ x,
+                                                         const float* __restrict__ wsg,
+                                                         float* __restrict__ logits, int T, int H,
+                                                         int E) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  float acc = 0.f;
+  for (int c = lane; c < H; c += 64) acc += wsg[c] * load_act<ACT>(x, (int64_t)t * H + c);
+  acc = warp_sum(acc);
+  if (lane == 0) logits[(int64_t)t * (E + 1) + E] = acc;
+}
+
+template <int ACT>
+hipError_t launch_router_gemv(const RouterArgs& a, hipStream_t s);
+
 template <int ACT>
 hipError_t launch_router_act(const RouterArgs& a, hipStream_t s) {
+  if (ACT == MOE_ACT_BF16 && a.T >= kRouterMfmaMinTokens && a.H % 64 == 0) {
+    hipLaunchKernelGGL(router_mfma_kernel,
+                       dim3((a.E + kRouterTile - 1) / kRouterTile, (a.T + kRouterTile - 1) / kRouterTile),
+                       dim3(256), 0, s, reinterpret_cast<const uint16_t*>(a.x), a.router_w,
+                       a.router_bias, a.logits, a.T, a.H, a.E);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (a.shared_gate_w) {
+      hipLaunchKernelGGL((gate_logit_kernel<ACT>), dim3((a.T + 3) / 4), dim3(256), 0, s, a.x,
+                         a.shared_gate_w, a.logits, a.T, a.H, a.E);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+  } else {
+    hipError_t e = launch_router_gemv<ACT>(a, s);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(topk_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a.logits, a.topk_idx,
+                     a.topk_w, a.gamma, a.T, a.E, a.k, a.shared_gate_w ? 1 : 0);
+  return hipGetLastError();
+}
+
+template <int ACT>
+hipError_t launch_router_gemv(const RouterArgs& a, hipStream_t s) {
   const int R = a.E + (a.shared_gate_w ? 1 : 0);
   const int TT = max(1, min(min(a.T, kRouterMaxTT), 16384 / a.H));
   const size_t lds = sizeof(float) * (size_t)TT * a.H;
-  const dim3 grid((R + kRouterWaves - 1) / kRouterWaves);
+  const int nchunk = (a.T + TT - 1) / TT;
+  const int rblk = (R + kRouterWaves - 1) / kRouterWaves;
+  const dim3 grid(rblk, max(1, min(nchunk, 4096 / rblk)));
   const int nit = (a.H + 255) / 256;
 #define MOE_ROUTER_CASE(N)                                                                 \
   case N:                                                                                  \
@@ -183,10 +331,6 @@ hipError_t launch_router_act(const RouterArgs& a, hipStream_t s) {
                          a.router_bias, a.shared_gate_w, a.logits, a.T, a.H, a.E, TT);
   }
 #undef MOE_ROUTER_CASE
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a.logits, a.topk_idx,
-                     a.topk_w, a.gamma, a.T, a.E, a.k, a.shared_gate_w ? 1 : 0);
   return hipGetLastError();
 }
 
