@@ -40,7 +40,10 @@ def parse():
     p.add_argument("--layers", type=int, default=0, help="override the number of layers")
     p.add_argument("--cpu-layers", type=int, default=8,
                    help="layers of the oracle's timed sample (0: skip the CPU baseline)")
-    p.add_argument("--no-roofline", action="store_true", help="skip the per-stage event pass")
+    p.add_argument("--no-roofline", action="store_true", help="skip the per-launch event pass")
+    p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                   help="also run one device-to-device copy of this many MiB (a reference "
+                        "kernel of known traffic for hardware byte counters)")
     return p.parse_args()
 
 
@@ -95,10 +98,16 @@ def main():
     ws = wl.workspace()
     stream = torch.cuda.Stream()
 
-    def chain(r):
+    def load_input(r):
         x.copy_(xs[r])
+
+    def forward():
         moe.moe_chain_forward(d, L, x, wl.router_w, wl.router_bias, wl.slab, wl.slot_tables,
                               wl.shared, wl.shared_stride, x_hat, out, ws)
+
+    def chain(r):
+        load_input(r)
+        forward()
 
     # eager run: routing statistics (unique experts per layer) per rotation
     pi, pw, pg = moe.moe_workspace_routing(d, ws)
@@ -142,6 +151,15 @@ def main():
         else:
             chain(s % N_ROTATE)
 
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     # warmup + timed region
     for s in range(args.warmup):
         step(s)
@@ -164,7 +182,7 @@ def main():
 
     roofline = None
     if not args.no_roofline:
-        roofline = chain_roofline(cfg, chain, bytes_per_rot)
+        roofline = chain_roofline(cfg, load_input, forward, bytes_per_rot)
 
     cpu = None
     if args.cpu_layers > 0:
@@ -211,33 +229,64 @@ def describe(cfg):
             f"{cfg.layers} chained layer(s)")
 
 
-def chain_roofline(cfg, chain, bytes_per_rot, reps=64):
-    """Average duration of one launch of the chain (for batch-1 bf16 int4
-    decode this is the single persistent kernel that streams every layer's
-    weights), timed with HIP events on the launch stream.  The stream is first
-    held by a device-side sleep so that all launches are queued before the
-    first one runs and the intervals contain no host gaps."""
+def chain_roofline(cfg, load_input, forward, bytes_per_rot, reps=64):
+    """Average duration of one moe_chain_forward launch (for batch-1 bf16
+    int4 decode this is the single persistent kernel that streams every
+    layer's weights), timed with HIP events on the launch stream around the
+    library call only (the input copy before it is outside the interval).
+    The stream is first held by a device-side sleep so that all launches are
+    queued before the first one runs and the intervals contain no host gaps."""
     import torch
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(reps)]
     torch.cuda.synchronize()
     torch.cuda._sleep(50_000_000)
     for i in range(reps):
+        load_input(i % N_ROTATE)
         evs[i][0].record()
-        chain(i % N_ROTATE)
+        forward()
         evs[i][1].record()
     torch.cuda.synchronize()
     durs = [a.elapsed_time(b) * 1e-3 for a, b in evs]
     avg_s = sum(durs) / len(durs)
     avg_b = sum(bytes_per_rot[i % N_ROTATE] for i in range(reps)) / reps
     achieved = avg_b / avg_s / 1e9
+    persistent = cfg.n_tokens == 1 and cfg.act == "bf16" and cfg.bits == 4
+    traffic = measured_traffic(cfg) if persistent else None
     return {"bound": "hbm",
-            "kernel": "moe_chain_forward: one launch of the whole decode chain "
-                      "(input copy + chain kernel(s))",
+            "kernel": ("chain_kernel<4, 8>: the persistent decode-chain kernel, one launch "
+                       f"per {cfg.layers}-layer step" if persistent else
+                       "moe_chain_forward: all kernels of one chain step"),
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
             "avg_launch_us": round(avg_s * 1e6, 3), "bytes_per_launch": int(avg_b),
             "launches": reps}
+
+
+def measured_traffic(cfg):
+    """HBM bytes per launch of the decode-chain kernel from the hardware-counter
+    summary in profiles/ (FETCH_SIZE + WRITE_SIZE, calibrated on a copy of
+    known size), or None when there is none for this workload or the kernel's
+    sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"chain_kernel_{cfg.name}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path, encoding="utf-8"):
+        if " = " in line:
+            key, val = line.strip().split(" = ", 1)
+            fields[key] = val
+    h = hashlib.sha256()
+    for f in ("chain.hip", "decode_common.h"):
+        with open(os.path.join(ROOT, "int4_group_quantized_moe_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if fields.get("kernel_source_sha256") != h.hexdigest():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(cfg, n_layers):

@@ -191,7 +191,9 @@ int moe_pack_expert(const moe_layer_desc* desc, int32_t inter, const uint8_t* q_
  * (expert i's q_gate at q_gate + i*inter*hidden, its sb_gate at
  * sb_gate + i*2*inter*(hidden/64), ...).  Expert i is written to
  * slab + dst_slots[i] * desc->expert_stride; dst_slots is a *host* int64
- * array of n slots.  Codes must already be in range (not checked).
+ * array of n slots.  Codes must already be in range (not checked).  The
+ * shared gate vector of a shared blob is not written by this packer; copy it
+ * to shared_gate_offset separately.
  */
 int moe_pack_experts_device(const moe_layer_desc* desc, int32_t inter, int32_t n,
                             const uint8_t* q_gate, const uint8_t* q_up, const uint8_t* q_down,
@@ -275,6 +277,14 @@ int moe_rmsnorm(const moe_layer_desc* desc, void* x, const void* out, void* x_ha
  *   shared_blobs  layer l at shared_blobs + l * shared_stride bytes
  *   shared_stride bytes between shared blobs, multiple of 256
  *   x_hat, out    [T x H] act_dtype scratch tensors (hold the last layer's)
+ *   ws            workspace of moe_workspace_bytes(desc) bytes.  For T = 1 the
+ *                 chain may run as one persistent cooperative kernel that
+ *                 exchanges data between workgroups through epoch-tagged words
+ *                 in ws: ws must be zero-filled before its first chain call and
+ *                 then reused only by chain calls of the same desc (it keeps the
+ *                 last epoch; 2^32 layers before the counter wraps).  A bounded
+ *                 wait that expires sets bit 0 of the 32-bit word after that
+ *                 counter (results of that call are then invalid).
  */
 int moe_chain_forward(const moe_layer_desc* desc, int32_t n_layers, void* x,
                       const float* router_w, const float* router_bias, const void* expert_slab,

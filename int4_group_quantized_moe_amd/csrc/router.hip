@@ -15,6 +15,17 @@ constexpr int kRouterMaxTT = 8;     // tokens per LDS chunk
 constexpr int kRouterMaxRegIt = 8;  // row cached in registers when H <= 64*4*8
 constexpr int kRouterMfmaMinTokens = 128;  // GEMM on the matrix cores from this batch size (bf16)
 
+template <int ACT>
+__device__ __forceinline__ float4 load_act4(const void* p, int64_t i) {
+  if constexpr (ACT == MOE_ACT_F32) {
+    return *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p) + i);
+  } else {
+    const uint2 v = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(p) + i);
+    return make_float4(bf16_bits_to_f32(v.x & 0xFFFFu), bf16_bits_to_f32(v.x >> 16),
+                       bf16_bits_to_f32(v.y & 0xFFFFu), bf16_bits_to_f32(v.y >> 16));
+  }
+}
+
 // logits[t][r] = sum_c W[r][c] * x[t][c] (+ bias[r]) for rows r < E, and the
 // shared-gate logit w_sg . x[t] as row E when w_sg is given.
 template <int ACT, int NIT>
@@ -50,9 +61,24 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const void* __restrict
   for (int t0 = blockIdx.y * TT; t0 < T; t0 += gridDim.y * TT) {
     const int tt_n = min(TT, T - t0);
     __syncthreads();
-    for (int i = threadIdx.x; i < tt_n * H; i += blockDim.x) {
-      const int tt = i / H, c = i - tt * H;
-      xs[i] = load_act<ACT>(x, (int64_t)(t0 + tt) * H + c);
+    // stage the chunk's rows (contiguous in x): 4 values per thread and
+    // iteration, all loads of a thread issued before its LDS stores
+    {
+      const int n4 = tt_n * H / 4;
+      constexpr int kU = 8;
+      for (int i0 = 0; i0 < n4; i0 += kU * 256) {
+        float4 v[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int i = i0 + u * 256 + threadIdx.x;
+          if (i < n4) v[u] = load_act4<ACT>(x, (int64_t)t0 * H + 4 * (int64_t)i);
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int i = i0 + u * 256 + threadIdx.x;
+          if (i < n4) reinterpret_cast<float4*>(xs)[i] = v[u];
+        }
+      }
     }
     __syncthreads();
     if (!active) continue;
