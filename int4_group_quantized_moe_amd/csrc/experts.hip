@@ -173,6 +173,7 @@ __device__ __forceinline__ float lane_dot(const uint4 q, const uint32_t* __restr
 // lane l owns row l/4 and chunk l%4 of each k-block.
 
 constexpr int kGuTokens = 4;  // tokens per LDS staging round
+constexpr int kGemvSlots = 1024;  // workgroups of the grid-stride bucketed GEMV kernels
 
 struct GuItem {
   const uint8_t* blob;
@@ -184,23 +185,26 @@ struct GuItem {
   int64_t hrow;   // decode: h row
 };
 
+#define MOE_GATEUP_PARAMS                                                                   \
+  const void* __restrict__ x, const int32_t* __restrict__ topk_idx,                          \
+      const uint8_t* __restrict__ slab, const int32_t* __restrict__ slot_table, int64_t stride, \
+      const uint8_t* __restrict__ shared_blob, const int32_t* __restrict__ counts,           \
+      const int32_t* __restrict__ offsets, const int32_t* __restrict__ pairs,                \
+      float* __restrict__ h, int T, int H, int E, int k, int I, int Is, int64_t gu_unit_r,     \
+      int64_t gu_tile_r, int64_t gu_unit_s, int64_t gu_tile_s, int bucketed, int has_shared,   \
+      int min_rows
+#define MOE_GATEUP_ARGS                                                                        \
+  x, topk_idx, slab, slot_table, stride, shared_blob, counts, offsets, pairs, h, T, H, E, k, I, \
+      Is, gu_unit_r, gu_tile_r, gu_unit_s, gu_tile_s, bucketed, has_shared, min_rows
+
 template <int BITS, int ACT>
-__global__ __launch_bounds__(256) void gateup_kernel(
-    const void* __restrict__ x, const int32_t* __restrict__ topk_idx,
-    const uint8_t* __restrict__ slab, const int32_t* __restrict__ slot_table, int64_t stride,
-    const uint8_t* __restrict__ shared_blob, const int32_t* __restrict__ counts,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ pairs,
-    float* __restrict__ h, int T, int H, int E, int k, int I, int Is, int64_t gu_unit_r,
-    int64_t gu_tile_r, int64_t gu_unit_s, int64_t gu_tile_s, int bucketed, int has_shared,
-    int min_rows) {
+__device__ __forceinline__ void gateup_item(MOE_GATEUP_PARAMS, int tile, int item) {
   constexpr int GPK = BITS == 4 ? 2 : 1;
   constexpr int CC = chunk_cols<BITS>();
   extern __shared__ uint8_t smem[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int tile = blockIdx.x;
 
   // resolve the work item
-  const int item = blockIdx.y;
   const uint8_t* blob;
   int n, start = 0, inter, kind, t_dec = 0;
   int64_t unit_b, tile_b, hbase;
@@ -323,6 +327,26 @@ __global__ __launch_bounds__(256) void gateup_kernel(
   }
 }
 
+// Small batch: grid (tiles, T*(k+has_shared)) work items.  Bucketed: a
+// grid-stride loop over (bucket, tile) pairs of the buckets listed in
+// small_list (those not on the MFMA grouped GEMMs), so that no workgroup is
+// launched for an empty or MFMA-handled bucket.
+template <int BITS, int ACT>
+__global__ __launch_bounds__(256) void gateup_kernel(MOE_GATEUP_PARAMS,
+                                                     const int32_t* __restrict__ small_list,
+                                                     const int32_t* __restrict__ n_small,
+                                                     int tiles) {
+  if (!bucketed) {
+    gateup_item<BITS, ACT>(MOE_GATEUP_ARGS, blockIdx.x, blockIdx.y);
+    return;
+  }
+  const int total = *n_small * tiles;
+  for (int q = blockIdx.x; q < total; q += gridDim.x) {
+    gateup_item<BITS, ACT>(MOE_GATEUP_ARGS, q % tiles, small_list[q / tiles]);
+    __syncthreads();
+  }
+}
+
 // ---------------------------------------------------------------------------
 // down + combine at small batch: one workgroup = one 16-row tile of the
 // output of one token; it walks the token's k routed items and the shared
@@ -416,22 +440,28 @@ __global__ __launch_bounds__(256) void down_decode_kernel(
 // batched: down per expert bucket, writing weighted per-(token, j) partial
 // rows; a combine kernel then sums each token's k+1 partials in order.
 
+constexpr int kDownTok = 4;  // tokens per round of the bucketed down GEMV
+
+#define MOE_DOWNB_PARAMS                                                                     \
+  const float* __restrict__ topk_w, const float* __restrict__ gamma,                           \
+      const uint8_t* __restrict__ slab, const int32_t* __restrict__ slot_table, int64_t stride, \
+      const uint8_t* __restrict__ shared_blob, const int32_t* __restrict__ counts,           \
+      const int32_t* __restrict__ offsets, const int32_t* __restrict__ pairs,                \
+      const float* __restrict__ h, float* __restrict__ partial, int T, int H, int E, int k,    \
+      int I, int Is, int64_t d_off_r, int64_t d_unit_r, int64_t d_tile_r, int64_t d_off_s,     \
+      int64_t d_unit_s, int64_t d_tile_s, int min_rows
+#define MOE_DOWNB_ARGS                                                                       \
+  topk_w, gamma, slab, slot_table, stride, shared_blob, counts, offsets, pairs, h, partial, T, \
+      H, E, k, I, Is, d_off_r, d_unit_r, d_tile_r, d_off_s, d_unit_s, d_tile_s, min_rows
+
 template <int BITS>
-__global__ __launch_bounds__(256) void down_bucket_kernel(
-    const float* __restrict__ topk_w, const float* __restrict__ gamma,
-    const uint8_t* __restrict__ slab, const int32_t* __restrict__ slot_table, int64_t stride,
-    const uint8_t* __restrict__ shared_blob, const int32_t* __restrict__ counts,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ pairs,
-    const float* __restrict__ h, float* __restrict__ partial, int T, int H, int E, int k, int I,
-    int Is, int64_t d_off_r, int64_t d_unit_r, int64_t d_tile_r, int64_t d_off_s,
-    int64_t d_unit_s, int64_t d_tile_s, int min_rows) {
+__device__ __forceinline__ void down_bucket_item(MOE_DOWNB_PARAMS, float (*red)[kDownTok][kRowTile],
+                                                 int tile, int item) {
   constexpr int GPK = BITS == 4 ? 2 : 1;
   constexpr int CC = chunk_cols<BITS>();
   constexpr int KBC = kRowBytes * (8 / BITS);
-  constexpr int kTok = 4;
-  __shared__ float red[4][kTok][kRowTile];
+  constexpr int kTok = kDownTok;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int tile = blockIdx.x, item = blockIdx.y;
   const int row = lane >> 2, c4 = lane & 3;
   const int sb_off = kCodeBlockBytes + (row * GPK + (c4 * CC) / kGroup) * 4;
   const uint8_t* tbase;
@@ -502,6 +532,19 @@ __global__ __launch_bounds__(256) void down_bucket_kernel(
   }
 }
 
+template <int BITS>
+__global__ __launch_bounds__(256) void down_bucket_kernel(MOE_DOWNB_PARAMS,
+                                                          const int32_t* __restrict__ small_list,
+                                                          const int32_t* __restrict__ n_small,
+                                                          int tiles) {
+  __shared__ float red[4][kDownTok][kRowTile];
+  const int total = *n_small * tiles;
+  for (int q = blockIdx.x; q < total; q += gridDim.x) {
+    down_bucket_item<BITS>(MOE_DOWNB_ARGS, red, q % tiles, small_list[q / tiles]);
+    __syncthreads();
+  }
+}
+
 template <int ACT>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ partial,
                                                       void* __restrict__ out, int H, int k,
@@ -544,38 +587,76 @@ __global__ __launch_bounds__(64) void bucket_mask_kernel(const int32_t* __restri
   for (int e = lane; e < E; e += 64) masks[(int64_t)b * E + e] = m[e];
 }
 
+// Per-expert counts and bucket offsets (exclusive scan over experts), the
+// per-block write offsets, and the list of buckets the GEMV kernels take:
+// experts with 1 .. min_rows-1 tokens, and the shared expert (bucket E) when
+// T < min_rows.  One workgroup of 1024 threads (E <= 1024).
 __global__ __launch_bounds__(1024) void bucket_scan_kernel(const uint64_t* __restrict__ masks,
                                                            int32_t* __restrict__ counts,
                                                            int32_t* __restrict__ offsets,
-                                                           int32_t* __restrict__ blkoff, int T,
-                                                           int E, int k, int nblk) {
-  __shared__ int wsum[16];
+                                                           int32_t* __restrict__ blkoff,
+                                                           int32_t* __restrict__ small_list,
+                                                           int32_t* __restrict__ n_small, int T,
+                                                           int E, int k, int nblk, int min_rows,
+                                                           int has_shared) {
+  __shared__ int wsum[16], wsmall[16];
   const int e = threadIdx.x, lane = e & 63, wave = e >> 6;
+  constexpr int kU = 8;
   int c = 0;
-  if (e < E)
-    for (int b = 0; b < nblk; ++b) c += __popcll(masks[(int64_t)b * E + e]);
-  // inclusive scan inside the wave
-  int v = c;
+  if (e < E) {
+    for (int b0 = 0; b0 < nblk; b0 += kU) {
+      uint64_t m[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) m[u] = b0 + u < nblk ? masks[(int64_t)(b0 + u) * E + e] : 0ull;
+#pragma unroll
+      for (int u = 0; u < kU; ++u) c += __popcll(m[u]);
+    }
+  }
+  // inclusive scans inside the wave: token counts, and small-bucket flags
+  const int sm = (e < E && c > 0 && c < min_rows) ? 1 : 0;
+  int v = c, vs = sm;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(v, off, 64);
-    if (lane >= off) v += o;
+    const int o = __shfl_up(v, off, 64), os = __shfl_up(vs, off, 64);
+    if (lane >= off) {
+      v += o;
+      vs += os;
+    }
   }
-  if (lane == 63) wsum[wave] = v;
+  if (lane == 63) {
+    wsum[wave] = v;
+    wsmall[wave] = vs;
+  }
   __syncthreads();
-  int wbase = 0;
-  for (int w = 0; w < wave; ++w) wbase += wsum[w];
+  int wbase = 0, sbase = 0;
+  for (int w = 0; w < wave; ++w) {
+    wbase += wsum[w];
+    sbase += wsmall[w];
+  }
   const int excl = wbase + v - c;
+  if (sm) small_list[sbase + vs - 1] = e;
   if (e < E) {
     counts[e] = c;
     offsets[e] = excl;
     int run = excl;
-    for (int b = 0; b < nblk; ++b) {
-      blkoff[(int64_t)b * E + e] = run;
-      run += __popcll(masks[(int64_t)b * E + e]);
+    for (int b0 = 0; b0 < nblk; b0 += kU) {
+      uint64_t m[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) m[u] = b0 + u < nblk ? masks[(int64_t)(b0 + u) * E + e] : 0ull;
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        if (b0 + u < nblk) {
+          blkoff[(int64_t)(b0 + u) * E + e] = run;
+          run += __popcll(m[u]);
+        }
+      }
     }
   }
-  if (e == 0) {
+  if (e == 1023) {
+    int ns = 0;
+    for (int w = 0; w < 16; ++w) ns += wsmall[w];
+    if (has_shared && T < min_rows) small_list[ns++] = E;
+    *n_small = ns;
     counts[E] = T;
     offsets[E] = T * k;
   }
@@ -703,7 +784,8 @@ hipError_t launch_experts_t(const ExpertArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((gateup_kernel<BITS, ACT>), dim3(tiles_gu, a.T * (a.k + hs)), dim3(256),
                        lds_gu, s, a.x, a.topk_idx, a.slab, a.slot_table, a.stride, a.shared_blob,
                        counts, offsets, pairs, h, a.T, a.H, a.E, a.k, a.L.inter, Is, a.L.gu_unit,
-                       a.L.gu_tile, a.Ls.gu_unit, a.Ls.gu_tile, 0, hs, 0);
+                       a.L.gu_tile, a.Ls.gu_unit, a.Ls.gu_tile, 0, hs, 0, nullptr, nullptr,
+                       0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((down_decode_kernel<BITS, ACT>), dim3(a.L.n_tiles_d, a.T), dim3(256), 0, s,
                        a.topk_idx, a.topk_w, a.gamma, a.slab, a.slot_table, a.stride,
@@ -717,8 +799,12 @@ hipError_t launch_experts_t(const ExpertArgs& a, hipStream_t s) {
   const int nblk = (a.T + 63) / 64;
   hipLaunchKernelGGL(bucket_mask_kernel, dim3(nblk), dim3(64), 0, s, a.topk_idx, masks, a.T, a.E,
                      a.k);
+  int32_t* small_list = reinterpret_cast<int32_t*>(a.ws + P.small);
+  int32_t* n_small = reinterpret_cast<int32_t*>(a.ws + P.nsmall);
+  // buckets below the MFMA threshold (all of them without the MFMA path)
+  const int min_rows = a.mfma ? kMfmaMinRows : 0x7FFFFFFF;
   hipLaunchKernelGGL(bucket_scan_kernel, dim3(1), dim3(1024), 0, s, masks, counts, offsets, blkoff,
-                     a.T, a.E, a.k, nblk);
+                     small_list, n_small, a.T, a.E, a.k, nblk, min_rows, hs);
   hipLaunchKernelGGL(bucket_scatter_kernel, dim3(nblk), dim3(64), 0, s, a.topk_idx, masks, blkoff,
                      pairs, a.T, a.E, a.k);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -755,17 +841,17 @@ hipError_t launch_experts_t(const ExpertArgs& a, hipStream_t s) {
     pa.min_rows = kMfmaMinRows;
     if ((e = launch_prefill(pa, s)) != hipSuccess) return e;
   }
-  // buckets below the MFMA threshold (all of them without the MFMA path)
-  const int min_rows = a.mfma ? kMfmaMinRows : 0x7FFFFFFF;
-  hipLaunchKernelGGL((gateup_kernel<BITS, ACT>), dim3(tiles_gu, a.E + hs), dim3(256), lds_gu, s,
+  hipLaunchKernelGGL((gateup_kernel<BITS, ACT>), dim3(kGemvSlots), dim3(256), lds_gu, s,
                      a.x, a.topk_idx, a.slab, a.slot_table, a.stride, a.shared_blob, counts,
                      offsets, pairs, h, a.T, a.H, a.E, a.k, a.L.inter, Is, a.L.gu_unit,
-                     a.L.gu_tile, a.Ls.gu_unit, a.Ls.gu_tile, 1, hs, min_rows);
+                     a.L.gu_tile, a.Ls.gu_unit, a.Ls.gu_tile, 1, hs, min_rows, small_list,
+                     n_small, tiles_gu);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((down_bucket_kernel<BITS>), dim3(a.L.n_tiles_d, a.E + hs), dim3(256), 0, s,
+  hipLaunchKernelGGL((down_bucket_kernel<BITS>), dim3(kGemvSlots), dim3(256), 0, s,
                      a.topk_w, a.gamma, a.slab, a.slot_table, a.stride, a.shared_blob, counts,
                      offsets, pairs, h, partial, a.T, a.H, a.E, a.k, a.L.inter, Is, a.L.d_off,
-                     a.L.d_unit, a.L.d_tile, a.Ls.d_off, a.Ls.d_unit, a.Ls.d_tile, min_rows);
+                     a.L.d_unit, a.L.d_tile, a.Ls.d_off, a.Ls.d_unit, a.Ls.d_tile, min_rows,
+                     small_list, n_small, a.L.n_tiles_d);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((combine_kernel<ACT>), dim3(a.T), dim3(256), 0, s, partial, a.out, a.H, a.k,
                      hs);

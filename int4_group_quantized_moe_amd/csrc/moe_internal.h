@@ -62,6 +62,7 @@ inline BlobLayout make_layout(int bits, int hidden, int inter) {
 struct WsPlan {
   size_t logits, idx, w, gamma, h, partial, counts, offsets, pairs, slots, masks, blkoff, xprep;
   size_t xsum, hsum;  // grouped-GEMM path: per-group sums of x_hat and of h
+  size_t small, nsmall;  // buckets left to the GEMV kernels, and their count
   size_t xw, lw, hw, ctr;  // persistent-chain exchange words (batch 1)
   size_t tiles, ntiles;    // grouped-GEMM tile list (large batches)
   int max_tiles;
@@ -96,6 +97,8 @@ inline WsPlan make_ws_plan(const moe_layer_desc& d) {
   p.blkoff = take(p.bucketed ? sizeof(int32_t) * nblk * E : 0);
   p.xprep = take(0);
   p.xsum = take(p.bucketed ? sizeof(float) * T * (H / kGroup) : 0);
+  p.small = take(p.bucketed ? sizeof(int32_t) * (E + 1) : 0);
+  p.nsmall = take(p.bucketed ? sizeof(int32_t) : 0);
   p.hsum = take(p.bucketed ? sizeof(float) * (T * k * (I / kGroup) + T * (Is / kGroup)) : 0);
   p.max_tiles = (int)((T * k + T) / 128 + E + 2);
   p.tiles = take(p.bucketed ? sizeof(int32_t) * 2 * p.max_tiles : 0);

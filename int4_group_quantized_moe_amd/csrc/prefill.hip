@@ -32,6 +32,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kMT = 128;          // rows (bucket entries) per tile
+constexpr int kPersistSlots = 1024;  // workgroups of the persistent GEMM grids (multiple of 8)
 constexpr int kLdsRow = kGroup + 8;  // padded LDS row of one group (bf16 elements)
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -40,29 +41,19 @@ __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
-// Order of the 8 K positions inside one MFMA operand chunk.  int4: the chunk
-// built from one 32-bit word of codes (codes c0..c7, nibble i = code i) holds
-// (c0,c4,c1,c5,c2,c6,c3,c7), which takes two instructions per pair to form;
-// the activations are permuted the same way so that the products pair up.
-// int8: natural order.
-template <int BITS>
-__device__ __forceinline__ u32x4 permute_chunk(u32x4 v) {
-  if constexpr (BITS == 4) {
-    return u32x4{__builtin_amdgcn_perm(v.z, v.x, 0x05040100u),
-                 __builtin_amdgcn_perm(v.z, v.x, 0x07060302u),
-                 __builtin_amdgcn_perm(v.w, v.y, 0x05040100u),
-                 __builtin_amdgcn_perm(v.w, v.y, 0x07060302u)};
-  } else {
-    return v;
-  }
-}
-
-// Exact bf16 operands from integer codes.  int4: the nibble goes into
-// mantissa bits 3..6 of 1.0, giving 1 + q/16 exactly; int8: the float of the
-// byte has at most 8 significant bits, so its upper half is q exactly.
+// Exact bf16 operands from integer codes, in natural K order.  int4: the
+// nibble goes into mantissa bits 3..6 of 1.0, giving 1 + q/16 exactly (a
+// 32-bit word of 8 codes becomes 4 bf16 pairs with 12 instructions); int8:
+// the float of the byte has at most 8 significant bits, so its upper half is
+// q exactly.
 __device__ __forceinline__ u32x4 code_frag4(uint32_t d) {
-  constexpr uint32_t M = 0x00780078u, O = 0x3F803F80u;
-  return u32x4{((d << 3) & M) | O, ((d >> 1) & M) | O, ((d >> 5) & M) | O, ((d >> 9) & M) | O};
+  constexpr uint32_t M = 0x78787878u, O = 0x3F803F80u;
+  const uint32_t lo = (d << 3) & M;  // codes 0,2,4,6 in bits 3..6 of bytes 0..3
+  const uint32_t hi = (d >> 1) & M;  // codes 1,3,5,7
+  return u32x4{__builtin_amdgcn_perm(hi, lo, 0x0C040C00u) | O,
+               __builtin_amdgcn_perm(hi, lo, 0x0C050C01u) | O,
+               __builtin_amdgcn_perm(hi, lo, 0x0C060C02u) | O,
+               __builtin_amdgcn_perm(hi, lo, 0x0C070C03u) | O};
 }
 __device__ __forceinline__ uint32_t hi_halves(float lo, float hi) {
   return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
@@ -134,6 +125,7 @@ struct RowAddr {
   const uint8_t* codes;  // row's codes in k-block 0, plus this lane's half
   const uint8_t* sb;     // row's (scale, bias) words in k-block 0
   int64_t unit_b;
+  RowAddr() = default;
   __device__ __forceinline__ RowAddr(const uint8_t* sec, int64_t unit, int64_t tile, int nmat,
                                      int mat, int row, int half)
       : unit_b(unit) {
@@ -159,13 +151,30 @@ __device__ __forceinline__ void bias_mfma(const float* const srow[2], const RowA
 #pragma unroll 1
   for (int j = 0; j < (G + 15) / 16; ++j) {
     u32x4 ah[2], al[2], bh[2], bl[2];
+    // all loads first (clamped indices, so they are unconditional), then
+    // the selects: one wait for the whole batch
+    float va[2][8];
+    uint32_t vb[2][8];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const float* p = srow[mb] != nullptr ? srow[mb] : srow[mb ^ 1];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int g = min(16 * j + 8 * half + i, G - 1);
+        va[mb][i] = p != nullptr ? p[g] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) vb[nb][i] = wr[nb].group_sb(min(16 * j + 8 * half + i, G - 1));
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       float v[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int g = 16 * j + 8 * half + i;
-        v[i] = (srow[mb] != nullptr && g < G) ? srow[mb][g] : 0.f;
+        v[i] = (srow[mb] != nullptr && g < G) ? va[mb][i] : 0.f;
       }
       split8(v, ah[mb], al[mb]);
     }
@@ -175,7 +184,7 @@ __device__ __forceinline__ void bias_mfma(const float* const srow[2], const RowA
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int g = 16 * j + 8 * half + i;
-        v[i] = g < G ? bias_coef<BITS>(wr[nb].group_sb(g)) : 0.f;
+        v[i] = g < G ? bias_coef<BITS>(vb[nb][i]) : 0.f;
       }
       split8(v, bh[nb], bl[nb]);
     }
@@ -189,6 +198,18 @@ __device__ __forceinline__ void bias_mfma(const float* const srow[2], const RowA
       }
   }
 }
+
+// Work-item order for the MI355X's 8 XCDs (each with its own L2): the
+// hardware hands linear workgroup w to XCD w % 8, so XCD c is given the
+// contiguous item range [c*per, (c+1)*per) of the (tile, column block)
+// items, column block fastest, per = ceil(items / 8).  The column blocks of
+// one row tile (which share its activation rows) and the row tiles of one
+// expert (which share its weights) then run on the same L2.  The item count
+// is only known on the device.
+struct XcdItem {
+  int tile, nb;
+  bool valid;
+};
 
 struct TileInfo {
   int e;        // expert, or E for the shared expert
@@ -297,25 +318,276 @@ __global__ __launch_bounds__(256) void group_sum_kernel(const uint16_t* __restri
 // 64 h values as bf16 (hi, lo) pairs in the K order the down GEMM stages,
 // and the row's group sum of h.
 
+#define MOE_PGU_PARAMS                                                                       \
+  const uint16_t* __restrict__ x, const float* __restrict__ xsum,                              \
+      const int32_t* __restrict__ pairs, const int32_t* __restrict__ counts,                  \
+      const int32_t* __restrict__ offsets, const int32_t* __restrict__ tiles,                 \
+      const int32_t* __restrict__ ntiles, const uint8_t* __restrict__ slab,                   \
+      const int32_t* __restrict__ slot_table, int64_t stride,                                 \
+      const uint8_t* __restrict__ shared_blob, uint16_t* __restrict__ h,                      \
+      float* __restrict__ hsum, int T, int H, int E, int k, int I, int Is, int64_t gu_unit_r,   \
+      int64_t gu_tile_r, int64_t gu_unit_s, int64_t gu_tile_s, int nbg
+#define MOE_PGU_ARGS                                                                       \
+  x, xsum, pairs, counts, offsets, tiles, ntiles, slab, slot_table, stride, shared_blob, h, \
+      hsum, T, H, E, k, I, Is, gu_unit_r, gu_tile_r, gu_unit_s, gu_tile_s, nbg
+
+// Gate/up K pipeline.  Everything a K stage (one quantisation group) needs
+// arrives by asynchronous global->LDS loads (global_load_lds): the 128
+// activation rows (16 KiB), the 128 weight rows' codes (4 or 8 KiB) and
+// their (scale, bias) words.  Each stage has its own __shared__ object, so
+// the compiler's wait accounting for these loads is per stage and a read of
+// stage s never waits for the loads of the stages behind it; kStages - 1
+// stages are in flight while one is multiplied.  Chunk c of activation row r
+// sits at r*8 + (c ^ (r & 7)), spreading the 32 rows of an MFMA operand read
+// over the LDS banks.
+constexpr int kStages = 3;
+constexpr int kStageChunks = kMT * kGroup / 8;  // 1024 chunks of 16 bytes
+typedef uint4 StageBuf[kStageChunks];
+
 template <int BITS>
-__global__ __launch_bounds__(256) void prefill_gateup_kernel(
-    const uint16_t* __restrict__ x, const float* __restrict__ xsum,
-    const int32_t* __restrict__ pairs, const int32_t* __restrict__ counts,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ tiles,
-    const int32_t* __restrict__ ntiles, const uint8_t* __restrict__ slab,
-    const int32_t* __restrict__ slot_table, int64_t stride, const uint8_t* __restrict__ shared_blob,
-    uint16_t* __restrict__ h, float* __restrict__ hsum, int T, int H, int E, int k, int I, int Is,
-    int64_t gu_unit_r, int64_t gu_tile_r, int64_t gu_unit_s, int64_t gu_tile_s) {
-  // two stages of 128 activation rows x 64 K; reused as the fp32 h tile
-  __shared__ __align__(16) uint16_t A[2 * kMT * kLdsRow];
-  __shared__ int32_t rowsrc[kMT];
+struct GuStage {
+  uint4 A[kStageChunks];               // activations
+  uint4 B[128 * (kGroup * BITS / 8) / 16];  // codes: 128 rows x 32 (int4) / 64 (int8) bytes
+  uint32_t S[256];                     // (scale, bias) of rows 0..127 (128..255 unused)
+};
+
+__device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ (r & 7)); }
+
+// Workgroup barrier for the K pipeline: waits for this wave's LDS reads
+// and writes (lgkmcnt) but not for its global->LDS loads in flight, which a
+// release fence would also wait for.  The asm "memory" clobber keeps the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// s_waitcnt vmcnt(N): at most N of this wave's vector memory loads
+// (including global->LDS loads) still outstanding; they complete in order.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+#define MOE_G1(p) ((const void __attribute__((address_space(1)))*)(p))
+#define MOE_L3(p) ((void __attribute__((address_space(3)))*)(p))
+
+// Loads a thread issues per stage: 4 activation chunks, BITS/4 code chunks,
+// one (scale, bias) word.
+template <int BITS>
+constexpr int gu_stage_loads() { return 4 + BITS / 4 + 1; }
+
+// Load sources of a stage: a uniform base (scalar registers) plus a 32-bit
+// per-lane byte offset, so that the loads use scalar-base addressing and the
+// per-stage advance is scalar arithmetic.
+template <int BITS>
+struct GuSrc {
+  const uint8_t* x;            // activations (uniform)
+  const uint8_t* sec;          // blob gate/up section (uniform)
+  int64_t unit_b;
+  uint32_t a[4];               // activation chunk offsets (stage 0)
+  uint32_t b[BITS / 4];        // code chunk offsets (k-block 0, group 0)
+  uint32_t sb;                 // (scale, bias) word offset (k-block 0, group 0)
+};
+
+template <int BITS>
+__device__ __forceinline__ void gu_issue(const GuSrc<BITS>& P, GuStage<BITS>& st, int g,
+                                         int wave) {
+  constexpr int GPK = kRowBytes * (8 / BITS) / kGroup;
+  constexpr int GBYTES = kGroup * BITS / 8;
+  const uint8_t* xa = P.x + (int64_t)g * kGroup * 2;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    __builtin_amdgcn_global_load_lds(MOE_G1(xa + P.a[j]), MOE_L3(&st.A[j * 256 + wave * 64]), 16,
+                                     0, 0);
+  const uint8_t* wb = P.sec + (int64_t)(g / GPK) * P.unit_b + (g % GPK) * GBYTES;
+#pragma unroll
+  for (int j = 0; j < BITS / 4; ++j)
+    __builtin_amdgcn_global_load_lds(MOE_G1(wb + P.b[j]), MOE_L3(&st.B[j * 256 + wave * 64]), 16,
+                                     0, 0);
+  const uint8_t* sbb = P.sec + (int64_t)(g / GPK) * P.unit_b + (g % GPK) * 4;
+  __builtin_amdgcn_global_load_lds(MOE_G1(sbb + P.sb), MOE_L3(&st.S[wave * 64]), 4, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)p;
+}
+
+// All LDS reads of one K stage for this lane, in one asm block that ends
+// with its own lgkmcnt wait: the A operands of both row blocks for the 4 K
+// steps, the lane's codes of both weight rows, and their (scale, bias)
+// words.  (The compiler's wait accounting for global->LDS loads does not
+// survive the pipeline's loop back-edge and would drain every load in
+// flight before the first read; the explicit vmcnt wait before the stage
+// barrier is what orders these reads after their loads.)  The outputs are
+// early-clobber: each is written while later reads still need addresses.
+template <int BITS>
+struct GuFrags {
+  u32x4 a[2][2];               // A operands of two K steps, both row blocks
+  u32x4 q[2][BITS / 4];        // the lane's codes of both weight rows
+  uint32_t sb[2];
+};
+
+// A operands of K steps k0, k0+1 (both row blocks); with `codes` also the
+// lane's codes and (scale, bias) words.
+template <int BITS, bool CODES>
+__device__ __forceinline__ void gu_read(const GuStage<BITS>& st, int k0, int wm, int wn, int l32,
+                                        int half, GuFrags<BITS>& f) {
+  const uint32_t a00 = lds_addr(&st.A[swz(64 * wm + l32, 4 * half + k0)]);
+  const uint32_t a01 = lds_addr(&st.A[swz(64 * wm + l32, 4 * half + k0 + 1)]);
+  const uint32_t a10 = lds_addr(&st.A[swz(64 * wm + 32 + l32, 4 * half + k0)]);
+  const uint32_t a11 = lds_addr(&st.A[swz(64 * wm + 32 + l32, 4 * half + k0 + 1)]);
+  if constexpr (!CODES) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %5\n\t"
+        "ds_read_b128 %2, %6\n\t"
+        "ds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(f.a[0][0]), "=&v"(f.a[0][1]), "=&v"(f.a[1][0]), "=&v"(f.a[1][1])
+        : "v"(a00), "v"(a01), "v"(a10), "v"(a11)
+        : "memory");
+  } else {
+    const int r0 = 32 * wn + l32, r1 = 64 + 32 * wn + l32;
+    constexpr int CPR = kGroup * BITS / 8 / 16;  // code chunks per row
+    const uint32_t b0 = lds_addr(&st.B[r0 * CPR + half * (CPR / 2)]);
+    const uint32_t b1 = lds_addr(&st.B[r1 * CPR + half * (CPR / 2)]);
+    const uint32_t s0 = lds_addr(&st.S[r0]), s1 = lds_addr(&st.S[r1]);
+    if constexpr (BITS == 4) {
+      asm volatile(
+          "ds_read_b128 %0, %8\n\t"
+          "ds_read_b128 %1, %9\n\t"
+          "ds_read_b128 %2, %10\n\t"
+          "ds_read_b128 %3, %11\n\t"
+          "ds_read_b128 %4, %12\n\t"
+          "ds_read_b128 %5, %13\n\t"
+          "ds_read_b32 %6, %14\n\t"
+          "ds_read_b32 %7, %15\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(f.a[0][0]), "=&v"(f.a[0][1]), "=&v"(f.a[1][0]), "=&v"(f.a[1][1]),
+            "=&v"(f.q[0][0]), "=&v"(f.q[1][0]), "=&v"(f.sb[0]), "=&v"(f.sb[1])
+          : "v"(a00), "v"(a01), "v"(a10), "v"(a11), "v"(b0), "v"(b1), "v"(s0), "v"(s1)
+          : "memory");
+    } else {
+      asm volatile(
+          "ds_read_b128 %0, %10\n\t"
+          "ds_read_b128 %1, %11\n\t"
+          "ds_read_b128 %2, %12\n\t"
+          "ds_read_b128 %3, %13\n\t"
+          "ds_read_b128 %4, %14\n\t"
+          "ds_read_b128 %5, %14 offset:16\n\t"
+          "ds_read_b128 %6, %15\n\t"
+          "ds_read_b128 %7, %15 offset:16\n\t"
+          "ds_read_b32 %8, %16\n\t"
+          "ds_read_b32 %9, %17\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(f.a[0][0]), "=&v"(f.a[0][1]), "=&v"(f.a[1][0]), "=&v"(f.a[1][1]),
+            "=&v"(f.q[0][0]), "=&v"(f.q[0][1]), "=&v"(f.q[1][0]), "=&v"(f.q[1][1]),
+            "=&v"(f.sb[0]), "=&v"(f.sb[1])
+          : "v"(a00), "v"(a01), "v"(a10), "v"(a11), "v"(b0), "v"(b1), "v"(s0), "v"(s1)
+          : "memory");
+    }
+  }
+}
+
+// MFMA operand of K step ks from the lane's codes of one weight row.
+template <int BITS>
+__device__ __forceinline__ u32x4 gu_bfrag(const u32x4 (&q)[BITS / 4], int ks) {
+  if constexpr (BITS == 4) {
+    const uint32_t d = ks == 0 ? q[0].x : ks == 1 ? q[0].y : ks == 2 ? q[0].z : q[0].w;
+    return code_frag4(d);
+  } else {
+    const u32x4 v = q[ks >> 1];
+    return (ks & 1) ? code_frag8(v.z, v.w) : code_frag8(v.x, v.y);
+  }
+}
+
+// One K stage: wait for this stage's loads (the later stages' stay in
+// flight); read K steps 0-1 with the codes, multiply; read K steps 2-3,
+// barrier (after which the stage may be refilled: `refill` runs there),
+// multiply; scale the group's sums into C.
+template <int BITS, typename F>
+__device__ __forceinline__ void gu_stage(const GuStage<BITS>& st, int later, int wm, int wn,
+                                         int l32, int half, f32x16 (&C)[2][2], F&& refill) {
+  constexpr int L = gu_stage_loads<BITS>();
+  static_assert(kStages == 3, "wait ladder below covers kStages - 1 = 2 later stages");
+  if (later >= 2) wait_vm<2 * L>();
+  else if (later == 1) wait_vm<L>();
+  else wait_vm<0>();
+  lds_barrier();
+  GuFrags<BITS> f;
+  const f32x16 zero = {};
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = zero;
+  gu_read<BITS, true>(st, 0, wm, wn, l32, half, f);
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    if (kk == 2) {
+      gu_read<BITS, false>(st, 2, wm, wn, l32, half, f);
+      lds_barrier();
+      refill();
+    }
+    u32x4 b[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) b[nb] = gu_bfrag<BITS>(f.q[nb], kk);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma(f.a[mb][kk & 1], b[nb], acc[mb][nb]);
+  }
+  const float scl[2] = {code_scale<BITS>(f.sb[0]), code_scale<BITS>(f.sb[1])};
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) C[mb][nb][r] += scl[nb] * acc[mb][nb][r];
+}
+
+// fp32 h tile halves in a stage's activation buffer: 64 rows x 64 floats,
+// 4-float chunks XOR-swizzled by the row.
+__device__ __forceinline__ void ht_store(StageBuf& buf, const f32x16 (&C)[2][2], int wn, int l32,
+                                         int half) {
+  float* ht = reinterpret_cast<float*>(&buf[0]);
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = 32 * mb + 8 * (r / 4) + 4 * half + (r % 4);  // row inside the half
+      const float gv = C[mb][0][r], uv = C[mb][1][r];
+      const int col = 32 * wn + l32;
+      ht[m * 64 + (((col >> 2) ^ (m & 15)) << 2) + (col & 3)] = gv / (1.0f + __expf(-gv)) * uv;
+    }
+}
+__device__ __forceinline__ void ht_load(const StageBuf& buf, int lr, int sc, float (&v)[32]) {
+  const float* hr = reinterpret_cast<const float*>(&buf[0]);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const float4 t =
+        *reinterpret_cast<const float4*>(hr + lr * 64 + (((8 * sc + q) ^ (lr & 15)) << 2));
+    v[4 * q] = t.x;
+    v[4 * q + 1] = t.y;
+    v[4 * q + 2] = t.z;
+    v[4 * q + 3] = t.w;
+  }
+}
+
+// One gate/up tile: 128 bucket rows x (64 gate + 64 up weight rows = 64 h
+// columns).  Waves (wm, wn) = (wave / 2, wave % 2) own rows 64 wm .. +63 and
+// h columns 32 wn .. +31 (block 0 gate, block 1 up).
+template <int BITS>
+__device__ __forceinline__ void prefill_gateup_item(MOE_PGU_PARAMS, GuStage<BITS>& s0,
+                                                    GuStage<BITS>& s1, GuStage<BITS>& s2,
+                                                    int32_t* rowsrc, XcdItem it) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, half = lane >> 5;
-  if ((int)blockIdx.y >= *ntiles) return;
-  const TileInfo ti = get_tile(tiles, counts, offsets, blockIdx.y, E);
+  const TileInfo ti = get_tile(tiles, counts, offsets, it.tile, E);
   const bool shared = ti.e == E;
   const int inter = shared ? Is : I;
-  const int n0 = blockIdx.x * kGroup;
+  const int n0 = it.nb * kGroup;
   if (n0 >= inter) return;
   const uint8_t* sec = shared ? shared_blob : slab + (int64_t)slot_table[ti.e] * stride;
   const int64_t unit_b = shared ? gu_unit_s : gu_unit_r, tile_b = shared ? gu_tile_s : gu_tile_r;
@@ -325,41 +597,36 @@ __global__ __launch_bounds__(256) void prefill_gateup_kernel(
     rowsrc[tid] = src;
   }
   __syncthreads();
-  // staging role: row sr, K half sc (32 columns = 4 chunks of 8)
-  const int sr = tid >> 1, sc = tid & 1;
-  const int ssrc = rowsrc[sr];
-  const uint16_t* xrow = x + (int64_t)(ssrc >= 0 ? ssrc : 0) * H + sc * 32;
-  const RowAddr<BITS> wr[2] = {RowAddr<BITS>(sec, unit_b, tile_b, 2, 0, n0 + 32 * wn + l32, half),
-                               RowAddr<BITS>(sec, unit_b, tile_b, 2, 1, n0 + 32 * wn + l32, half)};
   const int G = H / kGroup;
 
-  uint4 ra[4];
-  LaneCodes<BITS> cn[2];
-  uint32_t sbn[2];
-  auto load_stage = [&](int g) {
-    if (ssrc >= 0) {
-      const uint4* p = reinterpret_cast<const uint4*>(xrow + g * kGroup);
+  // load roles (fixed for the tile)
+  GuSrc<BITS> P;
+  P.x = reinterpret_cast<const uint8_t*>(x);
+  P.sec = sec;
+  P.unit_b = unit_b;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) ra[q] = p[q];
-    } else {
+  for (int j = 0; j < 4; ++j) {
+    // activation chunk j*256 + tid: row ch / 8, LDS slot ch % 8 holds column
+    // chunk (slot ^ (row & 7)); rows past the tile read row 0's token (their
+    // results are discarded)
+    const int ch = j * 256 + tid, r = ch >> 3, c = (ch & 7) ^ (r & 7);
+    const int src = r < ti.rows ? rowsrc[r] : rowsrc[0];
+    P.a[j] = (uint32_t)(((int64_t)src * H + c * 8) * 2);
+  }
+  {
+    constexpr int CPR = kGroup * BITS / 8 / 16;  // 16-byte code chunks per row and group
 #pragma unroll
-      for (int q = 0; q < 4; ++q) ra[q] = make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < BITS / 4; ++j) {
+      const int ch = j * 256 + tid, rr = ch / CPR, c = ch % CPR;
+      const RowAddr<BITS> ra(sec, unit_b, tile_b, 2, rr >> 6, n0 + (rr & 63), 0);
+      P.b[j] = (uint32_t)(ra.codes - sec) + c * 16;
     }
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      cn[nb].load(wr[nb].group_codes(g));
-      sbn[nb] = wr[nb].group_sb(g);
-    }
-  };
-  auto store_stage = [&](int buf) {
-    uint16_t* dst = A + buf * kMT * kLdsRow + sr * kLdsRow + sc * 32;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint4 v = ra[q];
-      const u32x4 p = permute_chunk<BITS>(u32x4{v.x, v.y, v.z, v.w});
-      *reinterpret_cast<u32x4*>(dst + 8 * q) = p;
-    }
-  };
+    // (scale, bias) words: lane `tid` of rows 0..127; rows 128..255 repeat them
+    const int rr = tid & 127;
+    const RowAddr<BITS> ra(sec, unit_b, tile_b, 2, rr >> 6, n0 + (rr & 63), 0);
+    P.sb = (uint32_t)(ra.sb - sec);
+  }
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
 
   f32x16 C[2][2];
   const f32x16 zero = {};
@@ -368,45 +635,31 @@ __global__ __launch_bounds__(256) void prefill_gateup_kernel(
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) C[mb][nb] = zero;
 
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
-  for (int g = 0; g < G; ++g) {
-    const LaneCodes<BITS> cc[2] = {cn[0], cn[1]};
-    const float scl[2] = {code_scale<BITS>(sbn[0]), code_scale<BITS>(sbn[1])};
-    if (g + 1 < G) load_stage(g + 1);
-    const uint16_t* As = A + (g & 1) * kMT * kLdsRow;
-    f32x16 acc[2][2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = zero;
-#pragma unroll
-    for (int ks = 0; ks < kGroup / 16; ++ks) {
-      u32x4 a[2], b[2];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-        a[mb] = *reinterpret_cast<const u32x4*>(As + (64 * wm + 32 * mb + l32) * kLdsRow +
-                                                32 * half + 8 * ks);
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) b[nb] = cc[nb].frag(ks);
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma(a[mb], b[nb], acc[mb][nb]);
-    }
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) C[mb][nb][r] += scl[nb] * acc[mb][nb][r];
-    if (g + 1 < G) store_stage((g + 1) & 1);
-    __syncthreads();
+  // Stage t lives in s[t % kStages]: it is multiplied at step t and its
+  // buffer is refilled with stage t + kStages right after.  The first pass
+  // (g < 0) only issues stages 0 .. kStages-1, from the same instructions as
+  // the steady state, so that the compiler sees one set of loads in flight.
+  for (int g = -kStages; g < G; g += kStages) {
+#define MOE_GU_STEP(I, BUF)                                                              \
+  if (g + I >= G) break;                                                                 \
+  {                                                                                      \
+    auto refill = [&]() {                                                                \
+      if (g + I + kStages < G) gu_issue<BITS>(P, BUF, g + I + kStages, wv);              \
+    };                                                                                   \
+    if (g >= 0) gu_stage<BITS>(BUF, min(kStages - 1, G - 1 - g - I), wm, wn, l32, half, C, \
+                               refill);                                                  \
+    else refill();                                                                       \
+  }
+    MOE_GU_STEP(0, s0)
+    MOE_GU_STEP(1, s1)
+    MOE_GU_STEP(2, s2)
+#undef MOE_GU_STEP
   }
 
   // bias terms from the group sums of the activation rows
   {
+    const RowAddr<BITS> wr[2] = {RowAddr<BITS>(sec, unit_b, tile_b, 2, 0, n0 + 32 * wn + l32, half),
+                                 RowAddr<BITS>(sec, unit_b, tile_b, 2, 1, n0 + 32 * wn + l32, half)};
     const float* srow[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
@@ -416,28 +669,17 @@ __global__ __launch_bounds__(256) void prefill_gateup_kernel(
     bias_mfma<BITS>(srow, wr, G, half, C);
   }
 
-  // epilogue: h = silu(g) * u into an fp32 LDS tile [128][64 + 4]
-  constexpr int HS = kGroup + 4;
-  float* ht = reinterpret_cast<float*>(A);
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = 64 * wm + 32 * mb + 8 * (r / 4) + 4 * half + (r % 4);
-      const float gv = C[mb][0][r], uv = C[mb][1][r];
-      ht[m * HS + 32 * wn + l32] = gv / (1.0f + __expf(-gv)) * uv;
-    }
+  // epilogue: h = silu(g) * u into fp32 LDS tiles (rows 0..63 in stage 0's
+  // activation buffer, 64..127 in stage 1's; separate branches so that every
+  // LDS access names its object)
+  if (wm == 0) ht_store(s0.A, C, wn, l32, half);
+  else ht_store(s1.A, C, wn, l32, half);
   __syncthreads();
   // row sr, columns 32 sc .. 32 sc + 31: group sum and (hi, lo) parts
+  const int sr = tid >> 1, sc = tid & 1;
   float v[32];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const float4 t = *reinterpret_cast<const float4*>(ht + sr * HS + 32 * sc + 4 * q);
-    v[4 * q] = t.x;
-    v[4 * q + 1] = t.y;
-    v[4 * q + 2] = t.z;
-    v[4 * q + 3] = t.w;
-  }
+  if (sr < 64) ht_load(s0.A, sr, sc, v);
+  else ht_load(s1.A, sr & 63, sc, v);
   float part = 0.f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) part += v[i];
@@ -458,8 +700,8 @@ __global__ __launch_bounds__(256) void prefill_gateup_kernel(
     for (int q = 0; q < 4; ++q) {
       u32x4 hi, lo;
       split8(v + 8 * q, hi, lo);
-      *reinterpret_cast<u32x4*>(h + hrow + n0 + 32 * sc + 8 * q) = permute_chunk<BITS>(hi);
-      *reinterpret_cast<u32x4*>(h + hrow + inter + n0 + 32 * sc + 8 * q) = permute_chunk<BITS>(lo);
+      *reinterpret_cast<u32x4*>(h + hrow + n0 + 32 * sc + 8 * q) = hi;
+      *reinterpret_cast<u32x4*>(h + hrow + inter + n0 + 32 * sc + 8 * q) = lo;
     }
   }
 }
@@ -469,28 +711,191 @@ __global__ __launch_bounds__(256) void prefill_gateup_kernel(
 // MFMAs per K step.  Writes the weighted expert output of every bucket entry
 // to partial[(t*(k+1) + j) * H + col] (fp32; the shared expert is j = k).
 
+#define MOE_PDN_PARAMS                                                                       \
+  const uint16_t* __restrict__ h, const float* __restrict__ hsum,                              \
+      const int32_t* __restrict__ pairs, const float* __restrict__ topk_w,                    \
+      const float* __restrict__ gamma, const int32_t* __restrict__ counts,                    \
+      const int32_t* __restrict__ offsets, const int32_t* __restrict__ tiles,                 \
+      const int32_t* __restrict__ ntiles, const uint8_t* __restrict__ slab,                   \
+      const int32_t* __restrict__ slot_table, int64_t stride,                                 \
+      const uint8_t* __restrict__ shared_blob, float* __restrict__ partial, int T, int H, int E, \
+      int k, int I, int Is, int64_t d_off_r, int64_t d_unit_r, int64_t d_tile_r,                \
+      int64_t d_off_s, int64_t d_unit_s, int64_t d_tile_s, int nbg
+#define MOE_PDN_ARGS                                                                           \
+  h, hsum, pairs, topk_w, gamma, counts, offsets, tiles, ntiles, slab, slot_table, stride,      \
+      shared_blob, partial, T, H, E, k, I, Is, d_off_r, d_unit_r, d_tile_r, d_off_s, d_unit_s, \
+      d_tile_s, nbg
+
+// Down K pipeline: the same scheme as gate/up, with the stage holding the
+// 128 h rows as bf16 (hi, lo) parts and the 128 output rows' codes.
 template <int BITS>
-__global__ __launch_bounds__(256) void prefill_down_kernel(
-    const uint16_t* __restrict__ h, const float* __restrict__ hsum,
-    const int32_t* __restrict__ pairs, const float* __restrict__ topk_w,
-    const float* __restrict__ gamma, const int32_t* __restrict__ counts,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ tiles,
-    const int32_t* __restrict__ ntiles, const uint8_t* __restrict__ slab,
-    const int32_t* __restrict__ slot_table, int64_t stride, const uint8_t* __restrict__ shared_blob,
-    float* __restrict__ partial, int T, int H, int E, int k, int I, int Is, int64_t d_off_r,
-    int64_t d_unit_r, int64_t d_tile_r, int64_t d_off_s, int64_t d_unit_s, int64_t d_tile_s) {
-  __shared__ __align__(16) uint16_t Ah[2 * kMT * kLdsRow];
-  __shared__ __align__(16) uint16_t Al[2 * kMT * kLdsRow];
-  __shared__ __align__(16) float HS[2 * kMT];  // group sums of the staged h rows
-  __shared__ int32_t rowdst[kMT];
-  __shared__ float roww[kMT];
+struct DnStage {
+  uint4 Ah[kStageChunks];
+  uint4 Al[kStageChunks];
+  uint4 B[128 * (kGroup * BITS / 8) / 16];
+  uint32_t S[256];
+};
+
+template <int BITS>
+constexpr int dn_stage_loads() { return 8 + BITS / 4 + 1; }
+
+struct DnSrc {
+  const uint8_t* h;    // h rows of the tile (uniform base)
+  const uint8_t* sec;  // blob down section (uniform)
+  int64_t unit_b;
+  int inter2;          // bytes from a row's hi part to its lo part
+  uint32_t a[4];       // h chunk offsets (stage 0, hi part)
+  uint32_t b[2];       // code chunk offsets (k-block 0, group 0)
+  uint32_t sb;         // (scale, bias) word offset
+};
+
+template <int BITS>
+__device__ __forceinline__ void dn_issue(const DnSrc& P, DnStage<BITS>& st, int g, int wave) {
+  constexpr int GPK = kRowBytes * (8 / BITS) / kGroup;
+  constexpr int GBYTES = kGroup * BITS / 8;
+  const uint8_t* ha = P.h + (int64_t)g * kGroup * 2;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    __builtin_amdgcn_global_load_lds(MOE_G1(ha + P.a[j]), MOE_L3(&st.Ah[j * 256 + wave * 64]), 16,
+                                     0, 0);
+  const uint8_t* la = ha + P.inter2;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    __builtin_amdgcn_global_load_lds(MOE_G1(la + P.a[j]), MOE_L3(&st.Al[j * 256 + wave * 64]), 16,
+                                     0, 0);
+  const uint8_t* wb = P.sec + (int64_t)(g / GPK) * P.unit_b + (g % GPK) * GBYTES;
+#pragma unroll
+  for (int j = 0; j < BITS / 4; ++j)
+    __builtin_amdgcn_global_load_lds(MOE_G1(wb + P.b[j]), MOE_L3(&st.B[j * 256 + wave * 64]), 16,
+                                     0, 0);
+  const uint8_t* sbb = P.sec + (int64_t)(g / GPK) * P.unit_b + (g % GPK) * 4;
+  __builtin_amdgcn_global_load_lds(MOE_G1(sbb + P.sb), MOE_L3(&st.S[wave * 64]), 4, 0, 0);
+}
+
+template <int BITS>
+struct DnFrags {
+  u32x4 ah[2][2], al[2][2];  // hi/lo A operands of two K steps, both row blocks
+  u32x4 q[2][BITS / 4];
+  uint32_t sb[2];
+};
+
+// hi and lo A operands of K steps k0, k0+1 (both row blocks); with CODES
+// also the lane's codes and (scale, bias) words of both output rows.
+template <int BITS, bool CODES>
+__device__ __forceinline__ void dn_read(const DnStage<BITS>& st, int k0, int wm, int wn, int l32,
+                                        int half, DnFrags<BITS>& f) {
+  const int i00 = swz(64 * wm + l32, 4 * half + k0), i01 = swz(64 * wm + l32, 4 * half + k0 + 1);
+  const int i10 = swz(64 * wm + 32 + l32, 4 * half + k0);
+  const int i11 = swz(64 * wm + 32 + l32, 4 * half + k0 + 1);
+  const uint32_t h00 = lds_addr(&st.Ah[i00]), h01 = lds_addr(&st.Ah[i01]);
+  const uint32_t h10 = lds_addr(&st.Ah[i10]), h11 = lds_addr(&st.Ah[i11]);
+  const uint32_t l00 = lds_addr(&st.Al[i00]), l01 = lds_addr(&st.Al[i01]);
+  const uint32_t l10 = lds_addr(&st.Al[i10]), l11 = lds_addr(&st.Al[i11]);
+  asm volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %9\n\t"
+      "ds_read_b128 %2, %10\n\t"
+      "ds_read_b128 %3, %11\n\t"
+      "ds_read_b128 %4, %12\n\t"
+      "ds_read_b128 %5, %13\n\t"
+      "ds_read_b128 %6, %14\n\t"
+      "ds_read_b128 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(f.ah[0][0]), "=&v"(f.ah[0][1]), "=&v"(f.ah[1][0]), "=&v"(f.ah[1][1]),
+        "=&v"(f.al[0][0]), "=&v"(f.al[0][1]), "=&v"(f.al[1][0]), "=&v"(f.al[1][1])
+      : "v"(h00), "v"(h01), "v"(h10), "v"(h11), "v"(l00), "v"(l01), "v"(l10), "v"(l11)
+      : "memory");
+  if constexpr (CODES) {
+    const int r0 = 64 * wn + l32, r1 = 64 * wn + 32 + l32;
+    constexpr int CPR = kGroup * BITS / 8 / 16;
+    const uint32_t b0 = lds_addr(&st.B[r0 * CPR + half * (CPR / 2)]);
+    const uint32_t b1 = lds_addr(&st.B[r1 * CPR + half * (CPR / 2)]);
+    const uint32_t s0 = lds_addr(&st.S[r0]), s1 = lds_addr(&st.S[r1]);
+    if constexpr (BITS == 4) {
+      asm volatile(
+          "ds_read_b128 %0, %4\n\t"
+          "ds_read_b128 %1, %5\n\t"
+          "ds_read_b32 %2, %6\n\t"
+          "ds_read_b32 %3, %7\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(f.q[0][0]), "=&v"(f.q[1][0]), "=&v"(f.sb[0]), "=&v"(f.sb[1])
+          : "v"(b0), "v"(b1), "v"(s0), "v"(s1)
+          : "memory");
+    } else {
+      asm volatile(
+          "ds_read_b128 %0, %6\n\t"
+          "ds_read_b128 %1, %6 offset:16\n\t"
+          "ds_read_b128 %2, %7\n\t"
+          "ds_read_b128 %3, %7 offset:16\n\t"
+          "ds_read_b32 %4, %8\n\t"
+          "ds_read_b32 %5, %9\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(f.q[0][0]), "=&v"(f.q[0][1]), "=&v"(f.q[1][0]), "=&v"(f.q[1][1]),
+            "=&v"(f.sb[0]), "=&v"(f.sb[1])
+          : "v"(b0), "v"(b1), "v"(s0), "v"(s1)
+          : "memory");
+    }
+  }
+}
+
+template <int BITS, typename F>
+__device__ __forceinline__ void dn_stage(const DnStage<BITS>& st, int later, int wm, int wn,
+                                         int l32, int half, f32x16 (&C)[2][2], F&& refill) {
+  constexpr int L = dn_stage_loads<BITS>();
+  static_assert(kStages == 3, "wait ladder below covers kStages - 1 = 2 later stages");
+  if (later >= 2) wait_vm<2 * L>();
+  else if (later == 1) wait_vm<L>();
+  else wait_vm<0>();
+  lds_barrier();
+  DnFrags<BITS> f;
+  const f32x16 zero = {};
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = zero;
+  dn_read<BITS, true>(st, 0, wm, wn, l32, half, f);
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    if (kk == 2) {
+      dn_read<BITS, false>(st, 2, wm, wn, l32, half, f);
+      lds_barrier();
+      refill();
+    }
+    u32x4 b[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) b[nb] = gu_bfrag<BITS>(f.q[nb], kk);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        acc[mb][nb] = mfma(f.ah[mb][kk & 1], b[nb], acc[mb][nb]);
+        acc[mb][nb] = mfma(f.al[mb][kk & 1], b[nb], acc[mb][nb]);
+      }
+  }
+  const float scl[2] = {code_scale<BITS>(f.sb[0]), code_scale<BITS>(f.sb[1])};
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) C[mb][nb][r] += scl[nb] * acc[mb][nb][r];
+}
+
+// One down tile: 128 bucket rows x 128 output columns (down weight rows
+// n0 .. n0+127).  Wave (wm, wn) owns rows 64 wm .. +63 and columns
+// 64 wn .. +63 (two blocks of 32).  Writes roww * (h . Wd^T) of every row to
+// its partial row.
+template <int BITS>
+__device__ __forceinline__ void prefill_down_item(MOE_PDN_PARAMS, DnStage<BITS>& s0,
+                                                  DnStage<BITS>& s1, DnStage<BITS>& s2,
+                                                  int32_t* rowdst, float* roww, XcdItem it) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, half = lane >> 5;
-  if ((int)blockIdx.y >= *ntiles) return;
-  const TileInfo ti = get_tile(tiles, counts, offsets, blockIdx.y, E);
+  const TileInfo ti = get_tile(tiles, counts, offsets, it.tile, E);
   const bool shared = ti.e == E;
   const int inter = shared ? Is : I;
-  const int n0 = blockIdx.x * 128;
+  const int n0 = it.nb * 128;
   const uint8_t* sec = shared ? shared_blob + d_off_s
                               : slab + (int64_t)slot_table[ti.e] * stride + d_off_r;
   const int64_t unit_b = shared ? d_unit_s : d_unit_r, tile_b = shared ? d_tile_s : d_tile_r;
@@ -517,49 +922,30 @@ __global__ __launch_bounds__(256) void prefill_down_kernel(
                                : (int64_t)ti.base * 2 * I;
   const int64_t sbase = shared ? (int64_t)T * k * (I / kGroup) + (int64_t)ti.base * G
                                : (int64_t)ti.base * G;
-  const int sr = tid >> 1, sc = tid & 1;
-  const bool srow_ok = sr < ti.rows;
-  const uint16_t* hrow = h + hbase + (int64_t)(srow_ok ? sr : 0) * 2 * inter + 32 * sc;
-  const RowAddr<BITS> wr[2] = {
-      RowAddr<BITS>(sec, unit_b, tile_b, 1, 0, n0 + 64 * wn + l32, half),
-      RowAddr<BITS>(sec, unit_b, tile_b, 1, 0, n0 + 64 * wn + 32 + l32, half)};
 
-  uint4 rh[4], rl[4];
-  LaneCodes<BITS> cn[2];
-  uint32_t sbn[2];
-  float rs = 0.f;
-  auto load_stage = [&](int g) {
-    if (tid < ti.rows) rs = hsum[sbase + (int64_t)tid * G + g];
-    if (srow_ok) {
-      const uint4* ph = reinterpret_cast<const uint4*>(hrow + g * kGroup);
-      const uint4* pl = reinterpret_cast<const uint4*>(hrow + inter + g * kGroup);
+  DnSrc P;
+  P.h = reinterpret_cast<const uint8_t*>(h + hbase);
+  P.sec = sec;
+  P.unit_b = unit_b;
+  P.inter2 = inter * 2;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        rh[q] = ph[q];
-        rl[q] = pl[q];
-      }
-    } else {
+  for (int j = 0; j < 4; ++j) {
+    const int ch = j * 256 + tid, r = ch >> 3, c = (ch & 7) ^ (r & 7);
+    const int rr = r < ti.rows ? r : 0;  // rows past the tile read row 0 (discarded)
+    P.a[j] = (uint32_t)(((int64_t)rr * 2 * inter + c * 8) * 2);
+  }
+  {
+    constexpr int CPR = kGroup * BITS / 8 / 16;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        rh[q] = make_uint4(0, 0, 0, 0);
-        rl[q] = make_uint4(0, 0, 0, 0);
-      }
+    for (int j = 0; j < BITS / 4; ++j) {
+      const int ch = j * 256 + tid, rr = ch / CPR, c = ch % CPR;
+      const RowAddr<BITS> ra(sec, unit_b, tile_b, 1, 0, n0 + rr, 0);
+      P.b[j] = (uint32_t)(ra.codes - sec) + c * 16;
     }
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      cn[nb].load(wr[nb].group_codes(g));
-      sbn[nb] = wr[nb].group_sb(g);
-    }
-  };
-  auto store_stage = [&](int buf) {
-    const int o = buf * kMT * kLdsRow + sr * kLdsRow + sc * 32;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      *reinterpret_cast<uint4*>(Ah + o + 8 * q) = rh[q];
-      *reinterpret_cast<uint4*>(Al + o + 8 * q) = rl[q];
-    }
-    if (tid < kMT) HS[buf * kMT + tid] = rs;
-  };
+    const RowAddr<BITS> ra(sec, unit_b, tile_b, 1, 0, n0 + (tid & 127), 0);
+    P.sb = (uint32_t)(ra.sb - sec);
+  }
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
 
   f32x16 C[2][2];
   const f32x16 zero = {};
@@ -568,62 +954,37 @@ __global__ __launch_bounds__(256) void prefill_down_kernel(
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) C[mb][nb] = zero;
 
+  for (int g = -kStages; g < G; g += kStages) {
+#define MOE_DN_STEP(I, BUF)                                                              \
+  if (g + I >= G) break;                                                                 \
+  {                                                                                      \
+    auto refill = [&]() {                                                                \
+      if (g + I + kStages < G) dn_issue<BITS>(P, BUF, g + I + kStages, wv);              \
+    };                                                                                   \
+    if (g >= 0) dn_stage<BITS>(BUF, min(kStages - 1, G - 1 - g - I), wm, wn, l32, half, C, \
+                               refill);                                                  \
+    else refill();                                                                       \
+  }
+    MOE_DN_STEP(0, s0)
+    MOE_DN_STEP(1, s1)
+    MOE_DN_STEP(2, s2)
+#undef MOE_DN_STEP
+  }
+  __syncthreads();  // rowdst / roww written before the loop
 
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
-  for (int g = 0; g < G; ++g) {
-    const LaneCodes<BITS> cc[2] = {cn[0], cn[1]};
-    const float scl[2] = {code_scale<BITS>(sbn[0]), code_scale<BITS>(sbn[1])};
-    const float bco[2] = {bias_coef<BITS>(sbn[0]), bias_coef<BITS>(sbn[1])};
-    if (g + 1 < G) load_stage(g + 1);
-    const int so = (g & 1) * kMT * kLdsRow;
-    f32x16 acc[2][2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = zero;
-#pragma unroll
-    for (int ks = 0; ks < kGroup / 16; ++ks) {
-      u32x4 ah[2], al[2], b[2];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const int o = so + (64 * wm + 32 * mb + l32) * kLdsRow + 32 * half + 8 * ks;
-        ah[mb] = *reinterpret_cast<const u32x4*>(Ah + o);
-        al[mb] = *reinterpret_cast<const u32x4*>(Al + o);
-      }
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) b[nb] = cc[nb].frag(ks);
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma(ah[mb], b[nb], acc[mb][nb]);
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma(al[mb], b[nb], acc[mb][nb]);
-    }
-    // C += scale * code sums + bias * (group sum of the row's h)
+  // bias terms from the group sums of the h rows
+  {
+    const RowAddr<BITS> wr[2] = {
+        RowAddr<BITS>(sec, unit_b, tile_b, 1, 0, n0 + 64 * wn + l32, half),
+        RowAddr<BITS>(sec, unit_b, tile_b, 1, 0, n0 + 64 * wn + 32 + l32, half)};
+    const float* srow[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      float4 hv[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        hv[q] = *reinterpret_cast<const float4*>(HS + (g & 1) * kMT + 64 * wm + 32 * mb + 8 * q +
-                                                 4 * half);
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float4 t = hv[r / 4];
-          const float hsv = (r % 4) == 0 ? t.x : (r % 4) == 1 ? t.y : (r % 4) == 2 ? t.z : t.w;
-          C[mb][nb][r] += scl[nb] * acc[mb][nb][r] + bco[nb] * hsv;
-        }
+      const int m = 64 * wm + 32 * mb + l32;
+      srow[mb] = m < ti.rows ? hsum + sbase + (int64_t)m * G : nullptr;
     }
-    if (g + 1 < G) store_stage((g + 1) & 1);
-    __syncthreads();
+    bias_mfma<BITS>(srow, wr, G, half, C);
   }
-
 
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
@@ -636,6 +997,43 @@ __global__ __launch_bounds__(256) void prefill_down_kernel(
         if (dst >= 0)
           partial[(int64_t)dst * H + n0 + 64 * wn + 32 * nb + l32] = roww[m] * C[mb][nb][r];
       }
+}
+
+// Persistent grids: workgroup w serves XCD w % 8 and walks that XCD's item
+// range (see xcd_item) with a stride of gridDim.x / 8.
+template <int BITS>
+__global__ __launch_bounds__(256, BITS == 4 ? 2 : 1) void prefill_gateup_kernel(MOE_PGU_PARAMS) {
+  __shared__ __align__(16) GuStage<BITS> s0;
+  __shared__ __align__(16) GuStage<BITS> s1;
+  __shared__ __align__(16) GuStage<BITS> s2;
+  __shared__ int32_t rowsrc[kMT];
+  const int total = *ntiles * nbg;
+  const int per = (total + 7) / 8, c = blockIdx.x & 7;
+  for (int i = blockIdx.x >> 3; i < per; i += gridDim.x >> 3) {
+    const int q = c * per + i;
+    if (q >= total) break;
+    prefill_gateup_item<BITS>(MOE_PGU_ARGS, s0, s1, s2, rowsrc,
+                              XcdItem{q / nbg, q % nbg, true});
+    __syncthreads();
+  }
+}
+
+template <int BITS>
+__global__ __launch_bounds__(256) void prefill_down_kernel(MOE_PDN_PARAMS) {
+  __shared__ __align__(16) DnStage<BITS> s0;
+  __shared__ __align__(16) DnStage<BITS> s1;
+  __shared__ __align__(16) DnStage<BITS> s2;
+  __shared__ int32_t rowdst[kMT];
+  __shared__ float roww[kMT];
+  const int total = *ntiles * nbg;
+  const int per = (total + 7) / 8, c = blockIdx.x & 7;
+  for (int i = blockIdx.x >> 3; i < per; i += gridDim.x >> 3) {
+    const int q = c * per + i;
+    if (q >= total) break;
+    prefill_down_item<BITS>(MOE_PDN_ARGS, s0, s1, s2, rowdst, roww,
+                            XcdItem{q / nbg, q % nbg, true});
+    __syncthreads();
+  }
 }
 
 template <int BITS>
@@ -651,16 +1049,19 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s) {
                      a.xsum, a.T, a.H);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int nbg = (max(a.I, a.Is) + kGroup - 1) / kGroup;
-  hipLaunchKernelGGL((prefill_gateup_kernel<BITS>), dim3(nbg, a.max_tiles), dim3(256), 0, s, a.x,
+  const unsigned slots_gu = (unsigned)min((a.max_tiles * nbg + 7) / 8 * 8, kPersistSlots);
+  hipLaunchKernelGGL((prefill_gateup_kernel<BITS>), dim3(slots_gu), dim3(256), 0, s, a.x,
                      a.xsum, a.pairs, a.counts, a.offsets, a.tiles, a.ntiles, a.slab, a.slot_table,
                      a.stride, a.shared_blob, a.h, a.hsum, a.T, a.H, a.E, a.k, a.I, a.Is,
-                     a.L.gu_unit, a.L.gu_tile, a.Ls.gu_unit, a.Ls.gu_tile);
+                     a.L.gu_unit, a.L.gu_tile, a.Ls.gu_unit, a.Ls.gu_tile, nbg);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((prefill_down_kernel<BITS>), dim3(a.H / 128, a.max_tiles), dim3(256), 0, s,
+  const int nbd = a.H / 128;
+  const unsigned slots_d = (unsigned)min((a.max_tiles * nbd + 7) / 8 * 8, kPersistSlots);
+  hipLaunchKernelGGL((prefill_down_kernel<BITS>), dim3(slots_d), dim3(256), 0, s,
                      a.h, a.hsum, a.pairs, a.topk_w, a.gamma, a.counts, a.offsets, a.tiles,
                      a.ntiles, a.slab, a.slot_table, a.stride, a.shared_blob, a.partial, a.T, a.H,
                      a.E, a.k, a.I, a.Is, a.L.d_off, a.L.d_unit, a.L.d_tile, a.Ls.d_off,
-                     a.Ls.d_unit, a.Ls.d_tile);
+                     a.Ls.d_unit, a.Ls.d_tile, nbd);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 return hipSuccess;
 }

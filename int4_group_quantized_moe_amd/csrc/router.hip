@@ -5,6 +5,7 @@
 // or 8 of 256 experts per layer and token; the routers stay resident).
 // Renormalised top-k weights equal the softmax over the k selected logits,
 // so the E-way softmax sum is never formed.
+#include "decode_common.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -125,64 +126,46 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const void* __restrict
   }
 }
 
-// One wave per token: k rounds of a wave-wide (max logit, lowest index)
-// reduction, then the softmax over the k selected logits.
+// One wave per token: the exact wavefront top-k (threshold from DPP wave
+// maxima, ballot compaction, rank; k rounds of argmax when more than 64
+// logits tie at the threshold), then the softmax over the k selected logits.
+template <int MPL>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits,
                                                    int32_t* __restrict__ topk_idx,
                                                    float* __restrict__ topk_w,
                                                    float* __restrict__ gamma, int T, int E,
                                                    int k, int has_gate) {
-  constexpr int kMaxPerLane = MOE_MAX_EXPERTS / 64;
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  __shared__ int32_t sel_idx[4][MOE_MAX_TOP_K];
+  __shared__ float sel_val[4][MOE_MAX_TOP_K], sel_w[4][MOE_MAX_TOP_K], gam[4];
+  __shared__ __align__(16) uint32_t cand_key[4][64];
+  __shared__ __align__(16) int32_t cand_idx[4][64];
+  __shared__ float cand_val[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
-  const float* l = logits + (int64_t)t * (E + 1);
-  float v[kMaxPerLane];
-  const int per_lane = (E + 63) / 64;
-#pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) {
-    const int e = i * 64 + lane;
-    v[i] = (i < per_lane && e < E) ? l[e] : -INFINITY;
+  dec::wave_topk<MPL>(logits + (int64_t)t * (E + 1), E, k, has_gate != 0, sel_idx[wave],
+                      sel_val[wave], sel_w[wave], &gam[wave], cand_key[wave], cand_idx[wave],
+                      cand_val[wave]);
+  if (lane < k) {
+    topk_idx[(int64_t)t * k + lane] = sel_idx[wave][lane];
+    topk_w[(int64_t)t * k + lane] = sel_w[wave][lane];
   }
-  unsigned taken = 0u;  // bit i: v[i] already selected
-  float sel_v[MOE_MAX_TOP_K];
-  int sel_i[MOE_MAX_TOP_K];
-  for (int r = 0; r < k; ++r) {
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
-#pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
-      const int e = i * 64 + lane;
-      if (i < per_lane && e < E && !((taken >> i) & 1u)) {
-        if (v[i] > bv || (v[i] == bv && e < bi)) {
-          bv = v[i];
-          bi = e;
-        }
-      }
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, 64);
-      const int oi = __shfl_xor(bi, off, 64);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    sel_v[r] = bv;
-    sel_i[r] = bi;
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-  }
-  if (lane == 0) {
-    float den = 0.0f;
-    for (int r = 0; r < k; ++r) den += __expf(sel_v[r] - sel_v[0]);
-    const float inv = 1.0f / den;
-    for (int r = 0; r < k; ++r) {
-      topk_idx[(int64_t)t * k + r] = sel_i[r];
-      topk_w[(int64_t)t * k + r] = __expf(sel_v[r] - sel_v[0]) * inv;
-    }
-    if (has_gate && gamma != nullptr) gamma[t] = 1.0f / (1.0f + __expf(-l[E]));
-  }
+  if (lane == 0 && has_gate && gamma != nullptr) gamma[t] = gam[wave];
+}
+
+hipError_t launch_topk(const RouterArgs& a, hipStream_t s) {
+  const dim3 grid((a.T + 3) / 4), block(256);
+  const int hg = a.shared_gate_w ? 1 : 0;
+  if (a.E <= 256)
+    hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, a.logits, a.topk_idx, a.topk_w,
+                       a.gamma, a.T, a.E, a.k, hg);
+  else if (a.E <= 512)
+    hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, s, a.logits, a.topk_idx, a.topk_w,
+                       a.gamma, a.T, a.E, a.k, hg);
+  else
+    hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, a.logits, a.topk_idx, a.topk_w,
+                       a.gamma, a.T, a.E, a.k, hg);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -323,9 +306,7 @@ hipError_t launch_router_act(const RouterArgs& a, hipStream_t s) {
     hipError_t e = launch_router_gemv<ACT>(a, s);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(topk_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a.logits, a.topk_idx,
-                     a.topk_w, a.gamma, a.T, a.E, a.k, a.shared_gate_w ? 1 : 0);
-  return hipGetLastError();
+  return launch_topk(a, s);
 }
 
 template <int ACT>
