@@ -15,7 +15,7 @@ constexpr int kRowBytes = 64;        // code bytes per row per k-block
 constexpr int kCodeBlockBytes = kRowTile * kRowBytes;  // 1 KiB
 constexpr int kGroup = 64;
 constexpr int kDecodeMaxTokens = 8;    // up to this many tokens: per-pair GEMV path
-constexpr int kMfmaMinRows = 16;  // bf16 buckets of this many tokens run on the MFMA grouped GEMMs
+constexpr int kMfmaMinRows = 4;  // bf16 buckets of this many tokens run on the MFMA grouped GEMMs
 
 inline int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
@@ -70,6 +70,9 @@ struct WsPlan {
   bool bucketed;
 };
 
+// Logit planes of the router GEMM's K split (small batches only).
+inline int router_planes(int64_t T) { return T < 1024 ? 8 : 1; }
+
 inline WsPlan make_ws_plan(const moe_layer_desc& d) {
   WsPlan p{};
   const int64_t T = d.n_tokens, E = d.n_experts, k = d.top_k, H = d.hidden;
@@ -83,7 +86,7 @@ inline WsPlan make_ws_plan(const moe_layer_desc& d) {
     return at;
   };
   p.bucketed = T > kDecodeMaxTokens;
-  p.logits = take(sizeof(float) * T * (E + 1));
+  p.logits = take(sizeof(float) * T * (E + 1) * router_planes(T));
   p.idx = take(sizeof(int32_t) * T * k);
   p.w = take(sizeof(float) * T * k);
   p.gamma = take(sizeof(float) * T);

@@ -726,47 +726,53 @@ __device__ __forceinline__ void prefill_gateup_item(MOE_PGU_PARAMS, GuStage<BITS
       shared_blob, partial, T, H, E, k, I, Is, d_off_r, d_unit_r, d_tile_r, d_off_s, d_unit_s, \
       d_tile_s, nbg
 
-// Down K pipeline: the same scheme as gate/up, with the stage holding the
-// 128 h rows as bf16 (hi, lo) parts and the 128 output rows' codes.
+// Down K pipeline: the same scheme as gate/up with 512 threads and a
+// 128-row x 256-column tile; a stage holds the 128 h rows as bf16 (hi, lo)
+// parts and the 256 output rows' codes and (scale, bias) words.
+constexpr int kDnThreads = 512;
+constexpr int kDnCols = 256;
+
 template <int BITS>
 struct DnStage {
   uint4 Ah[kStageChunks];
   uint4 Al[kStageChunks];
-  uint4 B[128 * (kGroup * BITS / 8) / 16];
-  uint32_t S[256];
+  uint4 B[kDnCols * (kGroup * BITS / 8) / 16];
+  uint32_t S[kDnThreads];  // (scale, bias) of rows 0..255 (256..511 repeat them)
 };
 
 template <int BITS>
-constexpr int dn_stage_loads() { return 8 + BITS / 4 + 1; }
+constexpr int dn_stage_loads() { return 4 + BITS / 4 + 1; }
 
+template <int BITS>
 struct DnSrc {
   const uint8_t* h;    // h rows of the tile (uniform base)
   const uint8_t* sec;  // blob down section (uniform)
   int64_t unit_b;
   int inter2;          // bytes from a row's hi part to its lo part
-  uint32_t a[4];       // h chunk offsets (stage 0, hi part)
-  uint32_t b[2];       // code chunk offsets (k-block 0, group 0)
+  uint32_t a[2];       // h chunk offsets (stage 0, hi part)
+  uint32_t b[BITS / 4];  // code chunk offsets (k-block 0, group 0)
   uint32_t sb;         // (scale, bias) word offset
 };
 
 template <int BITS>
-__device__ __forceinline__ void dn_issue(const DnSrc& P, DnStage<BITS>& st, int g, int wave) {
+__device__ __forceinline__ void dn_issue(const DnSrc<BITS>& P, DnStage<BITS>& st, int g,
+                                         int wave) {
   constexpr int GPK = kRowBytes * (8 / BITS) / kGroup;
   constexpr int GBYTES = kGroup * BITS / 8;
   const uint8_t* ha = P.h + (int64_t)g * kGroup * 2;
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    __builtin_amdgcn_global_load_lds(MOE_G1(ha + P.a[j]), MOE_L3(&st.Ah[j * 256 + wave * 64]), 16,
+  for (int j = 0; j < 2; ++j)
+    __builtin_amdgcn_global_load_lds(MOE_G1(ha + P.a[j]), MOE_L3(&st.Ah[j * 512 + wave * 64]), 16,
                                      0, 0);
   const uint8_t* la = ha + P.inter2;
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    __builtin_amdgcn_global_load_lds(MOE_G1(la + P.a[j]), MOE_L3(&st.Al[j * 256 + wave * 64]), 16,
+  for (int j = 0; j < 2; ++j)
+    __builtin_amdgcn_global_load_lds(MOE_G1(la + P.a[j]), MOE_L3(&st.Al[j * 512 + wave * 64]), 16,
                                      0, 0);
   const uint8_t* wb = P.sec + (int64_t)(g / GPK) * P.unit_b + (g % GPK) * GBYTES;
 #pragma unroll
   for (int j = 0; j < BITS / 4; ++j)
-    __builtin_amdgcn_global_load_lds(MOE_G1(wb + P.b[j]), MOE_L3(&st.B[j * 256 + wave * 64]), 16,
+    __builtin_amdgcn_global_load_lds(MOE_G1(wb + P.b[j]), MOE_L3(&st.B[j * 512 + wave * 64]), 16,
                                      0, 0);
   const uint8_t* sbb = P.sec + (int64_t)(g / GPK) * P.unit_b + (g % GPK) * 4;
   __builtin_amdgcn_global_load_lds(MOE_G1(sbb + P.sb), MOE_L3(&st.S[wave * 64]), 4, 0, 0);
@@ -882,20 +888,20 @@ __device__ __forceinline__ void dn_stage(const DnStage<BITS>& st, int later, int
       for (int r = 0; r < 16; ++r) C[mb][nb][r] += scl[nb] * acc[mb][nb][r];
 }
 
-// One down tile: 128 bucket rows x 128 output columns (down weight rows
-// n0 .. n0+127).  Wave (wm, wn) owns rows 64 wm .. +63 and columns
-// 64 wn .. +63 (two blocks of 32).  Writes roww * (h . Wd^T) of every row to
-// its partial row.
+// One down tile: 128 bucket rows x 256 output columns (down weight rows
+// n0 .. n0+255).  Wave (wm, wn) = (wave / 4, wave % 4) owns rows
+// 64 wm .. +63 and columns 64 wn .. +63 (two blocks of 32).  Writes
+// roww * (h . Wd^T) of every row to its partial row.
 template <int BITS>
 __device__ __forceinline__ void prefill_down_item(MOE_PDN_PARAMS, DnStage<BITS>& s0,
                                                   DnStage<BITS>& s1, DnStage<BITS>& s2,
                                                   int32_t* rowdst, float* roww, XcdItem it) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, half = lane >> 5;
+  const int wm = wave >> 2, wn = wave & 3, l32 = lane & 31, half = lane >> 5;
   const TileInfo ti = get_tile(tiles, counts, offsets, it.tile, E);
   const bool shared = ti.e == E;
   const int inter = shared ? Is : I;
-  const int n0 = it.nb * 128;
+  const int n0 = it.nb * kDnCols;
   const uint8_t* sec = shared ? shared_blob + d_off_s
                               : slab + (int64_t)slot_table[ti.e] * stride + d_off_r;
   const int64_t unit_b = shared ? d_unit_s : d_unit_r, tile_b = shared ? d_tile_s : d_tile_r;
@@ -923,14 +929,14 @@ __device__ __forceinline__ void prefill_down_item(MOE_PDN_PARAMS, DnStage<BITS>&
   const int64_t sbase = shared ? (int64_t)T * k * (I / kGroup) + (int64_t)ti.base * G
                                : (int64_t)ti.base * G;
 
-  DnSrc P;
+  DnSrc<BITS> P;
   P.h = reinterpret_cast<const uint8_t*>(h + hbase);
   P.sec = sec;
   P.unit_b = unit_b;
   P.inter2 = inter * 2;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int ch = j * 256 + tid, r = ch >> 3, c = (ch & 7) ^ (r & 7);
+  for (int j = 0; j < 2; ++j) {
+    const int ch = j * 512 + tid, r = ch >> 3, c = (ch & 7) ^ (r & 7);
     const int rr = r < ti.rows ? r : 0;  // rows past the tile read row 0 (discarded)
     P.a[j] = (uint32_t)(((int64_t)rr * 2 * inter + c * 8) * 2);
   }
@@ -938,11 +944,11 @@ __device__ __forceinline__ void prefill_down_item(MOE_PDN_PARAMS, DnStage<BITS>&
     constexpr int CPR = kGroup * BITS / 8 / 16;
 #pragma unroll
     for (int j = 0; j < BITS / 4; ++j) {
-      const int ch = j * 256 + tid, rr = ch / CPR, c = ch % CPR;
+      const int ch = j * 512 + tid, rr = ch / CPR, c = ch % CPR;
       const RowAddr<BITS> ra(sec, unit_b, tile_b, 1, 0, n0 + rr, 0);
       P.b[j] = (uint32_t)(ra.codes - sec) + c * 16;
     }
-    const RowAddr<BITS> ra(sec, unit_b, tile_b, 1, 0, n0 + (tid & 127), 0);
+    const RowAddr<BITS> ra(sec, unit_b, tile_b, 1, 0, n0 + (tid & (kDnCols - 1)), 0);
     P.sb = (uint32_t)(ra.sb - sec);
   }
   const int wv = __builtin_amdgcn_readfirstlane(wave);
@@ -970,7 +976,7 @@ __device__ __forceinline__ void prefill_down_item(MOE_PDN_PARAMS, DnStage<BITS>&
     MOE_DN_STEP(2, s2)
 #undef MOE_DN_STEP
   }
-  __syncthreads();  // rowdst / roww written before the loop
+  __syncthreads();
 
   // bias terms from the group sums of the h rows
   {
@@ -1019,7 +1025,7 @@ __global__ __launch_bounds__(256, BITS == 4 ? 2 : 1) void prefill_gateup_kernel(
 }
 
 template <int BITS>
-__global__ __launch_bounds__(256) void prefill_down_kernel(MOE_PDN_PARAMS) {
+__global__ __launch_bounds__(kDnThreads) void prefill_down_kernel(MOE_PDN_PARAMS) {
   __shared__ __align__(16) DnStage<BITS> s0;
   __shared__ __align__(16) DnStage<BITS> s1;
   __shared__ __align__(16) DnStage<BITS> s2;
@@ -1055,9 +1061,9 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s) {
                      a.stride, a.shared_blob, a.h, a.hsum, a.T, a.H, a.E, a.k, a.I, a.Is,
                      a.L.gu_unit, a.L.gu_tile, a.Ls.gu_unit, a.Ls.gu_tile, nbg);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int nbd = a.H / 128;
+  const int nbd = a.H / kDnCols;
   const unsigned slots_d = (unsigned)min((a.max_tiles * nbd + 7) / 8 * 8, kPersistSlots);
-  hipLaunchKernelGGL((prefill_down_kernel<BITS>), dim3(slots_d), dim3(256), 0, s,
+  hipLaunchKernelGGL((prefill_down_kernel<BITS>), dim3(slots_d), dim3(kDnThreads), 0, s,
                      a.h, a.hsum, a.pairs, a.topk_w, a.gamma, a.counts, a.offsets, a.tiles,
                      a.ntiles, a.slab, a.slot_table, a.stride, a.shared_blob, a.partial, a.T, a.H,
                      a.E, a.k, a.I, a.Is, a.L.d_off, a.L.d_unit, a.L.d_tile, a.Ls.d_off,
@@ -1076,7 +1082,7 @@ int prefill_max_tiles(int T, int E, int k, bool has_shared) {
 
 bool prefill_supported(int act, int H, int I, int Is, bool has_shared) {
   if (act != MOE_ACT_BF16) return false;
-  if (H % 128 != 0 || I % kGroup != 0 || (has_shared && Is % kGroup != 0)) return false;
+  if (H % kDnCols != 0 || I % kGroup != 0 || (has_shared && Is % kGroup != 0)) return false;
   return true;
 }
 

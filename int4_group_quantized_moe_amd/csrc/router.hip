@@ -14,7 +14,7 @@ namespace {
 constexpr int kRouterWaves = 4;     // rows per workgroup (one per wave)
 constexpr int kRouterMaxTT = 8;     // tokens per LDS chunk
 constexpr int kRouterMaxRegIt = 8;  // row cached in registers when H <= 64*4*8
-constexpr int kRouterMfmaMinTokens = 128;  // GEMM on the matrix cores from this batch size (bf16)
+constexpr int kRouterMfmaMinTokens = 16;  // GEMM on the matrix cores from this batch size (bf16)
 
 template <int ACT>
 __device__ __forceinline__ float4 load_act4(const void* p, int64_t i) {
@@ -134,16 +134,34 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
                                                    int32_t* __restrict__ topk_idx,
                                                    float* __restrict__ topk_w,
                                                    float* __restrict__ gamma, int T, int E,
-                                                   int k, int has_gate) {
+                                                   int k, int has_gate, int nplanes) {
   __shared__ int32_t sel_idx[4][MOE_MAX_TOP_K];
   __shared__ float sel_val[4][MOE_MAX_TOP_K], sel_w[4][MOE_MAX_TOP_K], gam[4];
   __shared__ __align__(16) uint32_t cand_key[4][64];
   __shared__ __align__(16) int32_t cand_idx[4][64];
   __shared__ float cand_val[4][64];
+  __shared__ float lsum[4][MPL * 64 + 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
-  dec::wave_topk<MPL>(logits + (int64_t)t * (E + 1), E, k, has_gate != 0, sel_idx[wave],
+  const float* lt = logits + (int64_t)t * (E + 1);
+  if (nplanes > 1) {
+    // logits split over K planes: add them in plane order (the shared-gate
+    // logit, row E, lives in plane 0 only)
+    const int64_t ps = (int64_t)T * (E + 1);
+    for (int e = lane; e <= E; e += 64) {
+      float p[8];
+#pragma unroll
+      for (int z = 0; z < 8; ++z) p[z] = (z < nplanes && (z == 0 || e < E)) ? lt[z * ps + e] : 0.f;
+      float v = p[0];
+#pragma unroll
+      for (int z = 1; z < 8; ++z) v += p[z];
+      lsum[wave][e] = v;
+    }
+    dec::lds_wave_sync();
+    lt = lsum[wave];
+  }
+  dec::wave_topk<MPL>(lt, E, k, has_gate != 0, sel_idx[wave],
                       sel_val[wave], sel_w[wave], &gam[wave], cand_key[wave], cand_idx[wave],
                       cand_val[wave]);
   if (lane < k) {
@@ -153,18 +171,18 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   if (lane == 0 && has_gate && gamma != nullptr) gamma[t] = gam[wave];
 }
 
-hipError_t launch_topk(const RouterArgs& a, hipStream_t s) {
+hipError_t launch_topk(const RouterArgs& a, hipStream_t s, int nplanes) {
   const dim3 grid((a.T + 3) / 4), block(256);
   const int hg = a.shared_gate_w ? 1 : 0;
   if (a.E <= 256)
     hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, a.logits, a.topk_idx, a.topk_w,
-                       a.gamma, a.T, a.E, a.k, hg);
+                       a.gamma, a.T, a.E, a.k, hg, nplanes);
   else if (a.E <= 512)
     hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, s, a.logits, a.topk_idx, a.topk_w,
-                       a.gamma, a.T, a.E, a.k, hg);
+                       a.gamma, a.T, a.E, a.k, hg, nplanes);
   else
     hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, a.logits, a.topk_idx, a.topk_w,
-                       a.gamma, a.T, a.E, a.k, hg);
+                       a.gamma, a.T, a.E, a.k, hg, nplanes);
   return hipGetLastError();
 }
 
@@ -194,24 +212,28 @@ __device__ __forceinline__ void split3_pair(float a, float b, uint32_t& p1, uint
   p3 = (__float_as_uint(sa) >> 16) | (__float_as_uint(sb) & 0xFFFF0000u);
 }
 
+// blockIdx.z splits K: split z sums columns [z*kseg, (z+1)*kseg) into its
+// own logit plane (logits + z*T*(E+1)); the top-k kernel adds the planes.
 __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __restrict__ x,
                                                           const float* __restrict__ W,
                                                           const float* __restrict__ bias,
                                                           float* __restrict__ logits, int T, int H,
-                                                          int E) {
+                                                          int E, int kseg) {
   __shared__ __align__(16) uint16_t A[2 * kRouterTile * kRouterLdsRow];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, half = lane >> 5;
   const int t0 = blockIdx.y * kRouterTile, e0 = blockIdx.x * kRouterTile;
+  const int k0 = blockIdx.z * kseg;
+  logits += (int64_t)blockIdx.z * T * (E + 1);
   // staging: token row sr, 16 columns (2 x 16 bytes) per thread
   const int sr = tid >> 2, sq = tid & 3;
   const bool srow_ok = t0 + sr < T;
-  const uint16_t* xrow = x + (int64_t)(srow_ok ? t0 + sr : 0) * H + 16 * sq;
+  const uint16_t* xrow = x + (int64_t)(srow_ok ? t0 + sr : 0) * H + k0 + 16 * sq;
   // B operand: expert row e, this lane's 32 K columns of each stage
   const int e = e0 + 32 * wn + l32;
   const bool e_ok = e < E;
-  const float* wrow = W + (int64_t)(e_ok ? e : 0) * H + 32 * half;
-  const int S = H / 64;
+  const float* wrow = W + (int64_t)(e_ok ? e : 0) * H + k0 + 32 * half;
+  const int S = kseg / 64;
 
   uint4 ra[2];
   float4 rb[8];
@@ -262,7 +284,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
     __syncthreads();
   }
   if (!e_ok) return;
-  const float b = bias != nullptr ? bias[e] : 0.0f;
+  const float b = (bias != nullptr && blockIdx.z == 0) ? bias[e] : 0.0f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int t = t0 + 32 * wm + 8 * (r / 4) + 4 * half + (r % 4);
@@ -279,8 +301,22 @@ __global__ __launch_bounds__(256) void gate_logit_kernel(const void* __restrict_
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
+  // 4 consecutive columns per lane and step, loads of a few steps in flight
   float acc = 0.f;
-  for (int c = lane; c < H; c += 64) acc += wsg[c] * load_act<ACT>(x, (int64_t)t * H + c);
+  constexpr int kU = 4;
+  for (int c0 = 4 * lane; c0 < H; c0 += 256 * kU) {
+    float4 xv[kU], wv[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int c = c0 + 256 * u;
+      const bool ok = c < H;
+      xv[u] = ok ? load_act4<ACT>(x, (int64_t)t * H + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+      wv[u] = ok ? *reinterpret_cast<const float4*>(wsg + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      acc += wv[u].x * xv[u].x + wv[u].y * xv[u].y + wv[u].z * xv[u].z + wv[u].w * xv[u].w;
+  }
   acc = warp_sum(acc);
   if (lane == 0) logits[(int64_t)t * (E + 1) + E] = acc;
 }
@@ -290,11 +326,18 @@ hipError_t launch_router_gemv(const RouterArgs& a, hipStream_t s);
 
 template <int ACT>
 hipError_t launch_router_act(const RouterArgs& a, hipStream_t s) {
+  int nplanes = 1;
   if (ACT == MOE_ACT_BF16 && a.T >= kRouterMfmaMinTokens && a.H % 64 == 0) {
+    // split K so that small batches still fill the chip (at most the planes
+    // the workspace holds)
+    const int tiles = ((a.E + kRouterTile - 1) / kRouterTile) * ((a.T + kRouterTile - 1) / kRouterTile);
+    const int maxp = router_planes(a.T);
+    while (nplanes < maxp && tiles * nplanes < 256 && (a.H / 64) % (2 * nplanes) == 0) nplanes *= 2;
     hipLaunchKernelGGL(router_mfma_kernel,
-                       dim3((a.E + kRouterTile - 1) / kRouterTile, (a.T + kRouterTile - 1) / kRouterTile),
+                       dim3((a.E + kRouterTile - 1) / kRouterTile,
+                            (a.T + kRouterTile - 1) / kRouterTile, nplanes),
                        dim3(256), 0, s, reinterpret_cast<const uint16_t*>(a.x), a.router_w,
-                       a.router_bias, a.logits, a.T, a.H, a.E);
+                       a.router_bias, a.logits, a.T, a.H, a.E, a.H / nplanes);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.shared_gate_w) {
@@ -306,7 +349,7 @@ hipError_t launch_router_act(const RouterArgs& a, hipStream_t s) {
     hipError_t e = launch_router_gemv<ACT>(a, s);
     if (e != hipSuccess) return e;
   }
-  return launch_topk(a, s);
+  return launch_topk(a, s, nplanes);
 }
 
 template <int ACT>
