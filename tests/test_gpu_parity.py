@@ -445,3 +445,26 @@ def test_grouped_mfma_path_80b(cfgname, T):
     check_layer(cfg, 0, x_np[tok], out[tok], idx[tok], wt[tok], g[tok], f"{cfgname} T={T}")
     del w
     _free()
+
+
+@pytest.mark.parametrize("T,k", [(15, 2), (16, 2), (17, 3), (40, 16), (127, 4), (128, 2),
+                                 (129, 5)])
+def test_bf16_batch_thresholds(T, k):
+    """bf16 batches around the MFMA router threshold (16 tokens; K split over
+    logit planes below 1024 tokens) and the grouped-GEMM bucket threshold (4
+    tokens), so that one layer mixes GEMV and MFMA buckets."""
+    wl = _wl()
+    cfg = configs.TINY.with_(n_tokens=T, top_k=k, act="bf16")
+    say(f"[thresholds] tiny bf16 T={T} k={k}")
+    w = wl.Workload(cfg, n_layers=1)
+    x_np = synth.activations(cfg)
+    x = wl.act_tensor(cfg, x_np)
+    out, idx, wt, g = run_layer(w, cfg, x)
+    counts = np.bincount(idx.cpu().numpy().ravel(), minlength=cfg.n_experts)
+    say(f"  bucket sizes {sorted(counts.tolist())}")
+    check_layer(cfg, 0, x_np, out, idx, wt, g, f"thresholds T={T} k={k}")
+    # same layer again: bitwise identical
+    out2 = run_layer(w, cfg, x)[0]
+    assert torch.equal(out, out2)
+    del w
+    _free()
