@@ -6,23 +6,25 @@
 // before the down projection).  Kernel boundaries cost about as much as an
 // in-kernel exchange plus a cold first load, so here the exchanges stay
 // inside the kernel: each producer stores 64-bit words (epoch << 32 | payload)
-// with relaxed device-scope atomics, each consumer polls them with relaxed
-// device-scope atomic loads.  A word is its own ready flag (no fences, no
-// counters, no contention).  The epoch is read from the workspace at start
+// with device-coherent stores, each consumer polls them with device-coherent
+// loads, two words per 16-byte access.  A word is its own ready flag (no
+// fences, no counters, no contention).  The epoch is read from the workspace at start
 // and advanced by workgroup 0 at the end, so graph replays never see stale
 // words.  Every poll is bounded: on expiry an error bit is set and the
 // workgroup carries on, so the grid always drains.
 //
 // Per layer l, workgroup w of NWG:
-//   prefetch  router row(s) w + NWG*wave, the layer's slot table, the
-//             shared expert's gate/up tiles and down units owned by w
-//   A         x_l (layer 0: input buffer; else polled), RMSNorm, x_hat
-//             staged for the gate/up dot products, router logits published
-//   B         shared-expert gate/up tiles first; then the top-k of the
-//             polled logits; the routed down units of phase C are issued;
-//             routed gate/up tiles; h published
-//   C         all h polled; down GEMV of 8 output rows over all selected
-//             experts in a fixed order; residual add; x_{l+1} published
+//   A   x_l (layer 0: input buffer; else polled), RMSNorm, router logit(s)
+//       published, then x_hat staged for the gate/up dot products
+//   B   wave 0 polls the logits and finds the top-k set while waves 1-3
+//       take their share of the shared expert's (prefetched) tile; the
+//       routed gate/up tiles are loaded; while they load, wave 0 computes
+//       the routing weights and its share of the shared tile, whose h is
+//       published; then the routed tiles; h published; then the down units
+//       of phase C are issued
+//   C   all h polled; the next layer's router row, slot table and shared
+//       tile are prefetched; down GEMV of 8 output rows over all selected
+//       experts in a fixed order; residual add; x_{l+1} published
 //
 // Routing: top-k of E experts per token plus an always-active shared expert
 // (page "Paquets Swiftlet 80B Qwen ..." on xix.ai, 4th paragraph); weights
@@ -38,37 +40,65 @@ constexpr uint32_t kSpinLimit = 1u << 18;
 constexpr int kChainMaxExperts = 512;  // top-k over at most 8 logits per lane
 template <int BITS>
 constexpr int max_down_units() { return BITS == 4 ? 6 : 12; }  // per half-wave
+constexpr int kHPairs = 8;     // h word pairs per thread per poll batch
+constexpr int kHqStride = 20;  // LDS words per staged 32-column chunk of h
+constexpr int kHTilePairs = 6; // exchange word pairs per 16-row tile of h
 
-__device__ __forceinline__ uint64_t ld_word(const uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+// Cache policy of every exchange access: sc1 (device scope), so loads are
+// served past the XCD-local L2 and see what other XCDs stored.
+constexpr int kCoherent = 16;
+
+// Buffer view of an exchange region of n 64-bit words, rounded up to a whole
+// pair (the workspace pads every region to 256 bytes).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t word_rsrc(const uint64_t* base, int n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint64_t*>(base), (short)0,
+                                           ((n + 1) & ~1) * 8, 0x00020000);
 }
+
 __device__ __forceinline__ void st_word(uint64_t* p, uint32_t ep, uint32_t payload) {
   __hip_atomic_store(p, ((uint64_t)ep << 32) | payload, __ATOMIC_RELAXED,
                      __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Polls words [0, n) of `base` until each carries epoch `ep`; thread `tid`
-// of a group of `gsize` threads handles words tid, tid + gsize, ...  All of a
-// thread's loads of one batch are in flight together.  f(i, payload) is
-// called once per word.
+// Publishes words 2q and 2q+1 with one 16-byte store; each aligned 8-byte
+// half is a whole word (payload low, epoch high).
+__device__ __forceinline__ void st_pair(__amdgpu_buffer_rsrc_t r, int q, uint32_t ep, uint32_t a,
+                                        uint32_t b) {
+  const i32x4 v = {(int)a, (int)ep, (int)b, (int)ep};
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, q * 16, 0, kCoherent);
+}
+
+// Polls words [0, n) of an exchange region two at a time until each carries
+// epoch `ep`: thread `tid` of a group of `gsize` threads handles the pairs
+// tid, tid + gsize, ...  All of a thread's loads of one batch are in flight
+// together and share one offset register.  f(q, w0, w1) is called once per
+// pair with the payloads of words 2q and 2q+1 (w1 means nothing when
+// 2q + 1 == n).
 template <int NB, class F>
-__device__ __forceinline__ void poll_words(const uint64_t* base, int n, int tid, int gsize,
+__device__ __forceinline__ void poll_pairs(__amdgpu_buffer_rsrc_t r, int n, int tid, int gsize,
                                            uint32_t ep, uint32_t* err, F&& f) {
-  for (int b0 = 0; b0 < n; b0 += NB * gsize) {
+  const int np = (n + 1) >> 1;
+  for (int b0 = 0; b0 < np; b0 += NB * gsize) {
     uint32_t pending = 0;
 #pragma unroll
     for (int m = 0; m < NB; ++m)
-      if (b0 + m * gsize + tid < n) pending |= 1u << m;
-    uint64_t v[NB];
+      if (b0 + m * gsize + tid < np) pending |= 1u << m;
+    i32x4 v[NB];
     uint32_t spins = 0;
     while (pending) {
+      __asm__ volatile("" ::: "memory");  // every round reloads
 #pragma unroll
       for (int m = 0; m < NB; ++m)
-        if ((pending >> m) & 1u) v[m] = ld_word(base + b0 + m * gsize + tid);
+        if ((pending >> m) & 1u)
+          v[m] = __builtin_amdgcn_raw_buffer_load_b128(r, tid * 16, (b0 + m * gsize) * 16,
+                                                       kCoherent);
 #pragma unroll
       for (int m = 0; m < NB; ++m) {
-        if (((pending >> m) & 1u) && (uint32_t)(v[m] >> 32) == ep) {
-          f(b0 + m * gsize + tid, (uint32_t)v[m]);
+        const int q = b0 + m * gsize + tid;
+        if (((pending >> m) & 1u) && (uint32_t)v[m].y == ep &&
+            (2 * q + 1 >= n || (uint32_t)v[m].w == ep)) {
+          f(q, (uint32_t)v[m].x, (uint32_t)v[m].z);
           pending &= ~(1u << m);
         }
       }
@@ -85,24 +115,41 @@ __device__ __forceinline__ void poll_words(const uint64_t* base, int n, int tid,
 
 __device__ __forceinline__ float bf16r(float v) { return bf16_bits_to_f32(f32_to_bf16_bits(v)); }
 
-__device__ __forceinline__ void st_u32(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t ld_u32(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t ld_u64(const uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Workgroup barrier for LDS traffic: this wave's LDS (and scalar) accesses
+// are complete before it arrives; its global loads and stores may still be
+// in flight.  (__syncthreads also waits for those: for the routed tiles just
+// requested, the next layer's prefetch, and the acknowledgement of every
+// exchange store.)  Every workgroup exchange in this kernel goes through LDS.
+__device__ __forceinline__ void wg_barrier() {
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int BITS, int NIT>
+// Weight addresses as global-memory pointers (an address read back from LDS
+// would otherwise be accessed with flat instructions, which also hold the
+// LDS counter).
+typedef const __attribute__((address_space(1))) uint8_t gbyte;
+__device__ __forceinline__ gbyte* gptr(const uint8_t* a) { return (gbyte*)a; }
+__device__ __forceinline__ gbyte* gptr(uint64_t a) { return (gbyte*)a; }
+typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 gload16(gbyte* a) {
+  const u32x4v v = *(const __attribute__((address_space(1))) u32x4v*)a;
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t gload4(gbyte* a) {
+  return *(const __attribute__((address_space(1))) uint32_t*)a;
+}
+
+template <int BITS, int NIT, bool SHARED>
 __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
+  static_assert(BITS == 4, "the chain runs int4 weights");
   using C = GuCfg<BITS>;
-  constexpr int CC = C::CC, GPK = C::GPK, KBC = C::KBC, XS = C::XS, CP = CC + 4;
+  constexpr int CC = C::CC, GPK = C::GPK, KBC = C::KBC, XS = C::XS;
   constexpr int H = NIT * 256;
   constexpr int NKB = H / KBC;       // gate/up k-blocks
   constexpr int NKW = NKB / 4;       // k-blocks per wave
   constexpr int NCH = H / CC;        // staged activation chunks
+  constexpr int NXP = H / 1024;      // x word pairs per thread
+  constexpr int hsh = SHARED ? 1 : 0;
   constexpr int kMaxDownUnits = max_down_units<BITS>();
 
   __shared__ __align__(16) float xs[H];
@@ -112,31 +159,39 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
   __shared__ int32_t slot_l[kChainMaxExperts];
   __shared__ int32_t sel_idx[MOE_MAX_TOP_K];
   __shared__ float sel_val[MOE_MAX_TOP_K], sel_w[MOE_MAX_TOP_K], gam;
+  __shared__ uint64_t sel_base[MOE_MAX_TOP_K];
+  __shared__ __align__(16) uint32_t mx[64];
   __shared__ __align__(16) uint32_t cand_key[64];
   __shared__ __align__(16) int32_t cand_idx[64];
   __shared__ float cand_val[64];
-  __shared__ float red[4][kRowTile][2];
+  __shared__ float red[4][kRowTile][2], red_s[4][kRowTile][2];
   __shared__ float dred[4][2][8];
   __shared__ float wsum[4];
-  extern __shared__ float hs[];  // h chunks (CP floats each), then chunk sums
+  __shared__ uint32_t tt[kRowTile];
+  // staged h of the down projection, per 32-column chunk (two 16-row
+  // tiles): 16 words of fp16 pairs (padded to 20 so that the 4 chunks a
+  // half-wave reads at once fall in distinct banks), then per tile (C, up)
+  extern __shared__ __align__(16) uint32_t hq[];
+  float* const hcst = reinterpret_cast<float*>(hq + (size_t)((p.k * p.I + (SHARED ? p.Is : 0)) / CC) * kHqStride);
+  float* const hsm = hcst + (size_t)((p.k * p.I + (SHARED ? p.Is : 0)) / CC) * 4;  // sum of h per tile
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int w = blockIdx.x, NWG = gridDim.x;
-  const int E = p.E, k = p.k, I = p.I, Is = p.Is, L = p.L;
-  const int hsh = p.has_shared;
+  const int E = p.E, k = p.k, I = p.I, L = p.L;
+  const int Is = SHARED ? p.Is : 0;
   const uint32_t ep0 = p.ctr[0] + 1u;  // epoch of layer 0; layer l uses ep0 + l
 
   // phase B items: shared tiles first, then routed (j, tile)
-  const int tiles_r = I / kRowTile, tiles_s = hsh ? Is / kRowTile : 0;
+  const int tiles_r = I / kRowTile, tiles_s = Is / kRowTile;
   const int NI = tiles_s + k * tiles_r;
-  const int NH = k * I + (hsh ? Is : 0);      // h values per layer
+  const int NH = k * I + Is;  // h values per layer
   const int nchh = NH / CC;
   // phase C: half-tile w (8 output rows)
   const bool has_c = w < H / 8;
   const int ctile = w >> 1, chalf = w & 1;
   const int hw = wave * 2 + (lane >> 5), l32 = lane & 31;
   const int row8 = l32 >> 2, c4 = lane & 3;
-  const int nkb_r = I / KBC, nkb_s = hsh ? Is / KBC : 0;
+  const int nkb_r = I / KBC, nkb_s = Is / KBC;
   const int n_units = k * nkb_r + nkb_s;
   const int dsb_off = kCodeBlockBytes + ((chalf * 8 + row8) * GPK + (c4 * CC) / kGroup) * 4;
   // gate/up lane geometry
@@ -146,27 +201,38 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
   // router row of this wave
   const int my_row = w + NWG * wave;
   const bool has_row = my_row < E + hsh;
+  const int item0 = w, item1 = w + NWG;
+  const auto rx = word_rsrc(p.xw, H / 2);
+  const auto rl = word_rsrc(p.lw, E + hsh);
+  const auto rh = word_rsrc(p.hw, NH);
 
-  uint4 qg[NKW], qu[NKW];
-  uint32_t sg[NKW], su[NKW];
+  struct GuRegs {
+    uint4 g[NKW], u[NKW];
+    uint32_t sg[NKW], su[NKW];
+  };
+  GuRegs rs, ra, rb;  // shared tile (prefetched), routed tiles
   uint4 dq[kMaxDownUnits];
   uint32_t dsb[kMaxDownUnits];
-  float dw[kMaxDownUnits];
+  float4 wr[NIT];
+  float rbias = 0.0f;
+  int32_t slot_r[kChainMaxExperts / 256];
 
-  auto issue_gu = [&](const uint8_t* blob, int tile, int64_t unit_b, int64_t tile_b) {
-    const uint8_t* tb = blob + (int64_t)tile * tile_b;
+  auto issue_gu = [&](GuRegs& R, gbyte* blob, int tile, int64_t unit_b, int64_t tile_b) {
+    gbyte* tb = blob + (int64_t)tile * tile_b;
 #pragma unroll
     for (int i = 0; i < NKW; ++i) {
-      const uint8_t* unit = tb + (int64_t)(wave + 4 * i) * unit_b;
-      qg[i] = *reinterpret_cast<const uint4*>(unit + lane * 16);
-      qu[i] = *reinterpret_cast<const uint4*>(unit + kCodeBlockBytes + lane * 16);
-      sg[i] = *reinterpret_cast<const uint32_t*>(unit + sbg_off);
-      su[i] = *reinterpret_cast<const uint32_t*>(unit + sbu_off);
+      gbyte* unit = tb + (int64_t)(wave + 4 * i) * unit_b;
+      R.g[i] = gload16(unit + lane * 16);
+      R.u[i] = gload16(unit + kCodeBlockBytes + lane * 16);
+      R.sg[i] = gload4(unit + sbg_off);
+      R.su[i] = gload4(unit + sbu_off);
     }
   };
-  // gate/up of one 16-row tile from registers + staged x; h published
-  // h exchange: one epoch-tagged word per h value
-  auto compute_gu = [&](int64_t hoff, int item, uint32_t ep) {
+  // dot products of one 16-row tile over this wave's k-blocks (wave + 4 i),
+  // from registers + staged x; the per-row partial sums go to rd[wave]
+  auto gu_dots = [&](const GuRegs& R, float (*rd)[kRowTile][2]) {
+    uint32_t mlo = 0x000F000Fu, mhi = 0x00F000F0u, magic = 0x64006400u;
+    asm volatile("" : "+v"(mlo), "+v"(mhi), "+v"(magic));  // keep in VGPRs: v_and_or_b32
     float g = 0.f, u = 0.f;
 #pragma unroll
     for (int i = 0; i < NKW; ++i) {
@@ -174,116 +240,138 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
       const int gc = kb * 4 + c4;
       const float2 c = cs[gc];
       float pg = 0.f, pu = 0.f;
-      const uint32_t dg[4] = {qg[i].x, qg[i].y, qg[i].z, qg[i].w};
-      const uint32_t du[4] = {qu[i].x, qu[i].y, qu[i].z, qu[i].w};
-      if constexpr (BITS == 4) {
-        const uint4* xq = reinterpret_cast<const uint4*>(xp + gc * XS);
+      const uint32_t dg[4] = {R.g[i].x, R.g[i].y, R.g[i].z, R.g[i].w};
+      const uint32_t du[4] = {R.u[i].x, R.u[i].y, R.u[i].z, R.u[i].w};
+      const uint4* xq = reinterpret_cast<const uint4*>(xp + gc * XS);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const uint4 X = xq[m];
-          const uint32_t eg = dg[m] >> 8, eu = du[m] >> 8;
-          pg = dot2((dg[m] & 0x000F000Fu) | 0x64006400u, X.x, pg);
-          pu = dot2((du[m] & 0x000F000Fu) | 0x64006400u, X.x, pu);
-          pg = dot2((dg[m] & 0x00F000F0u) | 0x64006400u, X.y, pg);
-          pu = dot2((du[m] & 0x00F000F0u) | 0x64006400u, X.y, pu);
-          pg = dot2((eg & 0x000F000Fu) | 0x64006400u, X.z, pg);
-          pu = dot2((eu & 0x000F000Fu) | 0x64006400u, X.z, pu);
-          pg = dot2((eg & 0x00F000F0u) | 0x64006400u, X.w, pg);
-          pu = dot2((eu & 0x00F000F0u) | 0x64006400u, X.w, pu);
-        }
-      } else {
-        const uint4* xq = reinterpret_cast<const uint4*>(xp + gc * XS);
-        const uint4 X0 = xq[0], X1 = xq[1];
-        const uint32_t xv[8] = {X0.x, X0.y, X0.z, X0.w, X1.x, X1.y, X1.z, X1.w};
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          pg = dot2(__builtin_amdgcn_perm(0x64646464u, dg[m], 0x04010400u), xv[2 * m], pg);
-          pg = dot2(__builtin_amdgcn_perm(0x64646464u, dg[m], 0x04030402u), xv[2 * m + 1], pg);
-          pu = dot2(__builtin_amdgcn_perm(0x64646464u, du[m], 0x04010400u), xv[2 * m], pu);
-          pu = dot2(__builtin_amdgcn_perm(0x64646464u, du[m], 0x04030402u), xv[2 * m + 1], pu);
-        }
+      for (int m = 0; m < 4; ++m) {
+        const uint4 X = xq[m];
+        const uint32_t eg = dg[m] >> 8, eu = du[m] >> 8;
+        pg = dot2((dg[m] & mlo) | magic, X.x, pg);
+        pu = dot2((du[m] & mlo) | magic, X.x, pu);
+        pg = dot2((dg[m] & mhi) | magic, X.y, pg);
+        pu = dot2((du[m] & mhi) | magic, X.y, pu);
+        pg = dot2((eg & mlo) | magic, X.z, pg);
+        pu = dot2((eu & mlo) | magic, X.z, pu);
+        pg = dot2((eg & mhi) | magic, X.w, pg);
+        pu = dot2((eu & mhi) | magic, X.w, pu);
       }
-      g += bf16_bits_to_f32(sg[i] & 0xFFFFu) * (pg - c.x) + bf16_bits_to_f32(sg[i] >> 16) * c.y;
-      u += bf16_bits_to_f32(su[i] & 0xFFFFu) * (pu - c.x) + bf16_bits_to_f32(su[i] >> 16) * c.y;
+      g += bf16_bits_to_f32(R.sg[i] & 0xFFFFu) * (pg - c.x) + bf16_bits_to_f32(R.sg[i] >> 16) * c.y;
+      u += bf16_bits_to_f32(R.su[i] & 0xFFFFu) * (pu - c.x) + bf16_bits_to_f32(R.su[i] >> 16) * c.y;
     }
-    g += __shfl_xor(g, 1, 64);
-    g += __shfl_xor(g, 2, 64);
-    u += __shfl_xor(u, 1, 64);
-    u += __shfl_xor(u, 2, 64);
+    g = quad_sum(g);
+    u = quad_sum(u);
     if (c4 == 0) {
-      red[wave][grow][0] = g;
-      red[wave][grow][1] = u;
+      rd[wave][grow][0] = g;
+      rd[wave][grow][1] = u;
     }
-    __syncthreads();
-    if (tid < kRowTile) {
-      const float gs = (red[0][tid][0] + red[1][tid][0]) + (red[2][tid][0] + red[3][tid][0]);
-      const float us = (red[0][tid][1] + red[1][tid][1]) + (red[2][tid][1] + red[3][tid][1]);
-      st_word(p.hw + hoff + tid, ep, __float_as_uint(silu_f32(gs) * us));
-    }
-    (void)item;
-    __syncthreads();
   };
-
-  for (int l = 0; l < L; ++l) {
-    const uint32_t ep = ep0 + (uint32_t)l;
-    const int32_t* st = p.slot_tables + (int64_t)l * E;
-    const float* Wr = p.router_w + (int64_t)l * E * H;
+  // wave 0, once all 4 waves' partial sums are in rd: the tile's h, staged
+  // and published as word pairs
+  auto gu_finish = [&](float (*rd)[kRowTile][2], int64_t hoff, uint32_t ep) {
+    if (wave == 0) {
+      // h of the tile's 16 rows, staged for the down dot products: scaled by
+      // a power of two so that the largest |h| lands in [2^13, 2^14), rounded
+      // to fp16, and paired (row s, row s + 4) within each group of 8 rows,
+      // the order in which the int4 code masks pick two nibbles of a code
+      // word.  Published as 6 word pairs: 4 of fp16 pairs, (1024 x the sum
+      // of the 16 staged values, the scale to undo), (the sum of h, 0).
+      float hv = 0.0f;
+      if (lane < kRowTile) {
+        const float gs = (rd[0][lane][0] + rd[1][lane][0]) + (rd[2][lane][0] + rd[3][lane][0]);
+        const float us = (rd[0][lane][1] + rd[1][lane][1]) + (rd[2][lane][1] + rd[3][lane][1]);
+        hv = silu_f32(gs) * us;
+      }
+      const uint32_t amax = wave_max_dpp(__float_as_uint(hv) & 0x7FFFFFFFu);
+      const int ex = max((int)(amax >> 23), 14);
+      const float down = __uint_as_float((uint32_t)(267 - ex) << 23);  // 2^(140 - ex)
+      const float up = __uint_as_float((uint32_t)(ex - 13) << 23);     // 2^(ex - 140)
+      // odd rows (picked by the code mask 0x00F000F0, i.e. as 16 q) are
+      // staged divided by 16
+      const _Float16 t = (_Float16)(hv * down * ((lane & 1) ? 0.0625f : 1.0f));
+      const float tsum = wave_sum_dpp(lane < kRowTile ? (float)t : 0.0f);
+      const float hsum = wave_sum_dpp(hv);
+      if (lane < kRowTile) tt[lane] = (uint32_t)__builtin_bit_cast(uint16_t, t);
+      lds_wave_sync();
+      const int tile = (int)(hoff >> 4);
+      if (lane < 4) {
+        uint32_t w2[2];
+#pragma unroll
+        for (int e2 = 0; e2 < 2; ++e2) {
+          const int wd = 2 * lane + e2, g8 = (wd >> 2) * 8, sl = wd & 3;
+          w2[e2] = tt[g8 + sl] | (tt[g8 + sl + 4] << 16);
+        }
+        st_pair(rh, tile * kHTilePairs + lane, ep, w2[0], w2[1]);
+      } else if (lane == 4) {
+        st_pair(rh, tile * kHTilePairs + 4, ep, __float_as_uint(1024.0f * tsum), __float_as_uint(up));
+      } else if (lane == 5) {
+        st_pair(rh, tile * kHTilePairs + 5, ep, __float_as_uint(hsum), 0u);
+      }
+    }
+  };
+  auto compute_gu = [&](const GuRegs& R, int64_t hoff, uint32_t ep) {
+    gu_dots(R, red);
+    wg_barrier();
+    gu_finish(red, hoff, ep);
+    wg_barrier();
+  };
+  // loads of layer l that do not depend on its input: the router row, the
+  // slot table and the shared expert's first gate/up tile.  Issued after the
+  // previous layer's h poll (whose wait retires every earlier load), so the
+  // down projection that follows never waits for them.
+  auto prefetch = [&](int l) {
     const uint8_t* sblob = p.shared_blobs + (int64_t)l * p.shared_stride;
-    uint64_t* lwl = p.lw;
-
-    // ---------------- prefetch (independent of x_l) ----------------
-    float4 wr[NIT];
-    float rbias = 0.f;
     if (has_row) {
-      const float* rowp = my_row < E ? Wr + (int64_t)my_row * H
+      const float* rowp = my_row < E ? p.router_w + ((int64_t)l * E + my_row) * H
                                      : reinterpret_cast<const float*>(sblob + p.sg_off);
 #pragma unroll
       for (int it = 0; it < NIT; ++it)
         wr[it] = *reinterpret_cast<const float4*>(rowp + it * 256 + lane * 4);
-      if (my_row < E && p.router_bias != nullptr) rbias = p.router_bias[(int64_t)l * E + my_row];
+      rbias = (p.router_bias != nullptr && my_row < E) ? p.router_bias[(int64_t)l * E + my_row]
+                                                       : 0.0f;
     }
-    int32_t slot_r[kChainMaxExperts / 256];
+    const int32_t* st = p.slot_tables + (int64_t)l * E;
 #pragma unroll
     for (int m = 0; m < kChainMaxExperts / 256; ++m)
       if (tid + 256 * m < E) slot_r[m] = st[tid + 256 * m];
-    const int item0 = w, item1 = w + NWG;
-    if (item0 < tiles_s) issue_gu(sblob, item0, p.gu_unit_s, p.gu_tile_s);
-    if (has_c) {  // shared-expert down units of this half-tile
-#pragma unroll
-      for (int i = 0; i < kMaxDownUnits; ++i) {
-        const int uidx = hw + 8 * i;
-        if (uidx >= k * nkb_r && uidx < n_units) {
-          const int kb = uidx - k * nkb_r;
-          const uint8_t* unit = sblob + p.d_off_s + (int64_t)ctile * p.d_tile_s +
-                                (int64_t)kb * p.d_unit_s;
-          dq[i] = *reinterpret_cast<const uint4*>(unit + chalf * 512 + l32 * 16);
-          dsb[i] = *reinterpret_cast<const uint32_t*>(unit + dsb_off);
-        }
-      }
-    }
+    if (SHARED && item0 < tiles_s) issue_gu(rs, gptr(sblob), item0, p.gu_unit_s, p.gu_tile_s);
+  };
+
+  prefetch(0);
+  for (int l = 0; l < L; ++l) {
+    const uint32_t ep = ep0 + (uint32_t)l;
+    const uint8_t* sblob = p.shared_blobs + (int64_t)l * p.shared_stride;
 
     // ---------------- A: input, RMSNorm, router ----------------
     {
-      // thread tid owns words tid + 256 m (bf16 pairs 2i, 2i+1); its sum of
-      // squares runs over them in a fixed order, so every workgroup gets
-      // the same bits whatever order the words arrive in
-      uint32_t xw4[H / 512];
+      // thread tid owns the word pairs tid + 256 m (x elements 4q .. 4q+3);
+      // its sum of squares runs over them in a fixed order, so every
+      // workgroup gets the same bits whatever order the words arrive in
+      uint32_t xw[2 * NXP];
       if (l == 0) {
 #pragma unroll
-        for (int m = 0; m < H / 512; ++m)
-          xw4[m] = *reinterpret_cast<const uint32_t*>(p.x + 2 * (tid + 256 * m));
+        for (int m = 0; m < NXP; ++m) {
+          const uint2 t = *reinterpret_cast<const uint2*>(p.x + 4 * (tid + 256 * m));
+          xw[2 * m] = t.x;
+          xw[2 * m + 1] = t.y;
+        }
       } else {
-        poll_words<H / 512>(p.xw, H / 2, tid, 256, ep - 1u, p.err,
-                            [&](int i, uint32_t v) { xw4[(i - tid) >> 8] = v; });
+        poll_pairs<NXP>(rx, H / 2, tid, 256, ep - 1u, p.err, [&](int q, uint32_t a, uint32_t b) {
+          const int m = (q - tid) >> 8;
+          xw[2 * m] = a;
+          xw[2 * m + 1] = b;
+        });
       }
       float ss = 0.f;
 #pragma unroll
-      for (int m = 0; m < H / 512; ++m) {
-        const int i = tid + 256 * m;
-        const float a = bf16_bits_to_f32(xw4[m] & 0xFFFFu), b = bf16_bits_to_f32(xw4[m] >> 16);
-        xs[2 * i] = a;
-        xs[2 * i + 1] = b;
-        ss += a * a + b * b;
+      for (int m = 0; m < NXP; ++m) {
+        const int q = tid + 256 * m;
+        const float a0 = bf16_bits_to_f32(xw[2 * m] & 0xFFFFu);
+        const float a1 = bf16_bits_to_f32(xw[2 * m] >> 16);
+        const float a2 = bf16_bits_to_f32(xw[2 * m + 1] & 0xFFFFu);
+        const float a3 = bf16_bits_to_f32(xw[2 * m + 1] >> 16);
+        *reinterpret_cast<float4*>(xs + 4 * q) = make_float4(a0, a1, a2, a3);
+        ss += (a0 * a0 + a1 * a1) + (a2 * a2 + a3 * a3);
       }
       ss = wave_sum_dpp(ss);
       if (lane == 0) wsum[wave] = ss;
@@ -291,8 +379,20 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
 #pragma unroll
     for (int m = 0; m < kChainMaxExperts / 256; ++m)
       if (tid + 256 * m < E) slot_l[tid + 256 * m] = slot_r[m];
-    __syncthreads();
+    wg_barrier();
     const float inv = 1.0f / sqrtf(((wsum[0] + wsum[1]) + (wsum[2] + wsum[3])) / (float)H + p.eps);
+    // the router logit first: its exchange gates the top-k
+    if (has_row) {
+      float acc = 0.f;
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const float4 xv = *reinterpret_cast<const float4*>(xs + it * 256 + lane * 4);
+        acc += wr[it].x * bf16r(xv.x * inv) + wr[it].y * bf16r(xv.y * inv) +
+               wr[it].z * bf16r(xv.z * inv) + wr[it].w * bf16r(xv.w * inv);
+      }
+      acc = wave_sum_dpp(acc);
+      if (lane == 0) st_word(p.lw + my_row, ep, __float_as_uint(acc + rbias));
+    }
     // x_hat: stage for the gate/up dot products (4 threads per chunk, each
     // 8 columns for int4 / 4 for int8); block 0 stores it
     {
@@ -327,46 +427,36 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
           sx = c;
         }
         // combine the 4 threads of the chunk (adjacent lanes), fixed order
-        c += __shfl_xor(c, 1, 64);
-        c += __shfl_xor(c, 2, 64);
-        sx += __shfl_xor(sx, 1, 64);
-        sx += __shfl_xor(sx, 2, 64);
+        c = quad_sum(c);
+        sx = quad_sum(sx);
         if (jj == 0) cs[ch] = make_float2(1024.0f * c, sx);
       }
     }
-    if (has_row) {
-      float acc = 0.f;
-#pragma unroll
-      for (int it = 0; it < NIT; ++it) {
-        const float4 xv = *reinterpret_cast<const float4*>(xs + it * 256 + lane * 4);
-        acc += wr[it].x * bf16r(xv.x * inv) + wr[it].y * bf16r(xv.y * inv) +
-               wr[it].z * bf16r(xv.z * inv) + wr[it].w * bf16r(xv.w * inv);
-      }
-      acc = wave_sum_dpp(acc);
-      if (lane == 0) st_word(lwl + my_row, ep, __float_as_uint(acc + rbias));
-    }
-    __syncthreads();
+    wg_barrier();
 
-    // ---------------- B: shared tiles, top-k, routed tiles ----------------
-    if (item0 < tiles_s) compute_gu((int64_t)k * I + item0 * kRowTile, item0, ep);
+    // ---------------- B: top-k, routed tiles, shared tile ----------------
+    // a workgroup with a shared tile: waves 1-3 take their share of its dot
+    // products while wave 0 polls the logits and finds the top-k; wave 0
+    // takes its share while the routed tiles load
+    const bool sh0 = SHARED && item0 < tiles_s;
+    if (sh0 && wave != 0) gu_dots(rs, red_s);
     if (wave == 0) {
-      poll_words<(kChainMaxExperts + 64) / 64>(lwl, E + hsh, lane, 64, ep, p.err,
-                                             [&](int i, uint32_t v) { lg[i] = __uint_as_float(v); });
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_s_waitcnt(0);
-      wave_topk<kChainMaxExperts / 64>(lg, E, k, hsh != 0, sel_idx, sel_val, sel_w, &gam, cand_key,
-                                       cand_idx, cand_val);
-      if (w == 0) {
-        if (lane < k) {
-          p.r_idx[lane] = sel_idx[lane];
-          p.r_w[lane] = sel_w[lane];
-        }
-        if (lane == 0 && hsh) *p.r_gamma = gam;
-      }
+      poll_pairs<(kChainMaxExperts + 128) / 128>(rl, E + hsh, lane, 64, ep, p.err,
+                                                 [&](int q, uint32_t a, uint32_t b) {
+                                                   lg[2 * q] = __uint_as_float(a);
+                                                   if (2 * q + 1 < E + hsh)
+                                                     lg[2 * q + 1] = __uint_as_float(b);
+                                                 });
+      lds_wave_sync();
+      wave_topk_set<kChainMaxExperts / 64>(lg, E, k, sel_idx, sel_val, mx, cand_key, cand_idx,
+                                           cand_val);
+      if (lane < k)
+        sel_base[lane] =
+            reinterpret_cast<uint64_t>(p.slab + (int64_t)slot_l[sel_idx[lane]] * p.stride);
     }
-    __syncthreads();
-    // routed gate/up tiles: loads of the first one go out before the down
-    // units of phase C (needed later)
+    wg_barrier();
+    // routed gate/up tiles of this workgroup (both issued before either is
+    // computed)
     int rj[2] = {-1, -1}, rt[2] = {0, 0};
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
@@ -377,111 +467,159 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
         rt[s2] = ii - rj[s2] * tiles_r;
       }
     }
-    if (rj[0] >= 0)
-      issue_gu(p.slab + (int64_t)slot_l[sel_idx[rj[0]]] * p.stride, rt[0], p.gu_unit_r,
-               p.gu_tile_r);
-    if (has_c) {  // routed down units of phase C
-#pragma unroll
-      for (int i = 0; i < kMaxDownUnits; ++i) {
-        const int uidx = hw + 8 * i;
-        if (uidx < k * nkb_r) {
-          const int jj = uidx / nkb_r, kb = uidx - jj * nkb_r;
-          const uint8_t* unit = p.slab + (int64_t)slot_l[sel_idx[jj]] * p.stride + p.d_off_r +
-                                (int64_t)ctile * p.d_tile_r + (int64_t)kb * p.d_unit_r;
-          dq[i] = *reinterpret_cast<const uint4*>(unit + chalf * 512 + l32 * 16);
-          dsb[i] = *reinterpret_cast<const uint32_t*>(unit + dsb_off);
-          dw[i] = sel_w[jj];
-        } else if (uidx < n_units) {
-          dw[i] = gam;
-        }
-      }
+    if (rj[0] >= 0) issue_gu(ra, gptr(sel_base[rj[0]]), rt[0], p.gu_unit_r, p.gu_tile_r);
+    if (rj[1] >= 0)
+      issue_gu(rb, gptr(sel_base[rj[1]]), rt[1], p.gu_unit_r, p.gu_tile_r);
+    else if (SHARED && item1 < tiles_s)
+      issue_gu(rb, gptr(sblob), item1, p.gu_unit_s, p.gu_tile_s);
+    // routing weights (needed from phase C on), off the load path
+    if (wave == 0) {
+      set_softmax(sel_val, k, sel_w);
+      if (lane == 0) gam = SHARED ? 1.0f / (1.0f + expf(-lg[E])) : 0.0f;
+      if (sh0) gu_dots(rs, red_s);
     }
-    if (rj[0] >= 0) compute_gu((int64_t)rj[0] * I + rt[0] * kRowTile, item0, ep);
-    if (rj[1] >= 0) {
-      issue_gu(p.slab + (int64_t)slot_l[sel_idx[rj[1]]] * p.stride, rt[1], p.gu_unit_r,
-               p.gu_tile_r);
-      compute_gu((int64_t)rj[1] * I + rt[1] * kRowTile, item1, ep);
-    } else if (item1 < tiles_s) {
-      issue_gu(sblob, item1, p.gu_unit_s, p.gu_tile_s);
-      compute_gu((int64_t)k * I + item1 * kRowTile, item1, ep);
+    if (sh0) {
+      wg_barrier();
+      gu_finish(red_s, (int64_t)k * I + item0 * kRowTile, ep);
     }
-
-    // ---------------- C: down + combine + residual ----------------
-    poll_words<24>(p.hw, NH, tid, 256, ep, p.err, [&](int i, uint32_t v) {
-      const int ch = i / CC;
-      hs[ch * CP + (i - ch * CC)] = __uint_as_float(v);
-    });
-    __syncthreads();
+    if (rj[0] >= 0) compute_gu(ra, (int64_t)rj[0] * I + rt[0] * kRowTile, ep);
+    if (rj[1] >= 0)
+      compute_gu(rb, (int64_t)rj[1] * I + rt[1] * kRowTile, ep);
+    else if (SHARED && item1 < tiles_s)
+      compute_gu(rb, (int64_t)k * I + item1 * kRowTile, ep);
+    // down units of phase C, routed then shared: issued once this
+    // workgroup's gate/up tiles have arrived, so that they do not compete
+    // with the gate/up loads every workgroup is still waiting for
     if (has_c) {
-      float acc = 0.f;
+      uint64_t ub[kMaxDownUnits];
+#pragma unroll
+      for (int i = 0; i < kMaxDownUnits; ++i) ub[i] = sel_base[min((hw + 8 * i) / nkb_r, k - 1)];
 #pragma unroll
       for (int i = 0; i < kMaxDownUnits; ++i) {
         const int uidx = hw + 8 * i;
         if (uidx < n_units) {
-          int hb, kb;
+          gbyte* unit;
           if (uidx < k * nkb_r) {
-            const int jj = uidx / nkb_r;
-            kb = uidx - jj * nkb_r;
-            hb = jj * I;
+            const int kb = uidx - (uidx / nkb_r) * nkb_r;
+            unit = gptr(ub[i]) + p.d_off_r + (int64_t)ctile * p.d_tile_r + (int64_t)kb * p.d_unit_r;
           } else {
-            kb = uidx - k * nkb_r;
-            hb = k * I;
+            const int kb = uidx - k * nkb_r;
+            unit = gptr(sblob) + p.d_off_s + (int64_t)ctile * p.d_tile_s +
+                   (int64_t)kb * p.d_unit_s;
           }
-          const int ch = (hb + kb * KBC) / CC + c4;
-          const float* hv = hs + ch * CP;
-          const uint32_t d[4] = {dq[i].x, dq[i].y, dq[i].z, dq[i].w};
-          float pp = 0.f, hsm = 0.f;
-          if constexpr (BITS == 4) {
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-              const float4 a = *reinterpret_cast<const float4*>(hv + 8 * m);
-              const float4 b = *reinterpret_cast<const float4*>(hv + 8 * m + 4);
-              const uint32_t lo = d[m] & 0x0F0F0F0Fu, hi = (d[m] >> 4) & 0x0F0F0F0Fu;
-              pp += (float)(lo & 0xFF) * a.x + (float)(hi & 0xFF) * a.y +
-                    (float)((lo >> 8) & 0xFF) * a.z + (float)((hi >> 8) & 0xFF) * a.w +
-                    (float)((lo >> 16) & 0xFF) * b.x + (float)((hi >> 16) & 0xFF) * b.y +
-                    (float)(lo >> 24) * b.z + (float)(hi >> 24) * b.w;
-              hsm += ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
-            }
-          } else {
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-              const float4 a = *reinterpret_cast<const float4*>(hv + 4 * m);
-              pp += (float)(d[m] & 0xFF) * a.x + (float)((d[m] >> 8) & 0xFF) * a.y +
-                    (float)((d[m] >> 16) & 0xFF) * a.z + (float)(d[m] >> 24) * a.w;
-              hsm += (a.x + a.y) + (a.z + a.w);
-            }
-          }
-          const float sc = bf16_bits_to_f32(dsb[i] & 0xFFFFu), bi = bf16_bits_to_f32(dsb[i] >> 16);
-          acc += dw[i] * (sc * pp + bi * hsm);
+          dq[i] = gload16(unit + chalf * 512 + l32 * 16);
+          dsb[i] = gload4(unit + dsb_off);
         }
       }
-      acc += __shfl_xor(acc, 1, 64);
-      acc += __shfl_xor(acc, 2, 64);
+    }
+
+    // ---------------- C: down + combine + residual ----------------
+    // h arrives staged: 6 word pairs per 16-row tile (4 of fp16 pairs, then
+    // (1024 x sum of the staged values, scale), (sum of h, 0))
+    poll_pairs<kHPairs>(rh, (NH >> 4) * 2 * kHTilePairs, tid, 256, ep, p.err,
+                        [&](int q, uint32_t a, uint32_t b) {
+      const int tile = q / kHTilePairs, slot = q - tile * kHTilePairs;
+      if (slot < 4)
+        *reinterpret_cast<uint2*>(hq + (tile >> 1) * kHqStride + (tile & 1) * 8 + 2 * slot) =
+            make_uint2(a, b);
+      else if (slot == 4)
+        *reinterpret_cast<float2*>(hcst + 4 * (tile >> 1) + 2 * (tile & 1)) =
+            make_float2(__uint_as_float(a), __uint_as_float(b));
+      else
+        hsm[tile] = __uint_as_float(a);
+    });
+    // every load issued so far has returned (the poll waited for them); say
+    // so, so that the down projection below does not wait for the prefetch
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    prefetch(min(l + 1, L - 1));
+    wg_barrier();
+    if (has_c) {
+      // units hw, hw + 8, ... of this half-wave (a unit past the last is
+      // computed on unit 0's data and dropped)
+      uint32_t mlo = 0x000F000Fu, mhi = 0x00F000F0u, magic = 0x64006400u;
+      asm volatile("" : "+v"(mlo), "+v"(mhi), "+v"(magic));  // keep in VGPRs: v_and_or_b32
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < kMaxDownUnits; ++i) {
+        const int uidx = hw + 8 * i;
+        const bool valid = uidx < n_units;
+        const int u = valid ? uidx : 0;
+        int hb, kb;
+        float dwi;
+        if (u < k * nkb_r) {
+          const int jj = u / nkb_r;
+          kb = u - jj * nkb_r;
+          hb = jj * I;
+          dwi = sel_w[jj];
+        } else {
+          kb = u - k * nkb_r;
+          hb = k * I;
+          dwi = gam;
+        }
+        const int ch = (hb + kb * KBC) / CC + c4;
+        const uint4* X = reinterpret_cast<const uint4*>(hq + ch * kHqStride);
+        const float4 K = *reinterpret_cast<const float4*>(hcst + 4 * ch);
+        const float2 S = *reinterpret_cast<const float2*>(hsm + 2 * ch);
+        // word m of the codes: nibbles (n, n + 4) pair up as the staging
+        // paired rows (s, s + 4); words 0-1 are the chunk's first tile
+        float pt[2];
+#pragma unroll
+        for (int tl = 0; tl < 2; ++tl) {
+          float pa = 0.f, pb = 0.f;
+#pragma unroll
+          for (int mm = 0; mm < 2; ++mm) {
+            const int m = 2 * tl + mm;
+            const uint32_t d = m == 0 ? dq[i].x : m == 1 ? dq[i].y : m == 2 ? dq[i].z : dq[i].w;
+            const uint32_t e = d >> 8;
+            const uint4 Xm = X[m];
+            pa = dot2((d & mlo) | magic, Xm.x, pa);
+            pb = dot2((d & mhi) | magic, Xm.y, pb);
+            pa = dot2((e & mlo) | magic, Xm.z, pa);
+            pb = dot2((e & mhi) | magic, Xm.w, pb);
+          }
+          pt[tl] = pa + pb;
+        }
+        const float sq = K.y * (pt[0] - K.x) + K.w * (pt[1] - K.z);  // sum of q h
+        const float sc = bf16_bits_to_f32(dsb[i] & 0xFFFFu), bi = bf16_bits_to_f32(dsb[i] >> 16);
+        const float term = dwi * (sc * sq + bi * (S.x + S.y));
+        acc += valid ? term : 0.0f;
+      }
+      acc = quad_sum(acc);
       if (c4 == 0) dred[wave][lane >> 5][row8] = acc;
     }
-    __syncthreads();
-    if (has_c && tid < 4) {
+    wg_barrier();
+    if (has_c && tid < 2) {  // rows 4 tid .. 4 tid + 3 of the half-tile
       uint32_t xb[2], ob[2];
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        const int r = 2 * tid + q;
-        float v = 0.f;
+        uint32_t xv[2], ov[2];
 #pragma unroll
-        for (int ww = 0; ww < 4; ++ww) v += dred[ww][0][r] + dred[ww][1][r];
-        const int orow = ctile * kRowTile + chalf * 8 + r;
-        ob[q] = f32_to_bf16_bits(v);
-        xb[q] = f32_to_bf16_bits(xs[orow] + bf16_bits_to_f32(ob[q]));
+        for (int e2 = 0; e2 < 2; ++e2) {
+          const int r = 4 * tid + 2 * q + e2;
+          float v = 0.f;
+#pragma unroll
+          for (int ww = 0; ww < 4; ++ww) v += dred[ww][0][r] + dred[ww][1][r];
+          const int orow = ctile * kRowTile + chalf * 8 + r;
+          ov[e2] = f32_to_bf16_bits(v);
+          xv[e2] = f32_to_bf16_bits(xs[orow] + bf16_bits_to_f32(ov[e2]));
+        }
+        xb[q] = xv[0] | (xv[1] << 16);
+        ob[q] = ov[0] | (ov[1] << 16);
       }
-      const int orow0 = ctile * kRowTile + chalf * 8 + 2 * tid;
+      const int orow0 = ctile * kRowTile + chalf * 8 + 4 * tid;
       if (l + 1 < L) {
-        st_word(p.xw + orow0 / 2, ep, xb[0] | (xb[1] << 16));
+        st_pair(rx, orow0 / 4, ep, xb[0], xb[1]);
       } else {
-        *reinterpret_cast<uint32_t*>(p.x + orow0) = xb[0] | (xb[1] << 16);
-        *reinterpret_cast<uint32_t*>(p.out + orow0) = ob[0] | (ob[1] << 16);
+        *reinterpret_cast<uint2*>(p.x + orow0) = make_uint2(xb[0], xb[1]);
+        *reinterpret_cast<uint2*>(p.out + orow0) = make_uint2(ob[0], ob[1]);
       }
     }
-    __syncthreads();
+    wg_barrier();
+  }
+  // the last layer's routing, in routing order
+  if (w == 0 && wave == 0) {
+    set_rank_out(sel_idx, sel_val, sel_w, k, p.r_idx, p.r_w);
+    if (lane == 0 && SHARED) *p.r_gamma = gam;
   }
   if (w == 0 && tid == 0) p.ctr[0] = ep0 + (uint32_t)(L - 1);
 }
@@ -500,6 +638,12 @@ int chain_grid(int device) {
   return g_num_cus[device];
 }
 
+size_t chain_lds_bytes(int bits, int NH) {
+  (void)bits;
+  const int nch = NH / 32;  // 32-column chunks (int4)
+  return (size_t)nch * (kHqStride * sizeof(uint32_t) + 6 * sizeof(float));
+}
+
 bool chain_supported(int nwg, int T, int act, int H, int E, int k, int bits, int I, int Is,
                      bool has_shared) {
   if (T != 1 || act != MOE_ACT_BF16 || H != 2048 || bits != 4 || nwg < 1) return false;
@@ -512,23 +656,19 @@ bool chain_supported(int nwg, int T, int act, int H, int E, int k, int bits, int
   const int n_units = k * (I / kbc) + (has_shared ? Is / kbc : 0);
   if (n_units > 8 * (bits == 4 ? max_down_units<4>() : max_down_units<8>())) return false;
   const int NH = k * I + (has_shared ? Is : 0);
-  const int cc = bits == 4 ? 32 : 16;
-  if ((size_t)(NH / cc * (cc + 4) + NH / cc) * sizeof(float) > 64 * 1024) return false;
+  if (chain_lds_bytes(bits, NH) > 64 * 1024) return false;
   if (NH > 24 * 256 * 4) return false;
   return true;
 }
 
-size_t chain_lds_bytes(int bits, int NH) {
-  const int cc = bits == 4 ? 32 : 16;
-  return sizeof(float) * (size_t)(NH / cc * (cc + 4) + NH / cc);
-}
 
 hipError_t launch_chain(const ChainParams& prm, int nwg, hipStream_t s) {
   const int NH = prm.k * prm.I + (prm.has_shared ? prm.Is : 0);
   const size_t lds = chain_lds_bytes(prm.bits_, NH);
   void* args[] = {const_cast<ChainParams*>(&prm)};
   if (prm.bits_ != 4 || prm.H != 2048) return hipErrorInvalidValue;
-  const void* fn = reinterpret_cast<const void*>(&chain_kernel<4, 8>);
+  const void* fn = prm.has_shared ? reinterpret_cast<const void*>(&chain_kernel<4, 8, true>)
+                                  : reinterpret_cast<const void*>(&chain_kernel<4, 8, false>);
   return hipLaunchCooperativeKernel(fn, dim3(nwg), dim3(256), args, (unsigned)lds, s);
 }
 

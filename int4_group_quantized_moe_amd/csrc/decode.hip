@@ -237,10 +237,8 @@ __global__ __launch_bounds__(256) void decode_gateup_kernel(
       u += bf16_bits_to_f32(su[i] & 0xFFFFu) * (pu - c.x) + bf16_bits_to_f32(su[i] >> 16) * c.y;
     }
   }
-  g += __shfl_xor(g, 1, 64);
-  g += __shfl_xor(g, 2, 64);
-  u += __shfl_xor(u, 1, 64);
-  u += __shfl_xor(u, 2, 64);
+  g = quad_sum(g);
+  u = quad_sum(u);
   if (c4 == 0) {
     red[wave][row][0] = g;
     red[wave][row][1] = u;
@@ -369,8 +367,7 @@ __global__ __launch_bounds__(256) void decode_down_kernel(
       acc += wgt[i] * (s * p + b * hsum[ch]);
     }
   }
-  acc += __shfl_xor(acc, 1, 64);
-  acc += __shfl_xor(acc, 2, 64);
+  acc = quad_sum(acc);
   if (c4 == 0) red[wave][lane >> 5][row8] = acc;
   __syncthreads();
   if (threadIdx.x < 8) {

@@ -63,6 +63,17 @@ __device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
+// Min over the 64 lanes, result in every lane.
+__device__ __forceinline__ uint32_t wave_min_dpp(uint32_t v) {
+  v = min(v, dpp_u<0x111, 0xF>(v, v));
+  v = min(v, dpp_u<0x112, 0xF>(v, v));
+  v = min(v, dpp_u<0x114, 0xF>(v, v));
+  v = min(v, dpp_u<0x118, 0xF>(v, v));
+  v = min(v, dpp_u<0x142, 0xA>(v, v));
+  v = min(v, dpp_u<0x143, 0xC>(v, v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 // Waits for this wave's LDS operations only (vmcnt and expcnt left open).
 __device__ __forceinline__ void lds_wave_sync() {
   __builtin_amdgcn_wave_barrier();
@@ -205,6 +216,169 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ logits, int 
   lds_wave_sync();
 }
 
+
+// The top-k SET of one token's E logits by one wave: the k experts with the
+// largest logits, ties to the lower index, listed by ascending expert index
+// (the order the decode chain lays out h in).  The weights are not needed to
+// start loading the selected experts, so they come later (set_softmax).
+//   1. every lane keeps the max key of its logits; tau = the k-th largest
+//      lane maximum, found by counting, in every lane, the lane maxima above
+//      its own (tau = the least lane maximum with fewer than k above it).  At
+//      least k logits are >= tau, and a logit below tau has k larger ones, so
+//      every top-k logit is >= tau;
+//   2. the logits >= tau are compacted into LDS in ascending index (about k
+//      of them; more when a lane holds two of the top k);
+//   3. with exactly k candidates they are the set; otherwise each candidate
+//      counts the candidates ranked above it, and those with fewer than k are
+//      the set, kept in ascending index.
+// More than 64 candidates (massive ties) take k rounds of wave argmax.
+// Writes set_idx[0..k), set_val[0..k) in LDS; mx, cand_* are LDS scratch.
+template <int MPL = kMaxPerLane>
+__device__ __forceinline__ void wave_topk_set(const float* __restrict__ logits, int E, int k,
+                                              int32_t* set_idx, float* set_val, uint32_t* mx,
+                                              uint32_t* cand_key, int32_t* cand_idx,
+                                              float* cand_val) {
+  const int lane = threadIdx.x & 63;
+  const int per = (E + 63) >> 6;
+  float v[MPL];
+  uint32_t u[MPL];
+  uint32_t M = 0;
+#pragma unroll
+  for (int i = 0; i < MPL; ++i) {
+    const int e = i * 64 + lane;
+    const bool ok = i < per && e < E;
+    v[i] = ok ? logits[e] : -INFINITY;
+    u[i] = ok ? order_key(v[i]) : 0u;
+    M = max(M, u[i]);
+  }
+  // 1. tau = the k-th largest lane maximum
+  mx[lane] = M;
+  lds_wave_sync();
+  uint32_t above = 0;
+#pragma unroll
+  for (int j = 0; j < 64; j += 4) {
+    const uint4 q = *reinterpret_cast<const uint4*>(mx + j);
+    above += (q.x > M ? 1u : 0u) + (q.y > M ? 1u : 0u) + (q.z > M ? 1u : 0u) + (q.w > M ? 1u : 0u);
+  }
+  const uint32_t tau = wave_min_dpp(above < (uint32_t)k ? M : 0xFFFFFFFFu);
+  // 2. compact the candidates, ascending index
+  uint32_t base = 0;
+#pragma unroll
+  for (int i = 0; i < MPL; ++i) {
+    if (i < per) {
+      const bool c = u[i] >= tau && (i * 64 + lane) < E;
+      const uint64_t m = ballot(c);
+      if (c) {
+        const uint32_t pos = base + mbcnt(m);
+        if (pos < 64) {
+          cand_key[pos] = u[i];
+          cand_idx[pos] = i * 64 + lane;
+          cand_val[pos] = v[i];
+        }
+      }
+      base += (uint32_t)__popcll(m);
+    }
+  }
+  lds_wave_sync();
+  const int ncand = (int)base;
+  if (ncand <= 64) {
+    // 3. the set: candidates ranked below k (key descending, index ascending)
+    bool sel = lane < ncand;
+    if (ncand > k && sel) {
+      const uint32_t K = cand_key[lane];
+      const int I = cand_idx[lane];
+      int rank = 0;
+      for (int j0 = 0; j0 < ncand; j0 += 4) {
+        const uint4 kk = *reinterpret_cast<const uint4*>(cand_key + j0);
+        const int4 ii = *reinterpret_cast<const int4*>(cand_idx + j0);
+        const uint32_t ks[4] = {kk.x, kk.y, kk.z, kk.w};
+        const int is[4] = {ii.x, ii.y, ii.z, ii.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          rank += (j0 + q < ncand && (ks[q] > K || (ks[q] == K && is[q] < I))) ? 1 : 0;
+      }
+      sel = rank < k;
+    }
+    const uint64_t m = ballot(sel);
+    if (sel) {
+      const uint32_t pos = mbcnt(m);
+      set_idx[pos] = cand_idx[lane];
+      set_val[pos] = cand_val[lane];
+    }
+  } else {
+    // k rounds of (max key, lowest index) over the whole wave; the winners
+    // go to cand_* in rank order, then to set_* by ascending index
+    uint32_t taken = 0u;
+    for (int r = 0; r < k; ++r) {
+      uint32_t bk = 0;
+      int bi = 0x7FFFFFFF;
+#pragma unroll
+      for (int i = 0; i < MPL; ++i) {
+        const int e = i * 64 + lane;
+        if (i < per && e < E && !((taken >> i) & 1u)) {
+          if (u[i] > bk || (u[i] == bk && e < bi)) {
+            bk = u[i];
+            bi = e;
+          }
+        }
+      }
+      uint32_t mk = bk;
+      for (int off = 32; off >= 1; off >>= 1) mk = max(mk, (uint32_t)__shfl_xor((int)mk, off, 64));
+      int mi = (bk == mk) ? bi : 0x7FFFFFFF;
+      for (int off = 32; off >= 1; off >>= 1) mi = min(mi, __shfl_xor(mi, off, 64));
+      if ((mi & 63) == lane) {
+        taken |= 1u << (mi >> 6);
+        float sv = 0.f;
+#pragma unroll
+        for (int i = 0; i < MPL; ++i)
+          if (i == (mi >> 6)) sv = v[i];
+        cand_idx[r] = mi;
+        cand_val[r] = sv;
+      }
+    }
+    lds_wave_sync();
+    if (lane < k) {
+      const int I = cand_idx[lane];
+      int pos = 0;
+      for (int j = 0; j < k; ++j) pos += cand_idx[j] < I ? 1 : 0;
+      set_idx[pos] = I;
+      set_val[pos] = cand_val[lane];
+    }
+  }
+  lds_wave_sync();
+}
+
+// Renormalised softmax over the k selected logits set_val[0..k) (max
+// subtracted, fixed-order DPP sum); weights in the same order.
+__device__ __forceinline__ void set_softmax(const float* set_val, int k, float* set_w) {
+  const int lane = threadIdx.x & 63;
+  const float x = lane < k ? set_val[lane] : -INFINITY;
+  const uint32_t mk = wave_max_dpp(lane < k ? order_key(x) : 0u);
+  const float xmax = __uint_as_float((mk & 0x80000000u) ? (mk & 0x7FFFFFFFu) : ~mk);
+  const float e = lane < k ? expf(x - xmax) : 0.0f;
+  const float den = wave_sum_dpp(e);
+  if (lane < k) set_w[lane] = e / den;
+  lds_wave_sync();
+}
+
+// Writes the set in routing order (logit descending, ties to the lower
+// index): idx_out[r], w_out[r] for r < k.
+__device__ __forceinline__ void set_rank_out(const int32_t* set_idx, const float* set_val,
+                                             const float* set_w, int k, int32_t* idx_out,
+                                             float* w_out) {
+  const int lane = threadIdx.x & 63;
+  if (lane < k) {
+    const uint32_t K = order_key(set_val[lane]);
+    const int I = set_idx[lane];
+    int rank = 0;
+    for (int j = 0; j < k; ++j) {
+      const uint32_t Kj = order_key(set_val[j]);
+      rank += (Kj > K || (Kj == K && set_idx[j] < I)) ? 1 : 0;
+    }
+    idx_out[rank] = I;
+    w_out[rank] = set_w[lane];
+  }
+}
 
 template <int BITS>
 struct GuCfg {

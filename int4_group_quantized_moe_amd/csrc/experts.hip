@@ -300,10 +300,8 @@ __device__ __forceinline__ void gateup_item(MOE_GATEUP_PARAMS, int tile, int ite
     // reduce the 4 lanes of a row, then the 4 waves
 #pragma unroll
     for (int tt = 0; tt < kGuTokens; ++tt) {
-      g[tt] += __shfl_xor(g[tt], 1, 64);
-      g[tt] += __shfl_xor(g[tt], 2, 64);
-      u[tt] += __shfl_xor(u[tt], 1, 64);
-      u[tt] += __shfl_xor(u[tt], 2, 64);
+      g[tt] = quad_sum(g[tt]);
+      u[tt] = quad_sum(u[tt]);
       if (c4 == 0) {
         red[((wave * kGuTokens + tt) * kRowTile + row) * 2 + 0] = g[tt];
         red[((wave * kGuTokens + tt) * kRowTile + row) * 2 + 1] = u[tt];
@@ -425,8 +423,7 @@ __global__ __launch_bounds__(256) void down_decode_kernel(
     const float p = lane_dot_h<BITS>(q, hv + kb * KBC + c4 * CC, hsum);
     acc += w * (bf16_bits_to_f32(sb & 0xFFFFu) * p + bf16_bits_to_f32(sb >> 16) * hsum);
   }
-  acc += __shfl_xor(acc, 1, 64);
-  acc += __shfl_xor(acc, 2, 64);
+  acc = quad_sum(acc);
   if (c4 == 0) red[wave][row] = acc;
   __syncthreads();
   if (threadIdx.x < kRowTile) {
@@ -506,8 +503,7 @@ __device__ __forceinline__ void down_bucket_item(MOE_DOWNB_PARAMS, float (*red)[
     }
 #pragma unroll
     for (int tt = 0; tt < kTok; ++tt) {
-      acc[tt] += __shfl_xor(acc[tt], 1, 64);
-      acc[tt] += __shfl_xor(acc[tt], 2, 64);
+      acc[tt] = quad_sum(acc[tt]);
       if (c4 == 0) red[wave][tt][row] = acc[tt];
     }
     __syncthreads();

@@ -150,6 +150,25 @@ __device__ __forceinline__ void store_act(void* p, int64_t i, float v) {
 
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
 
+// Reductions over the 4 lanes of each quad (lanes 4i .. 4i+3) with DPP quad
+// permutes (no LDS round trip, unlike a shuffle).  Every lane of the quad
+// gets the same bits: (v0 + v1) + (v2 + v3).
+template <int CTRL>
+__device__ __forceinline__ float quad_perm_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_sum(float v) {
+  v += quad_perm_f<0xB1>(v);  // lane ^ 1
+  v += quad_perm_f<0x4E>(v);  // lane ^ 2
+  return v;
+}
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, quad_perm_f<0xB1>(v));
+  v = fmaxf(v, quad_perm_f<0x4E>(v));
+  return v;
+}
+
 __device__ __forceinline__ float warp_sum(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);

@@ -275,6 +275,39 @@ def test_decode_massive_ties():
     _free()
 
 
+@pytest.mark.parametrize("cfgname", ["decode_35b", "decode_80b"])
+def test_chain_massive_ties(cfgname):
+    """The persistent chain on an all-zero router: every logit ties, so the
+    expert set is 0..k-1 (k rounds of wave argmax, not the candidate path),
+    reported in index order with weights 1/k."""
+    moe, wl = _moe(), _wl()
+    cfg = configs.CONFIGS[cfgname]
+    say(f"[chain ties] zero router, {cfgname}")
+    w = wl.Workload(cfg, n_layers=1)
+    w.router_w.zero_()
+    d = w.desc
+    k = cfg.top_k
+    x0_np = synth.activations(cfg)
+    x = wl.act_tensor(cfg, x0_np)
+    xh = torch.empty_like(x)
+    out = torch.empty_like(x)
+    ws = w.workspace()
+    pi, pw, pg = moe.moe_workspace_routing(d, ws)
+    base = ws.data_ptr()
+    rw, rb, st, sh = w.layer_args(0)
+    moe.moe_chain_forward(d, 1, x, rw, rb, w.slab, st, sh, w.shared_stride, xh, out, ws)
+    torch.cuda.synchronize()
+    idx = ws[pi - base: pi - base + 4 * k].view(torch.int32)
+    wt = ws[pw - base: pw - base + 4 * k].view(torch.float32)
+    assert idx.tolist() == list(range(k))
+    assert torch.allclose(wt, torch.full_like(wt, 1.0 / k), rtol=1e-6)
+    inp = oracle.LayerInputs(cfg, 0, overrides={"router_w": np.zeros((cfg.n_experts, cfg.hidden), np.float32)})
+    ref = oracle.oracle_layer(inp, wl.to_f64(xh))
+    check_out(out.float().cpu().numpy(), ref["out"], cfg.act, "chain ties")
+    del w
+    _free()
+
+
 @pytest.mark.parametrize("cfgname", ["batched_80b", "batched_80b_int8"])
 def test_batched_parity(cfgname):
     """64 tokens with a Zipf router bias: token->expert bucketing path."""
