@@ -130,6 +130,8 @@ __device__ __forceinline__ void wg_barrier() {
 typedef const __attribute__((address_space(1))) uint8_t gbyte;
 __device__ __forceinline__ gbyte* gptr(const uint8_t* a) { return (gbyte*)a; }
 __device__ __forceinline__ gbyte* gptr(uint64_t a) { return (gbyte*)a; }
+#define CH_G1(p) ((const void __attribute__((address_space(1)))*)(p))
+#define CH_L3(p) ((void __attribute__((address_space(3)))*)(p))
 typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 gload16(gbyte* a) {
   const u32x4v v = *(const __attribute__((address_space(1))) u32x4v*)a;
@@ -139,10 +141,14 @@ __device__ __forceinline__ uint32_t gload4(gbyte* a) {
   return *(const __attribute__((address_space(1))) uint32_t*)a;
 }
 
-template <int BITS, int NIT, bool SHARED>
+// IR, IS: intermediate size of the routed and of the shared experts; the
+// blob geometry is compile-time.
+template <int BITS, int NIT, bool SHARED, int IR, int IS>
 __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
   static_assert(BITS == 4, "the chain runs int4 weights");
   using C = GuCfg<BITS>;
+  constexpr BlobLayout LR = make_layout(BITS, NIT * 256, IR);
+  constexpr BlobLayout LS = make_layout(BITS, NIT * 256, SHARED ? IS : 64);
   constexpr int CC = C::CC, GPK = C::GPK, KBC = C::KBC, XS = C::XS;
   constexpr int H = NIT * 256;
   constexpr int NKB = H / KBC;       // gate/up k-blocks
@@ -168,21 +174,26 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
   __shared__ float dred[4][2][8];
   __shared__ float wsum[4];
   __shared__ uint32_t tt[kRowTile];
+  // the shared expert's gate/up tile of this workgroup (when it has one)
+  constexpr int kShChunks = SHARED ? (int)(LS.gu_tile / 1024) : 4;
+  static_assert(!SHARED || LS.gu_tile % 4096 == 0, "shared tile: whole 1 KiB chunks per wave");
+  __shared__ __align__(16) uint8_t sh_tile[SHARED ? LS.gu_tile : 16];
+  __shared__ uint32_t shcnt;  // waves 2-3: shared-tile partial sums written (count)
   // staged h of the down projection, per 32-column chunk (two 16-row
   // tiles): 16 words of fp16 pairs (padded to 20 so that the 4 chunks a
   // half-wave reads at once fall in distinct banks), then per tile (C, up)
   extern __shared__ __align__(16) uint32_t hq[];
-  float* const hcst = reinterpret_cast<float*>(hq + (size_t)((p.k * p.I + (SHARED ? p.Is : 0)) / CC) * kHqStride);
-  float* const hsm = hcst + (size_t)((p.k * p.I + (SHARED ? p.Is : 0)) / CC) * 4;  // sum of h per tile
+  float* const hcst = reinterpret_cast<float*>(hq + (size_t)((p.k * IR + (SHARED ? IS : 0)) / CC) * kHqStride);
+  float* const hsm = hcst + (size_t)((p.k * IR + (SHARED ? IS : 0)) / CC) * 4;  // sum of h per tile
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int w = blockIdx.x, NWG = gridDim.x;
-  const int E = p.E, k = p.k, I = p.I, L = p.L;
-  const int Is = SHARED ? p.Is : 0;
+  constexpr int I = IR, Is = SHARED ? IS : 0;
+  const int E = p.E, k = p.k, L = p.L;
   const uint32_t ep0 = p.ctr[0] + 1u;  // epoch of layer 0; layer l uses ep0 + l
 
   // phase B items: shared tiles first, then routed (j, tile)
-  const int tiles_r = I / kRowTile, tiles_s = Is / kRowTile;
+  constexpr int tiles_r = I / kRowTile, tiles_s = Is / kRowTile;
   const int NI = tiles_s + k * tiles_r;
   const int NH = k * I + Is;  // h values per layer
   const int nchh = NH / CC;
@@ -191,7 +202,7 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
   const int ctile = w >> 1, chalf = w & 1;
   const int hw = wave * 2 + (lane >> 5), l32 = lane & 31;
   const int row8 = l32 >> 2, c4 = lane & 3;
-  const int nkb_r = I / KBC, nkb_s = Is / KBC;
+  constexpr int nkb_r = I / KBC, nkb_s = Is / KBC;
   const int n_units = k * nkb_r + nkb_s;
   const int dsb_off = kCodeBlockBytes + ((chalf * 8 + row8) * GPK + (c4 * CC) / kGroup) * 4;
   // gate/up lane geometry
@@ -210,7 +221,7 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
     uint4 g[NKW], u[NKW];
     uint32_t sg[NKW], su[NKW];
   };
-  GuRegs rs, ra, rb;  // shared tile (prefetched), routed tiles
+  GuRegs ra, rb;  // routed tiles
   uint4 dq[kMaxDownUnits];
   uint32_t dsb[kMaxDownUnits];
   float4 wr[NIT];
@@ -228,37 +239,35 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
       R.su[i] = gload4(unit + sbu_off);
     }
   };
-  // dot products of one 16-row tile over this wave's k-blocks (wave + 4 i),
-  // from registers + staged x; the per-row partial sums go to rd[wave]
-  auto gu_dots = [&](const GuRegs& R, float (*rd)[kRowTile][2]) {
+  // one k-block (128 columns) of a 16-row gate/up tile against the staged
+  // x, accumulated into this lane's partial g, u (4 lanes per row)
+  auto gu_block = [&](int kb, const uint4 cg, const uint4 cu, uint32_t sgw, uint32_t suw, float& g,
+                      float& u) {
     uint32_t mlo = 0x000F000Fu, mhi = 0x00F000F0u, magic = 0x64006400u;
     asm volatile("" : "+v"(mlo), "+v"(mhi), "+v"(magic));  // keep in VGPRs: v_and_or_b32
-    float g = 0.f, u = 0.f;
+    const int gc = kb * 4 + c4;
+    const float2 c = cs[gc];
+    float pg = 0.f, pu = 0.f;
+    const uint32_t dg[4] = {cg.x, cg.y, cg.z, cg.w};
+    const uint32_t du[4] = {cu.x, cu.y, cu.z, cu.w};
+    const uint4* xq = reinterpret_cast<const uint4*>(xp + gc * XS);
 #pragma unroll
-    for (int i = 0; i < NKW; ++i) {
-      const int kb = wave + 4 * i;
-      const int gc = kb * 4 + c4;
-      const float2 c = cs[gc];
-      float pg = 0.f, pu = 0.f;
-      const uint32_t dg[4] = {R.g[i].x, R.g[i].y, R.g[i].z, R.g[i].w};
-      const uint32_t du[4] = {R.u[i].x, R.u[i].y, R.u[i].z, R.u[i].w};
-      const uint4* xq = reinterpret_cast<const uint4*>(xp + gc * XS);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const uint4 X = xq[m];
-        const uint32_t eg = dg[m] >> 8, eu = du[m] >> 8;
-        pg = dot2((dg[m] & mlo) | magic, X.x, pg);
-        pu = dot2((du[m] & mlo) | magic, X.x, pu);
-        pg = dot2((dg[m] & mhi) | magic, X.y, pg);
-        pu = dot2((du[m] & mhi) | magic, X.y, pu);
-        pg = dot2((eg & mlo) | magic, X.z, pg);
-        pu = dot2((eu & mlo) | magic, X.z, pu);
-        pg = dot2((eg & mhi) | magic, X.w, pg);
-        pu = dot2((eu & mhi) | magic, X.w, pu);
-      }
-      g += bf16_bits_to_f32(R.sg[i] & 0xFFFFu) * (pg - c.x) + bf16_bits_to_f32(R.sg[i] >> 16) * c.y;
-      u += bf16_bits_to_f32(R.su[i] & 0xFFFFu) * (pu - c.x) + bf16_bits_to_f32(R.su[i] >> 16) * c.y;
+    for (int m = 0; m < 4; ++m) {
+      const uint4 X = xq[m];
+      const uint32_t eg = dg[m] >> 8, eu = du[m] >> 8;
+      pg = dot2((dg[m] & mlo) | magic, X.x, pg);
+      pu = dot2((du[m] & mlo) | magic, X.x, pu);
+      pg = dot2((dg[m] & mhi) | magic, X.y, pg);
+      pu = dot2((du[m] & mhi) | magic, X.y, pu);
+      pg = dot2((eg & mlo) | magic, X.z, pg);
+      pu = dot2((eu & mlo) | magic, X.z, pu);
+      pg = dot2((eg & mhi) | magic, X.w, pg);
+      pu = dot2((eu & mhi) | magic, X.w, pu);
     }
+    g += bf16_bits_to_f32(sgw & 0xFFFFu) * (pg - c.x) + bf16_bits_to_f32(sgw >> 16) * c.y;
+    u += bf16_bits_to_f32(suw & 0xFFFFu) * (pu - c.x) + bf16_bits_to_f32(suw >> 16) * c.y;
+  };
+  auto gu_store = [&](float g, float u, float (*rd)[kRowTile][2]) {
     g = quad_sum(g);
     u = quad_sum(u);
     if (c4 == 0) {
@@ -266,10 +275,34 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
       rd[wave][grow][1] = u;
     }
   };
-  // wave 0, once all 4 waves' partial sums are in rd: the tile's h, staged
-  // and published as word pairs
+  // dot products of one 16-row tile over this wave's k-blocks (wave + 4 i),
+  // from registers; the per-row partial sums go to rd[wave]
+  auto gu_dots = [&](const GuRegs& R, float (*rd)[kRowTile][2]) {
+    float g = 0.f, u = 0.f;
+#pragma unroll
+    for (int i = 0; i < NKW; ++i) gu_block(wave + 4 * i, R.g[i], R.u[i], R.sg[i], R.su[i], g, u);
+    gu_store(g, u, rd);
+  };
+  // waves 1-3: the shared tile from LDS, k-blocks (wave - 1) + 3 i
+  auto gu_dots_shared = [&](float (*rd)[kRowTile][2], const uint8_t* sh_tile) {
+    float g = 0.f, u = 0.f;
+#pragma unroll
+    for (int i = 0; i < (NKB + 2) / 3; ++i) {
+      const int kb = (wave - 1) + 3 * i;
+      if (kb < NKB) {
+        const uint8_t* unit = sh_tile + kb * LS.gu_unit;
+        gu_block(kb, *reinterpret_cast<const uint4*>(unit + lane * 16),
+                 *reinterpret_cast<const uint4*>(unit + kCodeBlockBytes + lane * 16),
+                 *reinterpret_cast<const uint32_t*>(unit + sbg_off),
+                 *reinterpret_cast<const uint32_t*>(unit + sbu_off), g, u);
+      }
+    }
+    gu_store(g, u, rd);
+  };
+  // one wave, once all 4 waves' partial sums are in rd: the tile's h,
+  // staged and published as word pairs
   auto gu_finish = [&](float (*rd)[kRowTile][2], int64_t hoff, uint32_t ep) {
-    if (wave == 0) {
+    {
       // h of the tile's 16 rows, staged for the down dot products: scaled by
       // a power of two so that the largest |h| lands in [2^13, 2^14), rounded
       // to fp16, and paired (row s, row s + 4) within each group of 8 rows,
@@ -312,18 +345,18 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
   auto compute_gu = [&](const GuRegs& R, int64_t hoff, uint32_t ep) {
     gu_dots(R, red);
     wg_barrier();
-    gu_finish(red, hoff, ep);
+    if (wave == 0) gu_finish(red, hoff, ep);
     wg_barrier();
   };
   // loads of layer l that do not depend on its input: the router row, the
-  // slot table and the shared expert's first gate/up tile.  Issued after the
-  // previous layer's h poll (whose wait retires every earlier load), so the
-  // down projection that follows never waits for them.
+  // slot table and the shared expert's gate/up tile of this workgroup (into
+  // LDS).  Issued after the previous layer's h poll (whose wait retires
+  // every earlier load), so that the down projection never waits for them.
   auto prefetch = [&](int l) {
     const uint8_t* sblob = p.shared_blobs + (int64_t)l * p.shared_stride;
     if (has_row) {
       const float* rowp = my_row < E ? p.router_w + ((int64_t)l * E + my_row) * H
-                                     : reinterpret_cast<const float*>(sblob + p.sg_off);
+                                     : reinterpret_cast<const float*>(sblob + LS.sg_off);
 #pragma unroll
       for (int it = 0; it < NIT; ++it)
         wr[it] = *reinterpret_cast<const float4*>(rowp + it * 256 + lane * 4);
@@ -334,9 +367,23 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
 #pragma unroll
     for (int m = 0; m < kChainMaxExperts / 256; ++m)
       if (tid + 256 * m < E) slot_r[m] = st[tid + 256 * m];
-    if (SHARED && item0 < tiles_s) issue_gu(rs, gptr(sblob), item0, p.gu_unit_s, p.gu_tile_s);
+    // the shared tile: by all 4 waves, straight into LDS (1 KiB per wave
+    // instruction, each lane 16 bytes)
+    if (SHARED && item0 < tiles_s) {
+      const uint8_t* tb = sblob + (int64_t)item0 * LS.gu_tile;
+#pragma unroll
+      for (int j = 0; j < kShChunks / 4; ++j) {
+        const int c = wave + 4 * j;
+        __builtin_amdgcn_global_load_lds(CH_G1(tb + c * 1024 + lane * 16), CH_L3(sh_tile + c * 1024),
+                                         16, 0, 0);
+      }
+    }
   };
 
+
+
+  if (tid == 0) shcnt = 0u;
+  if (tid < 2 * kRowTile) red_s[0][tid >> 1][tid & 1] = 0.0f;  // wave 0 takes no share
   prefetch(0);
   for (int l = 0; l < L; ++l) {
     const uint32_t ep = ep0 + (uint32_t)l;
@@ -439,7 +486,26 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
     // products while wave 0 polls the logits and finds the top-k; wave 0
     // takes its share while the routed tiles load
     const bool sh0 = SHARED && item0 < tiles_s;
-    if (sh0 && wave != 0) gu_dots(rs, red_s);
+    if (sh0 && wave != 0) {
+      // waves 1-3: the whole shared tile, while wave 0 polls and ranks; wave
+      // 1 finishes it once waves 2-3 have written their partial sums
+      gu_dots_shared(red_s, sh_tile);
+      if (wave != 1) {
+        lds_wave_sync();
+        if (lane == 0) __hip_atomic_fetch_add(&shcnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      } else {
+        const uint32_t target = 2u * (uint32_t)(l + 1);
+        uint32_t spins = 0;
+        while (__hip_atomic_load(&shcnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
+          if (++spins > kSpinLimit) {
+            atomicOr(p.err, 1u);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+        gu_finish(red_s, (int64_t)k * I + item0 * kRowTile, ep);
+      }
+    }
     if (wave == 0) {
       poll_pairs<(kChainMaxExperts + 128) / 128>(rl, E + hsh, lane, 64, ep, p.err,
                                                  [&](int q, uint32_t a, uint32_t b) {
@@ -467,20 +533,15 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
         rt[s2] = ii - rj[s2] * tiles_r;
       }
     }
-    if (rj[0] >= 0) issue_gu(ra, gptr(sel_base[rj[0]]), rt[0], p.gu_unit_r, p.gu_tile_r);
+    if (rj[0] >= 0) issue_gu(ra, gptr(sel_base[rj[0]]), rt[0], LR.gu_unit, LR.gu_tile);
     if (rj[1] >= 0)
-      issue_gu(rb, gptr(sel_base[rj[1]]), rt[1], p.gu_unit_r, p.gu_tile_r);
+      issue_gu(rb, gptr(sel_base[rj[1]]), rt[1], LR.gu_unit, LR.gu_tile);
     else if (SHARED && item1 < tiles_s)
-      issue_gu(rb, gptr(sblob), item1, p.gu_unit_s, p.gu_tile_s);
+      issue_gu(rb, gptr(sblob), item1, LS.gu_unit, LS.gu_tile);
     // routing weights (needed from phase C on), off the load path
     if (wave == 0) {
       set_softmax(sel_val, k, sel_w);
       if (lane == 0) gam = SHARED ? 1.0f / (1.0f + expf(-lg[E])) : 0.0f;
-      if (sh0) gu_dots(rs, red_s);
-    }
-    if (sh0) {
-      wg_barrier();
-      gu_finish(red_s, (int64_t)k * I + item0 * kRowTile, ep);
     }
     if (rj[0] >= 0) compute_gu(ra, (int64_t)rj[0] * I + rt[0] * kRowTile, ep);
     if (rj[1] >= 0)
@@ -501,11 +562,11 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
           gbyte* unit;
           if (uidx < k * nkb_r) {
             const int kb = uidx - (uidx / nkb_r) * nkb_r;
-            unit = gptr(ub[i]) + p.d_off_r + (int64_t)ctile * p.d_tile_r + (int64_t)kb * p.d_unit_r;
+            unit = gptr(ub[i]) + LR.d_off + (int64_t)ctile * LR.d_tile + (int64_t)kb * LR.d_unit;
           } else {
             const int kb = uidx - k * nkb_r;
-            unit = gptr(sblob) + p.d_off_s + (int64_t)ctile * p.d_tile_s +
-                   (int64_t)kb * p.d_unit_s;
+            unit = gptr(sblob) + LS.d_off + (int64_t)ctile * LS.d_tile +
+                   (int64_t)kb * LS.d_unit;
           }
           dq[i] = gload16(unit + chalf * 512 + l32 * 16);
           dsb[i] = gload4(unit + dsb_off);
@@ -647,6 +708,8 @@ size_t chain_lds_bytes(int bits, int NH) {
 bool chain_supported(int nwg, int T, int act, int H, int E, int k, int bits, int I, int Is,
                      bool has_shared) {
   if (T != 1 || act != MOE_ACT_BF16 || H != 2048 || bits != 4 || nwg < 1) return false;
+  // the kernel is compiled for expert (and shared) intermediate size 512
+  if (I != 512 || (has_shared && Is != 512)) return false;
   if (E > kChainMaxExperts) return false;
   const int kbc = kRowBytes * (8 / bits);
   if (E + (has_shared ? 1 : 0) > 4 * nwg) return false;
@@ -666,9 +729,10 @@ hipError_t launch_chain(const ChainParams& prm, int nwg, hipStream_t s) {
   const int NH = prm.k * prm.I + (prm.has_shared ? prm.Is : 0);
   const size_t lds = chain_lds_bytes(prm.bits_, NH);
   void* args[] = {const_cast<ChainParams*>(&prm)};
-  if (prm.bits_ != 4 || prm.H != 2048) return hipErrorInvalidValue;
-  const void* fn = prm.has_shared ? reinterpret_cast<const void*>(&chain_kernel<4, 8, true>)
-                                  : reinterpret_cast<const void*>(&chain_kernel<4, 8, false>);
+  if (prm.bits_ != 4 || prm.H != 2048 || prm.I != 512) return hipErrorInvalidValue;
+  if (prm.has_shared && prm.Is != 512) return hipErrorInvalidValue;
+  const void* fn = prm.has_shared ? reinterpret_cast<const void*>(&chain_kernel<4, 8, true, 512, 512>)
+                                  : reinterpret_cast<const void*>(&chain_kernel<4, 8, false, 512, 512>);
   return hipLaunchCooperativeKernel(fn, dim3(nwg), dim3(256), args, (unsigned)lds, s);
 }
 

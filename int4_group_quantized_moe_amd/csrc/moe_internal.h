@@ -17,7 +17,7 @@ constexpr int kGroup = 64;
 constexpr int kDecodeMaxTokens = 8;    // up to this many tokens: per-pair GEMV path
 constexpr int kMfmaMinRows = 4;  // bf16 buckets of this many tokens run on the MFMA grouped GEMMs
 
-inline int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+constexpr int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
 // Byte layout of one blob.  Everything is a multiple of 64 bytes; blob sizes
 // are multiples of 256.
@@ -34,7 +34,7 @@ struct BlobLayout {
   int64_t blob, sg_off, shared_bytes;
 };
 
-inline BlobLayout make_layout(int bits, int hidden, int inter) {
+constexpr BlobLayout make_layout(int bits, int hidden, int inter) {
   BlobLayout L{};
   L.bits = bits;
   L.hidden = hidden;
