@@ -254,7 +254,7 @@ def chain_roofline(cfg, load_input, forward, bytes_per_rot, reps=64):
     persistent = cfg.n_tokens == 1 and cfg.act == "bf16" and cfg.bits == 4
     traffic = measured_traffic(cfg) if persistent else None
     return {"bound": "hbm",
-            "kernel": ("chain_kernel<4, 8>: the persistent decode-chain kernel, one launch "
+            "kernel": ("chain_kernel<4, 8, true, 512, 512>: the persistent decode-chain kernel, one launch "
                        f"per {cfg.layers}-layer step" if persistent else
                        "moe_chain_forward: all kernels of one chain step"),
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
