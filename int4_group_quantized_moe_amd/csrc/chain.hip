@@ -186,7 +186,8 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
   float* const hcst = reinterpret_cast<float*>(hq + (size_t)((p.k * IR + (SHARED ? IS : 0)) / CC) * kHqStride);
   float* const hsm = hcst + (size_t)((p.k * IR + (SHARED ? IS : 0)) / CC) * 4;  // sum of h per tile
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int w = blockIdx.x, NWG = gridDim.x;
   constexpr int I = IR, Is = SHARED ? IS : 0;
   const int E = p.E, k = p.k, L = p.L;
@@ -552,24 +553,27 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
     // workgroup's gate/up tiles have arrived, so that they do not compete
     // with the gate/up loads every workgroup is still waiting for
     if (has_c) {
-      uint64_t ub[kMaxDownUnits];
-#pragma unroll
-      for (int i = 0; i < kMaxDownUnits; ++i) ub[i] = sel_base[min((hw + 8 * i) / nkb_r, k - 1)];
+      // unit slot i of this wave: units u0 = 8 i + 2 wave (half-wave 0) and
+      // u0 + 1 (half-wave 1).  nkb_r and nkb_s are even, so both are of the
+      // same expert and kind: the blob base is wave-uniform, the rest a
+      // 32-bit per-lane offset
+      static_assert(nkb_r % 2 == 0 && (nkb_s % 2 == 0), "down units pair up per wave");
+      const uint32_t kbo = (uint32_t)(hw & (nkb_r - 1));  // k-block of this half-wave's unit
+      const uint32_t oc_r = (uint32_t)(LR.d_off + ctile * LR.d_tile + kbo * LR.d_unit) + chalf * 512 + l32 * 16;
+      const uint32_t os_r = (uint32_t)(LR.d_off + ctile * LR.d_tile + kbo * LR.d_unit) + dsb_off;
+      const uint32_t oc_s = (uint32_t)(LS.d_off + ctile * LS.d_tile + kbo * LS.d_unit) + chalf * 512 + l32 * 16;
+      const uint32_t os_s = (uint32_t)(LS.d_off + ctile * LS.d_tile + kbo * LS.d_unit) + dsb_off;
 #pragma unroll
       for (int i = 0; i < kMaxDownUnits; ++i) {
-        const int uidx = hw + 8 * i;
-        if (uidx < n_units) {
-          gbyte* unit;
-          if (uidx < k * nkb_r) {
-            const int kb = uidx - (uidx / nkb_r) * nkb_r;
-            unit = gptr(ub[i]) + LR.d_off + (int64_t)ctile * LR.d_tile + (int64_t)kb * LR.d_unit;
-          } else {
-            const int kb = uidx - k * nkb_r;
-            unit = gptr(sblob) + LS.d_off + (int64_t)ctile * LS.d_tile +
-                   (int64_t)kb * LS.d_unit;
-          }
-          dq[i] = gload16(unit + chalf * 512 + l32 * 16);
-          dsb[i] = gload4(unit + dsb_off);
+        const int u0 = 8 * i + 2 * wave;
+        if (u0 < n_units) {
+          const bool routed = u0 < k * nkb_r;
+          uint64_t b = routed ? sel_base[u0 / nkb_r] : reinterpret_cast<uint64_t>(sblob);
+          b = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+              (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+          gbyte* base = gptr(b);
+          dq[i] = gload16(base + (routed ? oc_r : oc_s));
+          dsb[i] = gload4(base + (routed ? os_r : os_s));
         }
       }
     }
