@@ -26,6 +26,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+# the stream-read ceiling measured on MI355X: a grid-stride read of a 16 GiB
+# buffer with 16-byte loads, 4 in flight per thread, 8192 workgroups of 256
+HBM_READ_CEILING_GBPS = 6045.7
 N_ROTATE = 8
 
 
@@ -249,6 +252,8 @@ def chain_roofline(cfg, load_input, forward, bytes_per_rot, reps=64):
     torch.cuda.synchronize()
     durs = [a.elapsed_time(b) * 1e-3 for a, b in evs]
     avg_s = sum(durs) / len(durs)
+    srt = sorted(durs)
+    pct = {q: srt[min(len(srt) - 1, int(q / 100 * len(srt)))] * 1e6 for q in (10, 50, 90)}
     avg_b = sum(bytes_per_rot[i % N_ROTATE] for i in range(reps)) / reps
     achieved = avg_b / avg_s / 1e9
     persistent = cfg.n_tokens == 1 and cfg.act == "bf16" and cfg.bits == 4
@@ -259,7 +264,10 @@ def chain_roofline(cfg, load_input, forward, bytes_per_rot, reps=64):
                        "moe_chain_forward: all kernels of one chain step"),
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-            "avg_launch_us": round(avg_s * 1e6, 3), "bytes_per_launch": int(avg_b),
+            "avg_launch_us": round(avg_s * 1e6, 3),
+            "launch_us_p10_p50_p90": [round(pct[10], 3), round(pct[50], 3), round(pct[90], 3)],
+            "frac_of_read_ceiling": round(achieved / HBM_READ_CEILING_GBPS, 4),
+            "bytes_per_launch": int(avg_b),
             "launches": reps}
 
 
@@ -316,11 +324,27 @@ def cpu_baseline(cfg, n_layers):
     per_layer = dt / n_layers
     tokens_per_s = cfg.n_tokens / (per_layer * cfg.layers)
     threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] + [1])
+    # one thread, first layer only
+    with threadpoolctl.threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        xh = oracle.chain_prologue(x0.astype(np.float64), cfg.rms_eps, cfg.act)
+        oracle.oracle_layer(inputs[0], xh)
+        per_layer_1t = time.perf_counter() - t0
+    model = "unknown"
+    try:
+        for ln in open("/proc/cpuinfo", encoding="utf-8"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": round(tokens_per_s, 6), "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{cfg.n_tokens} token(s) through layers 0..{n_layers - 1} of {cfg.layers} "
                       f"(numpy float64; {dt:.1f}s); scaled to the {cfg.layers}-layer chain",
-            "seconds_per_layer": round(per_layer, 4)}
+            "seconds_per_layer": round(per_layer, 4),
+            "seconds_per_layer_1_thread": round(per_layer_1t, 4),
+            "cpu_model": model, "nproc": os.cpu_count()}
 
 
 if __name__ == "__main__":

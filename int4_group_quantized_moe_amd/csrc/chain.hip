@@ -22,9 +22,10 @@
 //       the routing weights and its share of the shared tile, whose h is
 //       published; then the routed tiles; h published; then the down units
 //       of phase C are issued
-//   C   all h polled; the next layer's router row, slot table and shared
-//       tile are prefetched; down GEMV of 8 output rows over all selected
-//       experts in a fixed order; residual add; x_{l+1} published
+//   C   all h polled; the next layer's router row and slot table are
+//       prefetched; down GEMV of 8 output rows over all selected experts in
+//       a fixed order; the next layer's shared tile is requested; residual
+//       add; x_{l+1} published
 //
 // Routing: top-k of E experts per token plus an always-active shared expert
 // (page "Paquets Swiftlet 80B Qwen ..." on xix.ai, 4th paragraph); weights
@@ -349,10 +350,10 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
     if (wave == 0) gu_finish(red, hoff, ep);
     wg_barrier();
   };
-  // loads of layer l that do not depend on its input: the router row, the
-  // slot table and the shared expert's gate/up tile of this workgroup (into
-  // LDS).  Issued after the previous layer's h poll (whose wait retires
-  // every earlier load), so that the down projection never waits for them.
+  // loads of layer l that do not depend on its input: the router row and
+  // the slot table.  Issued after the previous layer's h poll (whose wait
+  // retires every earlier load), so that the down projection never waits
+  // for them.  (The shared tile: load_shared_tile.)
   auto prefetch = [&](int l) {
     const uint8_t* sblob = p.shared_blobs + (int64_t)l * p.shared_stride;
     if (has_row) {
@@ -368,10 +369,15 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
 #pragma unroll
     for (int m = 0; m < kChainMaxExperts / 256; ++m)
       if (tid + 256 * m < E) slot_r[m] = st[tid + 256 * m];
-    // the shared tile: by all 4 waves, straight into LDS (1 KiB per wave
-    // instruction, each lane 16 bytes)
+  };
+
+
+
+  // the shared tile of layer l: by all 4 waves, straight into LDS (1 KiB
+  // per wave instruction, each lane 16 bytes)
+  auto load_shared_tile = [&](int l) {
     if (SHARED && item0 < tiles_s) {
-      const uint8_t* tb = sblob + (int64_t)item0 * LS.gu_tile;
+      const uint8_t* tb = p.shared_blobs + (int64_t)l * p.shared_stride + (int64_t)item0 * LS.gu_tile;
 #pragma unroll
       for (int j = 0; j < kShChunks / 4; ++j) {
         const int c = wave + 4 * j;
@@ -380,12 +386,10 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
       }
     }
   };
-
-
-
   if (tid == 0) shcnt = 0u;
   if (tid < 2 * kRowTile) red_s[0][tid >> 1][tid & 1] = 0.0f;  // wave 0 takes no share
   prefetch(0);
+  load_shared_tile(0);
   for (int l = 0; l < L; ++l) {
     const uint32_t ep = ep0 + (uint32_t)l;
     const uint8_t* sblob = p.shared_blobs + (int64_t)l * p.shared_stride;
@@ -653,6 +657,9 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
       if (c4 == 0) dred[wave][lane >> 5][row8] = acc;
     }
     wg_barrier();
+    // the next layer's shared tile (this layer's was consumed in phase B),
+    // over the x exchange
+    if (l + 1 < L) load_shared_tile(l + 1);
     if (has_c && tid < 2) {  // rows 4 tid .. 4 tid + 3 of the half-tile
       uint32_t xb[2], ob[2];
 #pragma unroll
