@@ -133,6 +133,12 @@ __device__ __forceinline__ gbyte* gptr(const uint8_t* a) { return (gbyte*)a; }
 __device__ __forceinline__ gbyte* gptr(uint64_t a) { return (gbyte*)a; }
 #define CH_G1(p) ((const void __attribute__((address_space(1)))*)(p))
 #define CH_L3(p) ((void __attribute__((address_space(3)))*)(p))
+// A value the whole wave holds, moved to scalar registers (both halves
+// zero-extended).
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
+  return ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32)) << 32) |
+         (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+}
 typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 gload16(gbyte* a) {
   const u32x4v v = *(const __attribute__((address_space(1))) u32x4v*)a;
@@ -144,7 +150,8 @@ __device__ __forceinline__ uint32_t gload4(gbyte* a) {
 
 // IR, IS: intermediate size of the routed and of the shared experts; the
 // blob geometry is compile-time.
-template <int BITS, int NIT, bool SHARED, int IR, int IS>
+// EPL: logits per lane of the top-k wave (E <= 64 EPL).
+template <int BITS, int NIT, bool SHARED, int IR, int IS, int EPL>
 __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
   static_assert(BITS == 4, "the chain runs int4 weights");
   using C = GuCfg<BITS>;
@@ -162,8 +169,9 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
   __shared__ __align__(16) float xs[H];
   __shared__ __align__(16) uint32_t xp[NCH * XS];
   __shared__ float2 cs[NCH];
-  __shared__ float lg[kChainMaxExperts + 1];
-  __shared__ int32_t slot_l[kChainMaxExperts];
+  constexpr int EMAX = 64 * EPL;
+  __shared__ float lg[EMAX + 2];
+  __shared__ int32_t slot_l[EMAX];
   __shared__ int32_t sel_idx[MOE_MAX_TOP_K];
   __shared__ float sel_val[MOE_MAX_TOP_K], sel_w[MOE_MAX_TOP_K], gam;
   __shared__ uint64_t sel_base[MOE_MAX_TOP_K];
@@ -228,10 +236,10 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
   uint32_t dsb[kMaxDownUnits];
   float4 wr[NIT];
   float rbias = 0.0f;
-  int32_t slot_r[kChainMaxExperts / 256];
+  int32_t slot_r[(EMAX + 255) / 256];
 
   auto issue_gu = [&](GuRegs& R, gbyte* blob, int tile, int64_t unit_b, int64_t tile_b) {
-    gbyte* tb = blob + (int64_t)tile * tile_b;
+    gbyte* tb = gptr(uniform_u64(reinterpret_cast<uint64_t>(blob + (int64_t)tile * tile_b)));
 #pragma unroll
     for (int i = 0; i < NKW; ++i) {
       gbyte* unit = tb + (int64_t)(wave + 4 * i) * unit_b;
@@ -367,7 +375,7 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
     }
     const int32_t* st = p.slot_tables + (int64_t)l * E;
 #pragma unroll
-    for (int m = 0; m < kChainMaxExperts / 256; ++m)
+    for (int m = 0; m < (EMAX + 255) / 256; ++m)
       if (tid + 256 * m < E) slot_r[m] = st[tid + 256 * m];
   };
 
@@ -429,7 +437,7 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
       if (lane == 0) wsum[wave] = ss;
     }
 #pragma unroll
-    for (int m = 0; m < kChainMaxExperts / 256; ++m)
+    for (int m = 0; m < (EMAX + 255) / 256; ++m)
       if (tid + 256 * m < E) slot_l[tid + 256 * m] = slot_r[m];
     wg_barrier();
     const float inv = 1.0f / sqrtf(((wsum[0] + wsum[1]) + (wsum[2] + wsum[3])) / (float)H + p.eps);
@@ -512,14 +520,14 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
       }
     }
     if (wave == 0) {
-      poll_pairs<(kChainMaxExperts + 128) / 128>(rl, E + hsh, lane, 64, ep, p.err,
+      poll_pairs<(EMAX + 128) / 128>(rl, E + hsh, lane, 64, ep, p.err,
                                                  [&](int q, uint32_t a, uint32_t b) {
                                                    lg[2 * q] = __uint_as_float(a);
                                                    if (2 * q + 1 < E + hsh)
                                                      lg[2 * q + 1] = __uint_as_float(b);
                                                  });
       lds_wave_sync();
-      wave_topk_set<kChainMaxExperts / 64>(lg, E, k, sel_idx, sel_val, mx, cand_key, cand_idx,
+      wave_topk_set<EPL>(lg, E, k, sel_idx, sel_val, mx, cand_key, cand_idx,
                                            cand_val);
       if (lane < k)
         sel_base[lane] =
@@ -572,10 +580,7 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
         const int u0 = 8 * i + 2 * wave;
         if (u0 < n_units) {
           const bool routed = u0 < k * nkb_r;
-          uint64_t b = routed ? sel_base[u0 / nkb_r] : reinterpret_cast<uint64_t>(sblob);
-          b = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
-              (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
-          gbyte* base = gptr(b);
+          gbyte* base = gptr(uniform_u64(routed ? sel_base[u0 / nkb_r] : reinterpret_cast<uint64_t>(sblob)));
           dq[i] = gload16(base + (routed ? oc_r : oc_s));
           dsb[i] = gload4(base + (routed ? os_r : os_s));
         }
@@ -742,8 +747,13 @@ hipError_t launch_chain(const ChainParams& prm, int nwg, hipStream_t s) {
   void* args[] = {const_cast<ChainParams*>(&prm)};
   if (prm.bits_ != 4 || prm.H != 2048 || prm.I != 512) return hipErrorInvalidValue;
   if (prm.has_shared && prm.Is != 512) return hipErrorInvalidValue;
-  const void* fn = prm.has_shared ? reinterpret_cast<const void*>(&chain_kernel<4, 8, true, 512, 512>)
-                                  : reinterpret_cast<const void*>(&chain_kernel<4, 8, false, 512, 512>);
+  const bool small = prm.E <= 256;
+  const void* fn =
+      prm.has_shared
+          ? (small ? reinterpret_cast<const void*>(&chain_kernel<4, 8, true, 512, 512, 4>)
+                   : reinterpret_cast<const void*>(&chain_kernel<4, 8, true, 512, 512, 8>))
+          : (small ? reinterpret_cast<const void*>(&chain_kernel<4, 8, false, 512, 512, 4>)
+                   : reinterpret_cast<const void*>(&chain_kernel<4, 8, false, 512, 512, 8>));
   return hipLaunchCooperativeKernel(fn, dim3(nwg), dim3(256), args, (unsigned)lds, s);
 }
 
