@@ -150,8 +150,9 @@ __device__ __forceinline__ uint32_t gload4(gbyte* a) {
 
 // IR, IS: intermediate size of the routed and of the shared experts; the
 // blob geometry is compile-time.
-// EPL: logits per lane of the top-k wave (E <= 64 EPL).
-template <int BITS, int NIT, bool SHARED, int IR, int IS, int EPL>
+// EPL: logits per lane of the top-k wave (E <= 64 EPL).  EC, KC: the
+// number of experts and top-k when fixed at compile time (0: from p).
+template <int BITS, int NIT, bool SHARED, int IR, int IS, int EPL, int EC, int KC>
 __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
   static_assert(BITS == 4, "the chain runs int4 weights");
   using C = GuCfg<BITS>;
@@ -199,7 +200,7 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int w = blockIdx.x, NWG = gridDim.x;
   constexpr int I = IR, Is = SHARED ? IS : 0;
-  const int E = p.E, k = p.k, L = p.L;
+  const int E = EC ? EC : p.E, k = KC ? KC : p.k, L = p.L;
   const uint32_t ep0 = p.ctr[0] + 1u;  // epoch of layer 0; layer l uses ep0 + l
 
   // phase B items: shared tiles first, then routed (j, tile)
@@ -748,12 +749,17 @@ hipError_t launch_chain(const ChainParams& prm, int nwg, hipStream_t s) {
   if (prm.bits_ != 4 || prm.H != 2048 || prm.I != 512) return hipErrorInvalidValue;
   if (prm.has_shared && prm.Is != 512) return hipErrorInvalidValue;
   const bool small = prm.E <= 256;
-  const void* fn =
-      prm.has_shared
-          ? (small ? reinterpret_cast<const void*>(&chain_kernel<4, 8, true, 512, 512, 4>)
-                   : reinterpret_cast<const void*>(&chain_kernel<4, 8, true, 512, 512, 8>))
-          : (small ? reinterpret_cast<const void*>(&chain_kernel<4, 8, false, 512, 512, 4>)
-                   : reinterpret_cast<const void*>(&chain_kernel<4, 8, false, 512, 512, 8>));
+  const void* fn;
+  if (prm.has_shared && prm.E == 256 && prm.k == 8)
+    fn = reinterpret_cast<const void*>(&chain_kernel<4, 8, true, 512, 512, 4, 256, 8>);
+  else if (prm.has_shared && prm.E == 512 && prm.k == 10)
+    fn = reinterpret_cast<const void*>(&chain_kernel<4, 8, true, 512, 512, 8, 512, 10>);
+  else if (prm.has_shared)
+    fn = small ? reinterpret_cast<const void*>(&chain_kernel<4, 8, true, 512, 512, 4, 0, 0>)
+               : reinterpret_cast<const void*>(&chain_kernel<4, 8, true, 512, 512, 8, 0, 0>);
+  else
+    fn = small ? reinterpret_cast<const void*>(&chain_kernel<4, 8, false, 512, 512, 4, 0, 0>)
+               : reinterpret_cast<const void*>(&chain_kernel<4, 8, false, 512, 512, 8, 0, 0>);
   return hipLaunchCooperativeKernel(fn, dim3(nwg), dim3(256), args, (unsigned)lds, s);
 }
 

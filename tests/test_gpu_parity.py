@@ -275,6 +275,42 @@ def test_decode_massive_ties():
     _free()
 
 
+@pytest.mark.parametrize("top_k", [4, 6])
+def test_chain_other_top_k(top_k):
+    """The persistent chain for a top-k it has no specialised kernel for (the
+    kernel built with k and E read at run time), one layer against the
+    oracle, and two chained layers equal to two single-layer calls."""
+    moe, wl = _moe(), _wl()
+    cfg = configs.DECODE_35B.with_(name=f"decode_35b_top{top_k}", top_k=top_k, layers=2)
+    say(f"[chain] E=256 top-{top_k}")
+    w = wl.Workload(cfg)
+    d = w.desc
+    x0_np = synth.activations(cfg)
+    x = wl.act_tensor(cfg, x0_np)
+    xh = torch.empty_like(x)
+    out = torch.empty_like(x)
+    ws = w.workspace()
+    pi, pw, pg = moe.moe_workspace_routing(d, ws)
+    base = ws.data_ptr()
+    for i in range(cfg.layers):
+        x_before = x.clone()
+        rw, rb, st, sh = w.layer_args(i)
+        moe.moe_chain_forward(d, 1, x, rw, rb, w.slab, st, sh, w.shared_stride, xh, out, ws)
+        torch.cuda.synchronize()
+        idx = ws[pi - base: pi - base + 4 * top_k].view(torch.int32).view(1, top_k)
+        wt = ws[pw - base: pw - base + 4 * top_k].view(torch.float32).view(1, top_k)
+        g = ws[pg - base: pg - base + 4].view(torch.float32)
+        check_layer(cfg, i, wl.to_f64(xh), out, idx, wt, g, f"top-{top_k} layer {i}")
+        assert np.array_equal(wl.to_f64(x), oracle.chain_epilogue(wl.to_f64(x_before), wl.to_f64(out), cfg.act))
+    xc = wl.act_tensor(cfg, x0_np)
+    moe.moe_chain_forward(d, cfg.layers, xc, w.router_w, w.router_bias, w.slab, w.slot_tables,
+                          w.shared, w.shared_stride, torch.empty_like(xc), torch.empty_like(xc), ws)
+    torch.cuda.synchronize()
+    assert torch.equal(xc, x)
+    del w
+    _free()
+
+
 @pytest.mark.parametrize("cfgname", ["decode_35b", "decode_80b"])
 def test_chain_massive_ties(cfgname):
     """The persistent chain on an all-zero router: every logit ties, so the
