@@ -232,6 +232,16 @@ def describe(cfg):
             f"{cfg.layers} chained layer(s)")
 
 
+def chain_kernel_name(cfg):
+    """The instantiation of the persistent chain kernel that runs this
+    configuration (as the library dispatches it)."""
+    shared = "true" if cfg.shared_inter else "false"
+    epl = 4 if cfg.n_experts <= 256 else 8
+    spec = (cfg.n_experts, cfg.top_k) in ((256, 8), (512, 10)) and cfg.shared_inter
+    ec, kc = (cfg.n_experts, cfg.top_k) if spec else (0, 0)
+    return f"chain_kernel<4, 8, {shared}, {cfg.inter}, {cfg.shared_inter or 512}, {epl}, {ec}, {kc}>"
+
+
 def chain_roofline(cfg, load_input, forward, bytes_per_rot, reps=64):
     """Average duration of one moe_chain_forward launch (for batch-1 bf16
     int4 decode this is the single persistent kernel that streams every
@@ -259,7 +269,7 @@ def chain_roofline(cfg, load_input, forward, bytes_per_rot, reps=64):
     persistent = cfg.n_tokens == 1 and cfg.act == "bf16" and cfg.bits == 4
     traffic = measured_traffic(cfg) if persistent else None
     return {"bound": "hbm",
-            "kernel": ("chain_kernel<4, 8, true, 512, 512>: the persistent decode-chain kernel, one launch "
+            "kernel": (f"{chain_kernel_name(cfg)}: the persistent decode-chain kernel, one launch "
                        f"per {cfg.layers}-layer step" if persistent else
                        "moe_chain_forward: all kernels of one chain step"),
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
