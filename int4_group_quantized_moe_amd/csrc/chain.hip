@@ -164,6 +164,7 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
   constexpr int NKW = NKB / 4;       // k-blocks per wave
   constexpr int NCH = H / CC;        // staged activation chunks
   constexpr int NXP = H / 1024;      // x word pairs per thread
+  static_assert(NXP == 2 && CC == 32, "thread tid owns x elements 8 tid .. 8 tid + 7");
   constexpr int hsh = SHARED ? 1 : 0;
   constexpr int kMaxDownUnits = max_down_units<BITS>();
 
@@ -176,13 +177,16 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
   __shared__ int32_t sel_idx[MOE_MAX_TOP_K];
   __shared__ float sel_val[MOE_MAX_TOP_K], sel_w[MOE_MAX_TOP_K], gam;
   __shared__ uint64_t sel_base[MOE_MAX_TOP_K];
-  __shared__ __align__(16) uint32_t mx[64];
   __shared__ __align__(16) uint32_t cand_key[64];
   __shared__ __align__(16) int32_t cand_idx[64];
   __shared__ float cand_val[64];
   __shared__ float red[4][kRowTile][2], red_s[4][kRowTile][2];
   __shared__ float dred[4][2][8];
   __shared__ float wsum[4];
+  // router rows of this workgroup: w + NWG r.  The grid has at least H / 8
+  // = 256 workgroups, so at most this many rows fall to one workgroup
+  constexpr int kRR = ((EC ? EC : kChainMaxExperts) + hsh + 255) / 256;
+  __shared__ float rred[kRR][4];
   __shared__ uint32_t tt[kRowTile];
   // the shared expert's gate/up tile of this workgroup (when it has one)
   constexpr int kShChunks = SHARED ? (int)(LS.gu_tile / 1024) : 4;
@@ -220,9 +224,10 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
   const int grow = lane >> 2;
   const int sbg_off = 2 * kCodeBlockBytes + (grow * GPK + (c4 * CC) / kGroup) * 4;
   const int sbu_off = sbg_off + kRowTile * GPK * 4;
-  // router row of this wave
-  const int my_row = w + NWG * wave;
-  const bool has_row = my_row < E + hsh;
+  int nrows = 0;
+#pragma unroll
+  for (int r = 0; r < kRR; ++r)
+    if (w + NWG * r < E + hsh) nrows = r + 1;
   const int item0 = w, item1 = w + NWG;
   const auto rx = word_rsrc(p.xw, H / 2);
   const auto rl = word_rsrc(p.lw, E + hsh);
@@ -235,8 +240,8 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
   GuRegs ra, rb;  // routed tiles
   uint4 dq[kMaxDownUnits];
   uint32_t dsb[kMaxDownUnits];
-  float4 wr[NIT];
-  float rbias = 0.0f;
+  float4 wr[kRR][NXP];  // router rows: the weights of the owned x elements
+  float rbias = 0.0f;   // lane r: bias of router row r (when that row has one)
   int32_t slot_r[(EMAX + 255) / 256];
 
   auto issue_gu = [&](GuRegs& R, gbyte* blob, int tile, int64_t unit_b, int64_t tile_b) {
@@ -365,15 +370,20 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
   // for them.  (The shared tile: load_shared_tile.)
   auto prefetch = [&](int l) {
     const uint8_t* sblob = p.shared_blobs + (int64_t)l * p.shared_stride;
-    if (has_row) {
-      const float* rowp = my_row < E ? p.router_w + ((int64_t)l * E + my_row) * H
-                                     : reinterpret_cast<const float*>(sblob + LS.sg_off);
 #pragma unroll
-      for (int it = 0; it < NIT; ++it)
-        wr[it] = *reinterpret_cast<const float4*>(rowp + it * 256 + lane * 4);
-      rbias = (p.router_bias != nullptr && my_row < E) ? p.router_bias[(int64_t)l * E + my_row]
-                                                       : 0.0f;
+    for (int r = 0; r < kRR; ++r) {
+      const int row = w + NWG * r;
+      if (r < nrows) {
+        const float* rowp = row < E ? p.router_w + ((int64_t)l * E + row) * H
+                                    : reinterpret_cast<const float*>(sblob + LS.sg_off);
+#pragma unroll
+        for (int m = 0; m < NXP; ++m) wr[r][m] = *reinterpret_cast<const float4*>(rowp + 8 * tid + 4 * m);
+      }
     }
+    // every lane loads (a clamped row): a load under a lane mask followed by
+    // a read under the complement would wait for the whole prefetch
+    if (p.router_bias != nullptr)
+      rbias = p.router_bias[(int64_t)l * E + min(w + NWG * min(lane, kRR - 1), E - 1)];
     const int32_t* st = p.slot_tables + (int64_t)l * E;
 #pragma unroll
     for (int m = 0; m < (EMAX + 255) / 256; ++m)
@@ -405,7 +415,7 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
 
     // ---------------- A: input, RMSNorm, router ----------------
     {
-      // thread tid owns the word pairs tid + 256 m (x elements 4q .. 4q+3);
+      // thread tid polls the word pairs tid + 256 m (x elements 4q .. 4q+3);
       // its sum of squares runs over them in a fixed order, so every
       // workgroup gets the same bits whatever order the words arrive in
       uint32_t xw[2 * NXP];
@@ -426,12 +436,11 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
       float ss = 0.f;
 #pragma unroll
       for (int m = 0; m < NXP; ++m) {
-        const int q = tid + 256 * m;
         const float a0 = bf16_bits_to_f32(xw[2 * m] & 0xFFFFu);
         const float a1 = bf16_bits_to_f32(xw[2 * m] >> 16);
         const float a2 = bf16_bits_to_f32(xw[2 * m + 1] & 0xFFFFu);
         const float a3 = bf16_bits_to_f32(xw[2 * m + 1] >> 16);
-        *reinterpret_cast<float4*>(xs + 4 * q) = make_float4(a0, a1, a2, a3);
+        *reinterpret_cast<float4*>(xs + 4 * (tid + 256 * m)) = make_float4(a0, a1, a2, a3);
         ss += (a0 * a0 + a1 * a1) + (a2 * a2 + a3 * a3);
       }
       ss = wave_sum_dpp(ss);
@@ -442,56 +451,65 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
       if (tid + 256 * m < E) slot_l[tid + 256 * m] = slot_r[m];
     wg_barrier();
     const float inv = 1.0f / sqrtf(((wsum[0] + wsum[1]) + (wsum[2] + wsum[3])) / (float)H + p.eps);
-    // the router logit first: its exchange gates the top-k
-    if (has_row) {
-      float acc = 0.f;
-#pragma unroll
-      for (int it = 0; it < NIT; ++it) {
-        const float4 xv = *reinterpret_cast<const float4*>(xs + it * 256 + lane * 4);
-        acc += wr[it].x * bf16r(xv.x * inv) + wr[it].y * bf16r(xv.y * inv) +
-               wr[it].z * bf16r(xv.z * inv) + wr[it].w * bf16r(xv.w * inv);
-      }
-      acc = wave_sum_dpp(acc);
-      if (lane == 0) st_word(p.lw + my_row, ep, __float_as_uint(acc + rbias));
-    }
-    // x_hat: stage for the gate/up dot products (4 threads per chunk, each
-    // 8 columns for int4 / 4 for int8); block 0 stores it
+    // x_hat of the elements 8 tid .. 8 tid + 7 (quarter tid % 4 of staged
+    // chunk tid / 4), rounded to bf16: the router's and the experts' input
+    float xv[8];
     {
-      constexpr int SUB = CC / 4;  // columns per thread
-      for (int t = tid; t < NCH * 4; t += 256) {
-        const int ch = t >> 2, jj = t & 3;
-        const int c0 = ch * CC + jj * SUB;
-        float xv[SUB];
+      const float4 u0 = *reinterpret_cast<const float4*>(xs + 8 * tid);
+      const float4 u1 = *reinterpret_cast<const float4*>(xs + 8 * tid + 4);
+      xv[0] = bf16r(u0.x * inv);
+      xv[1] = bf16r(u0.y * inv);
+      xv[2] = bf16r(u0.z * inv);
+      xv[3] = bf16r(u0.w * inv);
+      xv[4] = bf16r(u1.x * inv);
+      xv[5] = bf16r(u1.y * inv);
+      xv[6] = bf16r(u1.z * inv);
+      xv[7] = bf16r(u1.w * inv);
+    }
+    // the router logits first (their exchange gates the top-k): each
+    // thread's partial dot product over its elements, summed per wave, then
+    // over the 4 waves in a fixed order
 #pragma unroll
-        for (int q = 0; q < SUB; ++q) xv[q] = bf16r(xs[c0 + q] * inv);
-        if (w == 0) {
+    for (int r = 0; r < kRR; ++r) {
+      if (r < nrows) {
+        float acc = 0.f;
 #pragma unroll
-          for (int q = 0; q < SUB; q += 2)
-            *reinterpret_cast<uint32_t*>(p.x_hat + c0 + q) =
-                (uint32_t)f32_to_bf16_bits(xv[q]) | ((uint32_t)f32_to_bf16_bits(xv[q + 1]) << 16);
-        }
-        float c, sx;
-        if constexpr (BITS == 4) {
-          const uint32_t pa = pack_f16x2(xv[0], xv[4]);
-          const uint32_t pb = pack_f16x2(xv[1] * 0.0625f, xv[5] * 0.0625f);
-          const uint32_t pc = pack_f16x2(xv[2], xv[6]);
-          const uint32_t pf = pack_f16x2(xv[3] * 0.0625f, xv[7] * 0.0625f);
-          *reinterpret_cast<uint4*>(xp + ch * XS + jj * 4) = make_uint4(pa, pb, pc, pf);
-          c = f16lo(pa) + f16hi(pa) + f16lo(pb) + f16hi(pb) + f16lo(pc) + f16hi(pc) + f16lo(pf) +
-              f16hi(pf);
-          sx = f16lo(pa) + f16hi(pa) + f16lo(pc) + f16hi(pc) +
-               16.0f * (f16lo(pb) + f16hi(pb) + f16lo(pf) + f16hi(pf));
-        } else {
-          const uint32_t p0 = pack_f16x2(xv[0], xv[1]), p1 = pack_f16x2(xv[2], xv[3]);
-          *reinterpret_cast<uint2*>(xp + ch * XS + jj * 2) = make_uint2(p0, p1);
-          c = f16lo(p0) + f16hi(p0) + f16lo(p1) + f16hi(p1);
-          sx = c;
-        }
-        // combine the 4 threads of the chunk (adjacent lanes), fixed order
-        c = quad_sum(c);
-        sx = quad_sum(sx);
-        if (jj == 0) cs[ch] = make_float2(1024.0f * c, sx);
+        for (int m = 0; m < NXP; ++m)
+          acc += (wr[r][m].x * xv[4 * m] + wr[r][m].y * xv[4 * m + 1]) +
+                 (wr[r][m].z * xv[4 * m + 2] + wr[r][m].w * xv[4 * m + 3]);
+        acc = wave_sum_dpp(acc);
+        if (lane == 0) rred[r][wave] = acc;
       }
+    }
+    wg_barrier();
+    if (wave == 0 && lane < nrows) {
+      const float b = (p.router_bias != nullptr && w + NWG * lane < E) ? rbias : 0.0f;
+      st_word(p.lw + w + NWG * lane, ep,
+              __float_as_uint(((rred[lane][0] + rred[lane][1]) + (rred[lane][2] + rred[lane][3])) + b));
+    }
+    // x_hat staged for the gate/up dot products: thread tid takes quarter
+    // tid % 4 of chunk tid / 4 (its own 8 elements); block 0 stores it
+    {
+      const int ch = tid >> 2, jj = tid & 3;
+      if (w == 0) {
+#pragma unroll
+        for (int q = 0; q < 8; q += 2)
+          *reinterpret_cast<uint32_t*>(p.x_hat + 8 * tid + q) =
+              (uint32_t)f32_to_bf16_bits(xv[q]) | ((uint32_t)f32_to_bf16_bits(xv[q + 1]) << 16);
+      }
+      const uint32_t pa = pack_f16x2(xv[0], xv[4]);
+      const uint32_t pb = pack_f16x2(xv[1] * 0.0625f, xv[5] * 0.0625f);
+      const uint32_t pc = pack_f16x2(xv[2], xv[6]);
+      const uint32_t pf = pack_f16x2(xv[3] * 0.0625f, xv[7] * 0.0625f);
+      *reinterpret_cast<uint4*>(xp + ch * XS + jj * 4) = make_uint4(pa, pb, pc, pf);
+      float c = f16lo(pa) + f16hi(pa) + f16lo(pb) + f16hi(pb) + f16lo(pc) + f16hi(pc) + f16lo(pf) +
+                f16hi(pf);
+      float sx = f16lo(pa) + f16hi(pa) + f16lo(pc) + f16hi(pc) +
+                 16.0f * (f16lo(pb) + f16hi(pb) + f16lo(pf) + f16hi(pf));
+      // combine the 4 threads of the chunk (adjacent lanes), fixed order
+      c = quad_sum(c);
+      sx = quad_sum(sx);
+      if (jj == 0) cs[ch] = make_float2(1024.0f * c, sx);
     }
     wg_barrier();
 
@@ -528,11 +546,10 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
                                                      lg[2 * q + 1] = __uint_as_float(b);
                                                  });
       lds_wave_sync();
-      wave_topk_set<EPL>(lg, E, k, sel_idx, sel_val, mx, cand_key, cand_idx,
-                                           cand_val);
-      if (lane < k)
-        sel_base[lane] =
-            reinterpret_cast<uint64_t>(p.slab + (int64_t)slot_l[sel_idx[lane]] * p.stride);
+      wave_topk_set<EPL>(lg, E, k, sel_idx, sel_val, cand_key, cand_idx, cand_val,
+                         [&](int pos, int idx) {
+                           sel_base[pos] = reinterpret_cast<uint64_t>(p.slab + (int64_t)slot_l[idx] * p.stride);
+                         });
     }
     wg_barrier();
     // routed gate/up tiles of this workgroup (both issued before either is

@@ -222,22 +222,28 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ logits, int 
 // (the order the decode chain lays out h in).  The weights are not needed to
 // start loading the selected experts, so they come later (set_softmax).
 //   1. every lane keeps the max key of its logits; tau = the k-th largest
-//      lane maximum, found by counting, in every lane, the lane maxima above
-//      its own (tau = the least lane maximum with fewer than k above it).  At
-//      least k logits are >= tau, and a logit below tau has k larger ones, so
-//      every top-k logit is >= tau;
+//      of the 16 maxima of 4 adjacent lanes (k <= 16), found by counting, in
+//      every lane, the group maxima above its own (tau = the least group
+//      maximum with fewer than k above it).  At least k logits are >= tau,
+//      and a logit below tau has k larger ones, so every top-k logit is >=
+//      tau;
 //   2. the logits >= tau are compacted into LDS in ascending index (about k
-//      of them; more when a lane holds two of the top k);
+//      of them; more when a group holds two of the top k);
 //   3. with exactly k candidates they are the set; otherwise each candidate
 //      counts the candidates ranked above it, and those with fewer than k are
 //      the set, kept in ascending index.
 // More than 64 candidates (massive ties) take k rounds of wave argmax.
-// Writes set_idx[0..k), set_val[0..k) in LDS; mx, cand_* are LDS scratch.
-template <int MPL = kMaxPerLane>
+// Writes set_idx[0..k), set_val[0..k) in LDS; cand_* are LDS scratch.
+// on_sel(pos, idx) runs in the lane that writes set_idx[pos] = idx.
+struct NoSel {
+  __device__ void operator()(int, int) const {}
+};
+template <int MPL = kMaxPerLane, class OnSel = NoSel>
 __device__ __forceinline__ void wave_topk_set(const float* __restrict__ logits, int E, int k,
-                                              int32_t* set_idx, float* set_val, uint32_t* mx,
+                                              int32_t* set_idx, float* set_val,
                                               uint32_t* cand_key, int32_t* cand_idx,
-                                              float* cand_val) {
+                                              float* cand_val, OnSel on_sel = OnSel()) {
+  static_assert(MOE_MAX_TOP_K <= 16, "the threshold takes the k-th of 16 group maxima");
   const int lane = threadIdx.x & 63;
   const int per = (E + 63) >> 6;
   float v[MPL];
@@ -251,16 +257,13 @@ __device__ __forceinline__ void wave_topk_set(const float* __restrict__ logits, 
     u[i] = ok ? order_key(v[i]) : 0u;
     M = max(M, u[i]);
   }
-  // 1. tau = the k-th largest lane maximum
-  mx[lane] = M;
-  lds_wave_sync();
+  // 1. tau = the k-th largest group maximum
+  uint32_t g = max(M, dpp_u<0xB1, 0xF>(M, M));  // lane ^ 1
+  g = max(g, dpp_u<0x4E, 0xF>(g, g));           // lane ^ 2
   uint32_t above = 0;
 #pragma unroll
-  for (int j = 0; j < 64; j += 4) {
-    const uint4 q = *reinterpret_cast<const uint4*>(mx + j);
-    above += (q.x > M ? 1u : 0u) + (q.y > M ? 1u : 0u) + (q.z > M ? 1u : 0u) + (q.w > M ? 1u : 0u);
-  }
-  const uint32_t tau = wave_min_dpp(above < (uint32_t)k ? M : 0xFFFFFFFFu);
+  for (int j = 0; j < 16; ++j) above += (uint32_t)__builtin_amdgcn_readlane((int)g, 4 * j) > g ? 1u : 0u;
+  const uint32_t tau = wave_min_dpp(above < (uint32_t)k ? g : 0xFFFFFFFFu);
   // 2. compact the candidates, ascending index
   uint32_t base = 0;
 #pragma unroll
@@ -284,26 +287,25 @@ __device__ __forceinline__ void wave_topk_set(const float* __restrict__ logits, 
   if (ncand <= 64) {
     // 3. the set: candidates ranked below k (key descending, index ascending)
     bool sel = lane < ncand;
-    if (ncand > k && sel) {
-      const uint32_t K = cand_key[lane];
-      const int I = cand_idx[lane];
+    if (ncand > k) {
+      // candidate j's key and index reach every lane by readlane
+      const uint32_t K = sel ? cand_key[lane] : 0u;
+      const int I = sel ? cand_idx[lane] : 0;
       int rank = 0;
-      for (int j0 = 0; j0 < ncand; j0 += 4) {
-        const uint4 kk = *reinterpret_cast<const uint4*>(cand_key + j0);
-        const int4 ii = *reinterpret_cast<const int4*>(cand_idx + j0);
-        const uint32_t ks[4] = {kk.x, kk.y, kk.z, kk.w};
-        const int is[4] = {ii.x, ii.y, ii.z, ii.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          rank += (j0 + q < ncand && (ks[q] > K || (ks[q] == K && is[q] < I))) ? 1 : 0;
+      for (int j = 0; j < ncand; ++j) {
+        const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)K, j);
+        const int ij = __builtin_amdgcn_readlane(I, j);
+        rank += (kj > K || (kj == K && ij < I)) ? 1 : 0;
       }
-      sel = rank < k;
+      sel = sel && rank < k;
     }
     const uint64_t m = ballot(sel);
     if (sel) {
       const uint32_t pos = mbcnt(m);
-      set_idx[pos] = cand_idx[lane];
+      const int I = cand_idx[lane];
+      set_idx[pos] = I;
       set_val[pos] = cand_val[lane];
+      on_sel((int)pos, I);
     }
   } else {
     // k rounds of (max key, lowest index) over the whole wave; the winners
@@ -343,6 +345,7 @@ __device__ __forceinline__ void wave_topk_set(const float* __restrict__ logits, 
       for (int j = 0; j < k; ++j) pos += cand_idx[j] < I ? 1 : 0;
       set_idx[pos] = I;
       set_val[pos] = cand_val[lane];
+      on_sel(pos, I);
     }
   }
   lds_wave_sync();
