@@ -166,7 +166,11 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
   constexpr int NXP = H / 1024;      // x word pairs per thread
   static_assert(NXP == 2 && CC == 32, "thread tid owns x elements 8 tid .. 8 tid + 7");
   constexpr int hsh = SHARED ? 1 : 0;
-  constexpr int kMaxDownUnits = max_down_units<BITS>();
+  // down units per half-wave: enough for the 8 half-waves to cover every
+  // unit (all k * I / KBC + Is / KBC of them) when k is compile-time
+  constexpr int kMaxDownUnits =
+      KC ? (KC * (IR / C::KBC) + (SHARED ? IS / C::KBC : 0) + 7) / 8 : max_down_units<BITS>();
+  static_assert(kMaxDownUnits <= max_down_units<BITS>(), "down units per half-wave");
 
   __shared__ __align__(16) float xs[H];
   __shared__ __align__(16) uint32_t xp[NCH * XS];
@@ -177,9 +181,7 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
   __shared__ int32_t sel_idx[MOE_MAX_TOP_K];
   __shared__ float sel_val[MOE_MAX_TOP_K], sel_w[MOE_MAX_TOP_K], gam;
   __shared__ uint64_t sel_base[MOE_MAX_TOP_K];
-  __shared__ __align__(16) uint32_t cand_key[64];
-  __shared__ __align__(16) int32_t cand_idx[64];
-  __shared__ float cand_val[64];
+  __shared__ __align__(16) uint64_t cand[66];  // top-k ranking words (+ a spare slot)
   __shared__ float red[4][kRowTile][2], red_s[4][kRowTile][2];
   __shared__ float dred[4][2][8];
   __shared__ float wsum[4];
@@ -546,7 +548,7 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
                                                      lg[2 * q + 1] = __uint_as_float(b);
                                                  });
       lds_wave_sync();
-      wave_topk_set<EPL>(lg, E, k, sel_idx, sel_val, cand_key, cand_idx, cand_val,
+      wave_topk_set<EPL>(lg, E, k, sel_idx, sel_val, cand,
                          [&](int pos, int idx) {
                            sel_base[pos] = reinterpret_cast<uint64_t>(p.slab + (int64_t)slot_l[idx] * p.stride);
                          });

@@ -222,94 +222,112 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ logits, int 
 // (the order the decode chain lays out h in).  The weights are not needed to
 // start loading the selected experts, so they come later (set_softmax).
 //   1. every lane keeps the max key of its logits; tau = the k-th largest
-//      of the 16 maxima of 4 adjacent lanes (k <= 16), found by counting, in
-//      every lane, the group maxima above its own (tau = the least group
-//      maximum with fewer than k above it).  At least k logits are >= tau,
-//      and a logit below tau has k larger ones, so every top-k logit is >=
-//      tau;
-//   2. the logits >= tau are compacted into LDS in ascending index (about k
-//      of them; more when a group holds two of the top k);
+//      of the 16 maxima of 4 adjacent lanes (k <= 16): the 16 maxima are
+//      read into scalar registers, every lane counts those above its own,
+//      and tau is the least group maximum with fewer than k above it (a
+//      scalar minimum over the ballot of those groups).  At least k logits
+//      are >= tau, and a logit below tau has k larger ones, so every top-k
+//      logit is >= tau;
+//   2. the logits >= tau are compacted into LDS in ascending index as
+//      64-bit ranking words (order key << 32 | ~index: a larger word is a
+//      larger logit, or an equal one with a lower index);
 //   3. with exactly k candidates they are the set; otherwise each candidate
-//      counts the candidates ranked above it, and those with fewer than k are
-//      the set, kept in ascending index.
+//      counts the words above its own, read 16 at a time as broadcast LDS
+//      loads (unused slots hold 0, below every word), and those with fewer
+//      than k above are the set, kept in ascending index.
 // More than 64 candidates (massive ties) take k rounds of wave argmax.
-// Writes set_idx[0..k), set_val[0..k) in LDS; cand_* are LDS scratch.
-// on_sel(pos, idx) runs in the lane that writes set_idx[pos] = idx.
+// Writes set_idx[0..k), set_val[0..k) in LDS; cand[0..65) is LDS scratch
+// (16-byte aligned).  on_sel(pos, idx) runs in the lane that writes
+// set_idx[pos] = idx.
 struct NoSel {
   __device__ void operator()(int, int) const {}
 };
+__device__ __forceinline__ float key_value(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
 template <int MPL = kMaxPerLane, class OnSel = NoSel>
 __device__ __forceinline__ void wave_topk_set(const float* __restrict__ logits, int E, int k,
-                                              int32_t* set_idx, float* set_val,
-                                              uint32_t* cand_key, int32_t* cand_idx,
-                                              float* cand_val, OnSel on_sel = OnSel()) {
+                                              int32_t* set_idx, float* set_val, uint64_t* cand,
+                                              OnSel on_sel = OnSel()) {
   static_assert(MOE_MAX_TOP_K <= 16, "the threshold takes the k-th of 16 group maxima");
   const int lane = threadIdx.x & 63;
   const int per = (E + 63) >> 6;
-  float v[MPL];
   uint32_t u[MPL];
   uint32_t M = 0;
 #pragma unroll
   for (int i = 0; i < MPL; ++i) {
     const int e = i * 64 + lane;
     const bool ok = i < per && e < E;
-    v[i] = ok ? logits[e] : -INFINITY;
-    u[i] = ok ? order_key(v[i]) : 0u;
+    u[i] = ok ? order_key(logits[e]) : 0u;
     M = max(M, u[i]);
   }
+  cand[lane] = 0ull;  // every slot below any ranking word
   // 1. tau = the k-th largest group maximum
   uint32_t g = max(M, dpp_u<0xB1, 0xF>(M, M));  // lane ^ 1
   g = max(g, dpp_u<0x4E, 0xF>(g, g));           // lane ^ 2
-  uint32_t above = 0;
+  uint32_t G[16];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) above += (uint32_t)__builtin_amdgcn_readlane((int)g, 4 * j) > g ? 1u : 0u;
-  const uint32_t tau = wave_min_dpp(above < (uint32_t)k ? g : 0xFFFFFFFFu);
-  // 2. compact the candidates, ascending index
-  uint32_t base = 0;
+  for (int j = 0; j < 16; ++j) G[j] = (uint32_t)__builtin_amdgcn_readlane((int)g, 4 * j);
+  uint32_t a[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 16; ++j) a[j & 3] += G[j] > g ? 1u : 0u;
+  const uint64_t below_k = ballot((a[0] + a[1]) + (a[2] + a[3]) < (uint32_t)k);
+  uint32_t tau = 0xFFFFFFFFu;
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    if ((below_k >> (4 * j)) & 1ull) tau = min(tau, G[j]);
+  // 2. compact the candidates, ascending index; a lane that is not one
+  //    writes to the spare slot 64
+  uint64_t m[MPL];
+  uint32_t base[MPL + 1];
+  base[0] = 0u;
 #pragma unroll
   for (int i = 0; i < MPL; ++i) {
-    if (i < per) {
-      const bool c = u[i] >= tau && (i * 64 + lane) < E;
-      const uint64_t m = ballot(c);
-      if (c) {
-        const uint32_t pos = base + mbcnt(m);
-        if (pos < 64) {
-          cand_key[pos] = u[i];
-          cand_idx[pos] = i * 64 + lane;
-          cand_val[pos] = v[i];
-        }
-      }
-      base += (uint32_t)__popcll(m);
-    }
+    m[i] = ballot(i < per && u[i] >= tau && (i * 64 + lane) < E);
+    base[i + 1] = base[i] + (i < per ? (uint32_t)__popcll(m[i]) : 0u);
   }
-  lds_wave_sync();
-  const int ncand = (int)base;
+  const int ncand = (int)base[MPL];
   if (ncand <= 64) {
-    // 3. the set: candidates ranked below k (key descending, index ascending)
+#pragma unroll
+    for (int i = 0; i < MPL; ++i) {
+      if (i < per) {
+        const bool c = (m[i] >> lane) & 1ull;
+        const uint32_t pos = c ? base[i] + mbcnt(m[i]) : 64u;
+        cand[pos] = ((uint64_t)u[i] << 32) | (uint32_t)~(uint32_t)(i * 64 + lane);
+      }
+    }
+    lds_wave_sync();
+    // 3. the set: candidates ranked below k
+    const uint64_t me = cand[lane];
     bool sel = lane < ncand;
     if (ncand > k) {
-      // candidate j's key and index reach every lane by readlane
-      const uint32_t K = sel ? cand_key[lane] : 0u;
-      const int I = sel ? cand_idx[lane] : 0;
-      int rank = 0;
-      for (int j = 0; j < ncand; ++j) {
-        const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)K, j);
-        const int ij = __builtin_amdgcn_readlane(I, j);
-        rank += (kj > K || (kj == K && ij < I)) ? 1 : 0;
+      uint32_t r[4] = {0u, 0u, 0u, 0u};
+      for (int j0 = 0; j0 < ncand; j0 += 16) {
+        const uint4* q = reinterpret_cast<const uint4*>(cand + j0);
+        uint4 w[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) w[t] = q[t];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const uint64_t c0 = ((uint64_t)w[t].y << 32) | w[t].x;
+          const uint64_t c1 = ((uint64_t)w[t].w << 32) | w[t].z;
+          r[t & 3] += (c0 > me ? 1u : 0u) + (c1 > me ? 1u : 0u);
+        }
       }
-      sel = sel && rank < k;
+      sel = sel && (r[0] + r[1]) + (r[2] + r[3]) < (uint32_t)k;
     }
-    const uint64_t m = ballot(sel);
+    const uint64_t ms = ballot(sel);
     if (sel) {
-      const uint32_t pos = mbcnt(m);
-      const int I = cand_idx[lane];
+      const uint32_t pos = mbcnt(ms);
+      const int I = (int)~(uint32_t)me;
       set_idx[pos] = I;
-      set_val[pos] = cand_val[lane];
+      set_val[pos] = key_value((uint32_t)(me >> 32));
       on_sel((int)pos, I);
     }
   } else {
     // k rounds of (max key, lowest index) over the whole wave; the winners
-    // go to cand_* in rank order, then to set_* by ascending index
+    // go to cand[0..k) in rank order as (key << 32 | index), then to set_*
+    // by ascending index
     uint32_t taken = 0u;
     for (int r = 0; r < k; ++r) {
       uint32_t bk = 0;
@@ -330,21 +348,17 @@ __device__ __forceinline__ void wave_topk_set(const float* __restrict__ logits, 
       for (int off = 32; off >= 1; off >>= 1) mi = min(mi, __shfl_xor(mi, off, 64));
       if ((mi & 63) == lane) {
         taken |= 1u << (mi >> 6);
-        float sv = 0.f;
-#pragma unroll
-        for (int i = 0; i < MPL; ++i)
-          if (i == (mi >> 6)) sv = v[i];
-        cand_idx[r] = mi;
-        cand_val[r] = sv;
+        cand[r] = ((uint64_t)mk << 32) | (uint32_t)mi;
       }
     }
     lds_wave_sync();
     if (lane < k) {
-      const int I = cand_idx[lane];
+      const uint64_t me = cand[lane];
+      const int I = (int)(uint32_t)me;
       int pos = 0;
-      for (int j = 0; j < k; ++j) pos += cand_idx[j] < I ? 1 : 0;
+      for (int j = 0; j < k; ++j) pos += (int)(uint32_t)cand[j] < I ? 1 : 0;
       set_idx[pos] = I;
-      set_val[pos] = cand_val[lane];
+      set_val[pos] = key_value((uint32_t)(me >> 32));
       on_sel(pos, I);
     }
   }

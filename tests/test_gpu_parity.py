@@ -312,6 +312,46 @@ def test_chain_other_top_k(top_k):
 
 
 @pytest.mark.parametrize("cfgname", ["decode_35b", "decode_80b"])
+def test_chain_boundary_ties(cfgname):
+    """The persistent chain when a few more than k experts tie for the top
+    logit (fewer than 64 candidates, so the ranked-candidate path, not the
+    argmax fallback): the set is the k lowest indices of the tied experts
+    and every weight is 1/k."""
+    moe, wl = _moe(), _wl()
+    cfg = configs.CONFIGS[cfgname]
+    E, H, k = cfg.n_experts, cfg.hidden, cfg.top_k
+    say(f"[chain boundary ties] {cfgname}")
+    w = wl.Workload(cfg, n_layers=1)
+    rng = np.random.default_rng(11)
+    tied = np.sort(rng.choice(E, size=k + 4, replace=False))
+    x0_np = synth.activations(cfg)
+    # a row along x_hat: its logit (about 0.05 H) is far above every other
+    rw_np = w.router_w.view(E, H).cpu().numpy().copy()
+    rw_np[tied] = (0.05 * oracle.chain_prologue(x0_np, cfg.rms_eps, cfg.act)).astype(np.float32)[0]
+    w.router_w.view(E, H).copy_(torch.from_numpy(rw_np))
+    d = w.desc
+    x = wl.act_tensor(cfg, x0_np)
+    xh = torch.empty_like(x)
+    out = torch.empty_like(x)
+    ws = w.workspace()
+    pi, pw, pg = moe.moe_workspace_routing(d, ws)
+    base = ws.data_ptr()
+    rw, rb, st, sh = w.layer_args(0)
+    moe.moe_chain_forward(d, 1, x, rw, rb, w.slab, st, sh, w.shared_stride, xh, out, ws)
+    torch.cuda.synchronize()
+    idx = ws[pi - base: pi - base + 4 * k].view(torch.int32)
+    wt = ws[pw - base: pw - base + 4 * k].view(torch.float32)
+    assert idx.tolist() == tied[:k].tolist()
+    assert torch.allclose(wt, torch.full_like(wt, 1.0 / k), rtol=1e-6)
+    inp = oracle.LayerInputs(cfg, 0, overrides={"router_w": rw_np})
+    ref = oracle.oracle_layer(inp, wl.to_f64(xh))
+    assert ref["idx"][0].tolist() == tied[:k].tolist()
+    check_out(out.float().cpu().numpy(), ref["out"], cfg.act, "chain boundary ties")
+    del w
+    _free()
+
+
+@pytest.mark.parametrize("cfgname", ["decode_35b", "decode_80b"])
 def test_chain_massive_ties(cfgname):
     """The persistent chain on an all-zero router: every logit ties, so the
     expert set is 0..k-1 (k rounds of wave argmax, not the candidate path),
