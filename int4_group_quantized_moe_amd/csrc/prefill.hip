@@ -17,11 +17,16 @@
 //    1 + q/16, int8 as q); the group's bf16 scale is applied in fp32 to the
 //    group's code sums, and the group's bias multiplies the group sum of the
 //    activations (w = s q + b factors as s * sum(q x) + b * sum(x));
-//  * the gate/up input x_hat is bf16 already; the down input h is carried
-//    as a pair of bf16 parts (hi + lo, 16 significant bits) and multiplied
-//    twice.
+//  * the gate/up input x_hat is bf16 already; the down GEMM runs on
+//    v_mfma_f32_32x32x16_f16: h is stored in fp16 (11 significant bits)
+//    after a power-of-two scale per (row tile, group) that puts the tile's
+//    largest |h| in [2^13, 2^14), and the codes enter as fp16 (int4 as
+//    1 + q/16, int8 as q), in a K order permuted within each 8-value chunk
+//    so that a code word expands with masks and shifts (the h chunks are
+//    written in the same order).
 // Dequantising to bf16 instead (s*q + b rounded, and h rounded to bf16)
-// would add ~2^-9 relative error per weight and per h value.
+// would add ~2^-9 relative error per weight and per h value; h in bf16
+// alone measured 0.01 rms of the output on the batched 80B layer.
 #include "moe_internal.h"
 
 namespace moe {
@@ -39,6 +44,38 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 
 __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f32x16 mfma_f16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// Exact fp16 operands from integer codes, in the permuted K order of the
+// down GEMM.  int4: word d of 8 codes becomes the fp16 pairs (q0, q4),
+// (q1, q5), (q2, q6), (q3, q7), each 1 + q/16 (the nibble in mantissa bits
+// 6..9 of 1.0): 8 instructions.  int8: each word of 4 codes becomes (q0, q2),
+// (q1, q3): 1024 + q by a mask into the mantissa of 1024.0, then 1024
+// subtracted in packed fp16, both exact.
+__device__ __forceinline__ u32x4 code_frag4_f16(uint32_t d) {
+  constexpr uint32_t M = 0x03C003C0u, O = 0x3C003C00u;
+  return u32x4{((d << 6) & M) | O, ((d << 2) & M) | O, ((d >> 2) & M) | O, ((d >> 6) & M) | O};
+}
+__device__ __forceinline__ uint32_t byte_pair_f16(uint32_t d) {
+  const f16x2 v = __builtin_bit_cast(f16x2, (d & 0x00FF00FFu) | 0x64006400u) - (f16x2){1024, 1024};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ u32x4 code_frag8_f16(uint32_t d0, uint32_t d1) {
+  return u32x4{byte_pair_f16(d0), byte_pair_f16(d0 >> 8), byte_pair_f16(d1), byte_pair_f16(d1 >> 8)};
+}
+// Position, in the natural K order of an 8-value chunk, of the value the
+// down GEMM's fp16 operands hold at slot j (the order the expansions above
+// produce).
+template <int BITS>
+__device__ __forceinline__ constexpr int dn_perm(int j) {
+  return BITS == 4 ? (j >> 1) + 4 * (j & 1) : (j & 4) + ((j & 3) >> 1) + 2 * (j & 1);
 }
 
 // Exact bf16 operands from integer codes, in natural K order.  int4: the
@@ -315,8 +352,12 @@ __global__ __launch_bounds__(256) void group_sum_kernel(const uint16_t* __restri
 // gate/up: grid (max(I, Is)/64, tiles).  Tile columns: 64 gate rows and the
 // 64 up rows of the same h columns; wave wn holds h columns n0 + 32 wn ..
 // n0 + 32 wn + 31 as block 0 (gate) and block 1 (up).  Writes per row the
-// 64 h values as bf16 (hi, lo) pairs in the K order the down GEMM stages,
-// and the row's group sum of h.
+// 64 h values in fp16 after the tile's power-of-two scale, in the K order the
+// down GEMM stages, the row's group sum of the stored values (unscaled), and
+// the scale's inverse.  An h row keeps the byte stride of the fp32 h rows of
+// the GEMV kernels (4 x inter bytes), so buckets of either path index the
+// one h buffer alike; the fp16 row fills the first half, and the second
+// half holds, per group g, the inverse scale as a float at element 2 g.
 
 #define MOE_PGU_PARAMS                                                                       \
   const uint16_t* __restrict__ x, const float* __restrict__ xsum,                              \
@@ -675,14 +716,34 @@ __device__ __forceinline__ void prefill_gateup_item(MOE_PGU_PARAMS, GuStage<BITS
   if (wm == 0) ht_store(s0.A, C, wn, l32, half);
   else ht_store(s1.A, C, wn, l32, half);
   __syncthreads();
-  // row sr, columns 32 sc .. 32 sc + 31: group sum and (hi, lo) parts
+  // row sr, columns 32 sc .. 32 sc + 31: the tile's scale (largest |h| of
+  // its rows to [2^13, 2^14)), the scaled values in fp16, their group sum
   const int sr = tid >> 1, sc = tid & 1;
   float v[32];
   if (sr < 64) ht_load(s0.A, sr, sc, v);
   else ht_load(s1.A, sr & 63, sc, v);
+  uint32_t amax = 0u;
+  if (sr < ti.rows) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = max(amax, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, off, 64));
+  __shared__ uint32_t wmax[4];
+  if (lane == 0) wmax[wave] = amax;
+  __syncthreads();
+  amax = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+  const int ex = max((int)(amax >> 23), 14);
+  const float down = __uint_as_float((uint32_t)(267 - ex) << 23);  // 2^(140 - ex)
+  const float up = __uint_as_float((uint32_t)(ex - 13) << 23);     // 2^(ex - 140)
+  _Float16 hv[32];
   float part = 0.f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) part += v[i];
+  for (int i = 0; i < 32; ++i) {
+    hv[i] = (_Float16)(v[i] * down);
+    part += (float)hv[i];
+  }
+  part *= up;
   const float other = __shfl_xor(part, 1, 64);
   const float total = sc == 0 ? part + other : other + part;
   if (sr < ti.rows) {
@@ -695,20 +756,25 @@ __device__ __forceinline__ void prefill_gateup_item(MOE_PGU_PARAMS, GuStage<BITS
       hrow = (int64_t)(ti.base + sr) * 2 * I;
       srow_i = (int64_t)(ti.base + sr) * (I / kGroup) + gi;
     }
-    if (sc == 0) hsum[srow_i] = total;
+    if (sc == 0) {
+      hsum[srow_i] = total;
+      *reinterpret_cast<float*>(h + hrow + inter + 2 * gi) = up;
+    }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      u32x4 hi, lo;
-      split8(v + 8 * q, hi, lo);
-      *reinterpret_cast<u32x4*>(h + hrow + n0 + 32 * sc + 8 * q) = hi;
-      *reinterpret_cast<u32x4*>(h + hrow + inter + n0 + 32 * sc + 8 * q) = lo;
+      uint32_t w4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        w4[j] = (uint32_t)__builtin_bit_cast(uint16_t, hv[8 * q + dn_perm<BITS>(2 * j)]) |
+                ((uint32_t)__builtin_bit_cast(uint16_t, hv[8 * q + dn_perm<BITS>(2 * j + 1)]) << 16);
+      *reinterpret_cast<u32x4*>(h + hrow + n0 + 32 * sc + 8 * q) = u32x4{w4[0], w4[1], w4[2], w4[3]};
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// down: grid (H/128 column blocks, tiles).  A = h as (hi, lo) bf16 parts, two
-// MFMAs per K step.  Writes the weighted expert output of every bucket entry
+// down: grid (H/128 column blocks, tiles).  A = h in scaled fp16, B = the
+// codes in fp16, one MFMA per K step and output block.  Writes the weighted expert output of every bucket entry
 // to partial[(t*(k+1) + j) * H + col] (fp32; the shared expert is j = k).
 
 #define MOE_PDN_PARAMS                                                                       \
@@ -727,28 +793,26 @@ __device__ __forceinline__ void prefill_gateup_item(MOE_PGU_PARAMS, GuStage<BITS
       d_tile_s, nbg
 
 // Down K pipeline: the same scheme as gate/up with 512 threads and a
-// 128-row x 256-column tile; a stage holds the 128 h rows as bf16 (hi, lo)
-// parts and the 256 output rows' codes and (scale, bias) words.
+// 128-row x 256-column tile; a stage holds the 128 h rows (fp16) and the
+// 256 output rows' codes and (scale, bias) words.
 constexpr int kDnThreads = 512;
 constexpr int kDnCols = 256;
 
 template <int BITS>
 struct DnStage {
   uint4 Ah[kStageChunks];
-  uint4 Al[kStageChunks];
   uint4 B[kDnCols * (kGroup * BITS / 8) / 16];
   uint32_t S[kDnThreads];  // (scale, bias) of rows 0..255 (256..511 repeat them)
 };
 
 template <int BITS>
-constexpr int dn_stage_loads() { return 4 + BITS / 4 + 1; }
+constexpr int dn_stage_loads() { return 2 + BITS / 4 + 1; }
 
 template <int BITS>
 struct DnSrc {
   const uint8_t* h;    // h rows of the tile (uniform base)
   const uint8_t* sec;  // blob down section (uniform)
   int64_t unit_b;
-  int inter2;          // bytes from a row's hi part to its lo part
   uint32_t a[2];       // h chunk offsets (stage 0, hi part)
   uint32_t b[BITS / 4];  // code chunk offsets (k-block 0, group 0)
   uint32_t sb;         // (scale, bias) word offset
@@ -764,11 +828,6 @@ __device__ __forceinline__ void dn_issue(const DnSrc<BITS>& P, DnStage<BITS>& st
   for (int j = 0; j < 2; ++j)
     __builtin_amdgcn_global_load_lds(MOE_G1(ha + P.a[j]), MOE_L3(&st.Ah[j * 512 + wave * 64]), 16,
                                      0, 0);
-  const uint8_t* la = ha + P.inter2;
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-    __builtin_amdgcn_global_load_lds(MOE_G1(la + P.a[j]), MOE_L3(&st.Al[j * 512 + wave * 64]), 16,
-                                     0, 0);
   const uint8_t* wb = P.sec + (int64_t)(g / GPK) * P.unit_b + (g % GPK) * GBYTES;
 #pragma unroll
   for (int j = 0; j < BITS / 4; ++j)
@@ -780,12 +839,12 @@ __device__ __forceinline__ void dn_issue(const DnSrc<BITS>& P, DnStage<BITS>& st
 
 template <int BITS>
 struct DnFrags {
-  u32x4 ah[2][2], al[2][2];  // hi/lo A operands of two K steps, both row blocks
+  u32x4 ah[2][2];  // A operands of two K steps, both row blocks
   u32x4 q[2][BITS / 4];
   uint32_t sb[2];
 };
 
-// hi and lo A operands of K steps k0, k0+1 (both row blocks); with CODES
+// A operands of K steps k0, k0+1 (both row blocks); with CODES
 // also the lane's codes and (scale, bias) words of both output rows.
 template <int BITS, bool CODES>
 __device__ __forceinline__ void dn_read(const DnStage<BITS>& st, int k0, int wm, int wn, int l32,
@@ -795,21 +854,14 @@ __device__ __forceinline__ void dn_read(const DnStage<BITS>& st, int k0, int wm,
   const int i11 = swz(64 * wm + 32 + l32, 4 * half + k0 + 1);
   const uint32_t h00 = lds_addr(&st.Ah[i00]), h01 = lds_addr(&st.Ah[i01]);
   const uint32_t h10 = lds_addr(&st.Ah[i10]), h11 = lds_addr(&st.Ah[i11]);
-  const uint32_t l00 = lds_addr(&st.Al[i00]), l01 = lds_addr(&st.Al[i01]);
-  const uint32_t l10 = lds_addr(&st.Al[i10]), l11 = lds_addr(&st.Al[i11]);
   asm volatile(
-      "ds_read_b128 %0, %8\n\t"
-      "ds_read_b128 %1, %9\n\t"
-      "ds_read_b128 %2, %10\n\t"
-      "ds_read_b128 %3, %11\n\t"
-      "ds_read_b128 %4, %12\n\t"
-      "ds_read_b128 %5, %13\n\t"
-      "ds_read_b128 %6, %14\n\t"
-      "ds_read_b128 %7, %15\n\t"
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(f.ah[0][0]), "=&v"(f.ah[0][1]), "=&v"(f.ah[1][0]), "=&v"(f.ah[1][1]),
-        "=&v"(f.al[0][0]), "=&v"(f.al[0][1]), "=&v"(f.al[1][0]), "=&v"(f.al[1][1])
-      : "v"(h00), "v"(h01), "v"(h10), "v"(h11), "v"(l00), "v"(l01), "v"(l10), "v"(l11)
+      : "=&v"(f.ah[0][0]), "=&v"(f.ah[0][1]), "=&v"(f.ah[1][0]), "=&v"(f.ah[1][1])
+      : "v"(h00), "v"(h01), "v"(h10), "v"(h11)
       : "memory");
   if constexpr (CODES) {
     const int r0 = 64 * wn + l32, r1 = 64 * wn + 32 + l32;
@@ -844,9 +896,25 @@ __device__ __forceinline__ void dn_read(const DnStage<BITS>& st, int k0, int wm,
   }
 }
 
+// MFMA operand of K step ks from the lane's codes of one output row, in
+// the down GEMM's fp16 K order.
+template <int BITS>
+__device__ __forceinline__ u32x4 dn_bfrag(const u32x4 (&q)[BITS / 4], int ks) {
+  if constexpr (BITS == 4) {
+    const uint32_t d = ks == 0 ? q[0].x : ks == 1 ? q[0].y : ks == 2 ? q[0].z : q[0].w;
+    return code_frag4_f16(d);
+  } else {
+    const u32x4 v = q[ks >> 1];
+    return (ks & 1) ? code_frag8_f16(v.z, v.w) : code_frag8_f16(v.x, v.y);
+  }
+}
+
+// hs: the inverse of the h scale of this stage's group (in LDS, read after
+// the stage barrier).
 template <int BITS, typename F>
 __device__ __forceinline__ void dn_stage(const DnStage<BITS>& st, int later, int wm, int wn,
-                                         int l32, int half, f32x16 (&C)[2][2], F&& refill) {
+                                         int l32, int half, f32x16 (&C)[2][2], F&& refill,
+                                         const float* hs) {
   constexpr int L = dn_stage_loads<BITS>();
   static_assert(kStages == 3, "wait ladder below covers kStages - 1 = 2 later stages");
   if (later >= 2) wait_vm<2 * L>();
@@ -870,16 +938,14 @@ __device__ __forceinline__ void dn_stage(const DnStage<BITS>& st, int later, int
     }
     u32x4 b[2];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) b[nb] = gu_bfrag<BITS>(f.q[nb], kk);
+    for (int nb = 0; nb < 2; ++nb) b[nb] = dn_bfrag<BITS>(f.q[nb], kk);
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        acc[mb][nb] = mfma(f.ah[mb][kk & 1], b[nb], acc[mb][nb]);
-        acc[mb][nb] = mfma(f.al[mb][kk & 1], b[nb], acc[mb][nb]);
-      }
+      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma_f16(f.ah[mb][kk & 1], b[nb], acc[mb][nb]);
   }
-  const float scl[2] = {code_scale<BITS>(f.sb[0]), code_scale<BITS>(f.sb[1])};
+  const float hsc = *hs;
+  const float scl[2] = {code_scale<BITS>(f.sb[0]) * hsc, code_scale<BITS>(f.sb[1]) * hsc};
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -895,7 +961,8 @@ __device__ __forceinline__ void dn_stage(const DnStage<BITS>& st, int later, int
 template <int BITS>
 __device__ __forceinline__ void prefill_down_item(MOE_PDN_PARAMS, DnStage<BITS>& s0,
                                                   DnStage<BITS>& s1, DnStage<BITS>& s2,
-                                                  int32_t* rowdst, float* roww, XcdItem it) {
+                                                  int32_t* rowdst, float* roww, float* hsl,
+                                                  XcdItem it) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3, l32 = lane & 31, half = lane >> 5;
   const TileInfo ti = get_tile(tiles, counts, offsets, it.tile, E);
@@ -926,6 +993,8 @@ __device__ __forceinline__ void prefill_down_item(MOE_PDN_PARAMS, DnStage<BITS>&
   // h rows and group-sum rows of the tile
   const int64_t hbase = shared ? (int64_t)T * k * 2 * I + (int64_t)ti.base * 2 * Is
                                : (int64_t)ti.base * 2 * I;
+  // the inverse h scale of each group of the tile (stored with its first row)
+  if (tid < G) hsl[tid] = *reinterpret_cast<const float*>(h + hbase + inter + 2 * tid);
   const int64_t sbase = shared ? (int64_t)T * k * (I / kGroup) + (int64_t)ti.base * G
                                : (int64_t)ti.base * G;
 
@@ -933,7 +1002,6 @@ __device__ __forceinline__ void prefill_down_item(MOE_PDN_PARAMS, DnStage<BITS>&
   P.h = reinterpret_cast<const uint8_t*>(h + hbase);
   P.sec = sec;
   P.unit_b = unit_b;
-  P.inter2 = inter * 2;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int ch = j * 512 + tid, r = ch >> 3, c = (ch & 7) ^ (r & 7);
@@ -968,7 +1036,7 @@ __device__ __forceinline__ void prefill_down_item(MOE_PDN_PARAMS, DnStage<BITS>&
       if (g + I + kStages < G) dn_issue<BITS>(P, BUF, g + I + kStages, wv);              \
     };                                                                                   \
     if (g >= 0) dn_stage<BITS>(BUF, min(kStages - 1, G - 1 - g - I), wm, wn, l32, half, C, \
-                               refill);                                                  \
+                               refill, hsl + g + I);                                     \
     else refill();                                                                       \
   }
     MOE_DN_STEP(0, s0)
@@ -1031,12 +1099,13 @@ __global__ __launch_bounds__(kDnThreads) void prefill_down_kernel(MOE_PDN_PARAMS
   __shared__ __align__(16) DnStage<BITS> s2;
   __shared__ int32_t rowdst[kMT];
   __shared__ float roww[kMT];
+  __shared__ float hsl[MOE_MAX_INTER / kGroup];
   const int total = *ntiles * nbg;
   const int per = (total + 7) / 8, c = blockIdx.x & 7;
   for (int i = blockIdx.x >> 3; i < per; i += gridDim.x >> 3) {
     const int q = c * per + i;
     if (q >= total) break;
-    prefill_down_item<BITS>(MOE_PDN_ARGS, s0, s1, s2, rowdst, roww,
+    prefill_down_item<BITS>(MOE_PDN_ARGS, s0, s1, s2, rowdst, roww, hsl,
                             XcdItem{q / nbg, q % nbg, true});
     __syncthreads();
   }
