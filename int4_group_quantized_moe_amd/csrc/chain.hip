@@ -452,7 +452,9 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
     for (int m = 0; m < (EMAX + 255) / 256; ++m)
       if (tid + 256 * m < E) slot_l[tid + 256 * m] = slot_r[m];
     wg_barrier();
-    const float inv = 1.0f / sqrtf(((wsum[0] + wsum[1]) + (wsum[2] + wsum[3])) / (float)H + p.eps);
+    // v_rsq_f32 (within 1 ulp; every workgroup computes the same bits)
+    const float inv =
+        __builtin_amdgcn_rsqf(((wsum[0] + wsum[1]) + (wsum[2] + wsum[3])) / (float)H + p.eps);
     // x_hat of the elements 8 tid .. 8 tid + 7 (quarter tid % 4 of staged
     // chunk tid / 4), rounded to bf16: the router's and the experts' input
     float xv[8];
@@ -685,30 +687,29 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
     // the next layer's shared tile (this layer's was consumed in phase B),
     // over the x exchange
     if (l + 1 < L) load_shared_tile(l + 1);
-    if (has_c && tid < 2) {  // rows 4 tid .. 4 tid + 3 of the half-tile
-      uint32_t xb[2], ob[2];
+    if (has_c && tid < 8) {
+      // lane r: row r of the half-tile; lanes 4 q .. 4 q + 3 gather their
+      // four rows into lane 4 q (DPP within the quad), which publishes them
+      const int r = tid;
+      float v = 0.f;
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        uint32_t xv[2], ov[2];
-#pragma unroll
-        for (int e2 = 0; e2 < 2; ++e2) {
-          const int r = 4 * tid + 2 * q + e2;
-          float v = 0.f;
-#pragma unroll
-          for (int ww = 0; ww < 4; ++ww) v += dred[ww][0][r] + dred[ww][1][r];
-          const int orow = ctile * kRowTile + chalf * 8 + r;
-          ov[e2] = f32_to_bf16_bits(v);
-          xv[e2] = f32_to_bf16_bits(xs[orow] + bf16_bits_to_f32(ov[e2]));
+      for (int ww = 0; ww < 4; ++ww) v += dred[ww][0][r] + dred[ww][1][r];
+      const int orow = ctile * kRowTile + chalf * 8 + r;
+      const uint32_t ov = f32_to_bf16_bits(v);
+      const uint32_t xv = f32_to_bf16_bits(xs[orow] + bf16_bits_to_f32(ov));
+      // quad_perm [1,1,3,3]: lanes 0, 2 take lanes 1, 3; [2,3,2,3]: lane 0 takes lane 2
+      const uint32_t x01 = xv | (dpp_u<0xF5, 0xF>(0u, xv) << 16);
+      const uint32_t o01 = ov | (dpp_u<0xF5, 0xF>(0u, ov) << 16);
+      const uint32_t x23 = dpp_u<0xEE, 0xF>(0u, x01);
+      const uint32_t o23 = dpp_u<0xEE, 0xF>(0u, o01);
+      if ((tid & 3) == 0) {
+        const int orow0 = ctile * kRowTile + chalf * 8 + tid;
+        if (l + 1 < L) {
+          st_pair(rx, orow0 / 4, ep, x01, x23);
+        } else {
+          *reinterpret_cast<uint2*>(p.x + orow0) = make_uint2(x01, x23);
+          *reinterpret_cast<uint2*>(p.out + orow0) = make_uint2(o01, o23);
         }
-        xb[q] = xv[0] | (xv[1] << 16);
-        ob[q] = ov[0] | (ov[1] << 16);
-      }
-      const int orow0 = ctile * kRowTile + chalf * 8 + 4 * tid;
-      if (l + 1 < L) {
-        st_pair(rx, orow0 / 4, ep, xb[0], xb[1]);
-      } else {
-        *reinterpret_cast<uint2*>(p.x + orow0) = make_uint2(xb[0], xb[1]);
-        *reinterpret_cast<uint2*>(p.out + orow0) = make_uint2(ob[0], ob[1]);
       }
     }
     wg_barrier();

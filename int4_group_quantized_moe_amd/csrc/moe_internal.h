@@ -124,10 +124,9 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
 }
 
 // fp32 -> bf16 bits, round to nearest even (finite inputs).
+// Round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 template <int ACT>
