@@ -674,6 +674,97 @@ __global__ __launch_bounds__(64) void bucket_scatter_kernel(const int32_t* __res
   }
 }
 
+// One token block (T <= 64) and E < 1024: the mask, scan and scatter of the
+// three kernels above in one workgroup of 1024 threads, with the masks in
+// LDS, the same arithmetic and so the same outputs; with tiles != nullptr
+// also the grouped GEMMs' tile list (buckets 0..E, bucket E the shared
+// expert's T rows, each of at least tile_min entries cut into tiles of mt
+// rows), as the tile-list kernel builds it.  Thread e owns expert e, thread
+// t < T token t.
+__global__ __launch_bounds__(1024) void bucket_small_kernel(
+    const int32_t* __restrict__ topk_idx, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ pairs, int32_t* __restrict__ small_list,
+    int32_t* __restrict__ n_small, int32_t* __restrict__ tiles, int32_t* __restrict__ ntiles,
+    int max_tiles, int mt, int tile_min, int T, int E, int k, int min_rows, int has_shared) {
+  __shared__ unsigned long long m[MOE_MAX_EXPERTS];
+  __shared__ int excl_l[MOE_MAX_EXPERTS];
+  __shared__ int wsum[16], wsmall[16];
+  const int e = threadIdx.x, lane = e & 63, wave = e >> 6;
+  if (e < E) m[e] = 0ull;
+  __syncthreads();
+  if (e < T)
+    for (int j = 0; j < k; ++j) atomicOr(&m[topk_idx[(int64_t)e * k + j]], 1ull << e);
+  __syncthreads();
+  const int c = e < E ? __popcll(m[e]) : 0;
+  const int sm = (e < E && c > 0 && c < min_rows) ? 1 : 0;
+  int v = c, vs = sm;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(v, off, 64), os = __shfl_up(vs, off, 64);
+    if (lane >= off) {
+      v += o;
+      vs += os;
+    }
+  }
+  if (lane == 63) {
+    wsum[wave] = v;
+    wsmall[wave] = vs;
+  }
+  __syncthreads();
+  int wbase = 0, sbase = 0;
+  for (int w = 0; w < wave; ++w) {
+    wbase += wsum[w];
+    sbase += wsmall[w];
+  }
+  const int excl = wbase + v - c;
+  if (sm) small_list[sbase + vs - 1] = e;
+  if (e < E) {
+    counts[e] = c;
+    offsets[e] = excl;
+    excl_l[e] = excl;
+  }
+  if (e == 1023) {
+    int ns = 0;
+    for (int w = 0; w < 16; ++w) ns += wsmall[w];
+    if (has_shared && T < min_rows) small_list[ns++] = E;
+    *n_small = ns;
+    counts[E] = T;
+    offsets[E] = T * k;
+  }
+  if (tiles != nullptr) {
+    const int nb = e < E ? c : (e == E && has_shared ? T : 0);
+    const int ct = nb >= tile_min ? (nb + mt - 1) / mt : 0;
+    int tv = ct;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(tv, off, 64);
+      if (lane >= off) tv += o;
+    }
+    __syncthreads();  // every thread has read wsum
+    if (lane == 63) wsum[wave] = tv;
+    __syncthreads();
+    int tb = 0;
+    for (int w = 0; w < wave; ++w) tb += wsum[w];
+    if (e == 1023) *ntiles = min(tb + tv, max_tiles);
+    const int tbase = tb + tv - ct;
+    for (int i = 0; i < ct; ++i) {
+      const int t = tbase + i;
+      if (t < max_tiles) {
+        tiles[2 * t] = e;
+        tiles[2 * t + 1] = i * mt;
+      }
+    }
+  }
+  __syncthreads();
+  if (e < T) {
+    const uint64_t below = (e == 0) ? 0ull : (~0ull >> (64 - e));
+    for (int j = 0; j < k; ++j) {
+      const int ee = topk_idx[(int64_t)e * k + j];
+      pairs[excl_l[ee] + __popcll(m[ee] & below)] = e * k + j;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // residual + RMSNorm (unit weight)
 
@@ -793,16 +884,26 @@ hipError_t launch_experts_t(const ExpertArgs& a, hipStream_t s) {
   int32_t* blkoff = reinterpret_cast<int32_t*>(a.ws + P.blkoff);
   float* partial = reinterpret_cast<float*>(a.ws + P.partial);
   const int nblk = (a.T + 63) / 64;
-  hipLaunchKernelGGL(bucket_mask_kernel, dim3(nblk), dim3(64), 0, s, a.topk_idx, masks, a.T, a.E,
-                     a.k);
   int32_t* small_list = reinterpret_cast<int32_t*>(a.ws + P.small);
   int32_t* n_small = reinterpret_cast<int32_t*>(a.ws + P.nsmall);
+  int32_t* tiles = reinterpret_cast<int32_t*>(a.ws + P.tiles);
+  int32_t* ntiles = reinterpret_cast<int32_t*>(a.ws + P.ntiles);
   // buckets below the MFMA threshold (all of them without the MFMA path)
   const int min_rows = a.mfma ? kMfmaMinRows : 0x7FFFFFFF;
-  hipLaunchKernelGGL(bucket_scan_kernel, dim3(1), dim3(1024), 0, s, masks, counts, offsets, blkoff,
-                     small_list, n_small, a.T, a.E, a.k, nblk, min_rows, hs);
-  hipLaunchKernelGGL(bucket_scatter_kernel, dim3(nblk), dim3(64), 0, s, a.topk_idx, masks, blkoff,
-                     pairs, a.T, a.E, a.k);
+  // one token block: buckets (and the MFMA tile list) in one launch
+  const bool small_batch = nblk == 1 && a.E < 1024;
+  if (small_batch) {
+    hipLaunchKernelGGL(bucket_small_kernel, dim3(1), dim3(1024), 0, s, a.topk_idx, counts,
+                       offsets, pairs, small_list, n_small, a.mfma ? tiles : nullptr, ntiles,
+                       P.max_tiles, kMfmaTileRows, kMfmaMinRows, a.T, a.E, a.k, min_rows, hs);
+  } else {
+    hipLaunchKernelGGL(bucket_mask_kernel, dim3(nblk), dim3(64), 0, s, a.topk_idx, masks, a.T,
+                       a.E, a.k);
+    hipLaunchKernelGGL(bucket_scan_kernel, dim3(1), dim3(1024), 0, s, masks, counts, offsets,
+                       blkoff, small_list, n_small, a.T, a.E, a.k, nblk, min_rows, hs);
+    hipLaunchKernelGGL(bucket_scatter_kernel, dim3(nblk), dim3(64), 0, s, a.topk_idx, masks,
+                       blkoff, pairs, a.T, a.E, a.k);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.mfma) {
     PrefillArgs pa{};
@@ -821,8 +922,9 @@ hipError_t launch_experts_t(const ExpertArgs& a, hipStream_t s) {
     pa.xsum = reinterpret_cast<float*>(a.ws + P.xsum);
     pa.hsum = reinterpret_cast<float*>(a.ws + P.hsum);
     pa.out = a.out;
-    pa.tiles = reinterpret_cast<int32_t*>(a.ws + P.tiles);
-    pa.ntiles = reinterpret_cast<int32_t*>(a.ws + P.ntiles);
+    pa.tiles = tiles;
+    pa.ntiles = ntiles;
+    pa.tiles_ready = small_batch;
     pa.max_tiles = P.max_tiles;
     pa.L = a.L;
     pa.Ls = a.Ls;

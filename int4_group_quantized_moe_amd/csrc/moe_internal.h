@@ -16,6 +16,7 @@ constexpr int kCodeBlockBytes = kRowTile * kRowBytes;  // 1 KiB
 constexpr int kGroup = 64;
 constexpr int kDecodeMaxTokens = 8;    // up to this many tokens: per-pair GEMV path
 constexpr int kMfmaMinRows = 4;  // bf16 buckets of this many tokens run on the MFMA grouped GEMMs
+constexpr int kMfmaTileRows = 128;  // rows (bucket entries) per grouped-GEMM tile
 
 constexpr int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
@@ -235,6 +236,7 @@ struct PrefillArgs {
   int32_t* ntiles;
   int max_tiles;
   int min_rows;                  // buckets with fewer tokens are left to the GEMV kernels
+  bool tiles_ready;              // the tile list was built with the buckets
   BlobLayout L, Ls;
   int T, H, E, k, I, Is, bits;
   bool has_shared;

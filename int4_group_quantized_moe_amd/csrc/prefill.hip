@@ -36,7 +36,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kMT = 128;          // rows (bucket entries) per tile
+constexpr int kMT = kMfmaTileRows;  // rows (bucket entries) per tile
 constexpr int kPersistSlots = 1024;  // workgroups of the persistent GEMM grids (multiple of 8)
 constexpr int kLdsRow = kGroup + 8;  // padded LDS row of one group (bf16 elements)
 
@@ -1114,10 +1114,12 @@ __global__ __launch_bounds__(kDnThreads) void prefill_down_kernel(MOE_PDN_PARAMS
 template <int BITS>
 hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s) {
   const int hs = a.has_shared ? 1 : 0;
-  hipLaunchKernelGGL(tile_list_kernel, dim3(1), dim3(1024), 0, s, a.counts, a.tiles, a.ntiles,
-                     a.E, hs, a.max_tiles, a.min_rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e;
+  if (!a.tiles_ready) {
+    hipLaunchKernelGGL(tile_list_kernel, dim3(1), dim3(1024), 0, s, a.counts, a.tiles, a.ntiles,
+                       a.E, hs, a.max_tiles, a.min_rows);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   const int G = a.H / kGroup;
   const int64_t nsum = (int64_t)a.T * G;
   hipLaunchKernelGGL(group_sum_kernel, dim3((unsigned)((nsum + 255) / 256)), dim3(256), 0, s, a.x,
