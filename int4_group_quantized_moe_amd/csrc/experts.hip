@@ -174,6 +174,10 @@ __device__ __forceinline__ float lane_dot(const uint4 q, const uint32_t* __restr
 
 constexpr int kGuTokens = 4;  // tokens per LDS staging round
 constexpr int kGemvSlots = 1024;  // workgroups of the grid-stride bucketed GEMV kernels
+// The down GEMV's items are one 16-row output tile of one bucket (H/16 per
+// bucket): 2048 workgroups (8 per CU, no dynamic LDS) take a few small
+// buckets in one round.
+constexpr int kDownSlots = 2048;
 
 struct GuItem {
   const uint8_t* blob;
@@ -258,9 +262,26 @@ __device__ __forceinline__ void gateup_item(MOE_GATEUP_PARAMS, int tile, int ite
   const int sbg_off = 2 * kCodeBlockBytes + (row * GPK + (c4 * CC) / kGroup) * 4;
   const int sbu_off = sbg_off + kRowTile * GPK * 4;
 
+  // The wave's first KU k-blocks of codes are requested before the tokens
+  // are staged, so the two memory round trips overlap (the staging barrier
+  // waits for both).  KU covers H = 2048; larger H runs the rest in a loop.
+  constexpr int KU = BITS == 4 ? 4 : 8;
   for (int t0 = 0; t0 < n; t0 += kGuTokens) {
     const int nt = min(kGuTokens, n - t0);
-    __syncthreads();
+    uint4 qg[KU], qu[KU];
+    uint32_t sbg[KU], sbu[KU];
+#pragma unroll
+    for (int i = 0; i < KU; ++i) {
+      const int kb = wave + 4 * i;
+      if (kb < n_kb) {
+        const uint8_t* unit = tbase + (int64_t)kb * unit_b;
+        qg[i] = *reinterpret_cast<const uint4*>(unit + lane * 16);
+        qu[i] = *reinterpret_cast<const uint4*>(unit + kCodeBlockBytes + lane * 16);
+        sbg[i] = *reinterpret_cast<const uint32_t*>(unit + sbg_off);
+        sbu[i] = *reinterpret_cast<const uint32_t*>(unit + sbu_off);
+      }
+    }
+    if (t0 > 0) __syncthreads();  // the previous round's staging and sums are read
     for (int tt = 0; tt < nt; ++tt) {
       int tok;
       if (kind == 0) tok = t_dec;
@@ -274,14 +295,9 @@ __device__ __forceinline__ void gateup_item(MOE_GATEUP_PARAMS, int tile, int ite
     float g[kGuTokens], u[kGuTokens];
 #pragma unroll
     for (int tt = 0; tt < kGuTokens; ++tt) g[tt] = u[tt] = 0.f;
-    for (int kb = wave; kb < n_kb; kb += 4) {
-      const uint8_t* unit = tbase + (int64_t)kb * unit_b;
-      const uint4 qg = *reinterpret_cast<const uint4*>(unit + lane * 16);
-      const uint4 qu = *reinterpret_cast<const uint4*>(unit + kCodeBlockBytes + lane * 16);
-      const uint32_t sbg = *reinterpret_cast<const uint32_t*>(unit + sbg_off);
-      const uint32_t sbu = *reinterpret_cast<const uint32_t*>(unit + sbu_off);
-      const float sg = bf16_bits_to_f32(sbg & 0xFFFFu), bg = bf16_bits_to_f32(sbg >> 16);
-      const float su = bf16_bits_to_f32(sbu & 0xFFFFu), bu = bf16_bits_to_f32(sbu >> 16);
+    auto kblock = [&](int kb, const uint4& cg, const uint4& cu, uint32_t wg, uint32_t wu) {
+      const float sg = bf16_bits_to_f32(wg & 0xFFFFu), bg = bf16_bits_to_f32(wg >> 16);
+      const float su = bf16_bits_to_f32(wu & 0xFFFFu), bu = bf16_bits_to_f32(wu >> 16);
       const int gc = kb * 4 + c4;
 #pragma unroll
       for (int tt = 0; tt < kGuTokens; ++tt) {
@@ -290,12 +306,24 @@ __device__ __forceinline__ void gateup_item(MOE_GATEUP_PARAMS, int tile, int ite
           const uint32_t* xp = reinterpret_cast<const uint32_t*>(st);
           const float2 cs =
               reinterpret_cast<const float2*>(st + XStage<BITS, ACT>::dwords(H) * 4)[gc];
-          const float pg = lane_dot<BITS, ACT>(qg, xp, gc) - cs.x;
-          const float pu = lane_dot<BITS, ACT>(qu, xp, gc) - cs.x;
+          const float pg = lane_dot<BITS, ACT>(cg, xp, gc) - cs.x;
+          const float pu = lane_dot<BITS, ACT>(cu, xp, gc) - cs.x;
           g[tt] += sg * pg + bg * cs.y;
           u[tt] += su * pu + bu * cs.y;
         }
       }
+    };
+#pragma unroll
+    for (int i = 0; i < KU; ++i) {
+      const int kb = wave + 4 * i;
+      if (kb < n_kb) kblock(kb, qg[i], qu[i], sbg[i], sbu[i]);
+    }
+    for (int kb = wave + 4 * KU; kb < n_kb; kb += 4) {
+      const uint8_t* unit = tbase + (int64_t)kb * unit_b;
+      kblock(kb, *reinterpret_cast<const uint4*>(unit + lane * 16),
+             *reinterpret_cast<const uint4*>(unit + kCodeBlockBytes + lane * 16),
+             *reinterpret_cast<const uint32_t*>(unit + sbg_off),
+             *reinterpret_cast<const uint32_t*>(unit + sbu_off));
     }
     // reduce the 4 lanes of a row, then the 4 waves
 #pragma unroll
@@ -482,6 +510,23 @@ __device__ __forceinline__ void down_bucket_item(MOE_DOWNB_PARAMS, float (*red)[
   nkb = inter / KBC;
   for (int t0 = 0; t0 < n; t0 += kTok) {
     const int nt = min(kTok, n - t0);
+    // the destination of this thread's output (token, slot, weight), read
+    // while the codes load
+    int otok = 0, oj = 0;
+    float ow = 0.f;
+    if (threadIdx.x < nt * kRowTile) {
+      const int tt = threadIdx.x / kRowTile;
+      if (!shared) {
+        const int p = pairs[start + t0 + tt];
+        otok = p / k;
+        oj = p - otok * k;
+        ow = topk_w[p];
+      } else {
+        otok = t0 + tt;
+        oj = k;
+        ow = gamma[otok];
+      }
+    }
     float acc[kTok];
 #pragma unroll
     for (int tt = 0; tt < kTok; ++tt) acc[tt] = 0.f;
@@ -510,19 +555,7 @@ __device__ __forceinline__ void down_bucket_item(MOE_DOWNB_PARAMS, float (*red)[
     if (threadIdx.x < nt * kRowTile) {
       const int tt = threadIdx.x / kRowTile, r = threadIdx.x % kRowTile;
       const float v = (red[0][tt][r] + red[1][tt][r]) + (red[2][tt][r] + red[3][tt][r]);
-      int tok, j;
-      float w;
-      if (!shared) {
-        const int p = pairs[start + t0 + tt];
-        tok = p / k;
-        j = p - tok * k;
-        w = topk_w[p];
-      } else {
-        tok = t0 + tt;
-        j = k;
-        w = gamma[tok];
-      }
-      partial[((int64_t)tok * (k + 1) + j) * H + tile * kRowTile + r] = w * v;
+      partial[((int64_t)otok * (k + 1) + oj) * H + tile * kRowTile + r] = ow * v;
     }
     __syncthreads();
   }
@@ -768,23 +801,81 @@ __global__ __launch_bounds__(1024) void bucket_small_kernel(
 // ---------------------------------------------------------------------------
 // residual + RMSNorm (unit weight)
 
+// Eight consecutive activations (16-byte aligned: rows start at multiples of
+// H, a multiple of 64) as fp32, and back with RNE rounding to the act dtype.
+template <int ACT>
+__device__ __forceinline__ void load_act8(const void* p, int64_t i, float (&v)[8]) {
+  if constexpr (ACT == MOE_ACT_F32) {
+    const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p) + i);
+    const float4 b = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p) + i + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    const uint4 q = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p) + i);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = bf16_bits_to_f32(w[j] & 0xFFFFu);
+      v[2 * j + 1] = bf16_bits_to_f32(w[j] >> 16);
+    }
+  }
+}
+template <int ACT>
+__device__ __forceinline__ void store_act8(void* p, int64_t i, const float (&v)[8]) {
+  if constexpr (ACT == MOE_ACT_F32) {
+    float* d = reinterpret_cast<float*>(p) + i;
+    *reinterpret_cast<float4*>(d) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(d + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  } else {
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = (uint32_t)f32_to_bf16_bits(v[2 * j]) | ((uint32_t)f32_to_bf16_bits(v[2 * j + 1]) << 16);
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p) + i) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+template <int ACT>
+__device__ __forceinline__ float round_act(float v) {
+  if constexpr (ACT == MOE_ACT_F32) return v;
+  else return bf16_bits_to_f32(f32_to_bf16_bits(v));
+}
+
+// One workgroup per token; thread i holds elements 8 (i + 256 r) .. +7 for
+// r < 4 (H <= 8192) in registers, so x is read once: the residual sum (x +
+// out, rounded to the act dtype and stored back), its sum of squares, and
+// the normalised row.
 template <int ACT>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(void* __restrict__ x,
                                                       const void* __restrict__ out,
                                                       void* __restrict__ x_hat, int H, float eps,
                                                       int do_norm) {
+  constexpr int kR = MOE_MAX_HIDDEN / (256 * 8);
   __shared__ float wsum[4];
   const int t = blockIdx.x;
   const int64_t base = (int64_t)t * H;
-  float ss = 0.f;
-  for (int c = threadIdx.x; c < H; c += blockDim.x) {
-    float v = load_act<ACT>(x, base + c);
-    if (out != nullptr) {
-      v += load_act<ACT>(out, base + c);
-      store_act<ACT>(x, base + c, v);
-      v = load_act<ACT>(x, base + c);  // the stored value
+  float v[kR][8];
+  float o[kR][8];
+#pragma unroll
+  for (int r = 0; r < kR; ++r) {
+    const int c = (r * 256 + (int)threadIdx.x) * 8;
+    if (c < H) {
+      load_act8<ACT>(x, base + c, v[r]);
+      if (out != nullptr) load_act8<ACT>(out, base + c, o[r]);
     }
-    ss += v * v;
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int r = 0; r < kR; ++r) {
+    const int c = (r * 256 + (int)threadIdx.x) * 8;
+    if (c < H) {
+      if (out != nullptr) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[r][j] = round_act<ACT>(v[r][j] + o[r][j]);
+        store_act8<ACT>(x, base + c, v[r]);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ss += v[r][j] * v[r][j];
+    }
   }
   if (!do_norm) return;
   ss = warp_sum(ss);
@@ -792,8 +883,15 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(void* __restrict__ x,
   __syncthreads();
   const float tot = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
   const float inv = 1.0f / sqrtf(tot / (float)H + eps);
-  for (int c = threadIdx.x; c < H; c += blockDim.x)
-    store_act<ACT>(x_hat, base + c, load_act<ACT>(x, base + c) * inv);
+#pragma unroll
+  for (int r = 0; r < kR; ++r) {
+    const int c = (r * 256 + (int)threadIdx.x) * 8;
+    if (c < H) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[r][j] *= inv;
+      store_act8<ACT>(x_hat, base + c, v[r]);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -945,7 +1043,7 @@ hipError_t launch_experts_t(const ExpertArgs& a, hipStream_t s) {
                      a.L.gu_tile, a.Ls.gu_unit, a.Ls.gu_tile, 1, hs, min_rows, small_list,
                      n_small, tiles_gu);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((down_bucket_kernel<BITS>), dim3(kGemvSlots), dim3(256), 0, s,
+  hipLaunchKernelGGL((down_bucket_kernel<BITS>), dim3(kDownSlots), dim3(256), 0, s,
                      a.topk_w, a.gamma, a.slab, a.slot_table, a.stride, a.shared_blob, counts,
                      offsets, pairs, h, partial, a.T, a.H, a.E, a.k, a.L.inter, Is, a.L.d_off,
                      a.L.d_unit, a.L.d_tile, a.Ls.d_off, a.Ls.d_unit, a.Ls.d_tile, min_rows,
