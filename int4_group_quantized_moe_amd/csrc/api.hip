@@ -127,8 +127,13 @@ int enqueue_decode(const moe_layer_desc* d, const void* x_in, void* x_hat, bool 
 
 int enqueue_experts(const moe_layer_desc* d, const void* x, const int32_t* idx, const float* w,
                     const float* gamma, const void* slab, const int32_t* slot_table,
-                    const void* shared_blob, void* out, uint8_t* ws, hipStream_t s) {
+                    const void* shared_blob, void* out, uint8_t* ws, hipStream_t s,
+                    int epi = 0, void* x_res = nullptr, void* x_hat_next = nullptr) {
   ExpertArgs a{};
+  a.epi = epi;
+  a.x_res = x_res;
+  a.x_hat_next = x_hat_next;
+  a.eps = d->rms_eps;
   a.x = x;
   a.topk_idx = idx;
   a.topk_w = w;
@@ -151,6 +156,30 @@ int enqueue_experts(const moe_layer_desc* d, const void* x, const int32_t* idx, 
   a.bits = d->bits;
   a.mfma = a.plan.bucketed && prefill_supported(a.act, a.H, d->inter, a.Ls.inter, a.has_shared);
   return to_status(launch_experts(a, s));
+}
+
+
+// One layer of a bucketed chain (T > kDecodeMaxTokens): router and experts on
+// x_hat, with the residual add and, unless this is the last layer, the next
+// layer's RMSNorm fused into the combine.
+int chain_layer_bucketed(const moe_layer_desc* desc, void* x, void* x_hat, const float* router_w,
+                         const float* router_bias, const void* expert_slab,
+                         const int32_t* slot_table, const void* shared_blob, void* out,
+                         uint8_t* w8, bool last, hipStream_t stream) {
+  const bool shared = (desc->flags & MOE_FLAG_SHARED) != 0;
+  const WsPlan P = make_ws_plan(*desc);
+  int32_t* idx = reinterpret_cast<int32_t*>(w8 + P.idx);
+  float* w = reinterpret_cast<float*>(w8 + P.w);
+  float* gamma = reinterpret_cast<float*>(w8 + P.gamma);
+  const float* wsg = nullptr;
+  if (shared) {
+    const BlobLayout Ls = make_layout(desc->bits, desc->hidden, desc->shared_inter);
+    wsg = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(shared_blob) + Ls.sg_off);
+  }
+  MOE_TRY(enqueue_router(desc, x_hat, router_w, router_bias, wsg, idx, w,
+                         shared ? gamma : nullptr, w8, stream));
+  return enqueue_experts(desc, x_hat, idx, w, shared ? gamma : nullptr, expert_slab, slot_table,
+                         shared_blob, out, w8, stream, last ? 1 : 2, x, x_hat);
 }
 
 }  // namespace
@@ -375,6 +404,7 @@ int moe_layer_forward(const moe_layer_desc* desc, const void* x, const float* ro
                          shared_blob, out, w8, stream);
 }
 
+
 int moe_rmsnorm(const moe_layer_desc* desc, void* x, const void* out, void* x_hat,
                 hipStream_t stream) {
   MOE_TRY(check_shape(desc));
@@ -475,6 +505,21 @@ int moe_chain_forward(const moe_layer_desc* desc, int32_t n_layers, void* x,
       MOE_TRY(enqueue_decode(desc, x, x_hat, true, router_w + l * EH, rb, expert_slab,
                              slot_tables + (int64_t)l * desc->n_experts, sb, out, x,
                              reinterpret_cast<uint8_t*>(ws), stream));
+    }
+    return MOE_OK;
+  }
+  if (make_ws_plan(*desc).bucketed) {
+    MOE_TRY(to_status(launch_rmsnorm(x, nullptr, x_hat, desc->n_tokens, desc->hidden,
+                                     desc->act_dtype, desc->rms_eps, true, stream)));
+    for (int l = 0; l < n_layers; ++l) {
+      const float* rb = (desc->flags & MOE_FLAG_ROUTER_BIAS)
+                            ? router_bias + (int64_t)l * desc->n_experts
+                            : nullptr;
+      const void* sb = shared ? reinterpret_cast<const uint8_t*>(shared_blobs) + l * shared_stride
+                              : nullptr;
+      MOE_TRY(chain_layer_bucketed(desc, x, x_hat, router_w + l * EH, rb, expert_slab,
+                                   slot_tables + (int64_t)l * desc->n_experts, sb, out,
+                                   reinterpret_cast<uint8_t*>(ws), l == n_layers - 1, stream));
     }
     return MOE_OK;
   }

@@ -575,24 +575,91 @@ __global__ __launch_bounds__(256) void down_bucket_kernel(MOE_DOWNB_PARAMS,
 }
 
 template <int ACT>
+__device__ __forceinline__ float4 load_act4v(const void* p, int64_t i) {
+  if constexpr (ACT == MOE_ACT_F32) {
+    return *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p) + i);
+  } else {
+    const uint2 q = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(p) + i);
+    return make_float4(bf16_bits_to_f32(q.x & 0xFFFFu), bf16_bits_to_f32(q.x >> 16),
+                       bf16_bits_to_f32(q.y & 0xFFFFu), bf16_bits_to_f32(q.y >> 16));
+  }
+}
+template <int ACT>
+__device__ __forceinline__ void store_act4v(void* p, int64_t i, float4 v) {
+  if constexpr (ACT == MOE_ACT_F32) {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(p) + i) = v;
+  } else {
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p) + i) =
+        make_uint2((uint32_t)f32_to_bf16_bits(v.x) | ((uint32_t)f32_to_bf16_bits(v.y) << 16),
+                   (uint32_t)f32_to_bf16_bits(v.z) | ((uint32_t)f32_to_bf16_bits(v.w) << 16));
+  }
+}
+template <int ACT>
+__device__ __forceinline__ float round_act1(float v) {
+  if constexpr (ACT == MOE_ACT_F32) return v;
+  else return bf16_bits_to_f32(f32_to_bf16_bits(v));
+}
+
+// out[t] = sum over the token's k routed slots and the shared slot of the
+// weighted partial rows, in slot order, rounded to the act dtype.  One
+// workgroup per token; thread i holds columns 4 (i + 256 r) .. +3.  With
+// epi >= 1 it also adds the residual, x_res[t] = act(x_res[t] + out[t]), and
+// with epi == 2 writes the next layer's input act(rmsnorm(x_res[t])) (unit
+// weight), so a chain needs no separate launch between layers.
+template <int ACT>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ partial,
                                                       void* __restrict__ out, int H, int k,
-                                                      int has_shared) {
+                                                      int has_shared, void* __restrict__ x_res,
+                                                      void* __restrict__ x_hat, float eps,
+                                                      int epi) {
+  constexpr int kR = MOE_MAX_HIDDEN / 1024;
+  __shared__ float wsum[4];
   const int t = blockIdx.x;
   const int nj = k + has_shared;
-  for (int c = threadIdx.x * 4; c < H; c += 256 * 4) {
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < nj; ++j) {
-      const float4 p = *reinterpret_cast<const float4*>(partial + ((int64_t)t * (k + 1) + j) * H + c);
-      v.x += p.x;
-      v.y += p.y;
-      v.z += p.z;
-      v.w += p.w;
+  const int64_t base = (int64_t)t * H;
+  float4 v[kR];
+  float ss = 0.f;
+#pragma unroll
+  for (int r = 0; r < kR; ++r) {
+    const int c = (r * 256 + (int)threadIdx.x) * 4;
+    if (c >= H) continue;
+    float4 p[MOE_MAX_TOP_K + 1];
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOP_K + 1; ++j)
+      if (j < nj) p[j] = *reinterpret_cast<const float4*>(partial + ((int64_t)t * (k + 1) + j) * H + c);
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOP_K + 1; ++j) {
+      if (j < nj) {
+        a.x += p[j].x;
+        a.y += p[j].y;
+        a.z += p[j].z;
+        a.w += p[j].w;
+      }
     }
-    store_act<ACT>(out, (int64_t)t * H + c + 0, v.x);
-    store_act<ACT>(out, (int64_t)t * H + c + 1, v.y);
-    store_act<ACT>(out, (int64_t)t * H + c + 2, v.z);
-    store_act<ACT>(out, (int64_t)t * H + c + 3, v.w);
+    store_act4v<ACT>(out, base + c, a);
+    if (epi >= 1) {
+      const float4 xr = load_act4v<ACT>(x_res, base + c);
+      v[r] = make_float4(round_act1<ACT>(xr.x + round_act1<ACT>(a.x)),
+                         round_act1<ACT>(xr.y + round_act1<ACT>(a.y)),
+                         round_act1<ACT>(xr.z + round_act1<ACT>(a.z)),
+                         round_act1<ACT>(xr.w + round_act1<ACT>(a.w)));
+      store_act4v<ACT>(x_res, base + c, v[r]);
+      ss += (v[r].x * v[r].x + v[r].y * v[r].y) + (v[r].z * v[r].z + v[r].w * v[r].w);
+    }
+  }
+  if (epi < 2) return;
+  ss = warp_sum(ss);
+  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+  const float inv = 1.0f / sqrtf(tot / (float)H + eps);
+#pragma unroll
+  for (int r = 0; r < kR; ++r) {
+    const int c = (r * 256 + (int)threadIdx.x) * 4;
+    if (c < H)
+      store_act4v<ACT>(x_hat, base + c,
+                       make_float4(v[r].x * inv, v[r].y * inv, v[r].z * inv, v[r].w * inv));
   }
 }
 
@@ -1050,7 +1117,7 @@ hipError_t launch_experts_t(const ExpertArgs& a, hipStream_t s) {
                      small_list, n_small, a.L.n_tiles_d);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((combine_kernel<ACT>), dim3(a.T), dim3(256), 0, s, partial, a.out, a.H, a.k,
-                     hs);
+                     hs, a.x_res, a.x_hat_next, a.eps, a.epi);
   return hipGetLastError();
 }
 

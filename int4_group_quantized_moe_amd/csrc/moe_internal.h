@@ -212,6 +212,12 @@ struct ExpertArgs {
   int T, H, E, k, act, bits;
   bool has_shared;
   bool mfma;                     // large batch: grouped GEMMs on MFMA
+  // Chain epilogue fused into the combine (bucketed path only): 0 none;
+  // 1 x_res += out; 2 also x_hat = rmsnorm(x_res) with eps.
+  int epi;
+  void* x_res;
+  void* x_hat_next;
+  float eps;
 };
 hipError_t launch_experts(const ExpertArgs& a, hipStream_t s);
 

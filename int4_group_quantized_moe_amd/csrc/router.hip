@@ -147,12 +147,12 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   const float* lt = logits + (int64_t)t * (E + 1);
   if (nplanes > 1) {
     // logits split over K planes: add them in plane order (the shared-gate
-    // logit, row E, lives in plane 0 only)
+    // logit, row E, is split alike)
     const int64_t ps = (int64_t)T * (E + 1);
     for (int e = lane; e <= E; e += 64) {
       float p[8];
 #pragma unroll
-      for (int z = 0; z < 8; ++z) p[z] = (z < nplanes && (z == 0 || e < E)) ? lt[z * ps + e] : 0.f;
+      for (int z = 0; z < 8; ++z) p[z] = z < nplanes ? lt[z * ps + e] : 0.f;
       float v = p[0];
 #pragma unroll
       for (int z = 1; z < 8; ++z) v += p[z];
@@ -188,7 +188,8 @@ hipError_t launch_topk(const RouterArgs& a, hipStream_t s, int nplanes) {
 
 // ---------------------------------------------------------------------------
 // Large batches: the router as a GEMM on the matrix cores.  logits[t][e] for
-// e < E over 64-token x 64-expert tiles (4 waves, one 32x32 block each),
+// e < E, and the shared-gate logit w_sg . x[t] as row E when wsg is given,
+// over 64-token x 64-row tiles (4 waves, one 32x32 block each),
 // K staged 64 at a time.  Each fp32 router weight is split exactly into three
 // bf16 parts (8 significant bits each: w = w1 + w2 + w3, by truncation), so
 // that with bf16 activations every product is exact and only the fp32
@@ -217,6 +218,7 @@ __device__ __forceinline__ void split3_pair(float a, float b, uint32_t& p1, uint
 __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __restrict__ x,
                                                           const float* __restrict__ W,
                                                           const float* __restrict__ bias,
+                                                          const float* __restrict__ wsg,
                                                           float* __restrict__ logits, int T, int H,
                                                           int E, int kseg) {
   __shared__ __align__(16) uint16_t A[2 * kRouterTile * kRouterLdsRow];
@@ -231,8 +233,9 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
   const uint16_t* xrow = x + (int64_t)(srow_ok ? t0 + sr : 0) * H + k0 + 16 * sq;
   // B operand: expert row e, this lane's 32 K columns of each stage
   const int e = e0 + 32 * wn + l32;
-  const bool e_ok = e < E;
-  const float* wrow = W + (int64_t)(e_ok ? e : 0) * H + k0 + 32 * half;
+  const bool gate_row = e == E && wsg != nullptr;  // the shared-gate vector rides as row E
+  const bool e_ok = e < E || gate_row;
+  const float* wrow = (gate_row ? wsg : W + (int64_t)(e < E ? e : 0) * H) + k0 + 32 * half;
   const int S = kseg / 64;
 
   uint4 ra[2];
@@ -284,41 +287,12 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
     __syncthreads();
   }
   if (!e_ok) return;
-  const float b = (bias != nullptr && blockIdx.z == 0) ? bias[e] : 0.0f;
+  const float b = (bias != nullptr && blockIdx.z == 0 && e < E) ? bias[e] : 0.0f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int t = t0 + 32 * wm + 8 * (r / 4) + 4 * half + (r % 4);
     if (t < T) logits[(int64_t)t * (E + 1) + e] = acc[r] + b;
   }
-}
-
-// Shared-gate logit w_sg . x[t] (row E of the logits), one wave per token.
-template <int ACT>
-__global__ __launch_bounds__(256) void gate_logit_kernel(const void* __restrict__ x,
-                                                         const float* __restrict__ wsg,
-                                                         float* __restrict__ logits, int T, int H,
-                                                         int E) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  // 4 consecutive columns per lane and step, loads of a few steps in flight
-  float acc = 0.f;
-  constexpr int kU = 4;
-  for (int c0 = 4 * lane; c0 < H; c0 += 256 * kU) {
-    float4 xv[kU], wv[kU];
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int c = c0 + 256 * u;
-      const bool ok = c < H;
-      xv[u] = ok ? load_act4<ACT>(x, (int64_t)t * H + c) : make_float4(0.f, 0.f, 0.f, 0.f);
-      wv[u] = ok ? *reinterpret_cast<const float4*>(wsg + c) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-#pragma unroll
-    for (int u = 0; u < kU; ++u)
-      acc += wv[u].x * xv[u].x + wv[u].y * xv[u].y + wv[u].z * xv[u].z + wv[u].w * xv[u].w;
-  }
-  acc = warp_sum(acc);
-  if (lane == 0) logits[(int64_t)t * (E + 1) + E] = acc;
 }
 
 template <int ACT>
@@ -333,18 +307,14 @@ hipError_t launch_router_act(const RouterArgs& a, hipStream_t s) {
     const int tiles = ((a.E + kRouterTile - 1) / kRouterTile) * ((a.T + kRouterTile - 1) / kRouterTile);
     const int maxp = router_planes(a.T);
     while (nplanes < maxp && tiles * nplanes < 256 && (a.H / 64) % (2 * nplanes) == 0) nplanes *= 2;
+    const int rows = a.E + (a.shared_gate_w ? 1 : 0);  // the shared-gate logit is row E
     hipLaunchKernelGGL(router_mfma_kernel,
-                       dim3((a.E + kRouterTile - 1) / kRouterTile,
+                       dim3((rows + kRouterTile - 1) / kRouterTile,
                             (a.T + kRouterTile - 1) / kRouterTile, nplanes),
                        dim3(256), 0, s, reinterpret_cast<const uint16_t*>(a.x), a.router_w,
-                       a.router_bias, a.logits, a.T, a.H, a.E, a.H / nplanes);
+                       a.router_bias, a.shared_gate_w, a.logits, a.T, a.H, a.E, a.H / nplanes);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (a.shared_gate_w) {
-      hipLaunchKernelGGL((gate_logit_kernel<ACT>), dim3((a.T + 3) / 4), dim3(256), 0, s, a.x,
-                         a.shared_gate_w, a.logits, a.T, a.H, a.E);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
   } else {
     hipError_t e = launch_router_gemv<ACT>(a, s);
     if (e != hipSuccess) return e;

@@ -414,6 +414,58 @@ def test_batched_parity(cfgname):
     _free()
 
 
+@pytest.mark.parametrize("cfgname", ["batched_80b", "batched_80b_int8"])
+def test_batched_chain_fused_epilogue(cfgname):
+    """The chain entry point at 64 tokens fuses the residual add and the next
+    layer's RMSNorm into the combine.  One layer must equal RMSNorm + layer
+    forward + residual bit for bit; over two layers the fused x_hat must be
+    the RMSNorm of x_1 (to one bf16 rounding: the sum of squares is taken in
+    another order), and layer 1's output and residual bit-equal to the layer
+    forward run on that x_hat.  Layer 1 is then checked against the oracle,
+    teacher-forced on the fused x_hat."""
+    moe, wl = _moe(), _wl()
+    cfg = configs.CONFIGS[cfgname]
+    say(f"[batched chain] {cfgname}")
+    w = wl.Workload(cfg, n_layers=2)
+    d = w.desc
+    ws = w.workspace()
+    x0 = wl.act_tensor(cfg, synth.activations(cfg))
+
+    def chain(L):
+        xc, xh, out = x0.clone(), torch.empty_like(x0), torch.empty_like(x0)
+        moe.moe_chain_forward(d, L, xc, w.router_w, w.router_bias, w.slab, w.slot_tables,
+                              w.shared, w.shared_stride, xh, out, ws)
+        torch.cuda.synchronize()
+        return xc, xh, out
+
+    # one layer: RMSNorm, layer, residual through the separate entry points
+    x1, _, out1 = chain(1)
+    xb, xhb = x0.clone(), torch.empty_like(x0)
+    moe.moe_rmsnorm(d, xb, None, xhb)
+    ob, _, _, _ = run_layer(w, cfg, xhb, 0)
+    moe.moe_rmsnorm(d, xb, ob, torch.empty_like(x0))
+    torch.cuda.synchronize()
+    assert torch.equal(out1, ob), "layer 0 output"
+    assert torch.equal(x1, xb), "layer 0 residual"
+
+    # two layers: x_hat after the call is layer 1's input, from the fused norm
+    x2, xh1, out2 = chain(2)
+    xr, xh_ref = x1.clone(), torch.empty_like(x0)
+    moe.moe_rmsnorm(d, xr, None, xh_ref)
+    torch.cuda.synchronize()
+    a, b = wl.to_f64(xh1), wl.to_f64(xh_ref)
+    assert np.all(np.abs(a - b) <= np.abs(b) * 2.0 ** -7), "fused rmsnorm"
+    o1, idx, wt, g = run_layer(w, cfg, xh1, 1)
+    xe = x1.clone()
+    moe.moe_rmsnorm(d, xe, o1, torch.empty_like(x0))
+    torch.cuda.synchronize()
+    assert torch.equal(out2, o1), "layer 1 output"
+    assert torch.equal(x2, xe), "layer 1 residual"
+    check_layer(cfg, 1, wl.to_f64(xh1), o1, idx, wt, g, f"{cfgname} chain layer 1")
+    del w
+    _free()
+
+
 def test_prefill_parity():
     """4096-token chunk, one layer: full routing check, sampled outputs."""
     moe, wl = _moe(), _wl()
