@@ -15,6 +15,7 @@ constexpr int kRouterWaves = 4;     // rows per workgroup (one per wave)
 constexpr int kRouterMaxTT = 8;     // tokens per LDS chunk
 constexpr int kRouterMaxRegIt = 8;  // row cached in registers when H <= 64*4*8
 constexpr int kRouterMfmaMinTokens = 16;  // GEMM on the matrix cores from this batch size (bf16)
+constexpr int kRouterMaxPlanes = 8;       // K split of the router GEMM (logit planes)
 
 template <int ACT>
 __device__ __forceinline__ float4 load_act4(const void* p, int64_t i) {
@@ -142,21 +143,35 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   __shared__ float cand_val[4][64];
   __shared__ float lsum[4][MPL * 64 + 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t = blockIdx.x * 4 + wave;
+  const int t = blockIdx.x * (int)(blockDim.x >> 6) + wave;
   if (t >= T) return;
   const float* lt = logits + (int64_t)t * (E + 1);
   if (nplanes > 1) {
     // logits split over K planes: add them in plane order (the shared-gate
     // logit, row E, is split alike)
+    // (every load of the token's E + 1 logits over the planes in flight
+    // together: MPL * 64 + 1 >= E + 1 entries per lane group)
     const int64_t ps = (int64_t)T * (E + 1);
-    for (int e = lane; e <= E; e += 64) {
-      float p[8];
+    float v[MPL + 1];
 #pragma unroll
-      for (int z = 0; z < 8; ++z) p[z] = z < nplanes ? lt[z * ps + e] : 0.f;
-      float v = p[0];
+    for (int m = 0; m <= MPL; ++m) v[m] = 0.f;
 #pragma unroll
-      for (int z = 1; z < 8; ++z) v += p[z];
-      lsum[wave][e] = v;
+    for (int z = 0; z < kRouterMaxPlanes; ++z) {
+      if (z < nplanes) {
+        float p[MPL + 1];
+#pragma unroll
+        for (int m = 0; m <= MPL; ++m) {
+          const int e = lane + 64 * m;
+          p[m] = e <= E ? lt[z * ps + e] : 0.f;
+        }
+#pragma unroll
+        for (int m = 0; m <= MPL; ++m) v[m] = z == 0 ? p[m] : v[m] + p[m];
+      }
+    }
+#pragma unroll
+    for (int m = 0; m <= MPL; ++m) {
+      const int e = lane + 64 * m;
+      if (e <= E) lsum[wave][e] = v[m];
     }
     dec::lds_wave_sync();
     lt = lsum[wave];
@@ -172,7 +187,10 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 }
 
 hipError_t launch_topk(const RouterArgs& a, hipStream_t s, int nplanes) {
-  const dim3 grid((a.T + 3) / 4), block(256);
+  // one wave per token; small batches one wave per workgroup, so that the
+  // tokens' logit loads spread over more compute units
+  const int wpb = a.T <= 1024 ? 1 : 4;
+  const dim3 grid((a.T + wpb - 1) / wpb), block(64 * wpb);
   const int hg = a.shared_gate_w ? 1 : 0;
   if (a.E <= 256)
     hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, a.logits, a.topk_idx, a.topk_w,
