@@ -26,6 +26,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0  # dense bf16 / fp16 matrix-core peak of MI355X
 # the stream-read ceiling measured on MI355X: a grid-stride read of a 16 GiB
 # buffer with 16-byte loads, 4 in flight per thread, 8192 workgroups of 256
 HBM_READ_CEILING_GBPS = 6045.7
@@ -65,6 +66,16 @@ def algorithmic_bytes(cfg, wl, unique_per_layer):
         b += 2 * T * H * act                 # x_hat in, out out
         per_layer.append(b)
     return per_layer
+
+
+def algorithmic_flops(cfg):
+    """Flops of one layer (a multiply-add counts 2): per token the router's E
+    rows and the shared-gate row, gate, up and down of the k routed experts,
+    and of the shared expert."""
+    T, E, H, k, I, Is = (cfg.n_tokens, cfg.n_experts, cfg.hidden, cfg.top_k, cfg.inter,
+                         cfg.shared_inter)
+    per_token = 2 * ((E + (1 if Is else 0)) * H + k * 3 * H * I + 3 * H * Is)
+    return T * per_token
 
 
 def main():
@@ -179,13 +190,15 @@ def main():
     step_bytes = sum(bytes_per_rot[s % N_ROTATE] for s in range(args.steps)) / args.steps
     tokens_per_s = T / (ms_per_step / 1e3)
     gbps = step_bytes / (ms_per_step / 1e3) / 1e9
+    step_flops = algorithmic_flops(cfg) * L
+    tflops = step_flops / (ms_per_step / 1e3) / 1e12
 
     # correctness guard of the timed state: finite residual stream
     assert torch.isfinite(x.float()).all(), "non-finite output"
 
     roofline = None
     if not args.no_roofline:
-        roofline = chain_roofline(cfg, load_input, forward, bytes_per_rot)
+        roofline = chain_roofline(cfg, load_input, forward, bytes_per_rot, step_flops)
 
     cpu = None
     if args.cpu_layers > 0:
@@ -216,6 +229,9 @@ def main():
         "hbm_gbps": round(gbps, 1),
         "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_step": int(step_bytes),
+        "mfma_tflops": round(tflops, 2),
+        "mfma_frac_of_peak": round(tflops / MFMA_PEAK_TFLOPS, 4),
+        "algorithmic_flops_per_step": int(step_flops),
         "us_per_layer": round(ms_per_step * 1e3 / L, 3),
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -242,7 +258,7 @@ def chain_kernel_name(cfg):
     return f"chain_kernel<4, 8, {shared}, {cfg.inter}, {cfg.shared_inter or 512}, {epl}, {ec}, {kc}>"
 
 
-def chain_roofline(cfg, load_input, forward, bytes_per_rot, reps=64):
+def chain_roofline(cfg, load_input, forward, bytes_per_rot, flops, reps=64):
     """Average duration of one moe_chain_forward launch (for batch-1 bf16
     int4 decode this is the single persistent kernel that streams every
     layer's weights), timed with HIP events on the launch stream around the
@@ -268,6 +284,19 @@ def chain_roofline(cfg, load_input, forward, bytes_per_rot, reps=64):
     achieved = avg_b / avg_s / 1e9
     persistent = cfg.n_tokens == 1 and cfg.act == "bf16" and cfg.bits == 4
     traffic = measured_traffic(cfg) if persistent else None
+    if flops / avg_b > MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9):
+        # above the ridge point (a prefill chunk): the matrix cores bound it
+        tf = flops / avg_s / 1e12
+        return {"bound": "mfma",
+                "kernel": "moe_chain_forward: all kernels of one chain step (bf16 MFMA grouped "
+                          "GEMMs, fp32 accumulate)",
+                "achieved": round(tf, 2), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tf / MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                "avg_launch_us": round(avg_s * 1e6, 3),
+                "launch_us_p10_p50_p90": [round(pct[10], 3), round(pct[50], 3),
+                                          round(pct[90], 3)],
+                "flops_per_launch": int(flops), "bytes_per_launch": int(avg_b),
+                "launches": reps}
     return {"bound": "hbm",
             "kernel": (f"{chain_kernel_name(cfg)}: the persistent decode-chain kernel, one launch "
                        f"per {cfg.layers}-layer step" if persistent else
