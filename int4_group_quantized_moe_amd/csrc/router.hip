@@ -16,6 +16,7 @@ constexpr int kRouterMaxTT = 8;     // tokens per LDS chunk
 constexpr int kRouterMaxRegIt = 8;  // row cached in registers when H <= 64*4*8
 constexpr int kRouterMfmaMinTokens = 16;  // GEMM on the matrix cores from this batch size (bf16)
 constexpr int kRouterMaxPlanes = 8;       // K split of the router GEMM (logit planes)
+constexpr int kRouterFoldMaxBlocks = 256;  // router GEMM grid that still runs in one round
 
 template <int ACT>
 __device__ __forceinline__ float4 load_act4(const void* p, int64_t i) {
@@ -147,8 +148,9 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   if (t >= T) return;
   const float* lt = logits + (int64_t)t * (E + 1);
   if (nplanes > 1) {
-    // logits split over K planes: add them in plane order (the shared-gate
-    // logit, row E, is split alike)
+    // logits split over K planes: add them in plane order (row E, the
+    // shared-gate logit, too: a partial per plane, or the whole logit in
+    // plane 0 and zeros in the others)
     // (every load of the token's E + 1 logits over the planes in flight
     // together: MPL * 64 + 1 >= E + 1 entries per lane group)
     const int64_t ps = (int64_t)T * (E + 1);
@@ -313,6 +315,39 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
   }
 }
 
+// Shared-gate logit w_sg . x[t] (row E of plane 0 of the logits; row E of
+// the other planes is zeroed, as the top-k adds the planes), one wave per
+// token.  Used where folding w_sg into the router GEMM as row E would cost
+// the GEMM another round of workgroups.
+template <int ACT>
+__global__ __launch_bounds__(256) void gate_logit_kernel(const void* __restrict__ x,
+                                                         const float* __restrict__ wsg,
+                                                         float* __restrict__ logits, int T, int H,
+                                                         int E, int nplanes) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  // 4 consecutive columns per lane and step, loads of a few steps in flight
+  float acc = 0.f;
+  constexpr int kU = 4;
+  for (int c0 = 4 * lane; c0 < H; c0 += 256 * kU) {
+    float4 xv[kU], wv[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int c = c0 + 256 * u;
+      const bool ok = c < H;
+      xv[u] = ok ? load_act4<ACT>(x, (int64_t)t * H + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+      wv[u] = ok ? *reinterpret_cast<const float4*>(wsg + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      acc += wv[u].x * xv[u].x + wv[u].y * xv[u].y + wv[u].z * xv[u].z + wv[u].w * xv[u].w;
+  }
+  acc = warp_sum(acc);
+  if (lane == 0) logits[(int64_t)t * (E + 1) + E] = acc;
+  if (lane > 0 && lane < nplanes) logits[((int64_t)lane * T + t) * (E + 1) + E] = 0.f;
+}
+
 template <int ACT>
 hipError_t launch_router_gemv(const RouterArgs& a, hipStream_t s);
 
@@ -325,14 +360,25 @@ hipError_t launch_router_act(const RouterArgs& a, hipStream_t s) {
     const int tiles = ((a.E + kRouterTile - 1) / kRouterTile) * ((a.T + kRouterTile - 1) / kRouterTile);
     const int maxp = router_planes(a.T);
     while (nplanes < maxp && tiles * nplanes < 256 && (a.H / 64) % (2 * nplanes) == 0) nplanes *= 2;
-    const int rows = a.E + (a.shared_gate_w ? 1 : 0);  // the shared-gate logit is row E
-    hipLaunchKernelGGL(router_mfma_kernel,
-                       dim3((rows + kRouterTile - 1) / kRouterTile,
-                            (a.T + kRouterTile - 1) / kRouterTile, nplanes),
+    // the shared-gate vector rides as row E of the GEMM when that costs no
+    // extra round of workgroups (a free row in the last tile, or the grid
+    // still within one workgroup per CU); else its own small kernel
+    const int etiles = (a.E + kRouterTile - 1) / kRouterTile;
+    const int gtiles = (a.E + 1 + kRouterTile - 1) / kRouterTile;
+    const int ytiles = (a.T + kRouterTile - 1) / kRouterTile;
+    const bool fold = a.shared_gate_w != nullptr &&
+                      (gtiles == etiles || gtiles * ytiles * nplanes <= kRouterFoldMaxBlocks);
+    hipLaunchKernelGGL(router_mfma_kernel, dim3(fold ? gtiles : etiles, ytiles, nplanes),
                        dim3(256), 0, s, reinterpret_cast<const uint16_t*>(a.x), a.router_w,
-                       a.router_bias, a.shared_gate_w, a.logits, a.T, a.H, a.E, a.H / nplanes);
+                       a.router_bias, fold ? a.shared_gate_w : nullptr, a.logits, a.T, a.H, a.E,
+                       a.H / nplanes);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (a.shared_gate_w != nullptr && !fold) {
+      hipLaunchKernelGGL((gate_logit_kernel<ACT>), dim3((a.T + 3) / 4), dim3(256), 0, s, a.x,
+                         a.shared_gate_w, a.logits, a.T, a.H, a.E, nplanes);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
   } else {
     hipError_t e = launch_router_gemv<ACT>(a, s);
     if (e != hipSuccess) return e;
