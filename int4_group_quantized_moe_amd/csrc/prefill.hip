@@ -531,6 +531,73 @@ __device__ __forceinline__ void gu_read(const GuStage<BITS>& st, int k0, int wm,
   }
 }
 
+// Every LDS read of one K stage in one asm block with one wait: the A
+// operands of the 4 K steps (both row blocks; a2 holds steps 2-3), the
+// lane's codes of both weight rows and their (scale, bias) words.
+template <int BITS>
+__device__ __forceinline__ void gu_read_all(const GuStage<BITS>& st, int wm, int wn, int l32,
+                                            int half, GuFrags<BITS>& f, u32x4 (&a2)[2][2]) {
+  const uint32_t a00 = lds_addr(&st.A[swz(64 * wm + l32, 4 * half + 0)]);
+  const uint32_t a01 = lds_addr(&st.A[swz(64 * wm + l32, 4 * half + 1)]);
+  const uint32_t a10 = lds_addr(&st.A[swz(64 * wm + 32 + l32, 4 * half + 0)]);
+  const uint32_t a11 = lds_addr(&st.A[swz(64 * wm + 32 + l32, 4 * half + 1)]);
+  const uint32_t c00 = lds_addr(&st.A[swz(64 * wm + l32, 4 * half + 2)]);
+  const uint32_t c01 = lds_addr(&st.A[swz(64 * wm + l32, 4 * half + 3)]);
+  const uint32_t c10 = lds_addr(&st.A[swz(64 * wm + 32 + l32, 4 * half + 2)]);
+  const uint32_t c11 = lds_addr(&st.A[swz(64 * wm + 32 + l32, 4 * half + 3)]);
+  const int r0 = 32 * wn + l32, r1 = 64 + 32 * wn + l32;
+  constexpr int CPR = kGroup * BITS / 8 / 16;  // code chunks per row
+  const uint32_t b0 = lds_addr(&st.B[r0 * CPR + half * (CPR / 2)]);
+  const uint32_t b1 = lds_addr(&st.B[r1 * CPR + half * (CPR / 2)]);
+  const uint32_t s0 = lds_addr(&st.S[r0]), s1 = lds_addr(&st.S[r1]);
+  if constexpr (BITS == 4) {
+    asm volatile(
+        "ds_read_b128 %0, %12\n\t"
+        "ds_read_b128 %1, %13\n\t"
+        "ds_read_b128 %2, %14\n\t"
+        "ds_read_b128 %3, %15\n\t"
+        "ds_read_b128 %4, %16\n\t"
+        "ds_read_b128 %5, %17\n\t"
+        "ds_read_b128 %6, %18\n\t"
+        "ds_read_b128 %7, %19\n\t"
+        "ds_read_b128 %8, %20\n\t"
+        "ds_read_b128 %9, %21\n\t"
+        "ds_read_b32 %10, %22\n\t"
+        "ds_read_b32 %11, %23\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(f.a[0][0]), "=&v"(f.a[0][1]), "=&v"(f.a[1][0]), "=&v"(f.a[1][1]),
+          "=&v"(a2[0][0]), "=&v"(a2[0][1]), "=&v"(a2[1][0]), "=&v"(a2[1][1]),
+          "=&v"(f.q[0][0]), "=&v"(f.q[1][0]), "=&v"(f.sb[0]), "=&v"(f.sb[1])
+        : "v"(a00), "v"(a01), "v"(a10), "v"(a11), "v"(c00), "v"(c01), "v"(c10), "v"(c11),
+          "v"(b0), "v"(b1), "v"(s0), "v"(s1)
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b128 %0, %14\n\t"
+        "ds_read_b128 %1, %15\n\t"
+        "ds_read_b128 %2, %16\n\t"
+        "ds_read_b128 %3, %17\n\t"
+        "ds_read_b128 %4, %18\n\t"
+        "ds_read_b128 %5, %19\n\t"
+        "ds_read_b128 %6, %20\n\t"
+        "ds_read_b128 %7, %21\n\t"
+        "ds_read_b128 %8, %22\n\t"
+        "ds_read_b128 %9, %22 offset:16\n\t"
+        "ds_read_b128 %10, %23\n\t"
+        "ds_read_b128 %11, %23 offset:16\n\t"
+        "ds_read_b32 %12, %24\n\t"
+        "ds_read_b32 %13, %25\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(f.a[0][0]), "=&v"(f.a[0][1]), "=&v"(f.a[1][0]), "=&v"(f.a[1][1]),
+          "=&v"(a2[0][0]), "=&v"(a2[0][1]), "=&v"(a2[1][0]), "=&v"(a2[1][1]),
+          "=&v"(f.q[0][0]), "=&v"(f.q[0][1]), "=&v"(f.q[1][0]), "=&v"(f.q[1][1]),
+          "=&v"(f.sb[0]), "=&v"(f.sb[1])
+        : "v"(a00), "v"(a01), "v"(a10), "v"(a11), "v"(c00), "v"(c01), "v"(c10), "v"(c11),
+          "v"(b0), "v"(b1), "v"(s0), "v"(s1)
+        : "memory");
+  }
+}
+
 // MFMA operand of K step ks from the lane's codes of one weight row.
 template <int BITS>
 __device__ __forceinline__ u32x4 gu_bfrag(const u32x4 (&q)[BITS / 4], int ks) {
@@ -563,21 +630,22 @@ __device__ __forceinline__ void gu_stage(const GuStage<BITS>& st, int later, int
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = zero;
-  gu_read<BITS, true>(st, 0, wm, wn, l32, half, f);
+  // all of the stage's operands in one read, then the stage may be refilled
+  // before its MFMAs
+  u32x4 a2[2][2];
+  gu_read_all<BITS>(st, wm, wn, l32, half, f, a2);
+  lds_barrier();
+  refill();
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    if (kk == 2) {
-      gu_read<BITS, false>(st, 2, wm, wn, l32, half, f);
-      lds_barrier();
-      refill();
-    }
     u32x4 b[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) b[nb] = gu_bfrag<BITS>(f.q[nb], kk);
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma(f.a[mb][kk & 1], b[nb], acc[mb][nb]);
+      for (int nb = 0; nb < 2; ++nb)
+        acc[mb][nb] = mfma(kk < 2 ? f.a[mb][kk & 1] : a2[mb][kk & 1], b[nb], acc[mb][nb]);
   }
   const float scl[2] = {code_scale<BITS>(f.sb[0]), code_scale<BITS>(f.sb[1])};
 #pragma unroll
