@@ -469,68 +469,6 @@ struct GuFrags {
   uint32_t sb[2];
 };
 
-// A operands of K steps k0, k0+1 (both row blocks); with `codes` also the
-// lane's codes and (scale, bias) words.
-template <int BITS, bool CODES>
-__device__ __forceinline__ void gu_read(const GuStage<BITS>& st, int k0, int wm, int wn, int l32,
-                                        int half, GuFrags<BITS>& f) {
-  const uint32_t a00 = lds_addr(&st.A[swz(64 * wm + l32, 4 * half + k0)]);
-  const uint32_t a01 = lds_addr(&st.A[swz(64 * wm + l32, 4 * half + k0 + 1)]);
-  const uint32_t a10 = lds_addr(&st.A[swz(64 * wm + 32 + l32, 4 * half + k0)]);
-  const uint32_t a11 = lds_addr(&st.A[swz(64 * wm + 32 + l32, 4 * half + k0 + 1)]);
-  if constexpr (!CODES) {
-    asm volatile(
-        "ds_read_b128 %0, %4\n\t"
-        "ds_read_b128 %1, %5\n\t"
-        "ds_read_b128 %2, %6\n\t"
-        "ds_read_b128 %3, %7\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(f.a[0][0]), "=&v"(f.a[0][1]), "=&v"(f.a[1][0]), "=&v"(f.a[1][1])
-        : "v"(a00), "v"(a01), "v"(a10), "v"(a11)
-        : "memory");
-  } else {
-    const int r0 = 32 * wn + l32, r1 = 64 + 32 * wn + l32;
-    constexpr int CPR = kGroup * BITS / 8 / 16;  // code chunks per row
-    const uint32_t b0 = lds_addr(&st.B[r0 * CPR + half * (CPR / 2)]);
-    const uint32_t b1 = lds_addr(&st.B[r1 * CPR + half * (CPR / 2)]);
-    const uint32_t s0 = lds_addr(&st.S[r0]), s1 = lds_addr(&st.S[r1]);
-    if constexpr (BITS == 4) {
-      asm volatile(
-          "ds_read_b128 %0, %8\n\t"
-          "ds_read_b128 %1, %9\n\t"
-          "ds_read_b128 %2, %10\n\t"
-          "ds_read_b128 %3, %11\n\t"
-          "ds_read_b128 %4, %12\n\t"
-          "ds_read_b128 %5, %13\n\t"
-          "ds_read_b32 %6, %14\n\t"
-          "ds_read_b32 %7, %15\n\t"
-          "s_waitcnt lgkmcnt(0)"
-          : "=&v"(f.a[0][0]), "=&v"(f.a[0][1]), "=&v"(f.a[1][0]), "=&v"(f.a[1][1]),
-            "=&v"(f.q[0][0]), "=&v"(f.q[1][0]), "=&v"(f.sb[0]), "=&v"(f.sb[1])
-          : "v"(a00), "v"(a01), "v"(a10), "v"(a11), "v"(b0), "v"(b1), "v"(s0), "v"(s1)
-          : "memory");
-    } else {
-      asm volatile(
-          "ds_read_b128 %0, %10\n\t"
-          "ds_read_b128 %1, %11\n\t"
-          "ds_read_b128 %2, %12\n\t"
-          "ds_read_b128 %3, %13\n\t"
-          "ds_read_b128 %4, %14\n\t"
-          "ds_read_b128 %5, %14 offset:16\n\t"
-          "ds_read_b128 %6, %15\n\t"
-          "ds_read_b128 %7, %15 offset:16\n\t"
-          "ds_read_b32 %8, %16\n\t"
-          "ds_read_b32 %9, %17\n\t"
-          "s_waitcnt lgkmcnt(0)"
-          : "=&v"(f.a[0][0]), "=&v"(f.a[0][1]), "=&v"(f.a[1][0]), "=&v"(f.a[1][1]),
-            "=&v"(f.q[0][0]), "=&v"(f.q[0][1]), "=&v"(f.q[1][0]), "=&v"(f.q[1][1]),
-            "=&v"(f.sb[0]), "=&v"(f.sb[1])
-          : "v"(a00), "v"(a01), "v"(a10), "v"(a11), "v"(b0), "v"(b1), "v"(s0), "v"(s1)
-          : "memory");
-    }
-  }
-}
-
 // Every LDS read of one K stage in one asm block with one wait: the A
 // operands of the 4 K steps (both row blocks; a2 holds steps 2-3), the
 // lane's codes of both weight rows and their (scale, bias) words.
