@@ -379,8 +379,9 @@ __global__ __launch_bounds__(256) void group_sum_kernel(const uint16_t* __restri
 // the compiler's wait accounting for these loads is per stage and a read of
 // stage s never waits for the loads of the stages behind it; kStages - 1
 // stages are in flight while one is multiplied.  Chunk c of activation row r
-// sits at r*8 + (c ^ (r & 7)), spreading the 32 rows of an MFMA operand read
-// over the LDS banks.
+// sits at r*8 + (c ^ ((r >> 1) & 7)): the 16 consecutive rows of a 16-lane
+// group of an MFMA operand read, all at the same chunk, then land on 16
+// distinct 16-byte slots of every 256-byte window of LDS banks.
 constexpr int kStages = 3;
 constexpr int kStageChunks = kMT * kGroup / 8;  // 1024 chunks of 16 bytes
 typedef uint4 StageBuf[kStageChunks];
@@ -392,7 +393,16 @@ struct GuStage {
   uint32_t S[256];                     // (scale, bias) of rows 0..127 (128..255 unused)
 };
 
-__device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ (r & 7)); }
+__device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
+
+// Code chunks (16 bytes) of weight row r in a stage: int4 rows hold two, and
+// rows 8..15 of every 16 swap them, so that the 16 rows a 16-lane group reads
+// (all at the same chunk) cover 16 distinct slots of a 256-byte bank window;
+// int8 rows (four chunks, read as pairs) keep the natural order.
+template <int BITS>
+__device__ __forceinline__ int code_chunk(int r, int c) {
+  return BITS == 4 ? c ^ ((r >> 3) & 1) : c;
+}
 
 // Workgroup barrier for the K pipeline: waits for this wave's LDS reads
 // and writes (lgkmcnt) but not for its global->LDS loads in flight, which a
@@ -485,8 +495,8 @@ __device__ __forceinline__ void gu_read_all(const GuStage<BITS>& st, int wm, int
   const uint32_t c11 = lds_addr(&st.A[swz(64 * wm + 32 + l32, 4 * half + 3)]);
   const int r0 = 32 * wn + l32, r1 = 64 + 32 * wn + l32;
   constexpr int CPR = kGroup * BITS / 8 / 16;  // code chunks per row
-  const uint32_t b0 = lds_addr(&st.B[r0 * CPR + half * (CPR / 2)]);
-  const uint32_t b1 = lds_addr(&st.B[r1 * CPR + half * (CPR / 2)]);
+  const uint32_t b0 = lds_addr(&st.B[r0 * CPR + code_chunk<BITS>(r0, half * (CPR / 2))]);
+  const uint32_t b1 = lds_addr(&st.B[r1 * CPR + code_chunk<BITS>(r1, half * (CPR / 2))]);
   const uint32_t s0 = lds_addr(&st.S[r0]), s1 = lds_addr(&st.S[r1]);
   if constexpr (BITS == 4) {
     asm volatile(
@@ -654,9 +664,9 @@ __device__ __forceinline__ void prefill_gateup_item(MOE_PGU_PARAMS, GuStage<BITS
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     // activation chunk j*256 + tid: row ch / 8, LDS slot ch % 8 holds column
-    // chunk (slot ^ (row & 7)); rows past the tile read row 0's token (their
+    // chunk (slot ^ ((row >> 1) & 7)); rows past the tile read row 0's token (their
     // results are discarded)
-    const int ch = j * 256 + tid, r = ch >> 3, c = (ch & 7) ^ (r & 7);
+    const int ch = j * 256 + tid, r = ch >> 3, c = (ch & 7) ^ ((r >> 1) & 7);
     const int src = r < ti.rows ? rowsrc[r] : rowsrc[0];
     P.a[j] = (uint32_t)(((int64_t)src * H + c * 8) * 2);
   }
@@ -664,7 +674,7 @@ __device__ __forceinline__ void prefill_gateup_item(MOE_PGU_PARAMS, GuStage<BITS
     constexpr int CPR = kGroup * BITS / 8 / 16;  // 16-byte code chunks per row and group
 #pragma unroll
     for (int j = 0; j < BITS / 4; ++j) {
-      const int ch = j * 256 + tid, rr = ch / CPR, c = ch % CPR;
+      const int ch = j * 256 + tid, rr = ch / CPR, c = code_chunk<BITS>(rr, ch % CPR);
       const RowAddr<BITS> ra(sec, unit_b, tile_b, 2, rr >> 6, n0 + (rr & 63), 0);
       P.b[j] = (uint32_t)(ra.codes - sec) + c * 16;
     }
@@ -872,8 +882,8 @@ __device__ __forceinline__ void dn_read(const DnStage<BITS>& st, int k0, int wm,
   if constexpr (CODES) {
     const int r0 = 64 * wn + l32, r1 = 64 * wn + 32 + l32;
     constexpr int CPR = kGroup * BITS / 8 / 16;
-    const uint32_t b0 = lds_addr(&st.B[r0 * CPR + half * (CPR / 2)]);
-    const uint32_t b1 = lds_addr(&st.B[r1 * CPR + half * (CPR / 2)]);
+    const uint32_t b0 = lds_addr(&st.B[r0 * CPR + code_chunk<BITS>(r0, half * (CPR / 2))]);
+    const uint32_t b1 = lds_addr(&st.B[r1 * CPR + code_chunk<BITS>(r1, half * (CPR / 2))]);
     const uint32_t s0 = lds_addr(&st.S[r0]), s1 = lds_addr(&st.S[r1]);
     if constexpr (BITS == 4) {
       asm volatile(
@@ -1010,7 +1020,7 @@ __device__ __forceinline__ void prefill_down_item(MOE_PDN_PARAMS, DnStage<BITS>&
   P.unit_b = unit_b;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int ch = j * 512 + tid, r = ch >> 3, c = (ch & 7) ^ (r & 7);
+    const int ch = j * 512 + tid, r = ch >> 3, c = (ch & 7) ^ ((r >> 1) & 7);
     const int rr = r < ti.rows ? r : 0;  // rows past the tile read row 0 (discarded)
     P.a[j] = (uint32_t)(((int64_t)rr * 2 * inter + c * 8) * 2);
   }
@@ -1018,7 +1028,7 @@ __device__ __forceinline__ void prefill_down_item(MOE_PDN_PARAMS, DnStage<BITS>&
     constexpr int CPR = kGroup * BITS / 8 / 16;
 #pragma unroll
     for (int j = 0; j < BITS / 4; ++j) {
-      const int ch = j * 512 + tid, rr = ch / CPR, c = ch % CPR;
+      const int ch = j * 512 + tid, rr = ch / CPR, c = code_chunk<BITS>(rr, ch % CPR);
       const RowAddr<BITS> ra(sec, unit_b, tile_b, 1, 0, n0 + rr, 0);
       P.b[j] = (uint32_t)(ra.codes - sec) + c * 16;
     }
