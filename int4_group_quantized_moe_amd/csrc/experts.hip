@@ -697,7 +697,7 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(const uint64_t* __res
                                                            int has_shared) {
   __shared__ int wsum[16], wsmall[16];
   const int e = threadIdx.x, lane = e & 63, wave = e >> 6;
-  constexpr int kU = 8;
+  constexpr int kU = 16;  // block masks in flight per thread and round
   int c = 0;
   if (e < E) {
     for (int b0 = 0; b0 < nblk; b0 += kU) {

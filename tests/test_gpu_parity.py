@@ -414,7 +414,7 @@ def test_batched_parity(cfgname):
     _free()
 
 
-@pytest.mark.parametrize("cfgname", ["batched_80b", "batched_80b_int8"])
+@pytest.mark.parametrize("cfgname", ["batched_80b", "batched_80b_int8", "tiny_t40"])
 def test_batched_chain_fused_epilogue(cfgname):
     """The chain entry point at 64 tokens fuses the residual add and the next
     layer's RMSNorm into the combine.  One layer must equal RMSNorm + layer
@@ -424,7 +424,9 @@ def test_batched_chain_fused_epilogue(cfgname):
     forward run on that x_hat.  Layer 1 is then checked against the oracle,
     teacher-forced on the fused x_hat."""
     moe, wl = _moe(), _wl()
-    cfg = configs.CONFIGS[cfgname]
+    # tiny_t40: the tiny fp32 layer at 40 tokens (bucketed GEMV path, fp32 epilogue)
+    cfg = (configs.TINY.with_(n_tokens=40, layers=2) if cfgname == "tiny_t40"
+           else configs.CONFIGS[cfgname])
     say(f"[batched chain] {cfgname}")
     w = wl.Workload(cfg, n_layers=2)
     d = w.desc
