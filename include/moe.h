@@ -276,7 +276,11 @@ int moe_rmsnorm(const moe_layer_desc* desc, void* x, const void* out, void* x_ha
  *   slot_tables   layer l at slot_tables + l * E
  *   shared_blobs  layer l at shared_blobs + l * shared_stride bytes
  *   shared_stride bytes between shared blobs, multiple of 256
- *   x_hat, out    [T x H] act_dtype scratch tensors (hold the last layer's)
+ *   x_hat, out    [T x H] act_dtype scratch tensors (hold the last layer's).
+ *                 For T > 8 the residual add and the next layer's RMSNorm run
+ *                 inside each layer's combine; its sum of squares is taken in
+ *                 another order than moe_rmsnorm's, so x_hat may differ from
+ *                 moe_rmsnorm's by one rounding of the act dtype.
  *   ws            workspace of moe_workspace_bytes(desc) bytes.  For T = 1 the
  *                 chain may run as one persistent cooperative kernel that
  *                 exchanges data between workgroups through epoch-tagged words

@@ -158,7 +158,6 @@ int enqueue_experts(const moe_layer_desc* d, const void* x, const int32_t* idx, 
   return to_status(launch_experts(a, s));
 }
 
-
 // One layer of a bucketed chain (T > kDecodeMaxTokens): router and experts on
 // x_hat, with the residual add and, unless this is the last layer, the next
 // layer's RMSNorm fused into the combine.
@@ -403,7 +402,6 @@ int moe_layer_forward(const moe_layer_desc* desc, const void* x, const float* ro
   return enqueue_experts(desc, x, idx, w, shared ? gamma : nullptr, expert_slab, slot_table,
                          shared_blob, out, w8, stream);
 }
-
 
 int moe_rmsnorm(const moe_layer_desc* desc, void* x, const void* out, void* x_hat,
                 hipStream_t stream) {
