@@ -62,9 +62,10 @@ int check_opt_ptr(const void* p, uintptr_t align = 16) {
 
 int enqueue_router(const moe_layer_desc* d, const void* x, const float* router_w,
                    const float* router_bias, const float* wsg, int32_t* idx, float* w,
-                   float* gamma, uint8_t* ws, hipStream_t s) {
+                   float* gamma, uint8_t* ws, hipStream_t s, float* xsum = nullptr) {
   const WsPlan P = make_ws_plan(*d);
   RouterArgs a{};
+  a.xsum = xsum;
   a.x = x;
   a.router_w = router_w;
   a.router_bias = (d->flags & MOE_FLAG_ROUTER_BIAS) ? router_bias : nullptr;
@@ -128,8 +129,10 @@ int enqueue_decode(const moe_layer_desc* d, const void* x_in, void* x_hat, bool 
 int enqueue_experts(const moe_layer_desc* d, const void* x, const int32_t* idx, const float* w,
                     const float* gamma, const void* slab, const int32_t* slot_table,
                     const void* shared_blob, void* out, uint8_t* ws, hipStream_t s,
-                    int epi = 0, void* x_res = nullptr, void* x_hat_next = nullptr) {
+                    int epi = 0, void* x_res = nullptr, void* x_hat_next = nullptr,
+                    bool xsum_ready = false) {
   ExpertArgs a{};
+  a.xsum_ready = xsum_ready;
   a.epi = epi;
   a.x_res = x_res;
   a.x_hat_next = x_hat_next;
@@ -158,6 +161,18 @@ int enqueue_experts(const moe_layer_desc* d, const void* x, const int32_t* idx, 
   return to_status(launch_experts(a, s));
 }
 
+// Whether the router of a layer call writes the activations' group sums the
+// grouped GEMMs need (both run on the matrix cores), and where.
+float* router_xsum(const moe_layer_desc* d, uint8_t* ws) {
+  const bool sh = (d->flags & MOE_FLAG_SHARED) != 0;
+  const WsPlan P = make_ws_plan(*d);
+  const bool mfma = P.bucketed && prefill_supported(d->act_dtype, d->hidden, d->inter,
+                                                    sh ? d->shared_inter : d->inter, sh);
+  return mfma && router_uses_mfma(d->act_dtype, d->n_tokens, d->hidden)
+             ? reinterpret_cast<float*>(ws + P.xsum)
+             : nullptr;
+}
+
 // One layer of a bucketed chain (T > kDecodeMaxTokens): router and experts on
 // x_hat, with the residual add and, unless this is the last layer, the next
 // layer's RMSNorm fused into the combine.
@@ -175,10 +190,11 @@ int chain_layer_bucketed(const moe_layer_desc* desc, void* x, void* x_hat, const
     const BlobLayout Ls = make_layout(desc->bits, desc->hidden, desc->shared_inter);
     wsg = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(shared_blob) + Ls.sg_off);
   }
+  float* xsum = router_xsum(desc, w8);
   MOE_TRY(enqueue_router(desc, x_hat, router_w, router_bias, wsg, idx, w,
-                         shared ? gamma : nullptr, w8, stream));
+                         shared ? gamma : nullptr, w8, stream, xsum));
   return enqueue_experts(desc, x_hat, idx, w, shared ? gamma : nullptr, expert_slab, slot_table,
-                         shared_blob, out, w8, stream, last ? 1 : 2, x, x_hat);
+                         shared_blob, out, w8, stream, last ? 1 : 2, x, x_hat, xsum != nullptr);
 }
 
 }  // namespace
@@ -397,10 +413,11 @@ int moe_layer_forward(const moe_layer_desc* desc, const void* x, const float* ro
     const BlobLayout Ls = make_layout(desc->bits, desc->hidden, desc->shared_inter);
     wsg = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(shared_blob) + Ls.sg_off);
   }
+  float* xsum = router_xsum(desc, w8);
   MOE_TRY(enqueue_router(desc, x, router_w, router_bias, wsg, idx, w, shared ? gamma : nullptr, w8,
-                         stream));
+                         stream, xsum));
   return enqueue_experts(desc, x, idx, w, shared ? gamma : nullptr, expert_slab, slot_table,
-                         shared_blob, out, w8, stream);
+                         shared_blob, out, w8, stream, 0, nullptr, nullptr, xsum != nullptr);
 }
 
 int moe_rmsnorm(const moe_layer_desc* desc, void* x, const void* out, void* x_hat,

@@ -1090,6 +1090,7 @@ hipError_t launch_experts_t(const ExpertArgs& a, hipStream_t s) {
     pa.tiles = tiles;
     pa.ntiles = ntiles;
     pa.tiles_ready = small_batch;
+    pa.xsum_ready = a.xsum_ready;
     pa.max_tiles = P.max_tiles;
     pa.L = a.L;
     pa.Ls = a.Ls;

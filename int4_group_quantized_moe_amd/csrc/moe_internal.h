@@ -191,9 +191,15 @@ struct RouterArgs {
   int32_t* topk_idx;
   float* topk_w;
   float* gamma;           // may be null
+  float* xsum;            // [T x H/64] group sums of x, written by the MFMA router if non-null
   int T, H, E, k, act;
 };
 hipError_t launch_router_topk(const RouterArgs& a, hipStream_t s);
+// The router runs as an MFMA GEMM (bf16 batches from 16 tokens, H a multiple of 64).
+constexpr int kRouterMfmaMinTokens = 16;
+inline bool router_uses_mfma(int act, int64_t T, int64_t H) {
+  return act == MOE_ACT_BF16 && T >= kRouterMfmaMinTokens && H % 64 == 0;
+}
 
 struct ExpertArgs {
   const void* x;                 // x_hat [T x H]
@@ -218,6 +224,7 @@ struct ExpertArgs {
   void* x_res;
   void* x_hat_next;
   float eps;
+  bool xsum_ready;               // the router already wrote the group sums of x
 };
 hipError_t launch_experts(const ExpertArgs& a, hipStream_t s);
 
@@ -243,6 +250,7 @@ struct PrefillArgs {
   int max_tiles;
   int min_rows;                  // buckets with fewer tokens are left to the GEMV kernels
   bool tiles_ready;              // the tile list was built with the buckets
+  bool xsum_ready;               // xsum was written by the router
   BlobLayout L, Ls;
   int T, H, E, k, I, Is, bits;
   bool has_shared;

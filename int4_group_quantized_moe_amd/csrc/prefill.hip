@@ -1138,9 +1138,11 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s) {
   }
   const int G = a.H / kGroup;
   const int64_t nsum = (int64_t)a.T * G;
-  hipLaunchKernelGGL(group_sum_kernel, dim3((unsigned)((nsum + 255) / 256)), dim3(256), 0, s, a.x,
-                     a.xsum, a.T, a.H);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (!a.xsum_ready) {
+    hipLaunchKernelGGL(group_sum_kernel, dim3((unsigned)((nsum + 255) / 256)), dim3(256), 0, s,
+                       a.x, a.xsum, a.T, a.H);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   const int nbg = (max(a.I, a.Is) + kGroup - 1) / kGroup;
   const unsigned slots_gu = (unsigned)min((a.max_tiles * nbg + 7) / 8 * 8, kPersistSlots);
   hipLaunchKernelGGL((prefill_gateup_kernel<BITS>), dim3(slots_gu), dim3(256), 0, s, a.x,

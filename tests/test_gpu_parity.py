@@ -606,6 +606,21 @@ def test_grouped_mfma_path_80b(cfgname, T):
     say(f"  largest bucket {counts.max()} tokens, {np.count_nonzero(counts)} experts used")
     tok = np.array([0, 1, 77, 150, T - 2, T - 1])
     check_layer(cfg, 0, x_np[tok], out[tok], idx[tok], wt[tok], g[tok], f"{cfgname} T={T}")
+    # moe_layer_forward takes the activations' group sums from the router GEMM;
+    # router + experts called separately compute them in their own kernel: the
+    # same bits either way
+    moe = _moe()
+    d = w.desc
+    ws = w.workspace()
+    rw, rb, st, sh = w.layer_args(0)
+    idx2, w2, g2 = torch.empty_like(idx), torch.empty_like(wt), torch.empty_like(g)
+    wsg = sh[w.slayout.shared_gate_offset: w.slayout.shared_gate_offset + 4 * cfg.hidden].view(torch.float32)
+    moe.moe_router_topk(d, x, rw, rb, wsg, idx2, w2, g2, ws)
+    out2 = torch.empty_like(out)
+    moe.moe_experts_forward(d, x, idx2, w2, g2, w.slab, st, sh, out2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(idx2, idx) and torch.equal(w2, wt) and torch.equal(g2, g)
+    assert torch.equal(out2, out)
     del w
     _free()
 
