@@ -67,53 +67,72 @@ struct XStage {
 };
 
 template <int BITS, int ACT>
-__device__ void stage_token(const void* __restrict__ x, int64_t row, int H, uint32_t* xp,
-                            float2* cs) {
+__device__ __forceinline__ void stage_chunk(const void* __restrict__ x, int64_t row, int ch, int H,
+                                            uint32_t* xp, float2* cs) {
   constexpr int CC = chunk_cols<BITS>();
-  const int nchunk = H / CC;
-  // one thread per chunk
-  for (int ch = threadIdx.x; ch < nchunk; ch += blockDim.x) {
-    const int64_t base = row * H + (int64_t)ch * CC;
-    float xv[CC];
+  // the chunk's CC activations with 16-byte loads (rows and chunks are
+  // 16-byte aligned: H is a multiple of 64)
+  const int64_t base = row * H + (int64_t)ch * CC;
+  float xv[CC];
+  if constexpr (ACT == MOE_ACT_F32) {
+    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + base);
 #pragma unroll
-    for (int i = 0; i < CC; ++i) xv[i] = load_act<ACT>(x, base + i);
-    if constexpr (ACT == MOE_ACT_F32) {
-      float s = 0.f;
+    for (int i = 0; i < CC / 4; ++i) {
+      const float4 v = p[i];
+      xv[4 * i] = v.x;
+      xv[4 * i + 1] = v.y;
+      xv[4 * i + 2] = v.z;
+      xv[4 * i + 3] = v.w;
+    }
+  } else {
+    const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + base);
 #pragma unroll
-      for (int i = 0; i < CC; ++i) {
-        xp[ch * CC + i] = __float_as_uint(xv[i]);
-        s += xv[i];
-      }
-      cs[ch] = make_float2(0.f, s);
-    } else if constexpr (BITS == 4) {
-      float c = 0.f, s = 0.f;
+    for (int i = 0; i < CC / 8; ++i) {
+      const uint4 v = p[i];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float* v = xv + 8 * j;
-        const uint32_t pa = pack_f16x2(v[0], v[4]);
-        const uint32_t pb = pack_f16x2(v[1] * 0.0625f, v[5] * 0.0625f);
-        const uint32_t pc = pack_f16x2(v[2], v[6]);
-        const uint32_t pf = pack_f16x2(v[3] * 0.0625f, v[7] * 0.0625f);
-        xp[ch * 16 + j * 4 + 0] = pa;
-        xp[ch * 16 + j * 4 + 1] = pb;
-        xp[ch * 16 + j * 4 + 2] = pc;
-        xp[ch * 16 + j * 4 + 3] = pf;
-        c += f16_lo(pa) + f16_hi(pa) + f16_lo(pb) + f16_hi(pb) + f16_lo(pc) + f16_hi(pc) +
-             f16_lo(pf) + f16_hi(pf);
-        s += f16_lo(pa) + f16_hi(pa) + f16_lo(pc) + f16_hi(pc) +
-             16.0f * (f16_lo(pb) + f16_hi(pb) + f16_lo(pf) + f16_hi(pf));
+        xv[8 * i + 2 * j] = bf16_bits_to_f32(w[j] & 0xFFFFu);
+        xv[8 * i + 2 * j + 1] = bf16_bits_to_f32(w[j] >> 16);
       }
-      cs[ch] = make_float2(1024.0f * c, s);
-    } else {
-      float c = 0.f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t p = pack_f16x2(xv[2 * j], xv[2 * j + 1]);
-        xp[ch * 8 + j] = p;
-        c += f16_lo(p) + f16_hi(p);
-      }
-      cs[ch] = make_float2(1024.0f * c, c);
     }
+  }
+  if constexpr (ACT == MOE_ACT_F32) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < CC; ++i) {
+      xp[ch * CC + i] = __float_as_uint(xv[i]);
+      s += xv[i];
+    }
+    cs[ch] = make_float2(0.f, s);
+  } else if constexpr (BITS == 4) {
+    float c = 0.f, s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float* v = xv + 8 * j;
+      const uint32_t pa = pack_f16x2(v[0], v[4]);
+      const uint32_t pb = pack_f16x2(v[1] * 0.0625f, v[5] * 0.0625f);
+      const uint32_t pc = pack_f16x2(v[2], v[6]);
+      const uint32_t pf = pack_f16x2(v[3] * 0.0625f, v[7] * 0.0625f);
+      xp[ch * 16 + j * 4 + 0] = pa;
+      xp[ch * 16 + j * 4 + 1] = pb;
+      xp[ch * 16 + j * 4 + 2] = pc;
+      xp[ch * 16 + j * 4 + 3] = pf;
+      c += f16_lo(pa) + f16_hi(pa) + f16_lo(pb) + f16_hi(pb) + f16_lo(pc) + f16_hi(pc) +
+           f16_lo(pf) + f16_hi(pf);
+      s += f16_lo(pa) + f16_hi(pa) + f16_lo(pc) + f16_hi(pc) +
+           16.0f * (f16_lo(pb) + f16_hi(pb) + f16_lo(pf) + f16_hi(pf));
+    }
+    cs[ch] = make_float2(1024.0f * c, s);
+  } else {
+    float c = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t p = pack_f16x2(xv[2 * j], xv[2 * j + 1]);
+      xp[ch * 8 + j] = p;
+      c += f16_lo(p) + f16_hi(p);
+    }
+    cs[ch] = make_float2(1024.0f * c, c);
   }
 }
 
@@ -282,14 +301,20 @@ __device__ __forceinline__ void gateup_item(MOE_GATEUP_PARAMS, int tile, int ite
       }
     }
     if (t0 > 0) __syncthreads();  // the previous round's staging and sums are read
-    for (int tt = 0; tt < nt; ++tt) {
-      int tok;
-      if (kind == 0) tok = t_dec;
-      else if (kind == 1) tok = pairs[start + t0 + tt] / k;
-      else tok = t0 + tt;
-      uint8_t* st = smem + tt * stage_bytes;
-      stage_token<BITS, ACT>(x, tok, H, reinterpret_cast<uint32_t*>(st),
-                             reinterpret_cast<float2*>(st + XStage<BITS, ACT>::dwords(H) * 4));
+    {
+      // every chunk of the round's tokens at once: thread i stages chunk
+      // i % nchunk of token i / nchunk
+      const int nchunk = H / chunk_cols<BITS>();
+      for (int i = threadIdx.x; i < nt * nchunk; i += blockDim.x) {
+        const int tt = i / nchunk, ch = i - tt * nchunk;
+        int tok;
+        if (kind == 0) tok = t_dec;
+        else if (kind == 1) tok = pairs[start + t0 + tt] / k;
+        else tok = t0 + tt;
+        uint8_t* st = smem + tt * stage_bytes;
+        stage_chunk<BITS, ACT>(x, tok, ch, H, reinterpret_cast<uint32_t*>(st),
+                               reinterpret_cast<float2*>(st + XStage<BITS, ACT>::dwords(H) * 4));
+      }
     }
     __syncthreads();
     float g[kGuTokens], u[kGuTokens];
