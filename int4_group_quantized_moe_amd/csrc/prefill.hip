@@ -389,8 +389,10 @@ typedef uint4 StageBuf[kStageChunks];
 template <int BITS>
 struct GuStage {
   uint4 A[kStageChunks];               // activations
-  uint4 B[128 * (kGroup * BITS / 8) / 16];  // codes: 128 rows x 32 (int4) / 64 (int8) bytes
-  uint32_t S[256];                     // (scale, bias) of rows 0..127 (128..255 unused)
+  // codes: 128 rows x 32 (int4) / 64 (int8) bytes of the stage's group, then
+  // of the second-half group when the wave rows split K (else a copy)
+  uint4 B[2 * 128 * (kGroup * BITS / 8) / 16];
+  uint32_t S[256];                     // (scale, bias) of rows 0..127, then of the second-half group
 };
 
 __device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
@@ -423,10 +425,10 @@ __device__ __forceinline__ void wait_vm() {
 #define MOE_G1(p) ((const void __attribute__((address_space(1)))*)(p))
 #define MOE_L3(p) ((void __attribute__((address_space(3)))*)(p))
 
-// Loads a thread issues per stage: 4 activation chunks, BITS/4 code chunks,
-// one (scale, bias) word.
+// Loads a thread issues per stage: 4 activation chunks, 2 x BITS/4 code
+// chunks (both K halves), one (scale, bias) word.
 template <int BITS>
-constexpr int gu_stage_loads() { return 4 + BITS / 4 + 1; }
+constexpr int gu_stage_loads() { return 4 + 2 * (BITS / 4) + 1; }
 
 // Load sources of a stage: a uniform base (scalar registers) plus a 32-bit
 // per-lane byte offset, so that the loads use scalar-base addressing and the
@@ -439,6 +441,7 @@ struct GuSrc {
   uint32_t a[4];               // activation chunk offsets (stage 0)
   uint32_t b[BITS / 4];        // code chunk offsets (k-block 0, group 0)
   uint32_t sb;                 // (scale, bias) word offset (k-block 0, group 0)
+  int g2off;                   // second-half group of a stage: g + g2off (uniform)
 };
 
 template <int BITS>
@@ -456,6 +459,12 @@ __device__ __forceinline__ void gu_issue(const GuSrc<BITS>& P, GuStage<BITS>& st
   for (int j = 0; j < BITS / 4; ++j)
     __builtin_amdgcn_global_load_lds(MOE_G1(wb + P.b[j]), MOE_L3(&st.B[j * 256 + wave * 64]), 16,
                                      0, 0);
+  const int g2 = g + P.g2off;
+  const uint8_t* wb2 = P.sec + (int64_t)(g2 / GPK) * P.unit_b + (g2 % GPK) * GBYTES;
+#pragma unroll
+  for (int j = 0; j < BITS / 4; ++j)
+    __builtin_amdgcn_global_load_lds(MOE_G1(wb2 + P.b[j]),
+                                     MOE_L3(&st.B[(BITS / 4 + j) * 256 + wave * 64]), 16, 0, 0);
   const uint8_t* sbb = P.sec + (int64_t)(g / GPK) * P.unit_b + (g % GPK) * 4;
   __builtin_amdgcn_global_load_lds(MOE_G1(sbb + P.sb), MOE_L3(&st.S[wave * 64]), 4, 0, 0);
 }
@@ -484,7 +493,8 @@ struct GuFrags {
 // lane's codes of both weight rows and their (scale, bias) words.
 template <int BITS>
 __device__ __forceinline__ void gu_read_all(const GuStage<BITS>& st, int wm, int wn, int l32,
-                                            int half, GuFrags<BITS>& f, u32x4 (&a2)[2][2]) {
+                                            int half, int khalf, GuFrags<BITS>& f,
+                                            u32x4 (&a2)[2][2]) {
   const uint32_t a00 = lds_addr(&st.A[swz(64 * wm + l32, 4 * half + 0)]);
   const uint32_t a01 = lds_addr(&st.A[swz(64 * wm + l32, 4 * half + 1)]);
   const uint32_t a10 = lds_addr(&st.A[swz(64 * wm + 32 + l32, 4 * half + 0)]);
@@ -495,9 +505,10 @@ __device__ __forceinline__ void gu_read_all(const GuStage<BITS>& st, int wm, int
   const uint32_t c11 = lds_addr(&st.A[swz(64 * wm + 32 + l32, 4 * half + 3)]);
   const int r0 = 32 * wn + l32, r1 = 64 + 32 * wn + l32;
   constexpr int CPR = kGroup * BITS / 8 / 16;  // code chunks per row
-  const uint32_t b0 = lds_addr(&st.B[r0 * CPR + code_chunk<BITS>(r0, half * (CPR / 2))]);
-  const uint32_t b1 = lds_addr(&st.B[r1 * CPR + code_chunk<BITS>(r1, half * (CPR / 2))]);
-  const uint32_t s0 = lds_addr(&st.S[r0]), s1 = lds_addr(&st.S[r1]);
+  const int kb = khalf * 128 * CPR, ks = khalf * 128;  // second-half codes and words
+  const uint32_t b0 = lds_addr(&st.B[kb + r0 * CPR + code_chunk<BITS>(r0, half * (CPR / 2))]);
+  const uint32_t b1 = lds_addr(&st.B[kb + r1 * CPR + code_chunk<BITS>(r1, half * (CPR / 2))]);
+  const uint32_t s0 = lds_addr(&st.S[ks + r0]), s1 = lds_addr(&st.S[ks + r1]);
   if constexpr (BITS == 4) {
     asm volatile(
         "ds_read_b128 %0, %12\n\t"
@@ -564,7 +575,8 @@ __device__ __forceinline__ u32x4 gu_bfrag(const u32x4 (&q)[BITS / 4], int ks) {
 // multiply; scale the group's sums into C.
 template <int BITS, typename F>
 __device__ __forceinline__ void gu_stage(const GuStage<BITS>& st, int later, int wm, int wn,
-                                         int l32, int half, f32x16 (&C)[2][2], F&& refill) {
+                                         int l32, int half, int khalf, f32x16 (&C)[2][2],
+                                         F&& refill) {
   constexpr int L = gu_stage_loads<BITS>();
   static_assert(kStages == 3, "wait ladder below covers kStages - 1 = 2 later stages");
   if (later >= 2) wait_vm<2 * L>();
@@ -581,7 +593,7 @@ __device__ __forceinline__ void gu_stage(const GuStage<BITS>& st, int later, int
   // all of the stage's operands in one read, then the stage may be refilled
   // before its MFMAs
   u32x4 a2[2][2];
-  gu_read_all<BITS>(st, wm, wn, l32, half, f, a2);
+  gu_read_all<BITS>(st, wm, wn, l32, half, khalf, f, a2);
   lds_barrier();
   refill();
 #pragma unroll
@@ -655,20 +667,33 @@ __device__ __forceinline__ void prefill_gateup_item(MOE_PGU_PARAMS, GuStage<BITS
   }
   __syncthreads();
   const int G = H / kGroup;
+  // A tile of at most 64 rows splits K between the wave rows: waves 0-1
+  // (wm = 0) take groups 0 .. G/2-1 of rows 0..63, waves 2-3 (wm = 1) groups
+  // G/2 .. G-1 of the same rows, held as LDS rows 64..127 of each stage; the
+  // halves are added before the epilogue.  (G/2 a multiple of the groups per
+  // k-block, so a stage's two groups sit at one k-block distance apart.)
+  constexpr int GPK = kRowBytes * (8 / BITS) / kGroup;
+  const bool split = ti.rows <= 64 && G % (2 * GPK) == 0;
+  const int Gs = split ? G / 2 : G;
+  const int khalf = split ? wm : 0;
 
   // load roles (fixed for the tile)
   GuSrc<BITS> P;
   P.x = reinterpret_cast<const uint8_t*>(x);
   P.sec = sec;
   P.unit_b = unit_b;
+  P.g2off = split ? G / 2 : 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    // activation chunk j*256 + tid: row ch / 8, LDS slot ch % 8 holds column
-    // chunk (slot ^ ((row >> 1) & 7)); rows past the tile read row 0's token (their
-    // results are discarded)
+    // activation chunk j*256 + tid: LDS row ch / 8, slot ch % 8 holds column
+    // chunk (slot ^ ((row >> 1) & 7)); rows past the tile read row 0's token
+    // (their results are discarded).  Split: LDS row r >= 64 holds token row
+    // r - 64 at the second-half group.
     const int ch = j * 256 + tid, r = ch >> 3, c = (ch & 7) ^ ((r >> 1) & 7);
-    const int src = r < ti.rows ? rowsrc[r] : rowsrc[0];
-    P.a[j] = (uint32_t)(((int64_t)src * H + c * 8) * 2);
+    const bool hi = split && r >= 64;
+    const int tr = hi ? r - 64 : r;
+    const int src = tr < ti.rows ? rowsrc[tr] : rowsrc[0];
+    P.a[j] = (uint32_t)(((int64_t)src * H + c * 8) * 2 + (hi ? (G / 2) * kGroup * 2 : 0));
   }
   {
     constexpr int CPR = kGroup * BITS / 8 / 16;  // 16-byte code chunks per row and group
@@ -678,10 +703,12 @@ __device__ __forceinline__ void prefill_gateup_item(MOE_PGU_PARAMS, GuStage<BITS
       const RowAddr<BITS> ra(sec, unit_b, tile_b, 2, rr >> 6, n0 + (rr & 63), 0);
       P.b[j] = (uint32_t)(ra.codes - sec) + c * 16;
     }
-    // (scale, bias) words: lane `tid` of rows 0..127; rows 128..255 repeat them
+    // (scale, bias) words: lane `tid` of rows 0..127; rows 128..255 repeat
+    // them, or with the split hold the second-half group's (G/2 groups on)
     const int rr = tid & 127;
     const RowAddr<BITS> ra(sec, unit_b, tile_b, 2, rr >> 6, n0 + (rr & 63), 0);
-    P.sb = (uint32_t)(ra.sb - sec);
+    P.sb = (uint32_t)(ra.sb - sec) +
+           ((split && tid >= 128) ? (uint32_t)((G / 2 / GPK) * unit_b) : 0u);
   }
   const int wv = __builtin_amdgcn_readfirstlane(wave);
 
@@ -696,21 +723,69 @@ __device__ __forceinline__ void prefill_gateup_item(MOE_PGU_PARAMS, GuStage<BITS
   // buffer is refilled with stage t + kStages right after.  The first pass
   // (g < 0) only issues stages 0 .. kStages-1, from the same instructions as
   // the steady state, so that the compiler sees one set of loads in flight.
-  for (int g = -kStages; g < G; g += kStages) {
+  for (int g = -kStages; g < Gs; g += kStages) {
 #define MOE_GU_STEP(I, BUF)                                                              \
-  if (g + I >= G) break;                                                                 \
+  if (g + I >= Gs) break;                                                                \
   {                                                                                      \
     auto refill = [&]() {                                                                \
-      if (g + I + kStages < G) gu_issue<BITS>(P, BUF, g + I + kStages, wv);              \
+      if (g + I + kStages < Gs) gu_issue<BITS>(P, BUF, g + I + kStages, wv);             \
     };                                                                                   \
-    if (g >= 0) gu_stage<BITS>(BUF, min(kStages - 1, G - 1 - g - I), wm, wn, l32, half, C, \
-                               refill);                                                  \
+    if (g >= 0) gu_stage<BITS>(BUF, min(kStages - 1, Gs - 1 - g - I), wm, wn, l32, half,  \
+                               khalf, C, refill);                                        \
     else refill();                                                                       \
   }
     MOE_GU_STEP(0, s0)
     MOE_GU_STEP(1, s1)
     MOE_GU_STEP(2, s2)
 #undef MOE_GU_STEP
+  }
+
+  // split K: the wm = 1 waves' sums (second half of K for rows 0..63) are
+  // added to the wm = 0 waves' through LDS (stage 0's activations for wn = 0,
+  // stage 1's for wn = 1; separate branches so that every LDS access names
+  // its object)
+  if (split) {
+    __syncthreads();  // every wave is done with the stage buffers
+    if (wm == 1) {
+      if (wn == 0) {
+        float* rd = reinterpret_cast<float*>(&s0.A[0]);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) rd[((mb * 2 + nb) * 16 + r) * 64 + lane] = C[mb][nb][r];
+      } else {
+        float* rd = reinterpret_cast<float*>(&s1.A[0]);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) rd[((mb * 2 + nb) * 16 + r) * 64 + lane] = C[mb][nb][r];
+      }
+    }
+    __syncthreads();
+    if (wm == 0) {
+      if (wn == 0) {
+        const float* rd = reinterpret_cast<const float*>(&s0.A[0]);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) C[mb][nb][r] += rd[((mb * 2 + nb) * 16 + r) * 64 + lane];
+      } else {
+        const float* rd = reinterpret_cast<const float*>(&s1.A[0]);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) C[mb][nb][r] += rd[((mb * 2 + nb) * 16 + r) * 64 + lane];
+      }
+    }
+    __syncthreads();  // before the epilogue reuses the stage buffers
   }
 
   // bias terms from the group sums of the activation rows
