@@ -892,12 +892,14 @@ constexpr int kDnCols = 256;
 template <int BITS>
 struct DnStage {
   uint4 Ah[kStageChunks];
-  uint4 B[kDnCols * (kGroup * BITS / 8) / 16];
-  uint32_t S[kDnThreads];  // (scale, bias) of rows 0..255 (256..511 repeat them)
+  // codes of the stage's group, then of the second-half group when the wave
+  // rows split K (else a copy)
+  uint4 B[2 * kDnCols * (kGroup * BITS / 8) / 16];
+  uint32_t S[kDnThreads];  // (scale, bias) of rows 0..255, then of the second-half group
 };
 
 template <int BITS>
-constexpr int dn_stage_loads() { return 2 + BITS / 4 + 1; }
+constexpr int dn_stage_loads() { return 2 + 2 * (BITS / 4) + 1; }
 
 template <int BITS>
 struct DnSrc {
@@ -907,6 +909,7 @@ struct DnSrc {
   uint32_t a[2];       // h chunk offsets (stage 0, hi part)
   uint32_t b[BITS / 4];  // code chunk offsets (k-block 0, group 0)
   uint32_t sb;         // (scale, bias) word offset
+  int g2off;           // second-half group of a stage: g + g2off (uniform)
 };
 
 template <int BITS>
@@ -924,6 +927,12 @@ __device__ __forceinline__ void dn_issue(const DnSrc<BITS>& P, DnStage<BITS>& st
   for (int j = 0; j < BITS / 4; ++j)
     __builtin_amdgcn_global_load_lds(MOE_G1(wb + P.b[j]), MOE_L3(&st.B[j * 512 + wave * 64]), 16,
                                      0, 0);
+  const int g2 = g + P.g2off;
+  const uint8_t* wb2 = P.sec + (int64_t)(g2 / GPK) * P.unit_b + (g2 % GPK) * GBYTES;
+#pragma unroll
+  for (int j = 0; j < BITS / 4; ++j)
+    __builtin_amdgcn_global_load_lds(MOE_G1(wb2 + P.b[j]),
+                                     MOE_L3(&st.B[(BITS / 4 + j) * 512 + wave * 64]), 16, 0, 0);
   const uint8_t* sbb = P.sec + (int64_t)(g / GPK) * P.unit_b + (g % GPK) * 4;
   __builtin_amdgcn_global_load_lds(MOE_G1(sbb + P.sb), MOE_L3(&st.S[wave * 64]), 4, 0, 0);
 }
@@ -939,7 +948,7 @@ struct DnFrags {
 // also the lane's codes and (scale, bias) words of both output rows.
 template <int BITS, bool CODES>
 __device__ __forceinline__ void dn_read(const DnStage<BITS>& st, int k0, int wm, int wn, int l32,
-                                        int half, DnFrags<BITS>& f) {
+                                        int half, int khalf, DnFrags<BITS>& f) {
   const int i00 = swz(64 * wm + l32, 4 * half + k0), i01 = swz(64 * wm + l32, 4 * half + k0 + 1);
   const int i10 = swz(64 * wm + 32 + l32, 4 * half + k0);
   const int i11 = swz(64 * wm + 32 + l32, 4 * half + k0 + 1);
@@ -957,9 +966,10 @@ __device__ __forceinline__ void dn_read(const DnStage<BITS>& st, int k0, int wm,
   if constexpr (CODES) {
     const int r0 = 64 * wn + l32, r1 = 64 * wn + 32 + l32;
     constexpr int CPR = kGroup * BITS / 8 / 16;
-    const uint32_t b0 = lds_addr(&st.B[r0 * CPR + code_chunk<BITS>(r0, half * (CPR / 2))]);
-    const uint32_t b1 = lds_addr(&st.B[r1 * CPR + code_chunk<BITS>(r1, half * (CPR / 2))]);
-    const uint32_t s0 = lds_addr(&st.S[r0]), s1 = lds_addr(&st.S[r1]);
+    const int kb = khalf * kDnCols * CPR, ks = khalf * kDnCols;  // second-half codes, words
+    const uint32_t b0 = lds_addr(&st.B[kb + r0 * CPR + code_chunk<BITS>(r0, half * (CPR / 2))]);
+    const uint32_t b1 = lds_addr(&st.B[kb + r1 * CPR + code_chunk<BITS>(r1, half * (CPR / 2))]);
+    const uint32_t s0 = lds_addr(&st.S[ks + r0]), s1 = lds_addr(&st.S[ks + r1]);
     if constexpr (BITS == 4) {
       asm volatile(
           "ds_read_b128 %0, %4\n\t"
@@ -1004,8 +1014,8 @@ __device__ __forceinline__ u32x4 dn_bfrag(const u32x4 (&q)[BITS / 4], int ks) {
 // the stage barrier).
 template <int BITS, typename F>
 __device__ __forceinline__ void dn_stage(const DnStage<BITS>& st, int later, int wm, int wn,
-                                         int l32, int half, f32x16 (&C)[2][2], F&& refill,
-                                         const float* hs) {
+                                         int l32, int half, int khalf, f32x16 (&C)[2][2],
+                                         F&& refill, const float* hs) {
   constexpr int L = dn_stage_loads<BITS>();
   static_assert(kStages == 3, "wait ladder below covers kStages - 1 = 2 later stages");
   if (later >= 2) wait_vm<2 * L>();
@@ -1019,11 +1029,11 @@ __device__ __forceinline__ void dn_stage(const DnStage<BITS>& st, int later, int
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = zero;
-  dn_read<BITS, true>(st, 0, wm, wn, l32, half, f);
+  dn_read<BITS, true>(st, 0, wm, wn, l32, half, khalf, f);
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     if (kk == 2) {
-      dn_read<BITS, false>(st, 2, wm, wn, l32, half, f);
+      dn_read<BITS, false>(st, 2, wm, wn, l32, half, khalf, f);
       lds_barrier();
       refill();
     }
@@ -1089,15 +1099,26 @@ __device__ __forceinline__ void prefill_down_item(MOE_PDN_PARAMS, DnStage<BITS>&
   const int64_t sbase = shared ? (int64_t)T * k * (I / kGroup) + (int64_t)ti.base * G
                                : (int64_t)ti.base * G;
 
+  // A tile of at most 64 rows splits K between the wave rows, as in the
+  // gate/up GEMM: waves 0-3 take groups 0 .. G/2-1 of rows 0..63, waves 4-7
+  // groups G/2 .. G-1 of the same rows (LDS rows 64..127); the halves are
+  // added before the bias term.
+  constexpr int GPK = kRowBytes * (8 / BITS) / kGroup;
+  const bool split = ti.rows <= 64 && G % (2 * GPK) == 0;
+  const int Gs = split ? G / 2 : G;
+  const int khalf = split ? wm : 0;
   DnSrc<BITS> P;
   P.h = reinterpret_cast<const uint8_t*>(h + hbase);
   P.sec = sec;
   P.unit_b = unit_b;
+  P.g2off = split ? G / 2 : 0;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int ch = j * 512 + tid, r = ch >> 3, c = (ch & 7) ^ ((r >> 1) & 7);
-    const int rr = r < ti.rows ? r : 0;  // rows past the tile read row 0 (discarded)
-    P.a[j] = (uint32_t)(((int64_t)rr * 2 * inter + c * 8) * 2);
+    const bool hi = split && r >= 64;
+    const int tr = hi ? r - 64 : r;
+    const int rr = tr < ti.rows ? tr : 0;  // rows past the tile read row 0 (discarded)
+    P.a[j] = (uint32_t)(((int64_t)rr * 2 * inter + c * 8) * 2 + (hi ? (G / 2) * kGroup * 2 : 0));
   }
   {
     constexpr int CPR = kGroup * BITS / 8 / 16;
@@ -1107,8 +1128,11 @@ __device__ __forceinline__ void prefill_down_item(MOE_PDN_PARAMS, DnStage<BITS>&
       const RowAddr<BITS> ra(sec, unit_b, tile_b, 1, 0, n0 + rr, 0);
       P.b[j] = (uint32_t)(ra.codes - sec) + c * 16;
     }
+    // (scale, bias) words of rows 0..255; threads 256..511 repeat them, or
+    // with the split load the second-half group's
     const RowAddr<BITS> ra(sec, unit_b, tile_b, 1, 0, n0 + (tid & (kDnCols - 1)), 0);
-    P.sb = (uint32_t)(ra.sb - sec);
+    P.sb = (uint32_t)(ra.sb - sec) +
+           ((split && tid >= kDnCols) ? (uint32_t)((G / 2 / GPK) * unit_b) : 0u);
   }
   const int wv = __builtin_amdgcn_readfirstlane(wave);
 
@@ -1119,15 +1143,16 @@ __device__ __forceinline__ void prefill_down_item(MOE_PDN_PARAMS, DnStage<BITS>&
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) C[mb][nb] = zero;
 
-  for (int g = -kStages; g < G; g += kStages) {
+  const int hofs = khalf * (G / 2);  // this wave's groups of the per-group h scales
+  for (int g = -kStages; g < Gs; g += kStages) {
 #define MOE_DN_STEP(I, BUF)                                                              \
-  if (g + I >= G) break;                                                                 \
+  if (g + I >= Gs) break;                                                                \
   {                                                                                      \
     auto refill = [&]() {                                                                \
-      if (g + I + kStages < G) dn_issue<BITS>(P, BUF, g + I + kStages, wv);              \
+      if (g + I + kStages < Gs) dn_issue<BITS>(P, BUF, g + I + kStages, wv);             \
     };                                                                                   \
-    if (g >= 0) dn_stage<BITS>(BUF, min(kStages - 1, G - 1 - g - I), wm, wn, l32, half, C, \
-                               refill, hsl + g + I);                                     \
+    if (g >= 0) dn_stage<BITS>(BUF, min(kStages - 1, Gs - 1 - g - I), wm, wn, l32, half,  \
+                               khalf, C, refill, hsl + g + I + hofs);                    \
     else refill();                                                                       \
   }
     MOE_DN_STEP(0, s0)
@@ -1136,6 +1161,36 @@ __device__ __forceinline__ void prefill_down_item(MOE_PDN_PARAMS, DnStage<BITS>&
 #undef MOE_DN_STEP
   }
   __syncthreads();
+
+  // split K: the wm = 1 waves' sums (second half of K for rows 0..63) are
+  // added to the wm = 0 waves' through LDS, one 16 KiB buffer per column
+  // wave: stage 0, 1 and 2's activation buffers and stage 0's codes
+  // (separate branches so that every LDS access names its object)
+  if (split) {
+#define MOE_DN_RED(BUFEXPR, OP)                                                          \
+  {                                                                                      \
+    float* rd = reinterpret_cast<float*>(BUFEXPR);                                       \
+    _Pragma("unroll") for (int mb = 0; mb < 2; ++mb)                                     \
+    _Pragma("unroll") for (int nb = 0; nb < 2; ++nb)                                     \
+    _Pragma("unroll") for (int r = 0; r < 16; ++r) OP;                                   \
+  }
+#define MOE_DN_IDX (((mb * 2 + nb) * 16 + r) * 64 + lane)
+    if (wm == 1) {
+      if (wn == 0) MOE_DN_RED(&s0.Ah[0], rd[MOE_DN_IDX] = C[mb][nb][r])
+      else if (wn == 1) MOE_DN_RED(&s1.Ah[0], rd[MOE_DN_IDX] = C[mb][nb][r])
+      else if (wn == 2) MOE_DN_RED(&s2.Ah[0], rd[MOE_DN_IDX] = C[mb][nb][r])
+      else MOE_DN_RED(&s0.B[0], rd[MOE_DN_IDX] = C[mb][nb][r])
+    }
+    __syncthreads();
+    if (wm == 0) {
+      if (wn == 0) MOE_DN_RED(&s0.Ah[0], C[mb][nb][r] += rd[MOE_DN_IDX])
+      else if (wn == 1) MOE_DN_RED(&s1.Ah[0], C[mb][nb][r] += rd[MOE_DN_IDX])
+      else if (wn == 2) MOE_DN_RED(&s2.Ah[0], C[mb][nb][r] += rd[MOE_DN_IDX])
+      else MOE_DN_RED(&s0.B[0], C[mb][nb][r] += rd[MOE_DN_IDX])
+    }
+#undef MOE_DN_IDX
+#undef MOE_DN_RED
+  }
 
   // bias terms from the group sums of the h rows
   {
