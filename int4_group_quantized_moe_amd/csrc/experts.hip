@@ -1130,18 +1130,22 @@ hipError_t launch_experts_t(const ExpertArgs& a, hipStream_t s) {
     pa.min_rows = kMfmaMinRows;
     if ((e = launch_prefill(pa, s)) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((gateup_kernel<BITS, ACT>), dim3(kGemvSlots), dim3(256), lds_gu, s,
-                     a.x, a.topk_idx, a.slab, a.slot_table, a.stride, a.shared_blob, counts,
-                     offsets, pairs, h, a.T, a.H, a.E, a.k, a.L.inter, Is, a.L.gu_unit,
-                     a.L.gu_tile, a.Ls.gu_unit, a.Ls.gu_tile, 1, hs, min_rows, small_list,
-                     n_small, tiles_gu);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((down_bucket_kernel<BITS>), dim3(kDownSlots), dim3(256), 0, s,
-                     a.topk_w, a.gamma, a.slab, a.slot_table, a.stride, a.shared_blob, counts,
-                     offsets, pairs, h, partial, a.T, a.H, a.E, a.k, a.L.inter, Is, a.L.d_off,
-                     a.L.d_unit, a.L.d_tile, a.Ls.d_off, a.Ls.d_unit, a.Ls.d_tile, min_rows,
-                     small_list, n_small, a.L.n_tiles_d);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // the bucketed GEMVs own the buckets below the MFMA threshold (none when
+  // every bucket of at least one token runs on the grouped GEMMs)
+  if (min_rows > 1) {
+    hipLaunchKernelGGL((gateup_kernel<BITS, ACT>), dim3(kGemvSlots), dim3(256), lds_gu, s,
+                       a.x, a.topk_idx, a.slab, a.slot_table, a.stride, a.shared_blob, counts,
+                       offsets, pairs, h, a.T, a.H, a.E, a.k, a.L.inter, Is, a.L.gu_unit,
+                       a.L.gu_tile, a.Ls.gu_unit, a.Ls.gu_tile, 1, hs, min_rows, small_list,
+                       n_small, tiles_gu);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((down_bucket_kernel<BITS>), dim3(kDownSlots), dim3(256), 0, s,
+                       a.topk_w, a.gamma, a.slab, a.slot_table, a.stride, a.shared_blob, counts,
+                       offsets, pairs, h, partial, a.T, a.H, a.E, a.k, a.L.inter, Is, a.L.d_off,
+                       a.L.d_unit, a.L.d_tile, a.Ls.d_off, a.Ls.d_unit, a.Ls.d_tile, min_rows,
+                       small_list, n_small, a.L.n_tiles_d);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((combine_kernel<ACT>), dim3(a.T), dim3(256), 0, s, partial, a.out, a.H, a.k,
                      hs, a.x_res, a.x_hat_next, a.eps, a.epi);
   return hipGetLastError();

@@ -15,7 +15,10 @@ constexpr int kRowBytes = 64;        // code bytes per row per k-block
 constexpr int kCodeBlockBytes = kRowTile * kRowBytes;  // 1 KiB
 constexpr int kGroup = 64;
 constexpr int kDecodeMaxTokens = 8;    // up to this many tokens: per-pair GEMV path
-constexpr int kMfmaMinRows = 4;  // bf16 buckets of this many tokens run on the MFMA grouped GEMMs
+// bf16 buckets of this many tokens run on the MFMA grouped GEMMs: every
+// bucket (1), since a tile of at most 64 rows halves its K loop between the
+// wave rows and the grouped GEMMs' time is per-tile latency, not work
+constexpr int kMfmaMinRows = 1;
 constexpr int kMfmaTileRows = 128;  // rows (bucket entries) per grouped-GEMM tile
 
 constexpr int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
