@@ -1,12 +1,12 @@
 """Benchmark of the MoE-layer decode hot path on one MI355X.
 
-Default workload: the 35B-A3B-shaped decode chain -- hidden 2048, 256 experts,
-top-8, expert and shared intermediate 512, int4 group-64 weights, bf16
-activations, 1 token through 40 distinct chained layers (pre-RMSNorm, MoE
-layer, residual add).  A step is one token through all 40 layers.  The input
+Default workload: the 80B-A3B-shaped decode chain -- hidden 2048, 512 experts,
+top-10, expert and shared intermediate 512, int4 group-64 weights, bf16
+activations, 1 token through 48 distinct chained layers (pre-RMSNorm, MoE
+layer, residual add).  A step is one token through all 48 layers.  The input
 rotates over 8 seeded vectors so the routed experts change between steps and
-the 18 GB slab cannot be served from the 256 MB Infinity Cache.  Each rotation
-is one captured hipGraph of the whole chain.
+the 43.5 GB slab cannot be served from the 256 MB Infinity Cache.  Each
+rotation is one captured hipGraph of the whole chain.
 
 Prints ONE JSON line (see the keys below).  ``value`` is the chain throughput
 in tokens/s; the HBM figures use the algorithmic bytes of the step: router
@@ -27,9 +27,6 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0
 MFMA_PEAK_TFLOPS = 2500.0  # dense bf16 / fp16 matrix-core peak of MI355X
-# the stream-read ceiling measured on MI355X: a grid-stride read of a 16 GiB
-# buffer with 16-byte loads, 4 in flight per thread, 8192 workgroups of 256
-HBM_READ_CEILING_GBPS = 6045.7
 N_ROTATE = 8
 
 
@@ -38,12 +35,13 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--config", default="decode_35b",
-                   help="decode_35b (default), decode_80b, batched_80b, batched_80b_int8, "
+    p.add_argument("--config", default="decode_80b",
+                   help="decode_80b (default), decode_35b, batched_80b, batched_80b_int8, "
                         "prefill_35b, tiny")
     p.add_argument("--layers", type=int, default=0, help="override the number of layers")
-    p.add_argument("--cpu-layers", type=int, default=8,
-                   help="layers of the oracle's timed sample (0: skip the CPU baseline)")
+    p.add_argument("--cpu-layers", type=int, default=-1,
+                   help="layers of the oracle's timed sample (default: the whole chain for "
+                        "batch-1 decode, 1 layer otherwise; 0: skip the CPU baseline)")
     p.add_argument("--no-roofline", action="store_true", help="skip the per-launch event pass")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="also run one device-to-device copy of this many MiB (a reference "
@@ -193,16 +191,27 @@ def main():
     step_flops = algorithmic_flops(cfg) * L
     tflops = step_flops / (ms_per_step / 1e3) / 1e12
 
-    # correctness guard of the timed state: finite residual stream
+    # correctness guards of the timed state: finite residual stream, and no
+    # bounded wait of the persistent chain expired in any timed call
     assert torch.isfinite(x.float()).all(), "non-finite output"
+    check_chain_status(moe, d, ws, "timed region")
 
     roofline = None
     if not args.no_roofline:
         roofline = chain_roofline(cfg, load_input, forward, bytes_per_rot, step_flops)
+        check_chain_status(moe, d, ws, "roofline pass")
+
+    # release the captured graphs (they hold the cooperative chain launch)
+    # and drain the device while the runtime is whole, not at interpreter exit
+    for g in graphs:
+        g.reset()
+    graphs.clear()
+    torch.cuda.synchronize()
 
     cpu = None
-    if args.cpu_layers > 0:
-        cpu = cpu_baseline(cfg, min(args.cpu_layers, L))
+    n_cpu = args.cpu_layers if args.cpu_layers >= 0 else (L if T == 1 else 1)
+    if n_cpu > 0:
+        cpu = cpu_baseline(cfg, min(n_cpu, L))
 
     line = {
         "metric": "MoE-layer decode tokens/s and achieved HBM GB/s (% of peak), 1 GPU",
@@ -215,8 +224,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4 weights x bf16 activations, fp32 accumulate" if cfg.act == "bf16"
-                 else "int4 weights x fp32 activations, fp32 accumulate",
+        "dtype": f"int{cfg.bits} weights x {cfg.act} activations, fp32 accumulate",
         "data": "synthetic",
         "config": {
             "workload": describe(cfg),
@@ -236,9 +244,19 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
-    if cfg.name == "decode_35b":
-        line["config"]["bits"] = cfg.bits
+    line["config"]["bits"] = cfg.bits
     print(json.dumps(line), flush=True)
+
+
+def check_chain_status(moe, d, ws, what):
+    """Fail the run if the persistent chain's status word reports an expired
+    wait between workgroups (that call's results would be invalid)."""
+    import torch
+    off = moe.moe_chain_status(d, ws) - ws.data_ptr()
+    torch.cuda.synchronize()
+    st = int(ws[off:off + 4].view(torch.int32).item())
+    if st != 0:
+        raise SystemExit(f"chain status word {st:#x} after the {what}: a bounded wait expired")
 
 
 def describe(cfg):
@@ -305,7 +323,6 @@ def chain_roofline(cfg, load_input, forward, bytes_per_rot, flops, reps=64):
             "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
             "avg_launch_us": round(avg_s * 1e6, 3),
             "launch_us_p10_p50_p90": [round(pct[10], 3), round(pct[50], 3), round(pct[90], 3)],
-            "frac_of_read_ceiling": round(achieved / HBM_READ_CEILING_GBPS, 4),
             "bytes_per_launch": int(avg_b),
             "launches": reps}
 
@@ -337,38 +354,44 @@ def measured_traffic(cfg):
 
 
 def cpu_baseline(cfg, n_layers):
-    """The fp64 oracle, as it is, on a bounded sample: one token through the
-    first n_layers layers of the same chain (inputs generated beforehand and
-    not timed); tokens/s scaled to the full chain."""
+    """The C++ fp64 oracle, as it is, on a bounded sample: the first n_layers
+    layers of the same chain for the bench's first input (the inputs of the
+    selected experts are generated by an untimed first pass), on every host
+    thread OpenMP is given, then on one thread for the first layer; tokens/s
+    scaled to the full chain."""
     import numpy as np
-    import threadpoolctl
 
     import oracle
     import synth
+    from oracle import cpp
+    O = cpp.default()
     inputs = [oracle.LayerInputs(cfg, l) for l in range(n_layers)]
     x0 = synth.activations(cfg)
 
-    def run():
+    def run(layers):
         x = x0.astype(np.float64)
-        for l in range(n_layers):
-            xh = oracle.chain_prologue(x, cfg.rms_eps, cfg.act)
+        for l in range(layers):
+            xh = O.chain_prologue(x, cfg.rms_eps, cfg.act)
             r = oracle.oracle_layer(inputs[l], xh)
-            x = oracle.chain_epilogue(x, r["out"], cfg.act)
+            x = O.chain_epilogue(x, r["out"], cfg.act)
         return x
 
-    run()                                  # draws and caches the routed experts' inputs
+    run(n_layers)                         # draws and caches the routed experts' inputs
+    threads = O.num_threads()
     t0 = time.perf_counter()
-    run()
+    run(n_layers)
     dt = time.perf_counter() - t0
     per_layer = dt / n_layers
     tokens_per_s = cfg.n_tokens / (per_layer * cfg.layers)
-    threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] + [1])
-    # one thread, first layer only
-    with threadpoolctl.threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        xh = oracle.chain_prologue(x0.astype(np.float64), cfg.rms_eps, cfg.act)
-        oracle.oracle_layer(inputs[0], xh)
-        per_layer_1t = time.perf_counter() - t0
+    per_layer_1t = None
+    if per_layer * threads < 30.0:        # keep the one-thread figure within the sample budget
+        try:
+            O.set_num_threads(1)
+            t0 = time.perf_counter()
+            run(1)
+            per_layer_1t = time.perf_counter() - t0
+        finally:
+            O.set_num_threads(threads)
     model = "unknown"
     try:
         for ln in open("/proc/cpuinfo", encoding="utf-8"):
@@ -380,9 +403,11 @@ def cpu_baseline(cfg, n_layers):
     return {"value": round(tokens_per_s, 6), "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{cfg.n_tokens} token(s) through layers 0..{n_layers - 1} of {cfg.layers} "
-                      f"(numpy float64; {dt:.1f}s); scaled to the {cfg.layers}-layer chain",
-            "seconds_per_layer": round(per_layer, 4),
-            "seconds_per_layer_1_thread": round(per_layer_1t, 4),
+                      f"(C++ fp64 oracle, OpenMP, {threads} threads; {dt:.2f}s); scaled to the "
+                      f"{cfg.layers}-layer chain",
+            "seconds_per_layer": round(per_layer, 5),
+            "seconds_per_layer_1_thread": round(per_layer_1t, 5) if per_layer_1t else None,
+            "speedup_vs_1_thread": round(per_layer_1t / per_layer, 2) if per_layer_1t else None,
             "cpu_model": model, "nproc": os.cpu_count()}
 
 

@@ -10,8 +10,8 @@
  * MLX-style int4/int8 group-quantized and held as fixed-stride blobs, one
  * contiguous blob per expert, addressed with 64-bit offsets
  * (page "Paquets Swiftlet 80B Qwen ..." on xix.ai, 4th and last paragraphs;
- * page "Swiftlet — Swift + Metal рантайм" on news.bugfactory.tech,
- * 3rd paragraph; page "Swiftlet: 在 Mac 和 iPhone 上執行 80B 與 35B Qwen 模型"
+ * the untitled Swiftlet news item on news.bugfactory.tech, 3rd paragraph;
+ * page "Swiftlet: 在 Mac 和 iPhone 上執行 80B 與 35B Qwen 模型"
  * on agentlenshq.com, section "記憶體管理與權重串流").  On one MI355X the whole
  * expert pack fits in HBM, so a per-layer slot table maps expert -> slot of a
  * device-resident slab instead of a host-side pool.
@@ -42,8 +42,14 @@
  *   expert slab and every blob must be 256-byte aligned.
  * - Slab addressing is 64-bit: blob of expert e = slab + slot_table[e] *
  *   expert_stride.  slot_table entries are not range-checked on the device.
- * - No global mutable state: calls are reentrant; concurrent calls must use
- *   distinct workspaces.
+ * - Global state: only a per-device cache of the compute-unit count, filled
+ *   on first use with atomic stores.  Calls are otherwise reentrant;
+ *   concurrent calls must use distinct workspaces.
+ * - Citations: each declaration names the passage of the pages that defines
+ *   what it computes, by page title and paragraph or section.  Where the
+ *   pages are silent (the affine group format, SwiGLU, the sigmoid gate,
+ *   softmax -> top-k -> renormalise, the pre-RMSNorm chain) the declaration
+ *   says so: these are the workload definition this library implements.
  */
 #ifndef MOE_H_
 #define MOE_H_
@@ -98,7 +104,7 @@ enum moe_flags {
  *   expert_stride bytes between consecutive slab slots; >= the blob size of
  *                 moe_blob_layout(), multiple of 256
  *   flags         enum moe_flags
- *   rms_eps       epsilon of the RMSNorm used by moe_rmsnorm / chains
+ *   rms_eps       epsilon of the RMSNorm of moe_residual_rmsnorm / chains
  */
 typedef struct moe_layer_desc {
   int32_t n_tokens;
@@ -153,16 +159,23 @@ typedef struct moe_blob_layout_t {
   int32_t reserved0;
 } moe_blob_layout_t;
 
-/* Library version string, e.g. "moe-gfx950 0.1.0". */
+/* Library version string, e.g. "moe-gfx950 0.1.0".  Pure host function. */
 const char* moe_version(void);
 
-/* Human-readable name of a status code (never NULL). */
+/* Human-readable name of a status code (never NULL).  Pure host function. */
 const char* moe_status_string(int status);
 
 /*
  * Byte layout of one expert blob with intermediate size `inter` (pass
  * desc->inter for routed experts, desc->shared_inter for the shared blob).
  * `out` is host memory.  Pure host function; needs no device.
+ * Defined by: routed experts repacked into fixed-stride blocks, one read per
+ * expert (xix.ai page "Paquets Swiftlet 80B Qwen dans Mac avec 4,3 Go de
+ * mémoire ; iPhone 17 exécutera nativement 35B", 4th paragraph;
+ * agentlenshq.com page "Swiftlet: 在 Mac 和 iPhone 上執行 80B 與 35B Qwen 模型",
+ * section "記憶體管理與權重串流", item "固定步長 Blob"), with 64-bit offsets
+ * (xix.ai page, last paragraph).  The byte format itself is this library's.
+ * Errors: INVALID_ARG (null), UNSUPPORTED (bits, group, hidden or inter).
  */
 int moe_blob_layout(const moe_layer_desc* desc, int32_t inter, moe_blob_layout_t* out);
 
@@ -179,6 +192,10 @@ int moe_blob_layout(const moe_layer_desc* desc, int32_t inter, moe_blob_layout_t
  *   blob_out      host buffer of at least blob_bytes (shared_bytes when
  *                 shared_gate_w is given); padding bytes are zeroed
  * Codes out of range return MOE_ERR_INVALID_ARG.
+ * Defined by: the repack tool that builds the fixed-stride containers from
+ * MLX checkpoints (xix.ai page, 7th paragraph; agentlenshq.com page, section
+ * "實作與工具"); MLX-style int4/int8 group quantisation (xix.ai page, last
+ * paragraph).  Pure host function; needs no device.
  */
 int moe_pack_expert(const moe_layer_desc* desc, int32_t inter, const uint8_t* q_gate,
                     const uint8_t* q_up, const uint8_t* q_down, const uint16_t* sb_gate,
@@ -194,6 +211,9 @@ int moe_pack_expert(const moe_layer_desc* desc, int32_t inter, const uint8_t* q_
  * array of n slots.  Codes must already be in range (not checked).  The
  * shared gate vector of a shared blob is not written by this packer; copy it
  * to shared_gate_offset separately.
+ * Defined by: as moe_pack_expert.  Errors: INVALID_ARG (null, n < 0, a
+ * negative slot), UNSUPPORTED (shape), MISALIGNED (array alignment, stride),
+ * NO_DEVICE, LAUNCH.
  */
 int moe_pack_experts_device(const moe_layer_desc* desc, int32_t inter, int32_t n,
                             const uint8_t* q_gate, const uint8_t* q_up, const uint8_t* q_down,
@@ -201,7 +221,13 @@ int moe_pack_experts_device(const moe_layer_desc* desc, int32_t inter, int32_t n
                             const uint16_t* sb_down, void* slab, const int64_t* dst_slots,
                             hipStream_t stream);
 
-/* Workspace bytes needed by the compute entry points for `desc` (host). */
+/*
+ * Workspace bytes needed by the compute entry points for `desc` (host), or 0
+ * for an invalid descriptor.  The caller allocates the workspace (device
+ * memory); the library never allocates.  Not a passage of the pages: the
+ * scratch of this implementation (logits, routing, h, buckets, partial rows,
+ * exchange words).
+ */
 size_t moe_workspace_bytes(const moe_layer_desc* desc);
 
 /*
@@ -214,6 +240,14 @@ size_t moe_workspace_bytes(const moe_layer_desc* desc);
  *   topk_w        out [T x k] fp32, sums to 1 per token
  *   shared_gate   out [T] fp32 sigmoid(w_sg . x), or NULL (needs shared_gate_w)
  *   ws            workspace of moe_workspace_bytes(desc) bytes
+ * Defined by: every layer routes each token to 10 of 512 experts (80B) or 8
+ * of 256 (35B), with the routers resident (xix.ai page, 4th paragraph;
+ * news.bugfactory.tech Swiftlet item, 3rd paragraph); the shared expert is
+ * resident beside them (same passages).  softmax -> top-k -> renormalise and
+ * the sigmoid gate are the workload definition (the pages are silent).
+ * Errors: INVALID_ARG (null, shared_gate without shared_gate_w, router_bias
+ * missing with MOE_FLAG_ROUTER_BIAS), UNSUPPORTED, MISALIGNED, NO_DEVICE,
+ * LAUNCH.
  */
 int moe_router_topk(const moe_layer_desc* desc, const void* x, const float* router_w,
                     const float* router_bias, const float* shared_gate_w, int32_t* topk_idx,
@@ -230,6 +264,13 @@ int moe_router_topk(const moe_layer_desc* desc, const void* x, const float* rout
  *   slot_table   [E] int32 slab slot of each expert
  *   shared_blob  shared-expert blob (layout above) iff MOE_FLAG_SHARED
  *   out          out [T x H] act_dtype
+ * Defined by: high-sparsity MoE with a shared expert and MLX-style int4/int8
+ * group quantisation computed with byte-addressable kernels and 64-bit
+ * offsets (xix.ai page, last paragraph; news.bugfactory.tech item, last
+ * paragraph); one fixed-stride blob per expert (xix.ai page, 4th paragraph).
+ * SwiGLU and w = scale * q + bias per group of 64 are the workload
+ * definition.  Errors: INVALID_ARG, UNSUPPORTED, MISALIGNED (pointers,
+ * expert_stride), NO_DEVICE, LAUNCH.
  */
 int moe_experts_forward(const moe_layer_desc* desc, const void* x, const int32_t* topk_idx,
                         const float* topk_w, const float* shared_gate, const void* expert_slab,
@@ -240,6 +281,11 @@ int moe_experts_forward(const moe_layer_desc* desc, const void* x, const int32_t
  * One whole MoE layer: router + top-k + shared gate + experts + combine.
  * The shared gate weight is read from the shared blob.  The routing of the
  * call stays in the workspace and can be read with moe_workspace_routing().
+ * Arguments as for moe_router_topk and moe_experts_forward.
+ * Defined by: the sparse MoE block of each layer of the hybrid Qwen3-Next /
+ * Qwen3.5-3.6 models (xix.ai page, 4th and last paragraphs;
+ * news.bugfactory.tech item, 3rd paragraph).  Errors: as
+ * moe_experts_forward.
  */
 int moe_layer_forward(const moe_layer_desc* desc, const void* x, const float* router_w,
                       const float* router_bias, const void* expert_slab,
@@ -251,18 +297,27 @@ int moe_layer_forward(const moe_layer_desc* desc, const void* x, const float* ro
  * moe_layer_forward / moe_chain_forward layer that used `ws`:
  * topk_idx [T x k] int32, topk_w [T x k] fp32, shared_gate [T] fp32.
  * Any output pointer may be NULL.  Pure host arithmetic on `ws`.
+ * Not a passage of the pages: access to this implementation's workspace.
  */
 int moe_workspace_routing(const moe_layer_desc* desc, void* ws, int32_t** topk_idx,
                           float** topk_w, float** shared_gate);
 
 /*
  * Chain step around a layer: optional residual add, then RMSNorm.
- *   x        in/out [T x H] act_dtype residual stream.  If `out` is non-NULL,
- *            x <- act(x + out) first.
+ *   x_res    in/out [T x H] act_dtype residual stream.  If `out` is non-NULL,
+ *            x_res <- act(x_res + out) first.
  *   out      [T x H] act_dtype layer output, or NULL
- *   x_hat    out [T x H] act_dtype: act(x / sqrt(mean(x^2) + rms_eps))
- *            (unit weight)
+ *   x_next   out [T x H] act_dtype, the next layer's input:
+ *            act(x_res / sqrt(mean(x_res^2) + rms_eps)) (unit weight)
+ * Not a passage of the pages: the residual add and pre-RMSNorm around each
+ * MoE layer are the workload definition of a chain of layers.
+ * Errors: INVALID_ARG (null, negative or NaN rms_eps), UNSUPPORTED,
+ * MISALIGNED, NO_DEVICE, LAUNCH.
  */
+int moe_residual_rmsnorm(const moe_layer_desc* desc, void* x_res, const void* out,
+                         void* x_next, hipStream_t stream);
+
+/* The same call as moe_residual_rmsnorm, under its earlier name. */
 int moe_rmsnorm(const moe_layer_desc* desc, void* x, const void* out, void* x_hat,
                 hipStream_t stream);
 
@@ -287,14 +342,33 @@ int moe_rmsnorm(const moe_layer_desc* desc, void* x, const void* out, void* x_ha
  *                 in ws: ws must be zero-filled before its first chain call and
  *                 then reused only by chain calls of the same desc (it keeps the
  *                 last epoch; 2^32 layers before the counter wraps).  A bounded
- *                 wait that expires sets bit 0 of the 32-bit word after that
- *                 counter (results of that call are then invalid).
+ *                 wait that expires sets bit 0 of the chain status word
+ *                 (moe_chain_status); results of that call are then invalid.
+ * Defined by: each token's decode step runs every layer's forward pass in
+ * turn, the MoE block after the mixer (xix.ai page, 4th and 5th paragraphs;
+ * agentlenshq.com page, section "效能與模型支援": decode tokens/s of the
+ * whole model).  The residual add and pre-RMSNorm are the workload
+ * definition.  Errors: INVALID_ARG (n_layers < 1, null, rms_eps), MISALIGNED
+ * (pointers, strides), UNSUPPORTED, NO_DEVICE, LAUNCH.
  */
 int moe_chain_forward(const moe_layer_desc* desc, int32_t n_layers, void* x,
                       const float* router_w, const float* router_bias, const void* expert_slab,
                       const int32_t* slot_tables, const void* shared_blobs,
                       int64_t shared_stride, void* x_hat, void* out, void* ws,
                       hipStream_t stream);
+
+/*
+ * Device address, inside `ws`, of the persistent chain's status word
+ * (uint32).  Bit 0 is set when a bounded wait between workgroups of a
+ * moe_chain_forward call expired; the results of that call are then invalid.
+ * The word is zero in a zero-filled workspace, is never cleared by the
+ * library (it is sticky over calls), and is written only by the persistent
+ * batch-1 chain; the caller reads it after synchronising the stream and may
+ * reset it to 0 when no call using `ws` is in flight.  Pure host arithmetic
+ * on `ws`.  Not a passage of the pages: error reporting of this
+ * implementation.  Errors: INVALID_ARG (null), UNSUPPORTED (descriptor).
+ */
+int moe_chain_status(const moe_layer_desc* desc, void* ws, uint32_t** status_word);
 
 #ifdef __cplusplus
 }

@@ -91,7 +91,9 @@ _SIGS = {
     "moe_layer_forward": ([_DESC, _P, _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "moe_workspace_routing": ([_DESC, _P, ctypes.POINTER(_P), ctypes.POINTER(_P),
                                ctypes.POINTER(_P)], ctypes.c_int),
+    "moe_residual_rmsnorm": ([_DESC, _P, _P, _P, _P], ctypes.c_int),
     "moe_rmsnorm": ([_DESC, _P, _P, _P, _P], ctypes.c_int),
+    "moe_chain_status": ([_DESC, _P, ctypes.POINTER(_P)], ctypes.c_int),
     "moe_chain_forward": ([_DESC, _I32, _P, _P, _P, _P, _P, _P, _I64, _P, _P, _P, _P],
                           ctypes.c_int),
 }
@@ -215,9 +217,22 @@ def moe_workspace_routing(desc, ws):
     return a.value, b.value, c.value
 
 
+def moe_residual_rmsnorm(desc, x_res, out, x_next, stream=None):
+    _check(lib().moe_residual_rmsnorm(ctypes.byref(desc), _ptr(x_res), _ptr(out), _ptr(x_next),
+                                      _stream(stream)), "moe_residual_rmsnorm")
+
+
 def moe_rmsnorm(desc, x, out, x_hat, stream=None):
     _check(lib().moe_rmsnorm(ctypes.byref(desc), _ptr(x), _ptr(out), _ptr(x_hat), _stream(stream)),
            "moe_rmsnorm")
+
+
+def moe_chain_status(desc, ws) -> int:
+    """Device address (int) of the persistent chain's status word inside ws."""
+    a = _P()
+    _check(lib().moe_chain_status(ctypes.byref(desc), _ptr(ws), ctypes.byref(a)),
+           "moe_chain_status")
+    return a.value
 
 
 def moe_chain_forward(desc, n_layers, x, router_w, router_bias, expert_slab, slot_tables,

@@ -26,7 +26,8 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    srcs = sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
+    srcs = sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")) +
+                  glob.glob(os.path.join(PKG, "csrc", "*.cpp")))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), *HIP_FLAGS, "-I", os.path.join(ROOT, "include"),
            "-I", os.path.join(PKG, "csrc"), *srcs, "-o", tmp]

@@ -30,6 +30,8 @@
 // Routing: top-k of E experts per token plus an always-active shared expert
 // (page "Paquets Swiftlet 80B Qwen ..." on xix.ai, 4th paragraph); weights
 // are MLX-style group-quantised int4/int8 (same page, last paragraph).
+#include <atomic>
+
 #include "decode_common.h"
 
 namespace moe {
@@ -722,18 +724,23 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
   if (w == 0 && tid == 0) p.ctr[0] = ep0 + (uint32_t)(L - 1);
 }
 
-int g_num_cus[16];
+// Compute units of each device, read once.  Concurrent first calls may both
+// query the device; they store the same value, and the atomic makes the
+// store and the loads race-free.
+std::atomic<int> g_num_cus[16];
 
 }  // namespace
 
 int chain_grid(int device) {
   if (device < 0 || device >= 16) return 0;
-  if (g_num_cus[device] == 0) {
+  int n = g_num_cus[device].load(std::memory_order_relaxed);
+  if (n == 0) {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, device) != hipSuccess) return 0;
-    g_num_cus[device] = prop.multiProcessorCount;
+    n = prop.multiProcessorCount;
+    g_num_cus[device].store(n, std::memory_order_relaxed);
   }
-  return g_num_cus[device];
+  return n;
 }
 
 size_t chain_lds_bytes(int bits, int NH) {

@@ -12,7 +12,7 @@ import numpy as np
 
 import synth
 
-from .moe_oracle import moe_layer
+from . import moe_oracle
 
 
 class LayerInputs:
@@ -35,8 +35,20 @@ class LayerInputs:
         return synth.expert_arrays(self.cfg, self.layer, e)
 
 
-def oracle_layer(inputs: LayerInputs, x_hat: np.ndarray, routing=None) -> dict:
+def implementation(impl: str = "cpp"):
+    """The oracle implementation: "cpp" (the C++ library, the default) or
+    "numpy"; both have the same functions and are pinned by the same tests."""
+    if impl == "numpy":
+        return moe_oracle
+    if impl == "cpp":
+        from . import cpp
+        return cpp.default()
+    raise ValueError(impl)
+
+
+def oracle_layer(inputs: LayerInputs, x_hat: np.ndarray, routing=None, impl: str = "cpp") -> dict:
     """Run the oracle on one layer with input ``x_hat`` [T x H] (stored values)."""
     cfg = inputs.cfg
-    return moe_layer(x_hat, inputs.router_w, inputs.router_bias, inputs.w_sg,
-                     inputs.expert, inputs.shared, cfg.top_k, cfg.group, routing=routing)
+    return implementation(impl).moe_layer(x_hat, inputs.router_w, inputs.router_bias, inputs.w_sg,
+                                          inputs.expert, inputs.shared, cfg.top_k, cfg.group,
+                                          routing=routing)

@@ -28,6 +28,65 @@ def test_library_exports_every_declared_function():
         assert n in _ffi.exported_symbols(), n
 
 
+def test_boundary_names():
+    """The boundary exports the calls the layer's C ABI is specified with:
+    router + top-k, experts with a given routing, the whole layer, the chain
+    step around it (residual add + RMSNorm), layout, packer and workspace."""
+    names = set(header_functions())
+    for n in ("moe_router_topk", "moe_experts_forward", "moe_layer_forward",
+              "moe_residual_rmsnorm", "moe_blob_layout", "moe_pack_expert",
+              "moe_workspace_bytes", "moe_status_string", "moe_version", "moe_chain_forward",
+              "moe_chain_status"):
+        assert n in names, n
+
+
+def test_every_export_cites_its_passage():
+    """Each declaration's comment names the passage of the pages that defines
+    it, or says that it is not on the pages."""
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    for n in header_functions():
+        m = re.search(r"/\*((?:(?!\*/).)*?)\*/\s*(?:const char\*|int|size_t)\s+" + n + r"\s*\(",
+                      src, flags=re.S)
+        assert m, n
+        doc = m.group(1)
+        assert ("Defined by" in doc or "Not a passage" in doc or "Pure host function" in doc
+                or "same call as" in doc), n
+
+
+def test_chain_status_word_inside_workspace():
+    for T in (1, 4, 64):
+        d = moe.make_desc(T, 2048, 512, 10, 512, 512)
+        ws = np.zeros(moe.moe_workspace_bytes(d), np.uint8)
+        addr = moe.moe_chain_status(d, ws)
+        off = addr - ws.ctypes.data
+        assert 0 <= off and off + 4 <= ws.nbytes and off % 4 == 0
+        pi, _, _ = moe.moe_workspace_routing(d, ws)
+        assert pi != addr
+
+
+def test_host_code_under_sanitizers(tmp_path):
+    """host.cpp (validation, blob layout, workspace plan, host packer) built
+    with g++ under the address and undefined-behaviour sanitizers and driven
+    through its C ABI by tests/sanitize/host_checks.cpp."""
+    import shutil
+    import subprocess
+    if shutil.which("g++") is None:
+        pytest.skip("no g++")
+    csrc = os.path.join(ROOT, "int4_group_quantized_moe_amd", "csrc")
+    exe = str(tmp_path / "host_checks")
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-static-libasan",
+           "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", "-I", os.path.join(ROOT, "include"),
+           "-I", csrc, os.path.join(csrc, "host.cpp"),
+           os.path.join(ROOT, "tests", "sanitize", "host_checks.cpp"), "-o", exe]
+    subprocess.run(cmd, check=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=300,
+                       env=dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0",
+                                UBSAN_OPTIONS="print_stacktrace=1"))
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "host checks passed" in r.stdout
+
+
 def test_version_and_status_strings():
     assert moe.moe_version().startswith("moe-gfx950")
     for st in (0, -1, -2, -3, -4, -5):

@@ -48,6 +48,22 @@ def _free():
     torch.cuda.empty_cache()
 
 
+def chain_status(d, ws) -> int:
+    """The persistent chain's status word in ws (bit 0: a bounded wait
+    between workgroups expired).  Synchronises."""
+    moe = _moe()
+    off = moe.moe_chain_status(d, ws) - ws.data_ptr()
+    torch.cuda.synchronize()
+    return int(ws[off:off + 4].view(torch.int32).item())
+
+
+def chain(d, L, x, w_args, x_hat, out, ws):
+    """moe_chain_forward, then a check that no bounded wait expired."""
+    moe = _moe()
+    moe.moe_chain_forward(d, L, x, *w_args, x_hat, out, ws)
+    assert chain_status(d, ws) == 0, "chain status word set: a bounded wait expired"
+
+
 # ---------------------------------------------------------------------------
 # generator and packer
 
@@ -228,7 +244,7 @@ def test_decode_chain_parity(cfgname, check_layers):
         if not checking:
             continue
         say(f"  layer {i}")
-        torch.cuda.synchronize()
+        assert chain_status(d, ws) == 0
         xb = wl.to_f64(x_before)
         xh_ref = oracle.chain_prologue(xb, cfg.rms_eps, cfg.act)
         assert np.all(np.abs(wl.to_f64(xh) - xh_ref) <= np.abs(xh_ref) * 2.0 ** -7), "rmsnorm"
@@ -241,10 +257,10 @@ def test_decode_chain_parity(cfgname, check_layers):
     torch.cuda.synchronize()
     # the whole chain in one call runs the same kernels: bit-equal residual
     say("  chain entry point, all layers")
+    assert chain_status(d, ws) == 0
     xc = wl.act_tensor(cfg, x0_np)
-    moe.moe_chain_forward(d, cfg.layers, xc, w.router_w, w.router_bias, w.slab, w.slot_tables,
-                          w.shared, w.shared_stride, torch.empty_like(xc), torch.empty_like(xc), ws)
-    torch.cuda.synchronize()
+    chain(d, cfg.layers, xc, (w.router_w, w.router_bias, w.slab, w.slot_tables, w.shared,
+                              w.shared_stride), torch.empty_like(xc), torch.empty_like(xc), ws)
     assert torch.equal(xc, x)
     assert torch.isfinite(xc.float()).all()
     # and a single layer through moe_layer_forward equals the oracle as well
@@ -295,17 +311,15 @@ def test_chain_other_top_k(top_k):
     for i in range(cfg.layers):
         x_before = x.clone()
         rw, rb, st, sh = w.layer_args(i)
-        moe.moe_chain_forward(d, 1, x, rw, rb, w.slab, st, sh, w.shared_stride, xh, out, ws)
-        torch.cuda.synchronize()
+        chain(d, 1, x, (rw, rb, w.slab, st, sh, w.shared_stride), xh, out, ws)
         idx = ws[pi - base: pi - base + 4 * top_k].view(torch.int32).view(1, top_k)
         wt = ws[pw - base: pw - base + 4 * top_k].view(torch.float32).view(1, top_k)
         g = ws[pg - base: pg - base + 4].view(torch.float32)
         check_layer(cfg, i, wl.to_f64(xh), out, idx, wt, g, f"top-{top_k} layer {i}")
         assert np.array_equal(wl.to_f64(x), oracle.chain_epilogue(wl.to_f64(x_before), wl.to_f64(out), cfg.act))
     xc = wl.act_tensor(cfg, x0_np)
-    moe.moe_chain_forward(d, cfg.layers, xc, w.router_w, w.router_bias, w.slab, w.slot_tables,
-                          w.shared, w.shared_stride, torch.empty_like(xc), torch.empty_like(xc), ws)
-    torch.cuda.synchronize()
+    chain(d, cfg.layers, xc, (w.router_w, w.router_bias, w.slab, w.slot_tables, w.shared,
+                              w.shared_stride), torch.empty_like(xc), torch.empty_like(xc), ws)
     assert torch.equal(xc, x)
     del w
     _free()
@@ -337,8 +351,7 @@ def test_chain_boundary_ties(cfgname):
     pi, pw, pg = moe.moe_workspace_routing(d, ws)
     base = ws.data_ptr()
     rw, rb, st, sh = w.layer_args(0)
-    moe.moe_chain_forward(d, 1, x, rw, rb, w.slab, st, sh, w.shared_stride, xh, out, ws)
-    torch.cuda.synchronize()
+    chain(d, 1, x, (rw, rb, w.slab, st, sh, w.shared_stride), xh, out, ws)
     idx = ws[pi - base: pi - base + 4 * k].view(torch.int32)
     wt = ws[pw - base: pw - base + 4 * k].view(torch.float32)
     assert idx.tolist() == tied[:k].tolist()
@@ -371,8 +384,7 @@ def test_chain_massive_ties(cfgname):
     pi, pw, pg = moe.moe_workspace_routing(d, ws)
     base = ws.data_ptr()
     rw, rb, st, sh = w.layer_args(0)
-    moe.moe_chain_forward(d, 1, x, rw, rb, w.slab, st, sh, w.shared_stride, xh, out, ws)
-    torch.cuda.synchronize()
+    chain(d, 1, x, (rw, rb, w.slab, st, sh, w.shared_stride), xh, out, ws)
     idx = ws[pi - base: pi - base + 4 * k].view(torch.int32)
     wt = ws[pw - base: pw - base + 4 * k].view(torch.float32)
     assert idx.tolist() == list(range(k))
@@ -433,25 +445,24 @@ def test_batched_chain_fused_epilogue(cfgname):
     ws = w.workspace()
     x0 = wl.act_tensor(cfg, synth.activations(cfg))
 
-    def chain(L):
+    def run_chain(L):
         xc, xh, out = x0.clone(), torch.empty_like(x0), torch.empty_like(x0)
-        moe.moe_chain_forward(d, L, xc, w.router_w, w.router_bias, w.slab, w.slot_tables,
-                              w.shared, w.shared_stride, xh, out, ws)
-        torch.cuda.synchronize()
+        chain(d, L, xc, (w.router_w, w.router_bias, w.slab, w.slot_tables, w.shared,
+                         w.shared_stride), xh, out, ws)
         return xc, xh, out
 
     # one layer: RMSNorm, layer, residual through the separate entry points
-    x1, _, out1 = chain(1)
+    x1, _, out1 = run_chain(1)
     xb, xhb = x0.clone(), torch.empty_like(x0)
-    moe.moe_rmsnorm(d, xb, None, xhb)
+    moe.moe_residual_rmsnorm(d, xb, None, xhb)
     ob, _, _, _ = run_layer(w, cfg, xhb, 0)
-    moe.moe_rmsnorm(d, xb, ob, torch.empty_like(x0))
+    moe.moe_residual_rmsnorm(d, xb, ob, torch.empty_like(x0))
     torch.cuda.synchronize()
     assert torch.equal(out1, ob), "layer 0 output"
     assert torch.equal(x1, xb), "layer 0 residual"
 
     # two layers: x_hat after the call is layer 1's input, from the fused norm
-    x2, xh1, out2 = chain(2)
+    x2, xh1, out2 = run_chain(2)
     xr, xh_ref = x1.clone(), torch.empty_like(x0)
     moe.moe_rmsnorm(d, xr, None, xh_ref)
     torch.cuda.synchronize()
@@ -469,19 +480,20 @@ def test_batched_chain_fused_epilogue(cfgname):
 
 
 def test_prefill_parity():
-    """4096-token chunk, one layer: full routing check, sampled outputs."""
+    """4096-token chunk, one layer through moe_layer_forward (the call the
+    benchmark times): the routing of every token and every output row against
+    the oracle (each expert dequantised once and applied to its bucket)."""
     moe, wl = _moe(), _wl()
     cfg = configs.PREFILL_35B
-    say("[prefill] 4096 tokens")
+    say("[prefill] 4096 tokens, every row")
     w = wl.Workload(cfg, n_layers=1)
     x_np = oracle.chain_prologue(synth.activations(cfg), cfg.rms_eps, "bf16").astype(np.float32)
     x = wl.act_tensor(cfg, x_np)
     out, idx, wt, g = run_layer(w, cfg, x)
     counts = np.bincount(idx.cpu().numpy().ravel(), minlength=cfg.n_experts)
-    say(f"  tokens per expert: mean {counts.mean():.1f} min {counts.min()} max {counts.max()}")
-    rng = np.random.default_rng(4)
-    tok = np.sort(np.concatenate([[0, cfg.n_tokens - 1], rng.choice(cfg.n_tokens, 6, replace=False)]))
-    check_layer(cfg, 0, x_np[tok], out[tok], idx[tok], wt[tok], g[tok], "prefill sampled tokens")
+    say(f"  tokens per expert: mean {counts.mean():.1f} min {counts.min()} max {counts.max()}; "
+        f"{int(np.sum(counts % 128 <= 64))} experts end in a tile of at most 64 rows")
+    check_layer(cfg, 0, x_np, out, idx, wt, g, "prefill all 4096 tokens")
     del w
     _free()
 
@@ -594,7 +606,7 @@ def test_grouped_mfma_path_tiny(T, k, bits):
 @pytest.mark.parametrize("cfgname,T", [("batched_80b", 320), ("batched_80b_int8", 300)])
 def test_grouped_mfma_path_80b(cfgname, T):
     """80B-shaped layer with a Zipf-skewed router (one bucket holds most tokens)
-    through the grouped MFMA GEMMs; sampled tokens against the oracle."""
+    through the grouped MFMA GEMMs; every output row against the oracle."""
     wl = _wl()
     cfg = configs.CONFIGS[cfgname].with_(n_tokens=T)
     say(f"[mfma] {cfgname} T={T}")
@@ -604,8 +616,7 @@ def test_grouped_mfma_path_80b(cfgname, T):
     out, idx, wt, g = run_layer(w, cfg, x)
     counts = np.bincount(idx.cpu().numpy().ravel(), minlength=cfg.n_experts)
     say(f"  largest bucket {counts.max()} tokens, {np.count_nonzero(counts)} experts used")
-    tok = np.array([0, 1, 77, 150, T - 2, T - 1])
-    check_layer(cfg, 0, x_np[tok], out[tok], idx[tok], wt[tok], g[tok], f"{cfgname} T={T}")
+    check_layer(cfg, 0, x_np, out, idx, wt, g, f"{cfgname} T={T} every row")
     # moe_layer_forward takes the activations' group sums from the router GEMM;
     # router + experts called separately compute them in their own kernel: the
     # same bits either way
@@ -629,8 +640,9 @@ def test_grouped_mfma_path_80b(cfgname, T):
                                  (129, 5)])
 def test_bf16_batch_thresholds(T, k):
     """bf16 batches around the MFMA router threshold (16 tokens; K split over
-    logit planes below 1024 tokens) and the grouped-GEMM bucket threshold (4
-    tokens), so that one layer mixes GEMV and MFMA buckets."""
+    logit planes below 1024 tokens) and the grouped-GEMM tile edges (128-row
+    tiles; tiles of at most 64 rows split K between the wave rows).  Every
+    bucket of at least 1 token runs on the grouped MFMA GEMMs."""
     wl = _wl()
     cfg = configs.TINY.with_(n_tokens=T, top_k=k, act="bf16")
     say(f"[thresholds] tiny bf16 T={T} k={k}")
@@ -644,5 +656,112 @@ def test_bf16_batch_thresholds(T, k):
     # same layer again: bitwise identical
     out2 = run_layer(w, cfg, x)[0]
     assert torch.equal(out, out2)
+    del w
+    _free()
+
+
+@pytest.mark.parametrize("cfgname", ["batched_80b", "batched_80b_int8"])
+def test_batched_deep_layers(cfgname):
+    """The 64-token Zipf-routed chain through all 48 layers, one layer per
+    chain call, teacher-forced at layers 0, 1, 24 and 47: the deep layers'
+    routing concentrates on few experts, so their buckets are the largest."""
+    moe, wl = _moe(), _wl()
+    cfg = configs.CONFIGS[cfgname]
+    say(f"[batched deep] {cfgname}: building {cfg.layers} layers")
+    w = wl.Workload(cfg)
+    d = w.desc
+    ws = w.workspace()
+    x = wl.act_tensor(cfg, synth.activations(cfg))
+    xh, out = torch.empty_like(x), torch.empty_like(x)
+    pi, pw, pg = moe.moe_workspace_routing(d, ws)
+    base = ws.data_ptr()
+    T, k = cfg.n_tokens, cfg.top_k
+    for i in range(cfg.layers):
+        x_before = x.clone() if i in (0, 1, 24, 47) else None
+        rw, rb, st, sh = w.layer_args(i)
+        chain(d, 1, x, (rw, rb, w.slab, st, sh, w.shared_stride), xh, out, ws)
+        if x_before is None:
+            continue
+        torch.cuda.synchronize()
+        idx = ws[pi - base: pi - base + 4 * T * k].view(torch.int32).view(T, k)
+        wt = ws[pw - base: pw - base + 4 * T * k].view(torch.float32).view(T, k)
+        g = ws[pg - base: pg - base + 4 * T].view(torch.float32)
+        counts = np.bincount(idx.cpu().numpy().ravel(), minlength=cfg.n_experts)
+        say(f"  layer {i}: {np.count_nonzero(counts)} unique experts, largest bucket "
+            f"{counts.max()} tokens")
+        xb = wl.to_f64(x_before)
+        xh_ref = oracle.chain_prologue(xb, cfg.rms_eps, cfg.act)
+        assert np.all(np.abs(wl.to_f64(xh) - xh_ref) <= np.abs(xh_ref) * 2.0 ** -7), "rmsnorm"
+        check_layer(cfg, i, wl.to_f64(xh), out, idx, wt, g, f"{cfgname} layer {i}")
+        assert np.array_equal(wl.to_f64(x), oracle.chain_epilogue(xb, wl.to_f64(out), cfg.act))
+    del w
+    _free()
+
+
+@pytest.mark.parametrize("cfgname,T", [("decode_35b", 2), ("decode_35b", 5), ("decode_80b", 8),
+                                       ("batched_80b_int8", 5), ("batched_80b", 3)])
+def test_small_bf16_batches(cfgname, T):
+    """bf16 batches of 2 to 8 tokens: the per-pair GEMV path (no bucketing),
+    against the oracle, and each row equal to its token alone."""
+    wl = _wl()
+    cfg = configs.CONFIGS[cfgname].with_(n_tokens=T)
+    say(f"[small batch] {cfgname} T={T} int{cfg.bits}")
+    w = wl.Workload(cfg, n_layers=1)
+    x_np = oracle.chain_prologue(synth.activations(cfg), cfg.rms_eps, "bf16").astype(np.float32)
+    x = wl.act_tensor(cfg, x_np)
+    out, idx, wt, g = run_layer(w, cfg, x)
+    check_layer(cfg, 0, x_np, out, idx, wt, g, f"{cfgname} T={T}")
+    d1 = wl.desc_for(cfg, n_tokens=1)
+    for t in (0, T - 1):
+        o1, idx1, _, _ = run_layer(w, cfg, x[t:t + 1].contiguous(), 0, desc=d1)
+        assert sorted(idx1[0].tolist()) == sorted(idx[t].tolist())
+    del w
+    _free()
+
+
+def test_int8_batch1_decode():
+    """int8 codes at batch 1 (the three-kernel decode path with 8-bit codes)
+    through moe_layer_forward and a two-layer chain, against the oracle."""
+    moe, wl = _moe(), _wl()
+    cfg = configs.BATCHED_80B_INT8.with_(n_tokens=1, layers=2)
+    say("[int8 T=1] 80B shape, int8")
+    w = wl.Workload(cfg)
+    d = w.desc
+    x0_np = synth.activations(cfg)
+    xh0 = oracle.chain_prologue(x0_np, cfg.rms_eps, "bf16").astype(np.float32)
+    out, idx, wt, g = run_layer(w, cfg, wl.act_tensor(cfg, xh0))
+    check_layer(cfg, 0, xh0, out, idx, wt, g, "int8 T=1 layer_forward")
+    ws = w.workspace()
+    pi, pw, pg = moe.moe_workspace_routing(d, ws)
+    base = ws.data_ptr()
+    x = wl.act_tensor(cfg, x0_np)
+    xh, o = torch.empty_like(x), torch.empty_like(x)
+    for i in range(cfg.layers):
+        xb = wl.to_f64(x)
+        rw, rb, st, sh = w.layer_args(i)
+        chain(d, 1, x, (rw, rb, w.slab, st, sh, w.shared_stride), xh, o, ws)
+        torch.cuda.synchronize()
+        k = cfg.top_k
+        idx = ws[pi - base: pi - base + 4 * k].view(torch.int32).view(1, k)
+        wt = ws[pw - base: pw - base + 4 * k].view(torch.float32).view(1, k)
+        g = ws[pg - base: pg - base + 4].view(torch.float32)
+        check_layer(cfg, i, wl.to_f64(xh), o, idx, wt, g, f"int8 T=1 chain layer {i}")
+        assert np.array_equal(wl.to_f64(x), oracle.chain_epilogue(xb, wl.to_f64(o), cfg.act))
+    del w
+    _free()
+
+
+@pytest.mark.parametrize("T,bits", [(20, 4), (70, 8), (9, 4)])
+def test_bf16_bucketed_gemv_hidden_384(T, bits):
+    """bf16 batches of more than 8 tokens whose hidden size (384) the grouped
+    MFMA GEMMs do not take: every bucket on the bucketed GEMV kernels."""
+    wl = _wl()
+    cfg = configs.TINY.with_(n_tokens=T, hidden=384, act="bf16", bits=bits, top_k=3)
+    say(f"[gemv H=384] bf16 T={T} int{bits}")
+    w = wl.Workload(cfg, n_layers=1)
+    x_np = synth.activations(cfg)
+    x = wl.act_tensor(cfg, x_np)
+    out, idx, wt, g = run_layer(w, cfg, x)
+    check_layer(cfg, 0, x_np, out, idx, wt, g, f"H=384 T={T} int{bits}")
     del w
     _free()
