@@ -378,10 +378,15 @@ def cpu_baseline(cfg, n_layers):
 
     run(n_layers)                         # draws and caches the routed experts' inputs
     threads = O.num_threads()
+    reps = 0
     t0 = time.perf_counter()
-    run(n_layers)
-    dt = time.perf_counter() - t0
-    per_layer = dt / n_layers
+    while True:                           # repeat the sample for about 10 s of CPU work
+        run(n_layers)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= 10.0 or reps >= 64:
+            break
+    per_layer = dt / (reps * n_layers)
     tokens_per_s = cfg.n_tokens / (per_layer * cfg.layers)
     per_layer_1t = None
     if per_layer * threads < 30.0:        # keep the one-thread figure within the sample budget
@@ -402,9 +407,9 @@ def cpu_baseline(cfg, n_layers):
         pass
     return {"value": round(tokens_per_s, 6), "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{cfg.n_tokens} token(s) through layers 0..{n_layers - 1} of {cfg.layers} "
-                      f"(C++ fp64 oracle, OpenMP, {threads} threads; {dt:.2f}s); scaled to the "
-                      f"{cfg.layers}-layer chain",
+            "sample": f"{cfg.n_tokens} token(s) through layers 0..{n_layers - 1} of {cfg.layers}, "
+                      f"{reps} time(s) (C++ fp64 oracle, OpenMP, {threads} threads; {dt:.2f}s); "
+                      f"scaled to the {cfg.layers}-layer chain",
             "seconds_per_layer": round(per_layer, 5),
             "seconds_per_layer_1_thread": round(per_layer_1t, 5) if per_layer_1t else None,
             "speedup_vs_1_thread": round(per_layer_1t / per_layer, 2) if per_layer_1t else None,
