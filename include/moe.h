@@ -42,9 +42,11 @@
  *   expert slab and every blob must be 256-byte aligned.
  * - Slab addressing is 64-bit: blob of expert e = slab + slot_table[e] *
  *   expert_stride.  slot_table entries are not range-checked on the device.
- * - Global state: only a per-device cache of the compute-unit count, filled
- *   on first use with atomic stores.  Calls are otherwise reentrant;
- *   concurrent calls must use distinct workspaces.
+ * - Global state: a per-device cache of the compute-unit count, filled on
+ *   first use with atomic stores, and the per-device scratch of
+ *   moe_layer_forward_noalloc (with its address cache, filled under a lock).
+ *   Calls are otherwise reentrant; concurrent calls must use distinct
+ *   workspaces.
  * - Citations: each declaration names the passage of the pages that defines
  *   what it computes, by page title and paragraph or section.  Where the
  *   pages are silent (the affine group format, SwiGLU, the sigmoid gate,
@@ -70,7 +72,8 @@ enum moe_status {
   MOE_ERR_UNSUPPORTED = -2, /* bits, group, dtype or shape not implemented  */
   MOE_ERR_MISALIGNED = -3,  /* pointer or stride alignment violated         */
   MOE_ERR_NO_DEVICE = -4,   /* no HIP device visible                        */
-  MOE_ERR_LAUNCH = -5       /* a kernel launch returned an error            */
+  MOE_ERR_LAUNCH = -5,      /* a kernel launch returned an error            */
+  MOE_ERR_TOO_LARGE = -6    /* the call needs more than a fixed-size buffer */
 };
 
 /* activation dtypes */
@@ -87,6 +90,8 @@ enum moe_flags {
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_HIDDEN 8192
 #define MOE_MAX_INTER 4096
+/* Device scratch of moe_layer_forward_noalloc, per GPU (16 MiB). */
+#define MOE_NOALLOC_SCRATCH_BYTES (16u << 20)
 
 /*
  * Shape and format of one MoE layer.  Host memory, read at call time only.
@@ -356,6 +361,28 @@ int moe_chain_forward(const moe_layer_desc* desc, int32_t n_layers, void* x,
                       const int32_t* slot_tables, const void* shared_blobs,
                       int64_t shared_stride, void* x_hat, void* out, void* ws,
                       hipStream_t stream);
+
+/*
+ * moe_layer_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same kernels and results as
+ * moe_layer_forward, with the workspace taken from a device array of the
+ * library, MOE_NOALLOC_SCRATCH_BYTES per GPU, which each GPU the library runs
+ * on holds until the process ends.  Its device address is looked up on the
+ * first call on each device.  It allocates and frees nothing.
+ * Limit: calls whose moe_workspace_bytes(desc) exceeds
+ * MOE_NOALLOC_SCRATCH_BYTES return MOE_ERR_TOO_LARGE before anything is
+ * enqueued (at hidden 2048, 512 experts, top-10, inter 512: up to 128
+ * tokens).  Every call on a GPU shares that GPU's scratch, which keeps the
+ * last call's contents: calls that overlap on one GPU (other streams, other
+ * threads) race and must be serialised by the caller.  The routing stays in
+ * the scratch and is not exposed.  Arguments and other errors as for
+ * moe_layer_forward.
+ */
+int moe_layer_forward_noalloc(const moe_layer_desc* desc, const void* x, const float* router_w,
+                              const float* router_bias, const void* expert_slab,
+                              const int32_t* slot_table, const void* shared_blob, void* out,
+                              hipStream_t stream);
 
 /*
  * Device address, inside `ws`, of the persistent chain's status word

@@ -7,9 +7,11 @@ streams.
 """
 from ._ffi import (  # noqa: F401
     MOE_ACT_BF16, MOE_ACT_F32, MOE_ERR_INVALID_ARG, MOE_ERR_LAUNCH, MOE_ERR_MISALIGNED,
-    MOE_ERR_NO_DEVICE, MOE_ERR_UNSUPPORTED, MOE_FLAG_ROUTER_BIAS, MOE_FLAG_SHARED, MOE_OK,
+    MOE_ERR_NO_DEVICE, MOE_ERR_TOO_LARGE, MOE_ERR_UNSUPPORTED, MOE_FLAG_ROUTER_BIAS,
+    MOE_FLAG_SHARED, MOE_NOALLOC_SCRATCH_BYTES, MOE_OK,
     MoeError, exported_symbols, lib, moe_blob_layout, moe_blob_layout_t, moe_chain_forward,
-    moe_chain_status, moe_experts_forward, moe_layer_desc, moe_layer_forward, moe_pack_expert,
+    moe_chain_status, moe_experts_forward, moe_layer_desc, moe_layer_forward,
+    moe_layer_forward_noalloc, moe_pack_expert,
     moe_pack_experts_device, moe_residual_rmsnorm, moe_rmsnorm, moe_router_topk,
     moe_status_string, moe_version, moe_workspace_bytes, moe_workspace_routing,
 )

@@ -20,6 +20,8 @@ MOE_ERR_UNSUPPORTED = -2
 MOE_ERR_MISALIGNED = -3
 MOE_ERR_NO_DEVICE = -4
 MOE_ERR_LAUNCH = -5
+MOE_ERR_TOO_LARGE = -6
+MOE_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 MOE_ACT_F32 = 0
 MOE_ACT_BF16 = 1
@@ -89,6 +91,7 @@ _SIGS = {
     "moe_router_topk": ([_DESC, _P, _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "moe_experts_forward": ([_DESC, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "moe_layer_forward": ([_DESC, _P, _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+    "moe_layer_forward_noalloc": ([_DESC, _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "moe_workspace_routing": ([_DESC, _P, ctypes.POINTER(_P), ctypes.POINTER(_P),
                                ctypes.POINTER(_P)], ctypes.c_int),
     "moe_residual_rmsnorm": ([_DESC, _P, _P, _P, _P], ctypes.c_int),
@@ -207,6 +210,14 @@ def moe_layer_forward(desc, x, router_w, router_bias, expert_slab, slot_table, s
     _check(lib().moe_layer_forward(ctypes.byref(desc), _ptr(x), _ptr(router_w), _ptr(router_bias),
                                    _ptr(expert_slab), _ptr(slot_table), _ptr(shared_blob),
                                    _ptr(out), _ptr(ws), _stream(stream)), "moe_layer_forward")
+
+
+def moe_layer_forward_noalloc(desc, x, router_w, router_bias, expert_slab, slot_table,
+                              shared_blob, out, stream=None):
+    _check(lib().moe_layer_forward_noalloc(ctypes.byref(desc), _ptr(x), _ptr(router_w),
+                                           _ptr(router_bias), _ptr(expert_slab), _ptr(slot_table),
+                                           _ptr(shared_blob), _ptr(out), _stream(stream)),
+           "moe_layer_forward_noalloc")
 
 
 def moe_workspace_routing(desc, ws):

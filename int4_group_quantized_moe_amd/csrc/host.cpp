@@ -66,6 +66,7 @@ const char* moe_status_string(int status) {
     case MOE_ERR_MISALIGNED: return "misaligned pointer or stride";
     case MOE_ERR_NO_DEVICE: return "no HIP device";
     case MOE_ERR_LAUNCH: return "kernel launch failed";
+    case MOE_ERR_TOO_LARGE: return "problem exceeds a fixed-size buffer (the no-allocation scratch)";
     default: return "unknown status";
   }
 }
