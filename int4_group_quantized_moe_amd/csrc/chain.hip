@@ -43,7 +43,7 @@ constexpr uint32_t kSpinLimit = 1u << 18;
 constexpr int kChainMaxExperts = 512;  // top-k over at most 8 logits per lane
 template <int BITS>
 constexpr int max_down_units() { return BITS == 4 ? 6 : 12; }  // per half-wave
-constexpr int kHPairs = 8;     // h word pairs per thread per poll batch
+constexpr int kHPairs = 8;     // h word pairs per thread per poll batch (run-time k)
 constexpr int kHqStride = 20;  // LDS words per staged 32-column chunk of h
 constexpr int kHTilePairs = 6; // exchange word pairs per 16-row tile of h
 
@@ -173,7 +173,11 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
   constexpr int kMaxDownUnits =
       KC ? (KC * (IR / C::KBC) + (SHARED ? IS / C::KBC : 0) + 7) / 8 : max_down_units<BITS>();
   static_assert(kMaxDownUnits <= max_down_units<BITS>(), "down units per half-wave");
-
+  // h word pairs per thread of the h poll: with a compile-time k, all of a
+  // thread's pairs in one batch (a second batch would start only once the
+  // first has arrived: one more poll round trip); else kHPairs per batch
+  constexpr int kHPoll =
+      KC ? ((KC * IR + (SHARED ? IS : 0)) / kRowTile * kHTilePairs + 255) / 256 : kHPairs;
   __shared__ __align__(16) float xs[H];
   __shared__ __align__(16) uint32_t xp[NCH * XS];
   __shared__ float2 cs[NCH];
@@ -614,7 +618,7 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
     // ---------------- C: down + combine + residual ----------------
     // h arrives staged: 6 word pairs per 16-row tile (4 of fp16 pairs, then
     // (1024 x sum of the staged values, scale), (sum of h, 0))
-    poll_pairs<kHPairs>(rh, (NH >> 4) * 2 * kHTilePairs, tid, 256, ep, p.err,
+    poll_pairs<kHPoll>(rh, (NH >> 4) * 2 * kHTilePairs, tid, 256, ep, p.err,
                         [&](int q, uint32_t a, uint32_t b) {
       const int tile = q / kHTilePairs, slot = q - tile * kHTilePairs;
       if (slot < 4)
