@@ -22,6 +22,10 @@ def lib():
                                          ctypes.c_float, ctypes.c_float, ctypes.c_float,
                                          P, P, P, P, P, P, P]
         h.synth_fill_experts.restype = ctypes.c_int
+        h.synth_fill_uniform_bf16.argtypes = [ctypes.c_uint64, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_int, ctypes.c_int64, ctypes.c_float,
+                                              ctypes.c_float, P, P]
+        h.synth_fill_uniform_bf16.restype = ctypes.c_int
         _lib = h
     return _lib
 
@@ -36,3 +40,13 @@ def fill_experts(cfg, layer: int, expert0: int, n: int, inter: int, qg, qu, qd, 
                                   sbd.data_ptr(), stream)
     if st != 0:
         raise RuntimeError(f"synth_fill_experts failed: hip error {st}")
+
+
+def fill_uniform_bf16(seed: int, tensor: int, layer: int, expert: int, n: int, lo: float,
+                      hi: float, out, stream: int):
+    """Elements [0, n) of one bf16-uniform stream into a device tensor (bf16
+    or int16 storage of n elements)."""
+    st = lib().synth_fill_uniform_bf16(seed, tensor, layer, expert, n, lo, hi, out.data_ptr(),
+                                       stream)
+    if st != 0:
+        raise RuntimeError(f"synth_fill_uniform_bf16 failed: hip error {st}")
