@@ -75,10 +75,38 @@ class moe_blob_layout_t(ctypes.Structure):
     ]
 
 
+class moe_gdn_desc(ctypes.Structure):
+    _fields_ = [
+        ("n_seqs", ctypes.c_int32),
+        ("n_k_heads", ctypes.c_int32),
+        ("n_v_heads", ctypes.c_int32),
+        ("d_k", ctypes.c_int32),
+        ("d_v", ctypes.c_int32),
+        ("reserved0", ctypes.c_int32),
+        ("eps", ctypes.c_float),
+        ("scale", ctypes.c_float),
+    ]
+
+
+class moe_attn_desc(ctypes.Structure):
+    _fields_ = [
+        ("n_seqs", ctypes.c_int32),
+        ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("max_len", ctypes.c_int32),
+        ("reserved0", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("reserved1", ctypes.c_float),
+    ]
+
+
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
 _DESC = ctypes.POINTER(moe_layer_desc)
+_GDESC = ctypes.POINTER(moe_gdn_desc)
+_ADESC = ctypes.POINTER(moe_attn_desc)
 
 _SIGS = {
     "moe_version": ([], ctypes.c_char_p),
@@ -97,6 +125,9 @@ _SIGS = {
     "moe_residual_rmsnorm": ([_DESC, _P, _P, _P, _P], ctypes.c_int),
     "moe_rmsnorm": ([_DESC, _P, _P, _P, _P], ctypes.c_int),
     "moe_chain_status": ([_DESC, _P, ctypes.POINTER(_P)], ctypes.c_int),
+    "moe_gdn_decode": ([_GDESC, _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+    "moe_attn_workspace_bytes": ([_ADESC], ctypes.c_size_t),
+    "moe_attn_decode": ([_ADESC, _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "moe_chain_forward": ([_DESC, _I32, _P, _P, _P, _P, _P, _P, _I64, _P, _P, _P, _P],
                           ctypes.c_int),
 }
@@ -252,3 +283,38 @@ def moe_chain_forward(desc, n_layers, x, router_w, router_bias, expert_slab, slo
                                    _ptr(router_bias), _ptr(expert_slab), _ptr(slot_tables),
                                    _ptr(shared_blobs), int(shared_stride), _ptr(x_hat), _ptr(out),
                                    _ptr(ws), _stream(stream)), "moe_chain_forward")
+
+
+# ---------------------------------------------------------------------------
+# token mixers (include/moe_mixers.h)
+
+
+def make_gdn_desc(n_seqs, n_k_heads, n_v_heads, d_k, d_v, eps=1e-6, scale=0.0):
+    d = moe_gdn_desc()
+    d.n_seqs, d.n_k_heads, d.n_v_heads, d.d_k, d.d_v = n_seqs, n_k_heads, n_v_heads, d_k, d_v
+    d.eps, d.scale = eps, scale
+    return d
+
+
+def make_attn_desc(n_seqs, n_q_heads, n_kv_heads, head_dim, max_len, scale=0.0):
+    d = moe_attn_desc()
+    d.n_seqs, d.n_q_heads, d.n_kv_heads, d.head_dim, d.max_len = (n_seqs, n_q_heads, n_kv_heads,
+                                                                  head_dim, max_len)
+    d.scale = scale
+    return d
+
+
+def moe_gdn_decode(desc, q, k, v, g, beta, state, out, stream=None):
+    _check(lib().moe_gdn_decode(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                _ptr(beta), _ptr(state), _ptr(out), _stream(stream)),
+           "moe_gdn_decode")
+
+
+def moe_attn_workspace_bytes(desc) -> int:
+    return int(lib().moe_attn_workspace_bytes(ctypes.byref(desc)))
+
+
+def moe_attn_decode(desc, q, gate, k_cache, v_cache, lengths, out, ws, stream=None):
+    _check(lib().moe_attn_decode(ctypes.byref(desc), _ptr(q), _ptr(gate), _ptr(k_cache),
+                                 _ptr(v_cache), _ptr(lengths), _ptr(out), _ptr(ws),
+                                 _stream(stream)), "moe_attn_decode")

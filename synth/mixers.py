@@ -62,7 +62,7 @@ class GdnConfig:
         return replace(self, **kw)
 
 
-GDN_TINY = GdnConfig("gdn_tiny", seed=10, n_seqs=3, n_k_heads=2, n_v_heads=4, d_k=32, d_v=16,
+GDN_TINY = GdnConfig("gdn_tiny", seed=10, n_seqs=3, n_k_heads=2, n_v_heads=4, d_k=64, d_v=16,
                      steps=4)
 GDN_80B = GdnConfig("gdn_80b", seed=11, n_seqs=1, n_k_heads=16, n_v_heads=32, d_k=128, d_v=128)
 GDN_BATCHED = GDN_80B.with_(name="gdn_batched", seed=12, n_seqs=64)

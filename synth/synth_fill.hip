@@ -115,4 +115,15 @@ int synth_fill_experts(uint64_t seed, int bits, int hidden, int inter, int layer
   return (int)hipGetLastError();
 }
 
+// Elements [0, n) of one stream of bf16 uniforms U(lo, hi) (the definition of
+// the scale and bias planes above) into a device array of n bf16 bits.
+// Returns 0 or the HIP error code.
+int synth_fill_uniform_bf16(uint64_t seed, int tensor, int layer, int expert, int64_t n,
+                            float lo, float hi, uint16_t* out, hipStream_t stream) {
+  if (n <= 0) return 0;
+  hipLaunchKernelGGL(fill_uniform_bf16_kernel, grid_for(n, 1), dim3(256), 0, stream, seed, tensor,
+                     layer, expert, n, lo, hi, n, out);
+  return (int)hipGetLastError();
+}
+
 }  // extern "C"

@@ -13,10 +13,17 @@ from int4_group_quantized_moe_amd import _ffi
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
+def header_sources():
+    import glob
+    return [open(f).read() for f in sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))]
+
+
 def header_functions():
-    src = open(os.path.join(ROOT, "include", "moe.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+    names = set()
+    for src in header_sources():
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names |= set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_function():
@@ -43,7 +50,7 @@ def test_boundary_names():
 def test_every_export_cites_its_passage():
     """Each declaration's comment names the passage of the pages that defines
     it, or says that it is not on the pages."""
-    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = "\n".join(header_sources())
     for n in header_functions():
         m = re.search(r"/\*((?:(?!\*/).)*?)\*/\s*(?:const char\*|int|size_t)\s+" + n + r"\s*\(",
                       src, flags=re.S)
