@@ -37,7 +37,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", default="decode_80b",
                    help="decode_80b (default), decode_35b, batched_80b, batched_80b_int8, "
-                        "prefill_35b, tiny")
+                        "prefill_35b, tiny; the token mixers: gdn_80b, gdn_batched, att_80b, "
+                        "att_batched")
     p.add_argument("--layers", type=int, default=0, help="override the number of layers")
     p.add_argument("--cpu-layers", type=int, default=-1,
                    help="layers of the oracle's timed sample (default: the whole chain for "
@@ -90,7 +91,10 @@ def main():
     import synth
     import workload
     from synth import configs
+    from synth import mixers as sm
 
+    if args.config in sm.GDN_CONFIGS or args.config in sm.ATT_CONFIGS:
+        return mixer_bench(args)
     cfg = configs.CONFIGS[args.config]
     if args.layers:
         cfg = cfg.with_(layers=args.layers)
@@ -414,6 +418,142 @@ def cpu_baseline(cfg, n_layers):
             "seconds_per_layer_1_thread": round(per_layer_1t, 5) if per_layer_1t else None,
             "speedup_vs_1_thread": round(per_layer_1t / per_layer, 2) if per_layer_1t else None,
             "cpu_model": model, "nproc": os.cpu_count()}
+
+
+def mixer_bench(args):
+    """One decode step of a token mixer (Gated DeltaNet or gated GQA
+    attention) per step, inputs rotating over 8 steps' worth; HBM-bound, so
+    reported as algorithmic bytes per step over the step time against 8 TB/s."""
+    import numpy as np
+    import torch
+
+    import int4_group_quantized_moe_amd as moe
+    from oracle import mixer_oracle as mx
+    from synth import device as sd
+    from synth import mixers as sm
+    torch.cuda.set_device(0)
+    moe.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def bf16(x):
+        return torch.from_numpy(np.ascontiguousarray(x, np.float32)).cuda().to(torch.bfloat16)
+
+    def uniform(spec):
+        seed, t, layer, n, lo, hi = spec
+        buf = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+        sd.fill_uniform_bf16(seed, t, layer, 0xFFFFFE, n, lo, hi, buf, stream)
+        return buf
+
+    if args.config in sm.GDN_CONFIGS:
+        cfg = sm.GDN_CONFIGS[args.config]
+        B, Hk, Hv, dk, dv = cfg.n_seqs, cfg.n_k_heads, cfg.n_v_heads, cfg.d_k, cfg.d_v
+        d = moe.make_gdn_desc(B, Hk, Hv, dk, dv)
+        state = uniform(sm.gdn_state_spec(cfg)).float().view(B, Hv, dv, dk)
+        ins = [sm.gdn_inputs(cfg, r) for r in range(N_ROTATE)]
+        dev = [(bf16(i["q"]), bf16(i["k"]), bf16(i["v"]), torch.from_numpy(i["g"]).cuda(),
+                torch.from_numpy(i["beta"]).cuda()) for i in ins]
+        out = torch.empty(B, Hv, dv, dtype=torch.bfloat16, device="cuda")
+
+        def step(s):
+            q, k, v, g, b = dev[s % N_ROTATE]
+            moe.moe_gdn_decode(d, q, k, v, g, b, state, out)
+
+        step_bytes = B * Hv * dv * dk * 8 + B * (2 * Hk * dk * 2 + 2 * Hv * dv * 2 + Hv * 8)
+        kernel = f"gdn_decode_kernel<{dk}>"
+        workload = (f"{cfg.name}: Gated DeltaNet decode step, {B} sequence(s), {Hk} q/k heads, "
+                    f"{Hv} v heads, d_k {dk}, d_v {dv}, fp32 state")
+
+        def cpu_sample():
+            i0 = ins[0]
+            S = sm.gdn_state(cfg, seqs=[0]).astype(np.float64)
+            t0 = time.perf_counter()
+            reps = 0
+            while True:
+                mx.gdn_step(S, i0["q"][:1], i0["k"][:1], i0["v"][:1], i0["g"][:1], i0["beta"][:1])
+                reps += 1
+                if time.perf_counter() - t0 > 5.0:
+                    break
+            dt = (time.perf_counter() - t0) / reps
+            return 1.0 / dt, f"one sequence's step (all {Hv} heads), numpy float64, {reps} reps"
+    else:
+        cfg = sm.ATT_CONFIGS[args.config]
+        B, Hq, Hkv, D, N = cfg.n_seqs, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.max_len
+        d = moe.make_attn_desc(B, Hq, Hkv, D, N)
+        K = uniform(sm.attn_cache_spec(cfg, "k"))
+        V = uniform(sm.attn_cache_spec(cfg, "v"))
+        lengths = sm.attn_lengths(cfg)
+        lens = torch.from_numpy(lengths).cuda()
+        qs = [sm.attn_query(cfg, r) for r in range(N_ROTATE)]
+        dev = [(bf16(x["q"]), bf16(x["gate"])) for x in qs]
+        out = torch.empty(B, Hq, D, dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(max(moe.moe_attn_workspace_bytes(d), 256), dtype=torch.uint8,
+                         device="cuda")
+
+        def step(s):
+            q, g = dev[s % N_ROTATE]
+            moe.moe_attn_decode(d, q, g, K, V, lens, out, ws)
+
+        step_bytes = int(lengths.astype(np.int64).sum()) * Hkv * D * 2 * 2 + B * Hq * D * 2 * 3
+        kernel = f"attn_chunk_kernel<{D}, {8 if Hq // Hkv <= 8 else 16}> + attn_merge_kernel<{D}>"
+        workload = (f"{cfg.name}: gated GQA attention decode, {B} sequence(s), {Hq} q heads, "
+                    f"{Hkv} kv heads, head dim {D}, cache lengths "
+                    f"{'ragged up to' if cfg.ragged else ''} {N} (bf16 cache)")
+
+        def cpu_sample():
+            b = int(np.argmax(lengths))
+            n = int(lengths[b])
+            kv = [(sm.attn_cache(cfg, "k", b, c, n), sm.attn_cache(cfg, "v", b, c, n))
+                  for c in range(Hkv)]
+            t0 = time.perf_counter()
+            reps = 0
+            while True:
+                mx.attn_decode(qs[0]["q"][b:b + 1], qs[0]["gate"][b:b + 1],
+                               lambda i, c, nn: kv[c], [n], Hkv)
+                reps += 1
+                if time.perf_counter() - t0 > 5.0:
+                    break
+            dt = (time.perf_counter() - t0) / reps
+            return 1.0 / dt, f"sequence {b} ({n} positions, all heads), numpy float64, {reps} reps"
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda._sleep(20_000_000)             # queue every launch before the first runs
+    for s in range(args.steps):
+        evs[s][0].record()
+        step(s)
+        evs[s][1].record()
+    torch.cuda.synchronize()
+    durs = sorted(a.elapsed_time(b) for a, b in evs)
+    ms = sum(durs) / len(durs)
+    gbps = step_bytes / (ms / 1e3) / 1e9
+    cpu = None
+    if args.cpu_layers != 0:
+        import os as _os
+        rate, sample = cpu_sample()
+        cpu = {"value": round(rate, 3), "unit": "sequence-steps/s", "cores": 1, "kind": "oracle",
+               "sample": sample, "nproc": _os.cpu_count()}
+    line = {
+        "metric": "token-mixer decode step: sequences/s and achieved HBM GB/s (% of peak), 1 GPU",
+        "value": round(cfg.n_seqs / (ms / 1e3), 3),
+        "unit": "sequence-steps/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 activations and cache, fp32 state and arithmetic",
+        "data": "synthetic",
+        "config": {"workload": workload},
+        "hbm_gbps": round(gbps, 1),
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(gbps, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "avg_launch_us": round(ms * 1e3, 3),
+                     "launch_us_p10_p50_p90": [round(durs[int(q / 100 * (len(durs) - 1))] * 1e3, 3)
+                                               for q in (10, 50, 90)],
+                     "bytes_per_launch": int(step_bytes)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":

@@ -100,7 +100,7 @@ typedef struct moe_attn_desc {
 /*
  * Workspace bytes of moe_attn_decode for `desc`, or 0 when invalid.  Pure
  * host function.  Not a passage of the pages: the per-chunk partial sums of
- * this implementation (per sequence, query head and 256-position chunk: the
+ * this implementation (per sequence, query head and 128-position chunk: the
  * running max and sum, and D floats).
  */
 size_t moe_attn_workspace_bytes(const moe_attn_desc* desc);
@@ -117,8 +117,8 @@ size_t moe_attn_workspace_bytes(const moe_attn_desc* desc);
  *                  a length to [0, max_len], and a length of 0 gives zeros
  *   out            [B][Hq][D] bf16 (round to nearest even)
  *   ws             workspace of moe_attn_workspace_bytes(desc) bytes
- * Runs as chunks of 256 positions, whose partial softmax sums a second kernel
- * merges in chunk order (deterministic).
+ * Runs as chunks of 128 positions, whose partial softmax sums a second kernel
+ * merges in a fixed order (deterministic).
  * Defined by: the remaining layers use gated GQA attention (xix.ai page, last
  * paragraph; news.bugfactory.tech item, 5th paragraph): grouped-query
  * attention with a sigmoid output gate; the pages print no formula.

@@ -7,7 +7,7 @@
 // The cache is read once (2 x n x D bf16 per kv head), so the call is
 // HBM-bound; the G query heads of a kv head share every K and V row.
 //
-// attn_chunk_kernel: workgroup (chunk of 256 positions, kv head, sequence).
+// attn_chunk_kernel: workgroup (chunk of 128 positions, kv head, sequence).
 //   Scores on the matrix cores: v_mfma_f32_32x32x16_bf16 with A = 32 cache
 //   rows K_j (each lane loads 16 contiguous bytes of its row straight from
 //   memory) and B = the G query vectors (zero past G).  Then per head the
@@ -15,7 +15,7 @@
 //   on the vector units (each lane owns D / 64 columns, V rows read
 //   coalesced), the 4 waves' position ranges added through LDS in a fixed
 //   order.  Written: (m, l) and the unnormalised output per (head, chunk).
-// attn_merge_kernel: per (sequence, head) the chunks in order:
+// attn_merge_kernel: per (sequence, head) the chunks in a fixed order:
 //   M = max m_c, L = sum l_c e^(m_c - M), out = gate * sum O_c e^(m_c - M) / L.
 #include <math.h>
 
@@ -26,7 +26,7 @@
 namespace moe {
 namespace {
 
-constexpr int kAttnChunk = 256;  // positions per workgroup
+constexpr int kAttnChunk = 128;  // positions per workgroup (32 per wave)
 constexpr int kAttnMaxGroup = 16;  // query heads per kv head held in registers
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -72,7 +72,8 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(
     int nch, float scale) {
   constexpr int kSteps = D / 16;    // K steps of the score MFMAs
   constexpr int kCols = D / 64;     // output columns per lane
-  __shared__ float sc[GM][kAttnChunk];               // scores, then weights
+  __shared__ float sc[GM][kAttnChunk];               // scores
+  __shared__ __align__(16) float pt[kAttnChunk][GM];  // weights, position-major
   __shared__ float red[4][GM][D];                    // the waves' partial outputs
   __shared__ float hm[GM], hl[GM];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -100,22 +101,46 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(
       qb[s] = real ? u32x4_t{t.x, t.y, t.z, t.w} : u32x4_t{0u, 0u, 0u, 0u};
     }
   }
-  // scores: wave w takes row blocks w and w + 4 (32 positions each)
+  // this wave's 32 V rows (positions 32 wave ..; rows past the chunk's valid
+  // ones clamped in-bounds, weight 0) are requested first, so that they
+  // arrive while the scores and weights are computed
+  constexpr int kVB = kAttnChunk / 4;
+  const int jb = wave * kVB, je = min(jb + kVB, nj);
+  uint32_t vr[kVB][(kCols + 1) / 2];
 #pragma unroll
-  for (int rb = 0; rb < kAttnChunk / 32 / 4; ++rb) {
-    const int blk = wave + 4 * rb;
-    const int jl = blk * 32 + l32;                    // position in the chunk
+  for (int u = 0; u < kVB; ++u) {
+    const uint16_t* vp = vc + (row0 + j0 + min(jb + u, nj - 1)) * D + kCols * lane;
+    if constexpr (kCols == 4) {
+      const uint2 t = *reinterpret_cast<const uint2*>(vp);
+      vr[u][0] = t.x;
+      vr[u][1] = t.y;
+    } else if constexpr (kCols == 2) {
+      vr[u][0] = *reinterpret_cast<const uint32_t*>(vp);
+    } else {
+      vr[u][0] = *vp;
+    }
+  }
+  // scores: wave w takes row block w (32 positions); its K fragments are
+  // all requested before the multiplies
+  constexpr int kBlocks = kAttnChunk / 32 / 4;
+  u32x4_t ka[kBlocks][kSteps];
+#pragma unroll
+  for (int rb = 0; rb < kBlocks; ++rb) {
+    const int jl = (wave + 4 * rb) * 32 + l32;        // position in the chunk
     const int jr = j0 + min(jl, nj - 1);              // clamped row (past n: discarded)
     const uint16_t* kp = kc + (row0 + jr) * D + 8 * half;
-    u32x4_t ka[kSteps];
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
       const uint4 t = *reinterpret_cast<const uint4*>(kp + 16 * s);
-      ka[s] = u32x4_t{t.x, t.y, t.z, t.w};
+      ka[rb][s] = u32x4_t{t.x, t.y, t.z, t.w};
     }
+  }
+#pragma unroll
+  for (int rb = 0; rb < kBlocks; ++rb) {
+    const int blk = wave + 4 * rb;
     f32x16_t acc = {};
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) acc = mfma_bf16(ka[s], qb[s], acc);
+    for (int s = 0; s < kSteps; ++s) acc = mfma_bf16(ka[rb][s], qb[s], acc);
     // lane holds rows (positions) 8 (r / 4) + 4 half + r % 4 of column l32 (head)
     if (l32 < G) {
 #pragma unroll
@@ -140,7 +165,7 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(
 #pragma unroll
     for (int i = 0; i < kAttnChunk / 64; ++i) {
       const float e = expf(v[i] - m);  // -inf -> 0
-      sc[hh][lane + 64 * i] = e;
+      pt[lane + 64 * i][hh] = e;
       l += e;
     }
     l = wave_add(l);
@@ -157,28 +182,30 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(
   for (int hh = 0; hh < GM; ++hh)
 #pragma unroll
     for (int e = 0; e < kCols; ++e) acc[hh][e] = 0.0f;
-  const int jb = wave * 64, je = min(jb + 64, nj);
-  for (int j = jb; j < je; ++j) {
-    const uint16_t* vp = vc + (row0 + j0 + j) * D + kCols * lane;
-    float vv[kCols];
-    if constexpr (kCols == 4) {
-      const uint2 t = *reinterpret_cast<const uint2*>(vp);
-      vv[0] = bf16_bits_to_f32(t.x & 0xFFFFu);
-      vv[1] = bf16_bits_to_f32(t.x >> 16);
-      vv[2] = bf16_bits_to_f32(t.y & 0xFFFFu);
-      vv[3] = bf16_bits_to_f32(t.y >> 16);
-    } else if constexpr (kCols == 2) {
-      const uint32_t t = *reinterpret_cast<const uint32_t*>(vp);
-      vv[0] = bf16_bits_to_f32(t & 0xFFFFu);
-      vv[1] = bf16_bits_to_f32(t >> 16);
-    } else {
-      vv[0] = bf16_bits_to_f32(*vp);
-    }
+  {
+    const int j = jb;
 #pragma unroll
-    for (int hh = 0; hh < GM; ++hh) {
-      const float p = hh < G ? sc[hh][j] : 0.0f;
+    for (int u = 0; u < kVB; ++u) {
+      float vv[kCols];
 #pragma unroll
-      for (int e = 0; e < kCols; ++e) acc[hh][e] += p * vv[e];
+      for (int e = 0; e < kCols; ++e)
+        vv[e] = bf16_bits_to_f32((e & 1) ? (vr[u][e >> 1] >> 16) : (vr[u][e >> 1] & 0xFFFFu));
+      const bool ok = j + u < je;
+      float p[GM];
+#pragma unroll
+      for (int h4 = 0; h4 < GM; h4 += 4) {
+        const float4 t = *reinterpret_cast<const float4*>(&pt[min(j + u, kAttnChunk - 1)][h4]);
+        p[h4] = t.x;
+        p[h4 + 1] = t.y;
+        p[h4 + 2] = t.z;
+        p[h4 + 3] = t.w;
+      }
+#pragma unroll
+      for (int hh = 0; hh < GM; ++hh) {
+        const float w = (ok && hh < G) ? p[hh] : 0.0f;
+#pragma unroll
+        for (int e = 0; e < kCols; ++e) acc[hh][e] += w * vv[e];
+      }
     }
   }
 #pragma unroll
@@ -195,29 +222,66 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(
   if (tid < G) part_ml[(head0 + tid) * nch + chunk] = make_float2(hm[tid], hl[tid]);
 }
 
-template <int D>
-__global__ __launch_bounds__(D) void attn_merge_kernel(const float2* __restrict__ part_ml,
-                                                       const float* __restrict__ part_o,
-                                                       const uint16_t* __restrict__ gate,
-                                                       uint16_t* __restrict__ out, int Hq,
-                                                       int nch) {
-  const int d = threadIdx.x;
-  const size_t head = (size_t)blockIdx.y * Hq + blockIdx.x;
-  const float2* ml = part_ml + head * nch;
-  float M = -INFINITY;
-  for (int c = 0; c < nch; ++c) M = fmaxf(M, ml[c].x);
-  float L = 0.0f, o = 0.0f;
-  for (int c = 0; c < nch; ++c) {
-    const float2 t = ml[c];
-    if (t.y > 0.0f) {
-      const float f = expf(t.x - M);
-      L += t.y * f;
-      o += part_o[(head * nch + c) * D + d] * f;
-    }
+// Merge of one (sequence, query head, 64-column slice)'s chunk partials:
+// NG chunk groups x 64 columns (NG = 16 for long caches, fewer for short
+// ones).  Thread (group cg, column d) folds the chunks cg, cg + NG, ... into a
+// running (m, l, o) (8 chunk loads in flight at a time), then the NG groups'
+// triples are folded in group order:
+//   (m1, l1, o1) + (m2, l2, o2) = (M, l1 e^(m1-M) + l2 e^(m2-M), o1 e^(m1-M) + o2 e^(m2-M)).
+constexpr int kMergeCols = 64;
+
+__device__ __forceinline__ void fold(float& m, float& l, float& o, float m2, float l2, float o2) {
+  if (l2 <= 0.0f) return;          // an empty part
+  if (l <= 0.0f) {
+    m = m2;
+    l = l2;
+    o = o2;
+    return;
   }
-  const float gv = bf16_bits_to_f32(gate[head * D + d]);
-  const float r = L > 0.0f ? o / L : 0.0f;
-  out[head * D + d] = f32_to_bf16_bits(r / (1.0f + expf(-gv)));
+  const float M = fmaxf(m, m2);
+  const float a = expf(m - M), b = expf(m2 - M);
+  l = l * a + l2 * b;
+  o = o * a + o2 * b;
+  m = M;
+}
+
+template <int D, int NG>
+__global__ __launch_bounds__(NG * 64) void attn_merge_kernel(const float2* __restrict__ part_ml,
+                                                          const float* __restrict__ part_o,
+                                                          const uint16_t* __restrict__ gate,
+                                                          uint16_t* __restrict__ out, int Hq,
+                                                          int nch) {
+  constexpr int kMB = 8;
+  __shared__ float3 tri[NG][kMergeCols];
+  const int tid = threadIdx.x, dl = tid % kMergeCols, cg = tid / kMergeCols;
+  const int d = blockIdx.x * kMergeCols + dl;
+  const size_t head = (size_t)blockIdx.z * Hq + blockIdx.y;
+  const float2* ml = part_ml + head * nch;
+  float m = 0.0f, l = 0.0f, o = 0.0f;
+  for (int c0 = cg; c0 < nch; c0 += kMB * NG) {
+    float2 t[kMB];
+    float v[kMB];
+#pragma unroll
+    for (int u = 0; u < kMB; ++u) {
+      const int c = c0 + u * NG;
+      t[u] = c < nch ? ml[c] : make_float2(0.0f, 0.0f);
+      v[u] = (c < nch && t[u].y > 0.0f) ? part_o[(head * nch + c) * D + d] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kMB; ++u) fold(m, l, o, t[u].x, t[u].y, v[u]);
+  }
+  tri[cg][dl] = make_float3(m, l, o);
+  __syncthreads();
+  if (cg == 0) {
+#pragma unroll
+    for (int g2 = 1; g2 < NG; ++g2) {
+      const float3 t = tri[g2][dl];
+      fold(m, l, o, t.x, t.y, t.z);
+    }
+    const float gv = bf16_bits_to_f32(gate[head * D + d]);
+    const float r = l > 0.0f ? o / l : 0.0f;
+    out[head * D + d] = f32_to_bf16_bits(r / (1.0f + expf(-gv)));
+  }
 }
 
 int attn_check(const moe_attn_desc* d) {
@@ -243,8 +307,16 @@ void launch_attn_t(const moe_attn_desc* d, const uint16_t* q, const uint16_t* ga
   hipLaunchKernelGGL((attn_chunk_kernel<D, GM>), dim3(nch, d->n_kv_heads, d->n_seqs), dim3(256),
                      0, s, q, kc, vc, lengths, ml, po, d->n_q_heads, d->n_kv_heads, d->max_len,
                      nch, scale);
-  hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(d->n_q_heads, d->n_seqs), dim3(D), 0, s, ml, po,
-                     gate, out, d->n_q_heads, nch);
+  const dim3 mg(D / kMergeCols, d->n_q_heads, d->n_seqs);
+  if (nch >= 64)
+    hipLaunchKernelGGL((attn_merge_kernel<D, 16>), mg, dim3(16 * 64), 0, s, ml, po, gate, out,
+                       d->n_q_heads, nch);
+  else if (nch >= 8)
+    hipLaunchKernelGGL((attn_merge_kernel<D, 4>), mg, dim3(4 * 64), 0, s, ml, po, gate, out,
+                       d->n_q_heads, nch);
+  else
+    hipLaunchKernelGGL((attn_merge_kernel<D, 1>), mg, dim3(64), 0, s, ml, po, gate, out,
+                       d->n_q_heads, nch);
 }
 
 template <int D>
