@@ -38,12 +38,15 @@ def parse():
     p.add_argument("--config", default="decode_80b",
                    help="decode_80b (default), decode_35b, batched_80b, batched_80b_int8, "
                         "prefill_35b, tiny; the token mixers: gdn_80b, gdn_batched, att_80b, "
-                        "att_batched")
+                        "att_batched; pool_80b: decode through an expert slot pool over pinned "
+                        "host memory")
     p.add_argument("--layers", type=int, default=0, help="override the number of layers")
     p.add_argument("--cpu-layers", type=int, default=-1,
                    help="layers of the oracle's timed sample (default: the whole chain for "
                         "batch-1 decode, 1 layer otherwise; 0: skip the CPU baseline)")
     p.add_argument("--no-roofline", action="store_true", help="skip the per-launch event pass")
+    p.add_argument("--pool-frac", type=float, default=0.25,
+                   help="pool_80b: slots as a fraction of the experts of the pack")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="also run one device-to-device copy of this many MiB (a reference "
                         "kernel of known traffic for hardware byte counters)")
@@ -95,6 +98,8 @@ def main():
 
     if args.config in sm.GDN_CONFIGS or args.config in sm.ATT_CONFIGS:
         return mixer_bench(args)
+    if args.config == "pool_80b":
+        return pool_bench(args)
     cfg = configs.CONFIGS[args.config]
     if args.layers:
         cfg = cfg.with_(layers=args.layers)
@@ -418,6 +423,133 @@ def cpu_baseline(cfg, n_layers):
             "seconds_per_layer_1_thread": round(per_layer_1t, 5) if per_layer_1t else None,
             "speedup_vs_1_thread": round(per_layer_1t / per_layer, 2) if per_layer_1t else None,
             "cpu_model": model, "nproc": os.cpu_count()}
+
+
+def pool_bench(args):
+    """Batch-1 decode through an expert slot pool (include/moe_pool.h): the
+    80B-A3B shape, the whole 48-layer pack in pinned host memory, and a slab
+    of pool_frac x (48 x 512) slots in HBM.  Per layer: RMSNorm and the
+    router on the GPU, the routing read back, moe_pool_require (copies of the
+    missed blobs over the host link), the experts on the pool's slab.  A step
+    is one token through all layers; warm-up tokens fill the pool first.
+    Each (token, layer) reads its own independent N(0, 1) input row rather
+    than the previous layer's residual: with random weights the residual
+    stream of every token converges to one direction after a few layers (the
+    group biases give each expert an input-independent output), so deep
+    layers would route every token alike and the hit rate would measure that
+    artefact.  Expert popularity is set by an additive Zipf(s) router bias: s = 0 is
+    uniform routing, s = 1.1 concentrates each layer on a few experts; the
+    headline is s = 0.5.  Reported: tokens/s, the hit rate (the pages quote
+    43-70%) and a sweep over skews and pool sizes."""
+    import numpy as np
+    import torch
+
+    import int4_group_quantized_moe_amd as moe
+    import synth
+    import workload
+    from synth import configs
+    torch.cuda.set_device(0)
+    moe.lib()
+    cfg = configs.BATCHED_80B.with_(name="pool_80b", n_tokens=1)
+    if args.layers:
+        cfg = cfg.with_(layers=args.layers)
+    L, E, k, H = cfg.layers, cfg.n_experts, cfg.top_k, cfg.hidden
+    t0 = time.time()
+    wl = workload.Workload(cfg)
+    d = wl.desc
+    stride = wl.stride
+    pack = torch.empty(L * E * stride, dtype=torch.uint8, pin_memory=True)
+    pack.copy_(wl.slab)
+    torch.cuda.synchronize()
+    del wl.slab                      # the pack lives on the host only
+    torch.cuda.empty_cache()
+    print(f"# pack of {pack.numel() / 1e9:.1f} GB in pinned host memory ({time.time() - t0:.1f}s)",
+          file=sys.stderr, flush=True)
+    ws = wl.workspace()
+    idx = torch.empty(1, k, dtype=torch.int32, device="cuda")
+    wt = torch.empty(1, k, dtype=torch.float32, device="cuda")
+    gam = torch.empty(1, dtype=torch.float32, device="cuda")
+    n_rows = 4096            # distinct (token, layer) inputs before a repeat
+    xs = workload.act_tensor(cfg, synth.activations(cfg, variant=1, n_tokens=n_rows))
+    xh, out = torch.empty_like(xs[:1]), torch.empty_like(xs[:1])
+    wsg = [wl.shared[l][wl.slayout.shared_gate_offset:
+                        wl.slayout.shared_gate_offset + 4 * H].view(torch.float32)
+           for l in range(L)]
+
+    def set_skew(zs):
+        for l in range(L):
+            b = synth.router_bias(cfg.with_(zipf_s=zs), l) if zs else np.zeros(E, np.float32)
+            wl.router_bias[l].copy_(torch.from_numpy(b))
+
+    def run(frac, steps, warm):
+        n_slots = max(k, int(frac * L * E))
+        pslab = torch.empty(n_slots * stride, dtype=torch.uint8, device="cuda")
+        tables = torch.zeros(L, E, dtype=torch.int32, device="cuda")
+        pool = moe.MoePool(d, L, n_slots, pack, stride, pslab, tables)
+
+        def token(s):
+            for l in range(L):
+                r = (s * L + l) % n_rows
+                rw, rb, _, sh = wl.layer_args(l)
+                moe.moe_residual_rmsnorm(d, xs[r:r + 1], None, xh)
+                moe.moe_router_topk(d, xh, rw, rb, wsg[l], idx, wt, gam, ws)
+                need = sorted(set(idx.cpu().numpy().ravel().tolist()))   # synchronises
+                pool.require(l, need)
+                moe.moe_experts_forward(d, xh, idx, wt, gam, pslab, tables[l], sh, out, ws)
+
+        for s in range(warm):
+            token(s)
+        torch.cuda.synchronize()
+        st0 = pool.stats()
+        t1 = time.perf_counter()
+        for s in range(warm, warm + steps):
+            token(s)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t1
+        st1 = pool.stats()
+        look = st1["lookups"] - st0["lookups"]
+        hits = st1["hits"] - st0["hits"]
+        res = {"pool_frac": frac, "slots": n_slots, "tokens_per_s": round(steps / dt, 2),
+               "hit_rate": round(hits / max(look, 1), 4),
+               "misses_per_layer": round((look - hits) / (steps * L), 2),
+               "mib_copied_per_token": round((st1["bytes_copied"] - st0["bytes_copied"])
+                                             / steps / 2 ** 20, 1)}
+        assert torch.isfinite(out.float()).all()
+        del pool, pslab, tables
+        torch.cuda.empty_cache()
+        return res, dt / steps
+
+    sweep = []
+    main_res = s_per_tok = None
+    for zs in (0.5, 0.0, 1.1):
+        set_skew(zs)
+        for frac in (0.25, 0.1, 0.5):
+            headline = zs == 0.5 and frac == args.pool_frac
+            r, spt = run(frac, args.steps if headline else max(8, args.steps // 2), args.warmup)
+            r["zipf_s"] = zs
+            sweep.append(r)
+            print(f"# zipf {zs} pool {frac}: {r}", file=sys.stderr, flush=True)
+            if headline:
+                main_res, s_per_tok = r, spt
+    if main_res is None:
+        main_res, s_per_tok = sweep[0], 1.0 / sweep[0]["tokens_per_s"]
+    line = {
+        "metric": "MoE decode through an expert slot pool: tokens/s and hit rate, 1 GPU",
+        "value": main_res["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(s_per_tok * 1e3, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int4 weights x bf16 activations, fp32 accumulate", "data": "synthetic",
+        "config": {"workload": (f"pool_80b: hidden {H}, {E} experts top-{k} with a Zipf(0.5) "
+                                f"router bias, {L} layers, 1 token, an independent input per layer; the pack "
+                                f"({pack.numel() / 1e9:.1f} GB) in pinned host memory, "
+                                f"{main_res['slots']} HBM slots"),
+                   "pool_frac": main_res["pool_frac"], "zipf_s": 0.5},
+        "hit_rate": main_res["hit_rate"], "pages_hit_rate_range": [0.43, 0.70],
+        "misses_per_layer": main_res["misses_per_layer"],
+        "mib_copied_per_token": main_res["mib_copied_per_token"],
+        "sweep": sweep, "roofline": None, "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
 
 
 def mixer_bench(args):

@@ -15,7 +15,7 @@ from ._ffi import (  # noqa: F401
     moe_pack_experts_device, moe_residual_rmsnorm, moe_rmsnorm, moe_router_topk,
     moe_status_string, moe_version, moe_workspace_bytes, moe_workspace_routing,
     moe_gdn_desc, moe_attn_desc, make_gdn_desc, make_attn_desc, moe_gdn_decode,
-    moe_attn_workspace_bytes, moe_attn_decode,
+    moe_attn_workspace_bytes, moe_attn_decode, MoePool, MOE_POOL_HOST_ONLY,
 )
 
 

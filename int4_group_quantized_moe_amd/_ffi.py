@@ -101,6 +101,13 @@ class moe_attn_desc(ctypes.Structure):
     ]
 
 
+class moe_pool_stats_t(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("requests", "lookups", "hits", "misses",
+                                              "evictions", "bytes_copied")]
+
+
+MOE_POOL_HOST_ONLY = 1
+
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
@@ -128,6 +135,12 @@ _SIGS = {
     "moe_gdn_decode": ([_GDESC, _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "moe_attn_workspace_bytes": ([_ADESC], ctypes.c_size_t),
     "moe_attn_decode": ([_ADESC, _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+    "moe_pool_create": ([_DESC, _I32, _I32, _P, _I64, _P, _P, ctypes.c_uint32,
+                         ctypes.POINTER(_P)], ctypes.c_int),
+    "moe_pool_require": ([_P, _I32, _P, _I32, _P, _P], ctypes.c_int),
+    "moe_pool_stats": ([_P, ctypes.POINTER(moe_pool_stats_t)], ctypes.c_int),
+    "moe_pool_slot": ([_P, _I32, _I32], ctypes.c_int32),
+    "moe_pool_destroy": ([_P], None),
     "moe_chain_forward": ([_DESC, _I32, _P, _P, _P, _P, _P, _P, _I64, _P, _P, _P, _P],
                           ctypes.c_int),
 }
@@ -318,3 +331,55 @@ def moe_attn_decode(desc, q, gate, k_cache, v_cache, lengths, out, ws, stream=No
     _check(lib().moe_attn_decode(ctypes.byref(desc), _ptr(q), _ptr(gate), _ptr(k_cache),
                                  _ptr(v_cache), _ptr(lengths), _ptr(out), _ptr(ws),
                                  _stream(stream)), "moe_attn_decode")
+
+
+# ---------------------------------------------------------------------------
+# expert slot pool (include/moe_pool.h)
+
+
+class MoePool:
+    """A moe_pool handle (host object); destroyed with the Python object."""
+
+    def __init__(self, desc, n_layers, n_slots, host_pack=None, host_stride=0, device_slab=None,
+                 slot_tables=None, host_only=False):
+        self._h = _P()
+        _check(lib().moe_pool_create(ctypes.byref(desc), n_layers, n_slots, _ptr(host_pack),
+                                     int(host_stride), _ptr(device_slab), _ptr(slot_tables),
+                                     MOE_POOL_HOST_ONLY if host_only else 0,
+                                     ctypes.byref(self._h)), "moe_pool_create")
+
+    def require(self, layer, experts, stream=None) -> int:
+        """Makes the experts (a sequence of ints) of `layer` resident; returns the misses."""
+        arr = (ctypes.c_int32 * max(len(experts), 1))(*[int(e) for e in experts])
+        missed = ctypes.c_int32(0)
+        st = lib().moe_pool_require(self._h, layer, ctypes.cast(arr, _P), len(experts),
+                                    ctypes.cast(ctypes.byref(missed), _P),
+                                    _stream(stream) if self._needs_stream(stream) else None)
+        _check(st, "moe_pool_require")
+        return int(missed.value)
+
+    @staticmethod
+    def _needs_stream(stream):
+        if stream is not None:
+            return True
+        try:
+            import torch
+            return torch.cuda.is_available()
+        except ImportError:
+            return False
+
+    def stats(self) -> dict:
+        out = moe_pool_stats_t()
+        _check(lib().moe_pool_stats(self._h, ctypes.byref(out)), "moe_pool_stats")
+        return {n: int(getattr(out, n)) for n, _ in moe_pool_stats_t._fields_}
+
+    def slot(self, layer, expert) -> int:
+        return int(lib().moe_pool_slot(self._h, layer, expert))
+
+    def __del__(self):
+        try:
+            if self._h:
+                lib().moe_pool_destroy(self._h)
+                self._h = _P()
+        except Exception:  # noqa: BLE001  (interpreter shutdown)
+            pass

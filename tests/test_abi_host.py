@@ -52,7 +52,7 @@ def test_every_export_cites_its_passage():
     it, or says that it is not on the pages."""
     src = "\n".join(header_sources())
     for n in header_functions():
-        m = re.search(r"/\*((?:(?!\*/).)*?)\*/\s*(?:const char\*|int|size_t)\s+" + n + r"\s*\(",
+        m = re.search(r"/\*((?:(?!\*/).)*?)\*/\s*(?:const char\*|int|size_t|int32_t|void)\s+" + n + r"\s*\(",
                       src, flags=re.S)
         assert m, n
         doc = m.group(1)
