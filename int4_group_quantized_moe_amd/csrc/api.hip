@@ -35,6 +35,11 @@ int enqueue_router(const moe_layer_desc* d, const void* x, const float* router_w
   a.E = d->n_experts;
   a.k = d->top_k;
   a.act = d->act_dtype;
+  if (one_block_path(*d)) {
+    a.x16 = reinterpret_cast<uint16_t*>(ws + P.x16);
+    a.xe = reinterpret_cast<int32_t*>(ws + P.xe);
+    a.x16_bits = d->bits;
+  }
   return to_status(launch_router_topk(a, s));
 }
 
@@ -86,9 +91,10 @@ int enqueue_experts(const moe_layer_desc* d, const void* x, const int32_t* idx, 
                     const float* gamma, const void* slab, const int32_t* slot_table,
                     const void* shared_blob, void* out, uint8_t* ws, hipStream_t s,
                     int epi = 0, void* x_res = nullptr, void* x_hat_next = nullptr,
-                    bool xsum_ready = false) {
+                    bool xsum_ready = false, bool x16_ready = false) {
   ExpertArgs a{};
   a.xsum_ready = xsum_ready;
+  a.x16_ready = x16_ready;
   a.epi = epi;
   a.x_res = x_res;
   a.x_hat_next = x_hat_next;
@@ -120,6 +126,7 @@ int enqueue_experts(const moe_layer_desc* d, const void* x, const int32_t* idx, 
 // Whether the router of a layer call writes the activations' group sums the
 // grouped GEMMs need (both run on the matrix cores), and where.
 float* router_xsum(const moe_layer_desc* d, uint8_t* ws) {
+  if (one_block_path(*d)) return nullptr;  // those GEMMs fold the group bias into the weights
   const bool sh = (d->flags & MOE_FLAG_SHARED) != 0;
   const WsPlan P = make_ws_plan(*d);
   const bool mfma = P.bucketed && prefill_supported(d->act_dtype, d->hidden, d->inter,
@@ -150,7 +157,8 @@ int chain_layer_bucketed(const moe_layer_desc* desc, void* x, void* x_hat, const
   MOE_TRY(enqueue_router(desc, x_hat, router_w, router_bias, wsg, idx, w,
                          shared ? gamma : nullptr, w8, stream, xsum));
   return enqueue_experts(desc, x_hat, idx, w, shared ? gamma : nullptr, expert_slab, slot_table,
-                         shared_blob, out, w8, stream, last ? 1 : 2, x, x_hat, xsum != nullptr);
+                         shared_blob, out, w8, stream, last ? 1 : 2, x, x_hat, xsum != nullptr,
+                         true);
 }
 
 }  // namespace
@@ -259,7 +267,8 @@ int moe_layer_forward(const moe_layer_desc* desc, const void* x, const float* ro
   MOE_TRY(enqueue_router(desc, x, router_w, router_bias, wsg, idx, w, shared ? gamma : nullptr, w8,
                          stream, xsum));
   return enqueue_experts(desc, x, idx, w, shared ? gamma : nullptr, expert_slab, slot_table,
-                         shared_blob, out, w8, stream, 0, nullptr, nullptr, xsum != nullptr);
+                         shared_blob, out, w8, stream, 0, nullptr, nullptr, xsum != nullptr,
+                         true);
 }
 
 int moe_residual_rmsnorm(const moe_layer_desc* desc, void* x_res, const void* out,

@@ -1082,6 +1082,8 @@ hipError_t launch_experts_t(const ExpertArgs& a, hipStream_t s) {
   const int min_rows = a.mfma ? kMfmaMinRows : 0x7FFFFFFF;
   // one token block: buckets (and the MFMA tile list) in one launch
   const bool small_batch = nblk == 1 && a.E < 1024;
+  const bool one_block =
+      a.mfma && small_batch && batched_supported(a.act, a.T, a.H, a.L.inter, Is, a.has_shared);
   if (small_batch) {
     hipLaunchKernelGGL(bucket_small_kernel, dim3(1), dim3(1024), 0, s, a.topk_idx, counts,
                        offsets, pairs, small_list, n_small, a.mfma ? tiles : nullptr, ntiles,
@@ -1116,6 +1118,9 @@ hipError_t launch_experts_t(const ExpertArgs& a, hipStream_t s) {
     pa.ntiles = ntiles;
     pa.tiles_ready = small_batch;
     pa.xsum_ready = a.xsum_ready;
+    pa.x16 = reinterpret_cast<uint16_t*>(a.ws + P.x16);
+    pa.xe = reinterpret_cast<int32_t*>(a.ws + P.xe);
+    pa.x16_ready = a.x16_ready;
     pa.max_tiles = P.max_tiles;
     pa.L = a.L;
     pa.Ls = a.Ls;
@@ -1128,7 +1133,7 @@ hipError_t launch_experts_t(const ExpertArgs& a, hipStream_t s) {
     pa.bits = a.bits;
     pa.has_shared = a.has_shared;
     pa.min_rows = kMfmaMinRows;
-    if ((e = launch_prefill(pa, s)) != hipSuccess) return e;
+    if ((e = one_block ? launch_batched(pa, s) : launch_prefill(pa, s)) != hipSuccess) return e;
   }
   // the bucketed GEMVs own the buckets below the MFMA threshold (none when
   // every bucket of at least one token runs on the grouped GEMMs)

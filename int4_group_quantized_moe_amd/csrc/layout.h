@@ -20,6 +20,7 @@ constexpr int kDecodeMaxTokens = 8;    // up to this many tokens: per-pair GEMV 
 // wave rows and the grouped GEMMs' time is per-tile latency, not work
 constexpr int kMfmaMinRows = 1;
 constexpr int kMfmaTileRows = 128;  // rows (bucket entries) per grouped-GEMM tile
+constexpr int kOneBlockTokens = 64;  // batches up to this size: every bucket fits one 64-row tile
 
 constexpr int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
@@ -70,6 +71,7 @@ struct WsPlan {
   size_t xw, lw, hw;  // persistent-chain exchange words (batch 1)
   size_t ctr;         // persistent-chain epoch, then status word
   size_t tiles, ntiles;    // grouped-GEMM tile list (large batches)
+  size_t x16, xe;          // one token block: activations in fp16 and their row exponents
   int max_tiles;
   size_t total;
   bool bucketed;
@@ -111,6 +113,9 @@ inline WsPlan make_ws_plan(const moe_layer_desc& d) {
   p.max_tiles = (int)((T * k + T) / 128 + E + 2);
   p.tiles = take(p.bucketed ? sizeof(int32_t) * 2 * p.max_tiles : 0);
   p.ntiles = take(p.bucketed ? sizeof(int32_t) : 0);
+  const bool one_block = p.bucketed && T <= kOneBlockTokens;
+  p.x16 = take(one_block ? sizeof(uint16_t) * T * H : 0);
+  p.xe = take(one_block ? sizeof(int32_t) * T : 0);
   if (T == 1) {
     p.xw = take(sizeof(uint64_t) * (H / 2));
     p.lw = take(sizeof(uint64_t) * (E + 1));

@@ -77,6 +77,53 @@ __device__ __forceinline__ float warp_sum(float v) {
 
 namespace moe {
 
+// One wave converts a bf16 activation row of H values (H a multiple of 512)
+// to fp16 after a power-of-two scale: x16 = x * 2^-e, with e the exponent of
+// the row's largest magnitude minus 14 (0 for a zero row), so the largest
+// value lies in [2^14, 2^15) and every bf16 value at or above 2^-28 of it
+// converts exactly.  Within each chunk of 8 columns the values are stored in
+// the K order of the codes' fp16 expansion: (0, 4, 1, 5, 2, 6, 3, 7) for int4
+// and (0, 2, 1, 3, 4, 6, 5, 7) for int8.  Lane 0 writes e.
+__device__ __forceinline__ void x16_row(const uint16_t* __restrict__ xr, uint16_t* __restrict__ x16r,
+                                        int32_t* __restrict__ e_out, int H, int bits) {
+  const int lane = threadIdx.x & 63;
+  uint32_t m = 0;
+  for (int c = lane; c < H / 8; c += 64) {
+    const uint4 v = reinterpret_cast<const uint4*>(xr)[c];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = max(m, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+  // bf16 magnitude bits: exponent field in bits 7..14
+  int e = m == 0 ? 0 : (int)(m >> 7) - 127 - 14;
+  e = e < -100 ? -100 : (e > 100 ? 100 : e);
+  const float sc = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e
+  for (int c = lane; c < H / 8; c += 64) {
+    const uint4 v = reinterpret_cast<const uint4*>(xr)[c];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    _Float16 f[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = (_Float16)(bf16_bits_to_f32(w[i] & 0xFFFFu) * sc);
+      f[2 * i + 1] = (_Float16)(bf16_bits_to_f32(w[i] >> 16) * sc);
+    }
+    // stored slot j holds natural position p(j)
+    const int p4[8] = {0, 4, 1, 5, 2, 6, 3, 7}, p8[8] = {0, 2, 1, 3, 4, 6, 5, 7};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const _Float16 lo = bits == 4 ? f[p4[2 * i]] : f[p8[2 * i]];
+      const _Float16 hi = bits == 4 ? f[p4[2 * i + 1]] : f[p8[2 * i + 1]];
+      o[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+             ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+    reinterpret_cast<uint4*>(x16r)[c] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+  if (lane == 0) *e_out = e;
+}
+
 struct RouterArgs {
   const void* x;
   const float* router_w;
@@ -87,6 +134,9 @@ struct RouterArgs {
   float* topk_w;
   float* gamma;           // may be null
   float* xsum;            // [T x H/64] group sums of x, written by the MFMA router if non-null
+  uint16_t* x16;          // if non-null, the top-k kernel also writes x in fp16 (x16_row)
+  int32_t* xe;            //   and the rows' exponents; x16_bits selects the K order
+  int x16_bits;
   int T, H, E, k, act;
 };
 hipError_t launch_router_topk(const RouterArgs& a, hipStream_t s);
@@ -120,6 +170,7 @@ struct ExpertArgs {
   void* x_hat_next;
   float eps;
   bool xsum_ready;               // the router already wrote the group sums of x
+  bool x16_ready;                // the router's top-k kernel already wrote x16 / xe
 };
 hipError_t launch_experts(const ExpertArgs& a, hipStream_t s);
 
@@ -139,6 +190,9 @@ struct PrefillArgs {
   float* xsum;                   // [T][H/64] group sums of x
   float* hsum;                   // [T*k][I/64] then [T][Is/64] group sums of h
   float* partial;                // fp32 [T*(k+1)*H]
+  uint16_t* x16;                 // one token block: x in fp16 (x16_row) and row exponents
+  int32_t* xe;
+  bool x16_ready;                // written by the router's top-k kernel
   void* out;
   int32_t* tiles;
   int32_t* ntiles;
@@ -152,6 +206,24 @@ struct PrefillArgs {
 };
 bool prefill_supported(int act, int H, int I, int Is, bool has_shared);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
+// group sums of the activations: xsum[t][g] = sum of x[t][64 g .. 64 g + 63]
+hipError_t launch_group_sum(const uint16_t* x, float* xsum, int T, int H, hipStream_t s);
+// One token block (T <= 64): the same GEMMs with every weight tile requested
+// up front (batched.hip); h is written as fp32 rows of `inter` floats.
+bool batched_supported(int act, int T, int H, int I, int Is, bool has_shared);
+hipError_t launch_batched(const PrefillArgs& a, hipStream_t s);
+// x16 / xe of a batch (one wave per row) when the router did not write them
+hipError_t launch_x16(const uint16_t* x, uint16_t* x16, int32_t* xe, int T, int H, int bits,
+                      hipStream_t s);
+// Whether a layer call runs the one-token-block grouped GEMMs (and so needs
+// x16 / xe): bf16 batches of 9..64 tokens on the MFMA path.
+inline bool one_block_path(const moe_layer_desc& d) {
+  const bool sh = (d.flags & MOE_FLAG_SHARED) != 0;
+  const int Is = sh ? d.shared_inter : 0;
+  return d.n_tokens > kDecodeMaxTokens && d.n_tokens <= kOneBlockTokens && d.n_experts < 1024 &&
+         prefill_supported(d.act_dtype, d.hidden, d.inter, sh ? Is : d.inter, sh) &&
+         batched_supported(d.act_dtype, d.n_tokens, d.hidden, d.inter, Is, sh);
+}
 
 // Batch-1 bf16 decode fast path: three kernels per layer (router with an
 // optional fused RMSNorm; top-k + gate/up; down + combine with an optional

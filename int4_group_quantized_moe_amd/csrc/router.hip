@@ -127,24 +127,22 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const void* __restrict
   }
 }
 
-// One wave per token: the exact wavefront top-k (threshold from DPP wave
-// maxima, ballot compaction, rank; k rounds of argmax when more than 64
-// logits tie at the threshold), then the softmax over the k selected logits.
+// Top-k of token t by one wave: the exact wavefront top-k (threshold from
+// DPP wave maxima, ballot compaction, rank; k rounds of argmax when more than
+// 64 logits tie at the threshold), then the softmax over the k selected
+// logits.  The LDS arrays are the wave's own.  With x16, the wave also writes
+// the token's activation row in fp16 (x16_row).
 template <int MPL>
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits,
-                                                   int32_t* __restrict__ topk_idx,
-                                                   float* __restrict__ topk_w,
-                                                   float* __restrict__ gamma, int T, int E,
-                                                   int k, int has_gate, int nplanes) {
-  __shared__ int32_t sel_idx[4][MOE_MAX_TOP_K];
-  __shared__ float sel_val[4][MOE_MAX_TOP_K], sel_w[4][MOE_MAX_TOP_K], gam[4];
-  __shared__ __align__(16) uint32_t cand_key[4][64];
-  __shared__ __align__(16) int32_t cand_idx[4][64];
-  __shared__ float cand_val[4][64];
-  __shared__ float lsum[4][MPL * 64 + 1];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t = blockIdx.x * (int)(blockDim.x >> 6) + wave;
-  if (t >= T) return;
+__device__ __forceinline__ void topk_token(const float* __restrict__ logits, int32_t* __restrict__ topk_idx,
+                                           float* __restrict__ topk_w, float* __restrict__ gamma,
+                                           int T, int E, int k, int has_gate, int nplanes, int t,
+                                           int32_t* sel_idx, float* sel_val, float* sel_w,
+                                           float* gam, uint32_t* cand_key, int32_t* cand_idx,
+                                           float* cand_val, float* lsum,
+                                           const uint16_t* __restrict__ xsrc,
+                                           uint16_t* __restrict__ x16, int32_t* __restrict__ xe,
+                                           int H, int x16_bits) {
+  const int lane = threadIdx.x & 63;
   const float* lt = logits + (int64_t)t * (E + 1);
   if (nplanes > 1) {
     // logits split over K planes: add them in plane order (row E, the
@@ -172,19 +170,46 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 #pragma unroll
     for (int m = 0; m <= MPL; ++m) {
       const int e = lane + 64 * m;
-      if (e <= E) lsum[wave][e] = v[m];
+      if (e <= E) lsum[e] = v[m];
     }
     dec::lds_wave_sync();
-    lt = lsum[wave];
+    lt = lsum;
   }
-  dec::wave_topk<MPL>(lt, E, k, has_gate != 0, sel_idx[wave],
-                      sel_val[wave], sel_w[wave], &gam[wave], cand_key[wave], cand_idx[wave],
-                      cand_val[wave]);
+  dec::wave_topk<MPL>(lt, E, k, has_gate != 0, sel_idx, sel_val, sel_w, gam, cand_key, cand_idx,
+                      cand_val);
   if (lane < k) {
-    topk_idx[(int64_t)t * k + lane] = sel_idx[wave][lane];
-    topk_w[(int64_t)t * k + lane] = sel_w[wave][lane];
+    topk_idx[(int64_t)t * k + lane] = sel_idx[lane];
+    topk_w[(int64_t)t * k + lane] = sel_w[lane];
   }
-  if (lane == 0 && has_gate && gamma != nullptr) gamma[t] = gam[wave];
+  if (lane == 0 && has_gate && gamma != nullptr) gamma[t] = *gam;
+  // the token's activation row in fp16 for the one-token-block grouped GEMMs
+  if (x16 != nullptr)
+    x16_row(xsrc + (int64_t)t * H, x16 + (int64_t)t * H, xe + t, H, x16_bits);
+  dec::lds_wave_sync();  // the wave's LDS may be reused for its next token
+}
+
+// One wave per token.
+template <int MPL>
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits,
+                                                   int32_t* __restrict__ topk_idx,
+                                                   float* __restrict__ topk_w,
+                                                   float* __restrict__ gamma, int T, int E,
+                                                   int k, int has_gate, int nplanes,
+                                                   const uint16_t* __restrict__ xsrc,
+                                                   uint16_t* __restrict__ x16,
+                                                   int32_t* __restrict__ xe, int H, int x16_bits) {
+  __shared__ int32_t sel_idx[4][MOE_MAX_TOP_K];
+  __shared__ float sel_val[4][MOE_MAX_TOP_K], sel_w[4][MOE_MAX_TOP_K], gam[4];
+  __shared__ __align__(16) uint32_t cand_key[4][64];
+  __shared__ __align__(16) int32_t cand_idx[4][64];
+  __shared__ float cand_val[4][64];
+  __shared__ float lsum[4][MPL * 64 + 1];
+  const int wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * (int)(blockDim.x >> 6) + wave;
+  if (t >= T) return;
+  topk_token<MPL>(logits, topk_idx, topk_w, gamma, T, E, k, has_gate, nplanes, t, sel_idx[wave],
+                  sel_val[wave], sel_w[wave], &gam[wave], cand_key[wave], cand_idx[wave],
+                  cand_val[wave], lsum[wave], xsrc, x16, xe, H, x16_bits);
 }
 
 hipError_t launch_topk(const RouterArgs& a, hipStream_t s, int nplanes) {
@@ -193,15 +218,16 @@ hipError_t launch_topk(const RouterArgs& a, hipStream_t s, int nplanes) {
   const int wpb = a.T <= 1024 ? 1 : 4;
   const dim3 grid((a.T + wpb - 1) / wpb), block(64 * wpb);
   const int hg = a.shared_gate_w ? 1 : 0;
+  const uint16_t* xs = reinterpret_cast<const uint16_t*>(a.x);
   if (a.E <= 256)
     hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, a.logits, a.topk_idx, a.topk_w,
-                       a.gamma, a.T, a.E, a.k, hg, nplanes);
+                       a.gamma, a.T, a.E, a.k, hg, nplanes, xs, a.x16, a.xe, a.H, a.x16_bits);
   else if (a.E <= 512)
     hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, s, a.logits, a.topk_idx, a.topk_w,
-                       a.gamma, a.T, a.E, a.k, hg, nplanes);
+                       a.gamma, a.T, a.E, a.k, hg, nplanes, xs, a.x16, a.xe, a.H, a.x16_bits);
   else
     hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, a.logits, a.topk_idx, a.topk_w,
-                       a.gamma, a.T, a.E, a.k, hg, nplanes);
+                       a.gamma, a.T, a.E, a.k, hg, nplanes, xs, a.x16, a.xe, a.H, a.x16_bits);
   return hipGetLastError();
 }
 
@@ -258,9 +284,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
   const float* wrow = (gate_row ? wsg : W + (int64_t)(e < E ? e : 0) * H) + k0 + 32 * half;
   const int S = kseg / 64;
 
-  uint4 ra[2];
-  float4 rb[8];
-  auto load_stage = [&](int st) {
+  auto load_stage = [&](int st, uint4 (&ra)[2], float4 (&rb)[8]) {
 #pragma unroll
     for (int q = 0; q < 2; ++q)
       ra[q] = srow_ok ? reinterpret_cast<const uint4*>(xrow + st * 64)[q] : make_uint4(0, 0, 0, 0);
@@ -282,7 +306,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
             (bf16_bits_to_f32(v.z & 0xFFFFu) + bf16_bits_to_f32(v.z >> 16))) +
            (bf16_bits_to_f32(v.w & 0xFFFFu) + bf16_bits_to_f32(v.w >> 16));
   };
-  auto store_stage = [&](int buf, int st) {
+  auto store_stage = [&](int buf, int st, const uint4 (&ra)[2]) {
     uint16_t* dst = A + buf * kRouterTile * kRouterLdsRow + sr * kRouterLdsRow + 16 * sq;
 #pragma unroll
     for (int q = 0; q < 2; ++q) *reinterpret_cast<uint4*>(dst + 8 * q) = ra[q];
@@ -301,17 +325,10 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
       if (sq == 0 && srow_ok) xsum[(int64_t)(t0 + sr) * (H / 64) + k0 / 64 + st] = s;
     }
   };
-
+  // one stage of products: the fp32 router weights split exactly into three
+  // bf16 parts, smallest first
   rf32x16 acc = {};
-  load_stage(0);
-  store_stage(0, 0);
-  __syncthreads();
-  for (int st = 0; st < S; ++st) {
-    float4 cb[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) cb[i] = rb[i];
-    if (st + 1 < S) load_stage(st + 1);
-    const uint16_t* As = A + (st & 1) * kRouterTile * kRouterLdsRow;
+  auto multiply = [&](const uint16_t* As, const float4 (&cb)[8]) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const ru32x4 a = *reinterpret_cast<const ru32x4*>(
@@ -330,8 +347,23 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(rbf16x8, b2), acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(rbf16x8, b1), acc, 0, 0, 0);
     }
-    if (st + 1 < S) store_stage((st + 1) & 1, st + 1);
+  };
+
+  {
+    uint4 ra[2];
+    float4 rb[8];
+    load_stage(0, ra, rb);
+    store_stage(0, 0, ra);
     __syncthreads();
+    for (int st = 0; st < S; ++st) {
+      float4 cb[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) cb[i] = rb[i];
+      if (st + 1 < S) load_stage(st + 1, ra, rb);
+      multiply(A + (st & 1) * kRouterTile * kRouterLdsRow, cb);
+      if (st + 1 < S) store_stage((st + 1) & 1, st + 1, ra);
+      __syncthreads();
+    }
   }
   if (!e_ok) return;
   const float b = (bias != nullptr && blockIdx.z == 0 && e < E) ? bias[e] : 0.0f;
@@ -395,10 +427,11 @@ hipError_t launch_router_act(const RouterArgs& a, hipStream_t s) {
     const int ytiles = (a.T + kRouterTile - 1) / kRouterTile;
     const bool fold = a.shared_gate_w != nullptr &&
                       (gtiles == etiles || gtiles * ytiles * nplanes <= kRouterFoldMaxBlocks);
-    hipLaunchKernelGGL(router_mfma_kernel, dim3(fold ? gtiles : etiles, ytiles, nplanes),
-                       dim3(256), 0, s, reinterpret_cast<const uint16_t*>(a.x), a.router_w,
-                       a.router_bias, fold ? a.shared_gate_w : nullptr, a.logits, a.xsum, a.T,
-                       a.H, a.E, a.H / nplanes);
+    const dim3 grid(fold ? gtiles : etiles, ytiles, nplanes);
+    const uint16_t* xb = reinterpret_cast<const uint16_t*>(a.x);
+    const float* wg = fold ? a.shared_gate_w : nullptr;
+    hipLaunchKernelGGL(router_mfma_kernel, grid, dim3(256), 0, s, xb, a.router_w, a.router_bias,
+                       wg, a.logits, a.xsum, a.T, a.H, a.E, a.H / nplanes);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.shared_gate_w != nullptr && !fold) {

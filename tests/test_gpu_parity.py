@@ -765,3 +765,31 @@ def test_bf16_bucketed_gemv_hidden_384(T, bits):
     check_layer(cfg, 0, x_np, out, idx, wt, g, f"H=384 T={T} int{bits}")
     del w
     _free()
+
+
+@pytest.mark.parametrize("cfgname,T,hidden", [("batched_80b", 9, 2048), ("batched_80b", 33, 2048),
+                                              ("batched_80b_int8", 47, 2048),
+                                              ("decode_35b", 40, 2048),
+                                              ("batched_80b", 24, 1024),
+                                              ("batched_80b_int8", 64, 1024)])
+def test_one_block_grouped_gemms(cfgname, T, hidden):
+    """Batches of 9..64 bf16 tokens (one token block) run the grouped GEMMs
+    whose workgroups request their whole weight tile up front: ragged buckets
+    of 1..64 rows (one or two 32-row MFMA blocks), the shared expert's T rows,
+    hidden 2048 and 1024 (8 or 4 quantisation groups per wave), int4 and
+    int8; every output row and the routing against the oracle, and a second
+    call bit-equal to the first."""
+    wl = _wl()
+    cfg = configs.CONFIGS[cfgname].with_(n_tokens=T, hidden=hidden)
+    say(f"[one block] {cfgname} T={T} H={hidden}")
+    w = wl.Workload(cfg, n_layers=1)
+    x_np = oracle.chain_prologue(synth.activations(cfg), cfg.rms_eps, "bf16").astype(np.float32)
+    x = wl.act_tensor(cfg, x_np)
+    out, idx, wt, g = run_layer(w, cfg, x)
+    counts = np.bincount(idx.cpu().numpy().ravel(), minlength=cfg.n_experts)
+    say(f"  {np.count_nonzero(counts)} experts, largest bucket {counts.max()}")
+    check_layer(cfg, 0, x_np, out, idx, wt, g, f"{cfgname} T={T} H={hidden}")
+    out2 = run_layer(w, cfg, x)[0]
+    assert torch.equal(out, out2)
+    del w
+    _free()
