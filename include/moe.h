@@ -90,8 +90,8 @@ enum moe_flags {
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_HIDDEN 8192
 #define MOE_MAX_INTER 4096
-/* Device scratch of moe_layer_forward_noalloc, per GPU (16 MiB). */
-#define MOE_NOALLOC_SCRATCH_BYTES (16u << 20)
+/* Device scratch of moe_layer_forward_noalloc, per GPU (32 MiB). */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
 
 /*
  * Shape and format of one MoE layer.  Host memory, read at call time only.
@@ -372,7 +372,7 @@ int moe_chain_forward(const moe_layer_desc* desc, int32_t n_layers, void* x,
  * first call on each device.  It allocates and frees nothing.
  * Limit: calls whose moe_workspace_bytes(desc) exceeds
  * MOE_NOALLOC_SCRATCH_BYTES return MOE_ERR_TOO_LARGE before anything is
- * enqueued (at hidden 2048, 512 experts, top-10, inter 512: up to 128
+ * enqueued (at hidden 2048, 512 experts, top-10, inter 512: up to 251
  * tokens).  Every call on a GPU shares that GPU's scratch, which keeps the
  * last call's contents: calls that overlap on one GPU (other streams, other
  * threads) race and must be serialised by the caller.  The routing stays in

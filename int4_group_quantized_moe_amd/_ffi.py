@@ -21,7 +21,7 @@ MOE_ERR_MISALIGNED = -3
 MOE_ERR_NO_DEVICE = -4
 MOE_ERR_LAUNCH = -5
 MOE_ERR_TOO_LARGE = -6
-MOE_NOALLOC_SCRATCH_BYTES = 16 << 20
+MOE_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 MOE_ACT_F32 = 0
 MOE_ACT_BF16 = 1

@@ -18,10 +18,9 @@ int to_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; 
 
 int enqueue_router(const moe_layer_desc* d, const void* x, const float* router_w,
                    const float* router_bias, const float* wsg, int32_t* idx, float* w,
-                   float* gamma, uint8_t* ws, hipStream_t s, float* xsum = nullptr) {
+                   float* gamma, uint8_t* ws, hipStream_t s) {
   const WsPlan P = make_ws_plan(*d);
   RouterArgs a{};
-  a.xsum = xsum;
   a.x = x;
   a.router_w = router_w;
   a.router_bias = (d->flags & MOE_FLAG_ROUTER_BIAS) ? router_bias : nullptr;
@@ -35,7 +34,7 @@ int enqueue_router(const moe_layer_desc* d, const void* x, const float* router_w
   a.E = d->n_experts;
   a.k = d->top_k;
   a.act = d->act_dtype;
-  if (one_block_path(*d)) {
+  if (mfma_path(*d)) {
     a.x16 = reinterpret_cast<uint16_t*>(ws + P.x16);
     a.xe = reinterpret_cast<int32_t*>(ws + P.xe);
     a.x16_bits = d->bits;
@@ -91,9 +90,8 @@ int enqueue_experts(const moe_layer_desc* d, const void* x, const int32_t* idx, 
                     const float* gamma, const void* slab, const int32_t* slot_table,
                     const void* shared_blob, void* out, uint8_t* ws, hipStream_t s,
                     int epi = 0, void* x_res = nullptr, void* x_hat_next = nullptr,
-                    bool xsum_ready = false, bool x16_ready = false) {
+                    bool x16_ready = false) {
   ExpertArgs a{};
-  a.xsum_ready = xsum_ready;
   a.x16_ready = x16_ready;
   a.epi = epi;
   a.x_res = x_res;
@@ -119,21 +117,8 @@ int enqueue_experts(const moe_layer_desc* d, const void* x, const int32_t* idx, 
   a.k = d->top_k;
   a.act = d->act_dtype;
   a.bits = d->bits;
-  a.mfma = a.plan.bucketed && prefill_supported(a.act, a.H, d->inter, a.Ls.inter, a.has_shared);
+  a.mfma = a.plan.bucketed && prefill_supported(a.act, a.T, a.H, d->inter, a.Ls.inter, a.has_shared);
   return to_status(launch_experts(a, s));
-}
-
-// Whether the router of a layer call writes the activations' group sums the
-// grouped GEMMs need (both run on the matrix cores), and where.
-float* router_xsum(const moe_layer_desc* d, uint8_t* ws) {
-  if (one_block_path(*d)) return nullptr;  // those GEMMs fold the group bias into the weights
-  const bool sh = (d->flags & MOE_FLAG_SHARED) != 0;
-  const WsPlan P = make_ws_plan(*d);
-  const bool mfma = P.bucketed && prefill_supported(d->act_dtype, d->hidden, d->inter,
-                                                    sh ? d->shared_inter : d->inter, sh);
-  return mfma && router_uses_mfma(d->act_dtype, d->n_tokens, d->hidden)
-             ? reinterpret_cast<float*>(ws + P.xsum)
-             : nullptr;
 }
 
 // One layer of a bucketed chain (T > kDecodeMaxTokens): router and experts on
@@ -153,12 +138,10 @@ int chain_layer_bucketed(const moe_layer_desc* desc, void* x, void* x_hat, const
     const BlobLayout Ls = make_layout(desc->bits, desc->hidden, desc->shared_inter);
     wsg = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(shared_blob) + Ls.sg_off);
   }
-  float* xsum = router_xsum(desc, w8);
   MOE_TRY(enqueue_router(desc, x_hat, router_w, router_bias, wsg, idx, w,
-                         shared ? gamma : nullptr, w8, stream, xsum));
+                         shared ? gamma : nullptr, w8, stream));
   return enqueue_experts(desc, x_hat, idx, w, shared ? gamma : nullptr, expert_slab, slot_table,
-                         shared_blob, out, w8, stream, last ? 1 : 2, x, x_hat, xsum != nullptr,
-                         true);
+                         shared_blob, out, w8, stream, last ? 1 : 2, x, x_hat, true);
 }
 
 }  // namespace
@@ -263,12 +246,10 @@ int moe_layer_forward(const moe_layer_desc* desc, const void* x, const float* ro
     const BlobLayout Ls = make_layout(desc->bits, desc->hidden, desc->shared_inter);
     wsg = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(shared_blob) + Ls.sg_off);
   }
-  float* xsum = router_xsum(desc, w8);
   MOE_TRY(enqueue_router(desc, x, router_w, router_bias, wsg, idx, w, shared ? gamma : nullptr, w8,
-                         stream, xsum));
+                         stream));
   return enqueue_experts(desc, x, idx, w, shared ? gamma : nullptr, expert_slab, slot_table,
-                         shared_blob, out, w8, stream, 0, nullptr, nullptr, xsum != nullptr,
-                         true);
+                         shared_blob, out, w8, stream, 0, nullptr, nullptr, true);
 }
 
 int moe_residual_rmsnorm(const moe_layer_desc* desc, void* x_res, const void* out,

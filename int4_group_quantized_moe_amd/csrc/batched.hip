@@ -76,45 +76,6 @@ __device__ __forceinline__ void bt_lds_barrier() {
 constexpr int kBgChunk = 4;   // quantisation groups (256 columns) per staged activation chunk
 constexpr int kBgStages = 3;  // activation chunks in LDS (two in flight while one is used)
 
-// (scale, bias) word -> the fp16 pairs (S, S), (B, B) of w = S c + B, with c
-// the code's fp16 expansion (int4: c = 1 + q/16, so S = 16 s and B = b - 16 s;
-// int8: c = q, so S = s and B = b).
-template <int BITS>
-__device__ __forceinline__ void sb_f16(uint32_t sb, f16x2& S2, f16x2& B2) {
-  const float sc = bf16_bits_to_f32(sb & 0xFFFFu), bi = bf16_bits_to_f32(sb >> 16);
-  const _Float16 S = (_Float16)(BITS == 4 ? 16.0f * sc : sc);
-  const _Float16 B = (_Float16)(BITS == 4 ? bi - 16.0f * sc : bi);
-  S2 = f16x2{S, S};
-  B2 = f16x2{B, B};
-}
-
-// MFMA operand of K step kk: the lane's 8 weights of the step in fp16, in the
-// fp16 expansion's K order (int4 (0, 4, 1, 5, 2, 6, 3, 7); int8 (0, 2, 1, 3, 4,
-// 6, 5, 7) within the 8 codes).
-template <int BITS>
-__device__ __forceinline__ u32x4 w_frag_f16(const LaneCodes<BITS>& q, int kk, f16x2 S2, f16x2 B2) {
-  u32x4 c;
-  if constexpr (BITS == 4) {
-    const uint32_t d = kk == 0 ? q.q[0].x : kk == 1 ? q.q[0].y : kk == 2 ? q.q[0].z : q.q[0].w;
-    c = code_frag4_f16(d);
-  } else {
-    const uint4 v = q.q[kk >> 1];
-    c = (kk & 1) ? code_frag8_f16(v.z, v.w) : code_frag8_f16(v.x, v.y);
-  }
-  // (each element is taken as a value before its bit cast: a bit cast applied
-  // to an indexed vector element directly has been seen to read element 0)
-  uint32_t r[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t ci = c[i];
-    r[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(f16x2, ci), S2, B2));
-  }
-  return u32x4{r[0], r[1], r[2], r[3]};
-}
-
-// 2^e as a float (|e| <= 100)
-__device__ __forceinline__ float exp2i(int e) { return __uint_as_float((uint32_t)(127 + e) << 23); }
-
 // LDS of a gate/up workgroup for K = 64 G.
 template <int G>
 struct BgLds {

@@ -1111,13 +1111,10 @@ hipError_t launch_experts_t(const ExpertArgs& a, hipStream_t s) {
     pa.shared_blob = a.shared_blob;
     pa.h = reinterpret_cast<uint16_t*>(h);
     pa.partial = partial;
-    pa.xsum = reinterpret_cast<float*>(a.ws + P.xsum);
-    pa.hsum = reinterpret_cast<float*>(a.ws + P.hsum);
     pa.out = a.out;
     pa.tiles = tiles;
     pa.ntiles = ntiles;
     pa.tiles_ready = small_batch;
-    pa.xsum_ready = a.xsum_ready;
     pa.x16 = reinterpret_cast<uint16_t*>(a.ws + P.x16);
     pa.xe = reinterpret_cast<int32_t*>(a.ws + P.xe);
     pa.x16_ready = a.x16_ready;

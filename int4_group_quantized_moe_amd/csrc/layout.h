@@ -66,12 +66,11 @@ constexpr BlobLayout make_layout(int bits, int hidden, int inter) {
 // Workspace plan (byte offsets into the caller's workspace).
 struct WsPlan {
   size_t logits, idx, w, gamma, h, partial, counts, offsets, pairs, slots, masks, blkoff, xprep;
-  size_t xsum, hsum;  // grouped-GEMM path: per-group sums of x_hat and of h
   size_t small, nsmall;  // buckets left to the GEMV kernels, and their count
   size_t xw, lw, hw;  // persistent-chain exchange words (batch 1)
   size_t ctr;         // persistent-chain epoch, then status word
   size_t tiles, ntiles;    // grouped-GEMM tile list (large batches)
-  size_t x16, xe;          // one token block: activations in fp16 and their row exponents
+  size_t x16, xe;          // grouped GEMMs: activations in fp16 and their row exponents
   int max_tiles;
   size_t total;
   bool bucketed;
@@ -106,16 +105,14 @@ inline WsPlan make_ws_plan(const moe_layer_desc& d) {
   p.masks = take(p.bucketed ? sizeof(uint64_t) * nblk * E : 0);
   p.blkoff = take(p.bucketed ? sizeof(int32_t) * nblk * E : 0);
   p.xprep = take(0);
-  p.xsum = take(p.bucketed ? sizeof(float) * T * (H / kGroup) : 0);
   p.small = take(p.bucketed ? sizeof(int32_t) * (E + 1) : 0);
   p.nsmall = take(p.bucketed ? sizeof(int32_t) : 0);
-  p.hsum = take(p.bucketed ? sizeof(float) * (T * k * (I / kGroup) + T * (Is / kGroup)) : 0);
   p.max_tiles = (int)((T * k + T) / 128 + E + 2);
   p.tiles = take(p.bucketed ? sizeof(int32_t) * 2 * p.max_tiles : 0);
   p.ntiles = take(p.bucketed ? sizeof(int32_t) : 0);
-  const bool one_block = p.bucketed && T <= kOneBlockTokens;
-  p.x16 = take(one_block ? sizeof(uint16_t) * T * H : 0);
-  p.xe = take(one_block ? sizeof(int32_t) * T : 0);
+  const bool gemm = p.bucketed && d.act_dtype == MOE_ACT_BF16;
+  p.x16 = take(gemm ? sizeof(uint16_t) * T * H : 0);
+  p.xe = take(gemm ? sizeof(int32_t) * T : 0);
   if (T == 1) {
     p.xw = take(sizeof(uint64_t) * (H / 2));
     p.lw = take(sizeof(uint64_t) * (E + 1));

@@ -133,7 +133,6 @@ struct RouterArgs {
   int32_t* topk_idx;
   float* topk_w;
   float* gamma;           // may be null
-  float* xsum;            // [T x H/64] group sums of x, written by the MFMA router if non-null
   uint16_t* x16;          // if non-null, the top-k kernel also writes x in fp16 (x16_row)
   int32_t* xe;            //   and the rows' exponents; x16_bits selects the K order
   int x16_bits;
@@ -169,7 +168,6 @@ struct ExpertArgs {
   void* x_res;
   void* x_hat_next;
   float eps;
-  bool xsum_ready;               // the router already wrote the group sums of x
   bool x16_ready;                // the router's top-k kernel already wrote x16 / xe
 };
 hipError_t launch_experts(const ExpertArgs& a, hipStream_t s);
@@ -186,11 +184,9 @@ struct PrefillArgs {
   const int32_t* slot_table;
   int64_t stride;
   const uint8_t* shared_blob;
-  uint16_t* h;                   // per row: I bf16 high parts, then I bf16 low parts
-  float* xsum;                   // [T][H/64] group sums of x
-  float* hsum;                   // [T*k][I/64] then [T][Is/64] group sums of h
+  uint16_t* h;                   // h rows (fp32 GEMV layout; fp16 + scales on this path)
   float* partial;                // fp32 [T*(k+1)*H]
-  uint16_t* x16;                 // one token block: x in fp16 (x16_row) and row exponents
+  uint16_t* x16;                 // x in fp16 (x16_row) and the rows' exponents
   int32_t* xe;
   bool x16_ready;                // written by the router's top-k kernel
   void* out;
@@ -199,15 +195,12 @@ struct PrefillArgs {
   int max_tiles;
   int min_rows;                  // buckets with fewer tokens are left to the GEMV kernels
   bool tiles_ready;              // the tile list was built with the buckets
-  bool xsum_ready;               // xsum was written by the router
   BlobLayout L, Ls;
   int T, H, E, k, I, Is, bits;
   bool has_shared;
 };
-bool prefill_supported(int act, int H, int I, int Is, bool has_shared);
+bool prefill_supported(int act, int64_t T, int H, int I, int Is, bool has_shared);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
-// group sums of the activations: xsum[t][g] = sum of x[t][64 g .. 64 g + 63]
-hipError_t launch_group_sum(const uint16_t* x, float* xsum, int T, int H, hipStream_t s);
 // One token block (T <= 64): the same GEMMs with every weight tile requested
 // up front (batched.hip); h is written as fp32 rows of `inter` floats.
 bool batched_supported(int act, int T, int H, int I, int Is, bool has_shared);
@@ -215,13 +208,20 @@ hipError_t launch_batched(const PrefillArgs& a, hipStream_t s);
 // x16 / xe of a batch (one wave per row) when the router did not write them
 hipError_t launch_x16(const uint16_t* x, uint16_t* x16, int32_t* xe, int T, int H, int bits,
                       hipStream_t s);
-// Whether a layer call runs the one-token-block grouped GEMMs (and so needs
-// x16 / xe): bf16 batches of 9..64 tokens on the MFMA path.
+// Whether a layer call runs the grouped GEMMs on the matrix cores (bucketed
+// bf16 batches; they read x16 / xe).
+inline bool mfma_path(const moe_layer_desc& d) {
+  const bool sh = (d.flags & MOE_FLAG_SHARED) != 0;
+  return d.n_tokens > kDecodeMaxTokens &&
+         prefill_supported(d.act_dtype, d.n_tokens, d.hidden, d.inter, sh ? d.shared_inter : d.inter,
+                           sh);
+}
+// Whether it runs the one-token-block variant: batches of 9..64 tokens.
 inline bool one_block_path(const moe_layer_desc& d) {
   const bool sh = (d.flags & MOE_FLAG_SHARED) != 0;
   const int Is = sh ? d.shared_inter : 0;
   return d.n_tokens > kDecodeMaxTokens && d.n_tokens <= kOneBlockTokens && d.n_experts < 1024 &&
-         prefill_supported(d.act_dtype, d.hidden, d.inter, sh ? Is : d.inter, sh) &&
+         prefill_supported(d.act_dtype, d.n_tokens, d.hidden, d.inter, sh ? Is : d.inter, sh) &&
          batched_supported(d.act_dtype, d.n_tokens, d.hidden, d.inter, Is, sh);
 }
 

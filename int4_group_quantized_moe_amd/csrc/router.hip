@@ -265,7 +265,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
                                                           const float* __restrict__ bias,
                                                           const float* __restrict__ wsg,
                                                           float* __restrict__ logits,
-                                                          float* __restrict__ xsum, int T, int H,
+                                                          int T, int H,
                                                           int E, int kseg) {
   __shared__ __align__(16) uint16_t A[2 * kRouterTile * kRouterLdsRow];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -293,37 +293,10 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
       rb[i] = e_ok ? reinterpret_cast<const float4*>(wrow + st * 64)[i]
                    : make_float4(0.f, 0.f, 0.f, 0.f);
   };
-  // With xsum, the workgroups of the first row tile also write the group
-  // sums of the activations, xsum[t][g] = sum of x[t][64 g .. 64 g + 63]
-  // (stage st of this K segment is group k0 / 64 + st): each 8-value chunk
-  // summed as ((x0 + x1) + (x2 + x3)) + (x4 + x5) + (x6 + x7), the 8 chunks
-  // in order from 0, which is the order the grouped GEMMs' own group-sum
-  // kernel uses, so the sums are the same bits.
-  const bool do_xsum = xsum != nullptr && blockIdx.x == 0;
-  auto chunk_sum = [](uint4 v) {
-    return (((bf16_bits_to_f32(v.x & 0xFFFFu) + bf16_bits_to_f32(v.x >> 16)) +
-             (bf16_bits_to_f32(v.y & 0xFFFFu) + bf16_bits_to_f32(v.y >> 16))) +
-            (bf16_bits_to_f32(v.z & 0xFFFFu) + bf16_bits_to_f32(v.z >> 16))) +
-           (bf16_bits_to_f32(v.w & 0xFFFFu) + bf16_bits_to_f32(v.w >> 16));
-  };
   auto store_stage = [&](int buf, int st, const uint4 (&ra)[2]) {
     uint16_t* dst = A + buf * kRouterTile * kRouterLdsRow + sr * kRouterLdsRow + 16 * sq;
 #pragma unroll
     for (int q = 0; q < 2; ++q) *reinterpret_cast<uint4*>(dst + 8 * q) = ra[q];
-    if (do_xsum) {
-      // lane sq of the row's quad holds chunks 2 sq and 2 sq + 1
-      const float c0 = chunk_sum(ra[0]), c1 = chunk_sum(ra[1]);
-      float p[8];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        p[2 * j] = __shfl(c0, (threadIdx.x & ~3) + j, 64);
-        p[2 * j + 1] = __shfl(c1, (threadIdx.x & ~3) + j, 64);
-      }
-      float s = 0.f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) s += p[j];
-      if (sq == 0 && srow_ok) xsum[(int64_t)(t0 + sr) * (H / 64) + k0 / 64 + st] = s;
-    }
   };
   // one stage of products: the fp32 router weights split exactly into three
   // bf16 parts, smallest first
@@ -431,7 +404,7 @@ hipError_t launch_router_act(const RouterArgs& a, hipStream_t s) {
     const uint16_t* xb = reinterpret_cast<const uint16_t*>(a.x);
     const float* wg = fold ? a.shared_gate_w : nullptr;
     hipLaunchKernelGGL(router_mfma_kernel, grid, dim3(256), 0, s, xb, a.router_w, a.router_bias,
-                       wg, a.logits, a.xsum, a.T, a.H, a.E, a.H / nplanes);
+                       wg, a.logits, a.T, a.H, a.E, a.H / nplanes);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.shared_gate_w != nullptr && !fold) {
