@@ -486,8 +486,11 @@ template <int BITS, int MB>
 __device__ __forceinline__ void prefill_gateup_item(MOE_PGU_PARAMS, Stage<BITS>* st,
                                                     int32_t* rowsrc, int32_t* te, uint32_t* wmax,
                                                     const TileInfo& ti, int nb) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31,
-            half = lane >> 5;
+  // (the thread index passes through an empty asm so that nothing derived
+  // from it is hoisted out of the persistent loop into spilled registers)
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, wave = tid >> 6, l32 = lane & 31, half = lane >> 5;
   const bool shared = ti.e == E;
   const int inter = shared ? Is : I;
   const int n0 = nb * kHCols;
@@ -610,8 +613,9 @@ template <int BITS, int MB>
 __device__ __forceinline__ void prefill_down_item(MOE_PDN_PARAMS, Stage<BITS>* st,
                                                   int32_t* rowdst, float* roww, float* hsl,
                                                   const TileInfo& ti, int nb) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31,
-            half = lane >> 5;
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));  // (as in the gate/up item)
+  const int lane = tid & 63, wave = tid >> 6, l32 = lane & 31, half = lane >> 5;
   const bool shared = ti.e == E;
   const int inter = shared ? Is : I;
   const int n0 = nb * kTileN;
