@@ -723,8 +723,29 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(const uint64_t* __res
   __shared__ int wsum[16], wsmall[16];
   const int e = threadIdx.x, lane = e & 63, wave = e >> 6;
   constexpr int kU = 16;  // block masks in flight per thread and round
+  // with at most kPackedBlocks blocks the per-block counts are kept, a byte
+  // each, for the offsets below (no second read of the masks)
+  constexpr int kPackedBlocks = 64;
+  const bool packed = nblk <= kPackedBlocks;
+  uint32_t pc[kPackedBlocks / 4] = {};
   int c = 0;
-  if (e < E) {
+  if (e < E && packed) {
+#pragma unroll
+    for (int r = 0; r < kPackedBlocks / kU; ++r) {
+      uint64_t m[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int b = r * kU + u;
+        m[u] = b < nblk ? masks[(int64_t)b * E + e] : 0ull;
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int b = r * kU + u, n = __popcll(m[u]);
+        c += n;
+        pc[b >> 2] |= (uint32_t)n << (8 * (b & 3));
+      }
+    }
+  } else if (e < E) {
     for (int b0 = 0; b0 < nblk; b0 += kU) {
       uint64_t m[kU];
 #pragma unroll
@@ -760,7 +781,16 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(const uint64_t* __res
     counts[e] = c;
     offsets[e] = excl;
     int run = excl;
-    for (int b0 = 0; b0 < nblk; b0 += kU) {
+    if (packed) {
+#pragma unroll
+      for (int b = 0; b < kPackedBlocks; ++b) {
+        if (b < nblk) {
+          blkoff[(int64_t)b * E + e] = run;
+          run += (pc[b >> 2] >> (8 * (b & 3))) & 0xFFu;
+        }
+      }
+    }
+    for (int b0 = 0; !packed && b0 < nblk; b0 += kU) {
       uint64_t m[kU];
 #pragma unroll
       for (int u = 0; u < kU; ++u) m[u] = b0 + u < nblk ? masks[(int64_t)(b0 + u) * E + e] : 0ull;

@@ -246,6 +246,7 @@ typedef float rf32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kRouterTile = 64;
 constexpr int kRouterLdsRow = 72;  // 64 K columns + 8 bf16 padding
+constexpr int kRouterDepth = 4;    // K stages in flight per thread
 
 __device__ __forceinline__ void split3_pair(float a, float b, uint32_t& p1, uint32_t& p2,
                                             uint32_t& p3) {
@@ -322,20 +323,29 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
     }
   };
 
+  // a ring of kRouterDepth stages in registers: stage st is multiplied
+  // while stages st + 1 .. st + kRouterDepth - 1 are in flight, and its
+  // registers then take stage st + kRouterDepth (the activations pass
+  // through a double-buffered LDS tile one stage ahead)
   {
-    uint4 ra[2];
-    float4 rb[8];
-    load_stage(0, ra, rb);
-    store_stage(0, 0, ra);
-    __syncthreads();
-    for (int st = 0; st < S; ++st) {
-      float4 cb[8];
+    uint4 ra[kRouterDepth][2];
+    float4 rb[kRouterDepth][8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) cb[i] = rb[i];
-      if (st + 1 < S) load_stage(st + 1, ra, rb);
-      multiply(A + (st & 1) * kRouterTile * kRouterLdsRow, cb);
-      if (st + 1 < S) store_stage((st + 1) & 1, st + 1, ra);
-      __syncthreads();
+    for (int j = 0; j < kRouterDepth; ++j)
+      if (j < S) load_stage(j, ra[j], rb[j]);
+    store_stage(0, 0, ra[0]);
+    __syncthreads();
+    for (int st0 = 0; st0 < S; st0 += kRouterDepth) {
+#pragma unroll
+      for (int j = 0; j < kRouterDepth; ++j) {
+        const int st = st0 + j;
+        if (st < S) {
+          multiply(A + (st & 1) * kRouterTile * kRouterLdsRow, rb[j]);
+          if (st + kRouterDepth < S) load_stage(st + kRouterDepth, ra[j], rb[j]);
+          if (st + 1 < S) store_stage((st + 1) & 1, st + 1, ra[(j + 1) % kRouterDepth]);
+          __syncthreads();
+        }
+      }
     }
   }
   if (!e_ok) return;
