@@ -82,7 +82,9 @@ enum moe_act_dtype { MOE_ACT_F32 = 0, MOE_ACT_BF16 = 1 };
 /* desc.flags */
 enum moe_flags {
   MOE_FLAG_ROUTER_BIAS = 1u, /* an additive fp32 router bias [E] is given */
-  MOE_FLAG_SHARED = 2u       /* the layer has a sigmoid-gated shared expert */
+  MOE_FLAG_SHARED = 2u,      /* the layer has a sigmoid-gated shared expert */
+  MOE_FLAG_DENSE_Q4 = 4u     /* router rows and shared gate in 4 bits: `router_w`
+                                points to the layer's dense blob (moe_dense_layout) */
 };
 
 /* Limits of this implementation (validated). */
@@ -226,6 +228,51 @@ int moe_pack_experts_device(const moe_layer_desc* desc, int32_t inter, int32_t n
                             const uint16_t* sb_down, void* slab, const int64_t* dst_slots,
                             hipStream_t stream);
 
+/* Dense blob layout (moe_dense_layout): rows, byte offset of the words, size. */
+typedef struct moe_dense_layout_t {
+  int64_t rows;
+  int64_t words_offset;
+  int64_t bytes;
+} moe_dense_layout_t;
+
+/*
+ * The layer's dense weights in 4 bits (MOE_FLAG_DENSE_Q4): the E router rows
+ * and, with MOE_FLAG_SHARED, the shared expert's gate vector as row E, each
+ * of `hidden` values quantised like the experts' (w = scale * q + bias per
+ * group of 64 consecutive values, unsigned 4-bit codes, bf16 scale and
+ * bias).  One dense blob per layer, `rows` = E (+1 with MOE_FLAG_SHARED):
+ *   codes   rows x hidden/2 bytes from offset 0: value 2j of a row in the
+ *           low nibble of byte j, value 2j+1 in the high nibble
+ *   words   rows x hidden/64 uint32 from words_offset: scale bits in the
+ *           low half, bias bits in the high half
+ *   bytes   the blob size (a multiple of 256); consecutive layers of a
+ *           chain sit `bytes` apart
+ * With the flag, the `router_w` argument of every compute entry point points
+ * to this blob (device memory, 256-byte aligned; for moe_chain_forward the
+ * first of n_layers blobs), the shared gate comes from its row E (the shared
+ * blob's fp32 gate vector is not read), and moe_router_topk takes
+ * shared_gate_w = NULL.
+ * Defined by: the dense weights, routers and shared experts among them, kept
+ * resident in 4 bits (xix.ai page "Paquets Swiftlet 80B Qwen ...", 4th
+ * paragraph; agentlenshq.com page, section "記憶體管理與權重串流", item
+ * "常駐密集權重"; news.bugfactory.tech Swiftlet item, 3rd paragraph).  The
+ * byte format is this library's.
+ * Errors: INVALID_ARG (null), UNSUPPORTED (hidden, group).  Pure host
+ * function; needs no device.
+ */
+int moe_dense_layout(const moe_layer_desc* desc, moe_dense_layout_t* out);
+
+/*
+ * Host packer of a dense blob from logical arrays in host memory:
+ *   q         [rows x hidden] codes, one code per byte (0..15)
+ *   sb        scale then bias planes: 2 x [rows x hidden/64] bf16 bits
+ *   blob_out  host buffer of at least `bytes`; padding bytes are zeroed
+ * Codes out of range return MOE_ERR_INVALID_ARG.
+ * Defined by: as moe_dense_layout.  Pure host function; needs no device.
+ */
+int moe_pack_dense(const moe_layer_desc* desc, const uint8_t* q, const uint16_t* sb,
+                   void* blob_out);
+
 /*
  * Workspace bytes needed by the compute entry points for `desc` (host), or 0
  * for an invalid descriptor.  The caller allocates the workspace (device
@@ -238,21 +285,22 @@ size_t moe_workspace_bytes(const moe_layer_desc* desc);
 /*
  * Router, softmax, top-k and renormalisation, plus the shared gate.
  *   x             [T x H] act_dtype, the layer input x_hat
- *   router_w      [E x H] fp32
+ *   router_w      [E x H] fp32, or the dense blob with MOE_FLAG_DENSE_Q4
  *   router_bias   [E] fp32 or NULL (required iff MOE_FLAG_ROUTER_BIAS)
- *   shared_gate_w [H] fp32 or NULL
+ *   shared_gate_w [H] fp32 or NULL (NULL with MOE_FLAG_DENSE_Q4)
  *   topk_idx      out [T x k] int32, by logit descending (ties: lower index)
  *   topk_w        out [T x k] fp32, sums to 1 per token
- *   shared_gate   out [T] fp32 sigmoid(w_sg . x), or NULL (needs shared_gate_w)
+ *   shared_gate   out [T] fp32 sigmoid(w_sg . x), or NULL (needs shared_gate_w,
+ *                 or with MOE_FLAG_DENSE_Q4 MOE_FLAG_SHARED)
  *   ws            workspace of moe_workspace_bytes(desc) bytes
  * Defined by: every layer routes each token to 10 of 512 experts (80B) or 8
  * of 256 (35B), with the routers resident (xix.ai page, 4th paragraph;
  * news.bugfactory.tech Swiftlet item, 3rd paragraph); the shared expert is
  * resident beside them (same passages).  softmax -> top-k -> renormalise and
  * the sigmoid gate are the workload definition (the pages are silent).
- * Errors: INVALID_ARG (null, shared_gate without shared_gate_w, router_bias
- * missing with MOE_FLAG_ROUTER_BIAS), UNSUPPORTED, MISALIGNED, NO_DEVICE,
- * LAUNCH.
+ * Errors: INVALID_ARG (null, shared_gate without its gate vector,
+ * shared_gate_w given with MOE_FLAG_DENSE_Q4, router_bias missing with
+ * MOE_FLAG_ROUTER_BIAS), UNSUPPORTED, MISALIGNED, NO_DEVICE, LAUNCH.
  */
 int moe_router_topk(const moe_layer_desc* desc, const void* x, const float* router_w,
                     const float* router_bias, const float* shared_gate_w, int32_t* topk_idx,
@@ -284,8 +332,10 @@ int moe_experts_forward(const moe_layer_desc* desc, const void* x, const int32_t
 
 /*
  * One whole MoE layer: router + top-k + shared gate + experts + combine.
- * The shared gate weight is read from the shared blob.  The routing of the
- * call stays in the workspace and can be read with moe_workspace_routing().
+ * The shared gate weight is read from the shared blob (with
+ * MOE_FLAG_DENSE_Q4: row E of the dense blob that `router_w` points to).
+ * The routing of the call stays in the workspace and can be read with
+ * moe_workspace_routing().
  * Arguments as for moe_router_topk and moe_experts_forward.
  * Defined by: the sparse MoE block of each layer of the hybrid Qwen3-Next /
  * Qwen3.5-3.6 models (xix.ai page, 4th and last paragraphs;
@@ -330,7 +380,9 @@ int moe_rmsnorm(const moe_layer_desc* desc, void* x, const void* out, void* x_ha
  * A chain of n_layers distinct layers over one batch:
  *   for l: x_hat = rmsnorm(x); out = layer_l(x_hat); x <- act(x + out).
  *   x             in/out [T x H] act_dtype
- *   router_w      layer l at router_w + l * E * H (fp32)
+ *   router_w      layer l at router_w + l * E * H (fp32); with
+ *                 MOE_FLAG_DENSE_Q4 layer l's dense blob at l * bytes
+ *                 (moe_dense_layout) from router_w
  *   router_bias   layer l at router_bias + l * E, or NULL
  *   expert_slab   one slab for all layers
  *   slot_tables   layer l at slot_tables + l * E

@@ -28,6 +28,7 @@ MOE_ACT_BF16 = 1
 
 MOE_FLAG_ROUTER_BIAS = 1
 MOE_FLAG_SHARED = 2
+MOE_FLAG_DENSE_Q4 = 4
 
 MOE_MAX_TOP_K = 16
 MOE_MAX_EXPERTS = 1024
@@ -72,6 +73,14 @@ class moe_blob_layout_t(ctypes.Structure):
         ("kblock_cols", ctypes.c_int32),
         ("groups_per_kblock", ctypes.c_int32),
         ("reserved0", ctypes.c_int32),
+    ]
+
+
+class moe_dense_layout_t(ctypes.Structure):
+    _fields_ = [
+        ("rows", ctypes.c_int64),
+        ("words_offset", ctypes.c_int64),
+        ("bytes", ctypes.c_int64),
     ]
 
 
@@ -120,6 +129,8 @@ _SIGS = {
     "moe_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "moe_blob_layout": ([_DESC, _I32, ctypes.POINTER(moe_blob_layout_t)], ctypes.c_int),
     "moe_pack_expert": ([_DESC, _I32, _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+    "moe_dense_layout": ([_DESC, ctypes.POINTER(moe_dense_layout_t)], ctypes.c_int),
+    "moe_pack_dense": ([_DESC, _P, _P, _P], ctypes.c_int),
     "moe_pack_experts_device": ([_DESC, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P],
                                 ctypes.c_int),
     "moe_workspace_bytes": ([_DESC], ctypes.c_size_t),
@@ -219,6 +230,17 @@ def moe_pack_expert(desc, inter, q_gate, q_up, q_down, sb_gate, sb_up, sb_down, 
     _check(lib().moe_pack_expert(ctypes.byref(desc), inter, _ptr(q_gate), _ptr(q_up),
                                  _ptr(q_down), _ptr(sb_gate), _ptr(sb_up), _ptr(sb_down),
                                  _ptr(shared_gate_w), _ptr(blob_out)), "moe_pack_expert")
+
+
+def moe_dense_layout(desc: moe_layer_desc) -> moe_dense_layout_t:
+    out = moe_dense_layout_t()
+    _check(lib().moe_dense_layout(ctypes.byref(desc), ctypes.byref(out)), "moe_dense_layout")
+    return out
+
+
+def moe_pack_dense(desc, q, sb, blob_out):
+    _check(lib().moe_pack_dense(ctypes.byref(desc), _ptr(q), _ptr(sb), _ptr(blob_out)),
+           "moe_pack_dense")
 
 
 def moe_pack_experts_device(desc, inter, n, q_gate, q_up, q_down, sb_gate, sb_up, sb_down, slab,

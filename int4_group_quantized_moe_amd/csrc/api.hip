@@ -16,6 +16,11 @@ int device_ok() {
 
 int to_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
 
+// router_w: fp32 rows, or with MOE_FLAG_DENSE_Q4 a dense blob (256-byte aligned)
+uintptr_t router_align(const moe_layer_desc* d) {
+  return (d->flags & MOE_FLAG_DENSE_Q4) ? 256 : 16;
+}
+
 int enqueue_router(const moe_layer_desc* d, const void* x, const float* router_w,
                    const float* router_bias, const float* wsg, int32_t* idx, float* w,
                    float* gamma, uint8_t* ws, hipStream_t s) {
@@ -25,6 +30,18 @@ int enqueue_router(const moe_layer_desc* d, const void* x, const float* router_w
   a.router_w = router_w;
   a.router_bias = (d->flags & MOE_FLAG_ROUTER_BIAS) ? router_bias : nullptr;
   a.shared_gate_w = wsg;
+  if (d->flags & MOE_FLAG_DENSE_Q4) {
+    // router_w is the layer's dense blob: its rows (with the shared gate as
+    // row E) dequantised to fp32 for the GEMV / GEMM routers
+    const DenseLayout DL = make_dense_layout(*d);
+    float* dense = reinterpret_cast<float*>(ws + P.dense);
+    MOE_TRY(to_status(launch_dense_dequant(reinterpret_cast<const uint8_t*>(router_w),
+                                           (int)DL.rows, d->hidden, DL.words_off, dense, s)));
+    a.router_w = dense;
+    a.shared_gate_w = (gamma != nullptr && (d->flags & MOE_FLAG_SHARED))
+                          ? dense + (int64_t)d->n_experts * d->hidden
+                          : nullptr;
+  }
   a.logits = reinterpret_cast<float*>(ws + P.logits);
   a.topk_idx = idx;
   a.topk_w = w;
@@ -65,6 +82,12 @@ int enqueue_decode(const moe_layer_desc* d, const void* x_in, void* x_hat, bool 
       a.has_shared ? reinterpret_cast<const float*>(
                          reinterpret_cast<const uint8_t*>(shared_blob) + a.Ls.sg_off)
                    : nullptr;
+  if (d->flags & MOE_FLAG_DENSE_Q4) {  // router rows and shared gate from the dense blob
+    a.dense = reinterpret_cast<const uint8_t*>(router_w);
+    a.dense_words = make_dense_layout(*d).words_off;
+    a.router_w = nullptr;
+    a.shared_gate_w = nullptr;
+  }
   a.logits = reinterpret_cast<float*>(ws + P.logits);
   a.idx = reinterpret_cast<int32_t*>(ws + P.idx);
   a.w = reinterpret_cast<float*>(ws + P.w);
@@ -180,14 +203,21 @@ int moe_router_topk(const moe_layer_desc* desc, const void* x, const float* rout
   MOE_TRY(check_shape(desc));
   if (desc->n_tokens == 0) return MOE_OK;
   MOE_TRY(check_ptr(x));
-  MOE_TRY(check_ptr(router_w));
+  const bool q4 = (desc->flags & MOE_FLAG_DENSE_Q4) != 0;
+  MOE_TRY(check_ptr(router_w, router_align(desc)));
   MOE_TRY(check_ptr(topk_idx, 4));
   MOE_TRY(check_ptr(topk_w, 4));
   MOE_TRY(check_ptr(ws, 256));
   if (desc->flags & MOE_FLAG_ROUTER_BIAS) MOE_TRY(check_ptr(router_bias, 4));
   MOE_TRY(check_opt_ptr(shared_gate_w));
   MOE_TRY(check_opt_ptr(shared_gate, 4));
-  if (shared_gate != nullptr && shared_gate_w == nullptr) return MOE_ERR_INVALID_ARG;
+  if (q4) {
+    // the gate vector is row E of the dense blob
+    if (shared_gate_w != nullptr) return MOE_ERR_INVALID_ARG;
+    if (shared_gate != nullptr && !(desc->flags & MOE_FLAG_SHARED)) return MOE_ERR_INVALID_ARG;
+  } else if (shared_gate != nullptr && shared_gate_w == nullptr) {
+    return MOE_ERR_INVALID_ARG;
+  }
   MOE_TRY(device_ok());
   return enqueue_router(desc, x, router_w, router_bias, shared_gate_w, topk_idx, topk_w,
                         shared_gate, reinterpret_cast<uint8_t*>(ws), stream);
@@ -224,7 +254,7 @@ int moe_layer_forward(const moe_layer_desc* desc, const void* x, const float* ro
   MOE_TRY(check_stride(desc));
   if (desc->n_tokens == 0) return MOE_OK;
   MOE_TRY(check_ptr(x));
-  MOE_TRY(check_ptr(router_w));
+  MOE_TRY(check_ptr(router_w, router_align(desc)));
   if (desc->flags & MOE_FLAG_ROUTER_BIAS) MOE_TRY(check_ptr(router_bias, 4));
   MOE_TRY(check_ptr(expert_slab, 256));
   MOE_TRY(check_ptr(slot_table, 4));
@@ -280,7 +310,7 @@ int moe_chain_forward(const moe_layer_desc* desc, int32_t n_layers, void* x,
   if (n_layers < 1) return MOE_ERR_INVALID_ARG;
   if (desc->n_tokens == 0) return MOE_OK;
   MOE_TRY(check_ptr(x));
-  MOE_TRY(check_ptr(router_w));
+  MOE_TRY(check_ptr(router_w, router_align(desc)));
   if (desc->flags & MOE_FLAG_ROUTER_BIAS) MOE_TRY(check_ptr(router_bias, 4));
   MOE_TRY(check_ptr(expert_slab, 256));
   MOE_TRY(check_ptr(slot_tables, 4));
@@ -295,11 +325,18 @@ int moe_chain_forward(const moe_layer_desc* desc, int32_t n_layers, void* x,
   }
   if (!(desc->rms_eps >= 0.0f)) return MOE_ERR_INVALID_ARG;
   MOE_TRY(device_ok());
-  const int64_t EH = (int64_t)desc->n_experts * desc->hidden;
+  const bool q4 = (desc->flags & MOE_FLAG_DENSE_Q4) != 0;
+  // layer l's router rows: fp32 [E][H], or its dense blob
+  const int64_t router_step = q4 ? make_dense_layout(*desc).bytes
+                                 : (int64_t)desc->n_experts * desc->hidden * (int64_t)sizeof(float);
+  auto layer_router = [&](int l) {
+    return reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(router_w) +
+                                          (int64_t)l * router_step);
+  };
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_NO_DEVICE;
   const int nwg = chain_grid(dev);
-  if (chain_supported(nwg, desc->n_tokens, desc->act_dtype, desc->hidden, desc->n_experts,
+  if (!q4 && chain_supported(nwg, desc->n_tokens, desc->act_dtype, desc->hidden, desc->n_experts,
                       desc->top_k, desc->bits, desc->inter, shared ? desc->shared_inter : 0,
                       shared)) {
     const WsPlan P = make_ws_plan(*desc);
@@ -354,7 +391,7 @@ int moe_chain_forward(const moe_layer_desc* desc, int32_t n_layers, void* x,
                             : nullptr;
       const void* sb = shared ? reinterpret_cast<const uint8_t*>(shared_blobs) + l * shared_stride
                               : nullptr;
-      MOE_TRY(enqueue_decode(desc, x, x_hat, true, router_w + l * EH, rb, expert_slab,
+      MOE_TRY(enqueue_decode(desc, x, x_hat, true, layer_router(l), rb, expert_slab,
                              slot_tables + (int64_t)l * desc->n_experts, sb, out, x,
                              reinterpret_cast<uint8_t*>(ws), stream));
     }
@@ -369,7 +406,7 @@ int moe_chain_forward(const moe_layer_desc* desc, int32_t n_layers, void* x,
                             : nullptr;
       const void* sb = shared ? reinterpret_cast<const uint8_t*>(shared_blobs) + l * shared_stride
                               : nullptr;
-      MOE_TRY(chain_layer_bucketed(desc, x, x_hat, router_w + l * EH, rb, expert_slab,
+      MOE_TRY(chain_layer_bucketed(desc, x, x_hat, layer_router(l), rb, expert_slab,
                                    slot_tables + (int64_t)l * desc->n_experts, sb, out,
                                    reinterpret_cast<uint8_t*>(ws), l == n_layers - 1, stream));
     }
@@ -382,7 +419,7 @@ int moe_chain_forward(const moe_layer_desc* desc, int32_t n_layers, void* x,
                                                           : nullptr;
     const void* sb = shared ? reinterpret_cast<const uint8_t*>(shared_blobs) + l * shared_stride
                             : nullptr;
-    MOE_TRY(moe_layer_forward(desc, x_hat, router_w + l * EH, rb, expert_slab,
+    MOE_TRY(moe_layer_forward(desc, x_hat, layer_router(l), rb, expert_slab,
                               slot_tables + (int64_t)l * desc->n_experts, sb, out, ws, stream));
   }
   return to_status(launch_rmsnorm(x, out, x_hat, desc->n_tokens, desc->hidden, desc->act_dtype,

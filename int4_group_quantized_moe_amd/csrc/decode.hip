@@ -26,23 +26,44 @@ using namespace dec;
 // ---------------------------------------------------------------------------
 // A: router.  Block = one wave = one row (router rows 0..E-1, then the shared
 // gate row).  With do_norm, x is the residual stream and every wave
-// normalises it itself (x_hat = bf16(x / rms)); block 0 stores x_hat.
+// normalises it itself (x_hat = bf16(x / rms)); block 0 stores x_hat.  With
+// Q4 the rows come from the layer's dense blob (4-bit codes, (scale, bias)
+// per group of 64; the shared gate is its row E), dequantised in fp32.
 
-template <int NIT>
+template <int NIT, bool Q4>
 __global__ __launch_bounds__(64) void decode_router_kernel(
     const uint16_t* __restrict__ x, uint16_t* __restrict__ x_hat, const float* __restrict__ W,
-    const float* __restrict__ bias, const float* __restrict__ wsg, float* __restrict__ logits,
-    int H, int E, float eps, int do_norm) {
+    const float* __restrict__ bias, const float* __restrict__ wsg,
+    const uint8_t* __restrict__ dense, int64_t dense_words, float* __restrict__ logits, int H,
+    int E, float eps, int do_norm) {
   const int lane = threadIdx.x;
   const int r = blockIdx.x;
-  const float* wrow = r < E ? W + (int64_t)r * H : wsg;
   float4 w4[NIT];
   uint2 x4[NIT];
+  if constexpr (Q4) {
+    const uint8_t* crow = dense + (int64_t)r * (H / 2);
+    const uint32_t* words = reinterpret_cast<const uint32_t*>(dense + dense_words) + (int64_t)r * (H / kGroup);
+    uint32_t q[NIT], sb[NIT];
 #pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const int c = it * 256 + lane * 4;
-    w4[it] = *reinterpret_cast<const float4*>(wrow + c);
-    x4[it] = *reinterpret_cast<const uint2*>(x + c);
+    for (int it = 0; it < NIT; ++it) {
+      q[it] = *reinterpret_cast<const uint16_t*>(crow + it * 128 + lane * 2);
+      sb[it] = words[it * 4 + (lane >> 4)];
+      x4[it] = *reinterpret_cast<const uint2*>(x + it * 256 + lane * 4);
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const float sc = bf16_bits_to_f32(sb[it] & 0xFFFFu), bi = bf16_bits_to_f32(sb[it] >> 16);
+      w4[it] = make_float4(fmaf(sc, (float)(q[it] & 15u), bi), fmaf(sc, (float)((q[it] >> 4) & 15u), bi),
+                           fmaf(sc, (float)((q[it] >> 8) & 15u), bi), fmaf(sc, (float)(q[it] >> 12), bi));
+    }
+  } else {
+    const float* wrow = r < E ? W + (int64_t)r * H : wsg;
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int c = it * 256 + lane * 4;
+      w4[it] = *reinterpret_cast<const float4*>(wrow + c);
+      x4[it] = *reinterpret_cast<const uint2*>(x + c);
+    }
   }
   float xv[NIT][4];
   float ss = 0.f;
@@ -389,9 +410,14 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
   const int rows = a.E + (a.has_shared ? 1 : 0);
 #define MOE_A(N)                                                                               \
   case N:                                                                                      \
-    hipLaunchKernelGGL(decode_router_kernel<N>, dim3(rows), dim3(64), 0, s, a.x_in, a.x_hat,    \
-                       a.router_w, a.router_bias, a.shared_gate_w, a.logits, a.H, a.E, a.eps, \
-                       a.do_norm ? 1 : 0);                                                     \
+    if (a.dense != nullptr)                                                                    \
+      hipLaunchKernelGGL((decode_router_kernel<N, true>), dim3(rows), dim3(64), 0, s, a.x_in,   \
+                         a.x_hat, a.router_w, a.router_bias, a.shared_gate_w, a.dense,         \
+                         a.dense_words, a.logits, a.H, a.E, a.eps, a.do_norm ? 1 : 0);         \
+    else                                                                                       \
+      hipLaunchKernelGGL((decode_router_kernel<N, false>), dim3(rows), dim3(64), 0, s, a.x_in,  \
+                         a.x_hat, a.router_w, a.router_bias, a.shared_gate_w, a.dense,         \
+                         a.dense_words, a.logits, a.H, a.E, a.eps, a.do_norm ? 1 : 0);         \
     break;
   switch (nit) {
     MOE_A(1) MOE_A(2) MOE_A(3) MOE_A(4) MOE_A(5) MOE_A(6) MOE_A(7) MOE_A(8)

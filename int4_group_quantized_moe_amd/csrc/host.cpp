@@ -30,7 +30,8 @@ int check_shape(const moe_layer_desc* d) {
     if (d->shared_inter < kbc || d->shared_inter > MOE_MAX_INTER || d->shared_inter % kbc)
       return MOE_ERR_UNSUPPORTED;
   }
-  if (d->flags & ~(uint32_t)(MOE_FLAG_ROUTER_BIAS | MOE_FLAG_SHARED)) return MOE_ERR_INVALID_ARG;
+  if (d->flags & ~(uint32_t)(MOE_FLAG_ROUTER_BIAS | MOE_FLAG_SHARED | MOE_FLAG_DENSE_Q4))
+    return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
 
@@ -151,6 +152,42 @@ int moe_pack_expert(const moe_layer_desc* desc, int32_t inter, const uint8_t* q_
   pack_section(blob + L.gu_off, q_gate, q_up, sb_gate, sb_up, I, H, L.gu_unit, L.gu_tile);
   pack_section(blob + L.d_off, q_down, nullptr, sb_down, nullptr, H, I, L.d_unit, L.d_tile);
   if (shared_gate_w) memcpy(blob + L.sg_off, shared_gate_w, sizeof(float) * H);
+  return MOE_OK;
+}
+
+int moe_dense_layout(const moe_layer_desc* desc, moe_dense_layout_t* out) {
+  if (desc == nullptr || out == nullptr) return MOE_ERR_INVALID_ARG;
+  if (desc->group != kGroup) return MOE_ERR_UNSUPPORTED;
+  if (desc->hidden < kGroup || desc->hidden > MOE_MAX_HIDDEN || desc->hidden % kGroup)
+    return MOE_ERR_UNSUPPORTED;
+  if (desc->n_experts < 1 || desc->n_experts > MOE_MAX_EXPERTS) return MOE_ERR_INVALID_ARG;
+  const DenseLayout L = make_dense_layout(*desc);
+  out->rows = L.rows;
+  out->words_offset = L.words_off;
+  out->bytes = L.bytes;
+  return MOE_OK;
+}
+
+int moe_pack_dense(const moe_layer_desc* desc, const uint8_t* q, const uint16_t* sb,
+                   void* blob_out) {
+  moe_dense_layout_t dl;
+  MOE_TRY(moe_dense_layout(desc, &dl));
+  if (!q || !sb || !blob_out) return MOE_ERR_INVALID_ARG;
+  const int64_t H = desc->hidden, R = dl.rows, G = H / kGroup;
+  for (int64_t i = 0; i < R * H; ++i)
+    if (q[i] > 15) return MOE_ERR_INVALID_ARG;
+  uint8_t* blob = reinterpret_cast<uint8_t*>(blob_out);
+  memset(blob, 0, (size_t)dl.bytes);
+  for (int64_t r = 0; r < R; ++r) {
+    for (int64_t c = 0; c < H; ++c)
+      blob[r * (H / 2) + c / 2] |= (uint8_t)(q[r * H + c] << (4 * (c & 1)));
+    for (int64_t g = 0; g < G; ++g) {
+      const uint16_t sc = sb[r * G + g], bi = sb[R * G + r * G + g];
+      uint8_t* p = blob + dl.words_offset + (r * G + g) * 4;
+      memcpy(p, &sc, 2);
+      memcpy(p + 2, &bi, 2);
+    }
+  }
   return MOE_OK;
 }
 

@@ -63,6 +63,19 @@ constexpr BlobLayout make_layout(int bits, int hidden, int inter) {
   return L;
 }
 
+// Dense blob of a layer (MOE_FLAG_DENSE_Q4): rows x hidden/2 code bytes, then
+// rows x hidden/64 (scale, bias) words.
+struct DenseLayout {
+  int64_t rows, words_off, bytes;
+};
+inline DenseLayout make_dense_layout(const moe_layer_desc& d) {
+  DenseLayout L;
+  L.rows = (int64_t)d.n_experts + ((d.flags & MOE_FLAG_SHARED) ? 1 : 0);
+  L.words_off = align_up(L.rows * d.hidden / 2, 256);
+  L.bytes = align_up(L.words_off + L.rows * (d.hidden / kGroup) * 4, 256);
+  return L;
+}
+
 // Workspace plan (byte offsets into the caller's workspace).
 struct WsPlan {
   size_t logits, idx, w, gamma, h, partial, counts, offsets, pairs, slots, masks, blkoff, xprep;
@@ -71,6 +84,7 @@ struct WsPlan {
   size_t ctr;         // persistent-chain epoch, then status word
   size_t tiles, ntiles;    // grouped-GEMM tile list (large batches)
   size_t x16, xe;          // grouped GEMMs: activations in fp16 and their row exponents
+  size_t dense;            // MOE_FLAG_DENSE_Q4: the dense rows dequantised to fp32
   int max_tiles;
   size_t total;
   bool bucketed;
@@ -113,6 +127,7 @@ inline WsPlan make_ws_plan(const moe_layer_desc& d) {
   const bool gemm = p.bucketed && d.act_dtype == MOE_ACT_BF16;
   p.x16 = take(gemm ? sizeof(uint16_t) * T * H : 0);
   p.xe = take(gemm ? sizeof(int32_t) * T : 0);
+  p.dense = take((d.flags & MOE_FLAG_DENSE_Q4) ? sizeof(float) * (E + 1) * H : 0);
   if (T == 1) {
     p.xw = take(sizeof(uint64_t) * (H / 2));
     p.lw = take(sizeof(uint64_t) * (E + 1));

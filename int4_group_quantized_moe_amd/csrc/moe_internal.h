@@ -139,6 +139,9 @@ struct RouterArgs {
   int T, H, E, k, act;
 };
 hipError_t launch_router_topk(const RouterArgs& a, hipStream_t s);
+// MOE_FLAG_DENSE_Q4: the dense blob's rows dequantised to fp32 rows [rows][H]
+hipError_t launch_dense_dequant(const uint8_t* blob, int rows, int H, int64_t words_off, float* out,
+                                hipStream_t s);
 // The router runs as an MFMA GEMM (bf16 batches from 16 tokens, H a multiple of 64).
 constexpr int kRouterMfmaMinTokens = 16;
 inline bool router_uses_mfma(int act, int64_t T, int64_t H) {
@@ -234,6 +237,8 @@ struct DecodeArgs {
   const float* router_w;
   const float* router_bias;
   const float* shared_gate_w;    // null without shared expert
+  const uint8_t* dense;          // MOE_FLAG_DENSE_Q4: the dense blob (router_w unused), else null
+  int64_t dense_words;           //   offset of its (scale, bias) words
   float* logits;                 // ws
   int32_t* idx;                  // ws routing
   float* w;

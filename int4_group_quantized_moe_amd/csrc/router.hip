@@ -463,6 +463,37 @@ hipError_t launch_router_gemv(const RouterArgs& a, hipStream_t s) {
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Dense rows in 4 bits (MOE_FLAG_DENSE_Q4) for the GEMV / GEMM routers:
+// w[r][c] = s q + b per group of 64 into fp32 rows, one block per row, each
+// thread 8 consecutive values (one code word) per step.
+
+__global__ __launch_bounds__(256) void dense_dequant_kernel(const uint8_t* __restrict__ blob,
+                                                            float* __restrict__ out, int H,
+                                                            int64_t words_off) {
+  const int r = blockIdx.x;
+  const uint8_t* codes = blob + (int64_t)r * (H / 2);
+  const uint32_t* words = reinterpret_cast<const uint32_t*>(blob + words_off) + (int64_t)r * (H / kGroup);
+  for (int c0 = 8 * threadIdx.x; c0 < H; c0 += 8 * 256) {
+    const uint32_t q = *reinterpret_cast<const uint32_t*>(codes + c0 / 2);
+    const uint32_t sb = words[c0 / kGroup];
+    const float sc = bf16_bits_to_f32(sb & 0xFFFFu), bi = bf16_bits_to_f32(sb >> 16);
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = fmaf(sc, (float)((q >> (4 * i)) & 15u), bi);
+    float4* o = reinterpret_cast<float4*>(out + (int64_t)r * H + c0);
+    o[0] = make_float4(v[0], v[1], v[2], v[3]);
+    o[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+}
+
+hipError_t launch_dense_dequant(const uint8_t* blob, int rows, int H, int64_t words_off, float* out,
+                                hipStream_t s) {
+  hipLaunchKernelGGL(dense_dequant_kernel, dim3((unsigned)rows), dim3(256), 0, s, blob, out, H,
+                     words_off);
+  return hipGetLastError();
+}
+
 hipError_t launch_router_topk(const RouterArgs& a, hipStream_t s) {
   return a.act == MOE_ACT_F32 ? launch_router_act<MOE_ACT_F32>(a, s)
                               : launch_router_act<MOE_ACT_BF16>(a, s);

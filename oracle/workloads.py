@@ -18,10 +18,16 @@ from . import moe_oracle
 class LayerInputs:
     """Router, shared expert and (lazily, cached) routed experts of one layer."""
 
-    def __init__(self, cfg, layer: int, overrides: dict | None = None):
+    def __init__(self, cfg, layer: int, overrides: dict | None = None, dense_q4: bool = False):
         self.cfg = cfg
         self.layer = layer
         ov = overrides or {}
+        if dense_q4:
+            # router rows and shared gate in 4 bits: the values they encode
+            # (w = s q + b per group), row E the gate vector
+            a = synth.dense_q4_arrays(cfg, layer)
+            rows = moe_oracle.dequantize(a["q"], a["s"], a["b"], cfg.group)
+            ov = {"router_w": rows[:cfg.n_experts], "w_sg": rows[cfg.n_experts], **ov}
         self.router_w = ov.get("router_w", synth.router_weight(cfg, layer))
         self.router_bias = ov.get("router_bias", synth.router_bias(cfg, layer))
         self.w_sg = ov.get("w_sg", synth.shared_gate_weight(cfg, layer))

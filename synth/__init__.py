@@ -47,6 +47,7 @@ _MASK64 = (1 << 64) - 1
 T_QGATE, T_QUP, T_QDOWN = 1, 2, 3
 T_SGATE, T_BGATE, T_SUP, T_BUP, T_SDOWN, T_BDOWN = 4, 5, 6, 7, 8, 9
 T_ROUTER_W, T_ROUTER_BIAS, T_SHARED_GATE_W, T_X = 10, 11, 12, 13
+T_DENSE_Q, T_DENSE_S, T_DENSE_B = 14, 15, 16  # 4-bit dense rows (router + shared gate)
 SHARED_EXPERT = 0xFFFFFF  # expert field of the shared expert's streams
 NO_EXPERT = 0xFFFFFE      # expert field of per-layer dense tensors
 
@@ -226,6 +227,25 @@ def shared_gate_weight(cfg: "MoeConfig", layer: int) -> np.ndarray:
     """fp32 [hidden] weight of the shared expert's sigmoid gate, N(0, 0.02^2)."""
     key = stream_key(cfg.seed, T_SHARED_GATE_W, layer, NO_EXPERT)
     return (normal_f64(key, cfg.hidden) * 0.02).astype(np.float32)
+
+
+def dense_q4_arrays(cfg: "MoeConfig", layer: int) -> dict:
+    """The layer's dense rows in 4 bits: the E router rows and, with a shared
+    expert, its gate vector as row E.  Codes uniform 0..15, scale
+    ~U(0.8 c, 1.2 c) and bias ~U(-8.5 c, -6.5 c) per group of 64, c =
+    router_std / 4.61 (the standard deviation of q - 7.5), so that the rows
+    have about the fp32 router's spread and mean 0.
+
+    q: [rows x hidden] codes (one per byte); s, b: [rows x hidden/64] bf16 bits.
+    """
+    rows = cfg.n_experts + (1 if cfg.shared_inter > 0 else 0)
+    c = cfg.router_std / 4.61
+    G = cfg.hidden // cfg.group
+    return {
+        "q": quant_codes(cfg.seed, T_DENSE_Q, layer, NO_EXPERT, rows, cfg.hidden, 4),
+        "s": quant_sb(cfg.seed, T_DENSE_S, layer, NO_EXPERT, rows, G, 0.8 * c, 1.2 * c),
+        "b": quant_sb(cfg.seed, T_DENSE_B, layer, NO_EXPERT, rows, G, -8.5 * c, -6.5 * c),
+    }
 
 
 def activations(cfg: "MoeConfig", variant: int = 0, n_tokens: int | None = None) -> np.ndarray:

@@ -190,9 +190,47 @@ static void layouts() {
       }
 }
 
+// dense blob (MOE_FLAG_DENSE_Q4): pack, then read every code and word back
+// at the documented positions
+static void dense_round_trip(int H, int E, bool shared) {
+  moe_layer_desc d = make(1, H, E, 2, 128, 128, 4);
+  d.flags = (shared ? MOE_FLAG_SHARED : 0u) | MOE_FLAG_DENSE_Q4;
+  moe_dense_layout_t L;
+  CHECK(moe_dense_layout(&d, &L) == MOE_OK);
+  const int R = E + (shared ? 1 : 0), G = H / 64;
+  CHECK(L.rows == R);
+  CHECK(L.words_offset >= (int64_t)R * H / 2 && L.words_offset % 256 == 0);
+  CHECK(L.bytes % 256 == 0 && L.bytes >= L.words_offset + 4LL * R * G);
+  std::vector<uint8_t> q((size_t)R * H);
+  std::vector<uint16_t> sb((size_t)2 * R * G);
+  for (size_t i = 0; i < q.size(); ++i) q[i] = (uint8_t)((i * 7 + i / 13) % 16);
+  for (size_t i = 0; i < sb.size(); ++i) sb[i] = (uint16_t)(0x3c00 + i * 31);
+  std::vector<uint8_t> blob((size_t)L.bytes, 0xAB);
+  CHECK(moe_pack_dense(&d, q.data(), sb.data(), blob.data()) == MOE_OK);
+  for (int r = 0; r < R; ++r) {
+    for (int c = 0; c < H; ++c)
+      CHECK(((blob[(size_t)r * H / 2 + c / 2] >> (4 * (c & 1))) & 15) == q[(size_t)r * H + c]);
+    for (int g = 0; g < G; ++g) {
+      uint32_t w;
+      memcpy(&w, blob.data() + L.words_offset + 4 * ((size_t)r * G + g), 4);
+      CHECK((w & 0xFFFFu) == sb[(size_t)r * G + g]);
+      CHECK((w >> 16) == sb[(size_t)R * G + (size_t)r * G + g]);
+    }
+  }
+  q[5] = 16;
+  CHECK(moe_pack_dense(&d, q.data(), sb.data(), blob.data()) == MOE_ERR_INVALID_ARG);
+  CHECK(moe_pack_dense(&d, nullptr, sb.data(), blob.data()) == MOE_ERR_INVALID_ARG);
+  CHECK(moe_dense_layout(&d, nullptr) == MOE_ERR_INVALID_ARG);
+  d.hidden = 96;
+  CHECK(moe_dense_layout(&d, &L) == MOE_ERR_UNSUPPORTED);
+}
+
 int main() {
   validation();
   layouts();
+  dense_round_trip(256, 16, true);
+  dense_round_trip(2048, 512, true);
+  dense_round_trip(128, 3, false);
   packer_round_trip(4, 256, 128, true);
   packer_round_trip(8, 256, 128, false);
   packer_round_trip(4, 384, 256, false);

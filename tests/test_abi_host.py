@@ -43,7 +43,7 @@ def test_boundary_names():
     for n in ("moe_router_topk", "moe_experts_forward", "moe_layer_forward",
               "moe_residual_rmsnorm", "moe_blob_layout", "moe_pack_expert",
               "moe_workspace_bytes", "moe_status_string", "moe_version", "moe_chain_forward",
-              "moe_chain_status"):
+              "moe_chain_status", "moe_dense_layout", "moe_pack_dense"):
         assert n in names, n
 
 
@@ -175,6 +175,34 @@ def test_host_packer_round_trip(bits):
     # padding between sections is zero
     end = L.down_offset + (H // 16) * L.down_tile_bytes
     assert np.all(blob[end:L.blob_bytes] == 0)
+
+
+@pytest.mark.parametrize("H,E,shared", [(256, 16, True), (2048, 512, True), (128, 3, False)])
+def test_dense_packer_layout(H, E, shared):
+    """moe_pack_dense writes the documented dense-blob format: codes row after
+    row, value 2j in the low nibble of byte j; then one (scale, bias) word per
+    row and group from words_offset; rows = E (+1 for the shared gate)."""
+    rng = np.random.default_rng(11)
+    d = moe.make_desc(1, H, E, 2, 128, 128, shared=shared, dense_q4=True)
+    L = moe.moe_dense_layout(d)
+    R, G = E + (1 if shared else 0), H // 64
+    assert L.rows == R and L.words_offset % 256 == 0 and L.bytes % 256 == 0
+    assert L.words_offset >= R * H // 2 and L.bytes >= L.words_offset + 4 * R * G
+    q = rng.integers(0, 16, (R, H)).astype(np.uint8)
+    sb = rng.integers(0, 65536, (2, R, G)).astype(np.uint16)
+    blob = np.full(L.bytes, 0xAB, np.uint8)
+    moe.moe_pack_dense(d, q, sb, blob)
+    codes = blob[:R * H // 2].reshape(R, H // 2)
+    assert np.array_equal(codes & 15, q[:, 0::2]) and np.array_equal(codes >> 4, q[:, 1::2])
+    words = blob[L.words_offset:L.words_offset + 4 * R * G].view(np.uint32).reshape(R, G)
+    assert np.array_equal(words & 0xFFFF, sb[0]) and np.array_equal(words >> 16, sb[1])
+    assert np.all(blob[R * H // 2:L.words_offset] == 0)
+    assert np.all(blob[L.words_offset + 4 * R * G:] == 0)
+    bad = q.copy()
+    bad[0, 1] = 16
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_pack_dense(d, bad, sb, blob)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
 
 
 def test_host_packer_rejects_out_of_range_codes():

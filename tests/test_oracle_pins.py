@@ -212,6 +212,29 @@ def test_router_logits_bruteforce(O, rng):
             assert abs(l[t, e] - ref) <= 1e-12 * (1 + abs(ref))
 
 
+def test_dense_q4_router_bruteforce(O, rng):
+    """The 4-bit dense path: logits from router rows given as int4 codes with
+    bf16 (scale, bias) per group of 64 equal a scalar loop over the codes
+    (w = s q + b, then the dot product), and the shared gate reads row E."""
+    E, H, G = 3, 128, 2
+    q = rng.integers(0, 16, (E + 1, H)).astype(np.uint8)
+    s = mo.round_to_bf16(rng.uniform(0.001, 0.01, (E + 1, G)))
+    b = mo.round_to_bf16(rng.uniform(-0.08, 0.0, (E + 1, G)))
+    bits = lambda v: (np.asarray(v, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    rows = O.dequantize(q, bits(s), bits(b), 64)
+    x = rng.standard_normal((2, H))
+    l = O.router_logits(x, rows[:E])
+    gam = O.shared_gate(x, rows[E])
+    for t in range(2):
+        for e in range(E + 1):
+            ref = math.fsum((float(s[e, c // 64]) * int(q[e, c]) + float(b[e, c // 64])) * float(x[t, c])
+                            for c in range(H))
+            if e < E:
+                assert abs(l[t, e] - ref) <= 1e-12 * (1 + abs(ref))
+            else:
+                assert abs(gam[t] - 1.0 / (1.0 + math.exp(-ref))) <= 1e-12
+
+
 def test_topk_matches_best_subset(O, rng):
     for trial in range(40):
         E = int(rng.integers(3, 13))

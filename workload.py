@@ -16,11 +16,11 @@ import synth
 from synth import device as synth_device
 
 
-def desc_for(cfg, n_tokens: int | None = None):
+def desc_for(cfg, n_tokens: int | None = None, dense_q4: bool = False):
     return moe.make_desc(cfg.n_tokens if n_tokens is None else n_tokens, cfg.hidden,
                          cfg.n_experts, cfg.top_k, cfg.inter, cfg.shared_inter, bits=cfg.bits,
                          act=cfg.act, router_bias=bool(cfg.zipf_s), shared=True,
-                         rms_eps=cfg.rms_eps)
+                         rms_eps=cfg.rms_eps, dense_q4=dense_q4)
 
 
 def act_dtype(cfg):
@@ -35,16 +35,20 @@ class Workload:
     shared        uint8 [n_layers, shared_stride] (blob + w_sg)
     router_w      fp32  [n_layers, E, H]
     router_bias   fp32  [n_layers, E] or None
+    dense         uint8 [n_layers, dense bytes]: with dense_q4, the 4-bit router
+                  rows and shared gate (moe_pack_dense); the layer calls then
+                  take it as their router argument and the flag in `desc`
     """
 
     def __init__(self, cfg, n_layers: int | None = None, device="cuda", permute_seed=None,
-                 batch: int = 32, layers: list | None = None):
+                 batch: int = 32, layers: list | None = None, dense_q4: bool = False):
         self.cfg = cfg
         self.layer_ids = list(range(n_layers if n_layers is not None else cfg.layers)) \
             if layers is None else list(layers)
         L = len(self.layer_ids)
         E, H = cfg.n_experts, cfg.hidden
-        self.desc = desc_for(cfg)
+        self.dense_q4 = dense_q4
+        self.desc = desc_for(cfg, dense_q4=dense_q4)
         self.stride = int(self.desc.expert_stride)
         self.layout = moe.moe_blob_layout(self.desc, cfg.inter)
         self.slayout = moe.moe_blob_layout(self.desc, cfg.shared_inter)
@@ -62,6 +66,9 @@ class Workload:
         self.router_w = torch.empty(L, E, H, dtype=torch.float32, device=device)
         self.router_bias = (torch.empty(L, E, dtype=torch.float32, device=device)
                             if cfg.zipf_s else None)
+        self.dense_bytes = int(moe.moe_dense_layout(self.desc).bytes)
+        self.dense = (torch.empty(L, self.dense_bytes, dtype=torch.uint8, device=device)
+                      if dense_q4 else None)
         I, Is = cfg.inter, cfg.shared_inter
         G = cfg.group
         B = min(batch, E)
@@ -93,15 +100,35 @@ class Workload:
             off = int(self.slayout.shared_gate_offset)
             self.shared[i, off:off + 4 * H].copy_(wsg.view(torch.uint8))
             self.router_w[i].copy_(torch.from_numpy(synth.router_weight(cfg, l)))
+            if dense_q4:
+                a = synth.dense_q4_arrays(cfg, l)
+                blob = np.zeros(self.dense_bytes, np.uint8)
+                moe.moe_pack_dense(self.desc, np.ascontiguousarray(a["q"]),
+                                   np.ascontiguousarray(np.stack([a["s"], a["b"]])), blob)
+                self.dense[i].copy_(torch.from_numpy(blob))
             if self.router_bias is not None:
                 self.router_bias[i].copy_(torch.from_numpy(synth.router_bias(cfg, l)))
         torch.cuda.synchronize()
 
     # per-layer views -------------------------------------------------------
     def layer_args(self, i: int):
-        """(router_w, router_bias, slot_table, shared_blob) of layer index i."""
+        """(router_w, router_bias, slot_table, shared_blob) of layer index i
+        (router_w: the dense blob with dense_q4)."""
         rb = self.router_bias[i] if self.router_bias is not None else None
-        return self.router_w[i], rb, self.slot_tables[i], self.shared[i]
+        rw = self.dense[i] if self.dense_q4 else self.router_w[i]
+        return rw, rb, self.slot_tables[i], self.shared[i]
+
+    @property
+    def router_all(self):
+        """The router argument of a chain call over all layers."""
+        return self.dense if self.dense_q4 else self.router_w
+
+    def dense_rows(self, i: int) -> np.ndarray:
+        """Layer index i's dense rows (router rows, then the shared gate) as the
+        fp64 values they encode, through the oracle's dequantisation (tests)."""
+        import oracle
+        a = synth.dense_q4_arrays(self.cfg, self.layer_ids[i])
+        return oracle.dequantize(a["q"], a["s"], a["b"], self.cfg.group)
 
     def workspace(self, desc=None):
         """Zero-filled workspace (the chain's exchange words must start at zero)."""
