@@ -45,6 +45,8 @@ def parse():
                    help="layers of the oracle's timed sample (default: the whole chain for "
                         "batch-1 decode, 1 layer otherwise; 0: skip the CPU baseline)")
     p.add_argument("--no-roofline", action="store_true", help="skip the per-launch event pass")
+    p.add_argument("--dense-q4", action="store_true",
+                   help="router rows and shared gate in 4 bits (MOE_FLAG_DENSE_Q4)")
     p.add_argument("--pool-frac", type=float, default=0.25,
                    help="pool_80b: slots as a fraction of the experts of the pack")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -61,10 +63,15 @@ def algorithmic_bytes(cfg, wl, unique_per_layer):
     sblob = int(wl.slayout.blob_bytes)
     per_layer = []
     for U in unique_per_layer:
-        b = E * H * 4                        # router weights (fp32)
+        if wl.dense_q4:
+            # router rows and shared gate: 4-bit codes + (scale, bias) words
+            R = E + 1
+            b = R * H // 2 + R * (H // 64) * 4
+        else:
+            b = E * H * 4 + H * 4            # router weights and shared gate vector (fp32)
         b += E * 4 if cfg.zipf_s else 0      # router bias
         b += U * blob                        # routed experts, each read once
-        b += sblob + H * 4                   # shared expert blob + its gate vector
+        b += sblob                           # shared expert blob
         b += 2 * T * H * act                 # x_hat in, out out
         per_layer.append(b)
     return per_layer
@@ -108,7 +115,7 @@ def main():
     t0 = time.time()
     print(f"# building {cfg.name}: {cfg.layers} layers, T={cfg.n_tokens}", file=sys.stderr,
           flush=True)
-    wl = workload.Workload(cfg)
+    wl = workload.Workload(cfg, dense_q4=args.dense_q4)
     print(f"# built in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     d = wl.desc
     L, T = cfg.layers, cfg.n_tokens
@@ -123,7 +130,7 @@ def main():
         x.copy_(xs[r])
 
     def forward():
-        moe.moe_chain_forward(d, L, x, wl.router_w, wl.router_bias, wl.slab, wl.slot_tables,
+        moe.moe_chain_forward(d, L, x, wl.router_all, wl.router_bias, wl.slab, wl.slot_tables,
                               wl.shared, wl.shared_stride, x_hat, out, ws)
 
     def chain(r):
@@ -220,7 +227,7 @@ def main():
     cpu = None
     n_cpu = args.cpu_layers if args.cpu_layers >= 0 else (L if T == 1 else 1)
     if n_cpu > 0:
-        cpu = cpu_baseline(cfg, min(n_cpu, L))
+        cpu = cpu_baseline(cfg, min(n_cpu, L), dense_q4=args.dense_q4)
 
     line = {
         "metric": "MoE-layer decode tokens/s and achieved HBM GB/s (% of peak), 1 GPU",
@@ -236,7 +243,7 @@ def main():
         "dtype": f"int{cfg.bits} weights x {cfg.act} activations, fp32 accumulate",
         "data": "synthetic",
         "config": {
-            "workload": describe(cfg),
+            "workload": describe(cfg, args.dense_q4),
             "tokens_per_step": T,
             "layers": L,
             "input_rotations": N_ROTATE,
@@ -268,11 +275,12 @@ def check_chain_status(moe, d, ws, what):
         raise SystemExit(f"chain status word {st:#x} after the {what}: a bounded wait expired")
 
 
-def describe(cfg):
+def describe(cfg, dense_q4=False):
     return (f"{cfg.name}: hidden {cfg.hidden}, {cfg.n_experts} experts top-{cfg.top_k}, "
             f"inter {cfg.inter}, shared {cfg.shared_inter} (sigmoid gate), int{cfg.bits} "
             f"group {cfg.group}, {cfg.act} activations, {cfg.n_tokens} token(s), "
-            f"{cfg.layers} chained layer(s)")
+            f"{cfg.layers} chained layer(s)"
+            + (", router and shared gate int4 group 64" if dense_q4 else ""))
 
 
 def chain_kernel_name(cfg):
@@ -362,7 +370,7 @@ def measured_traffic(cfg):
         return None
 
 
-def cpu_baseline(cfg, n_layers):
+def cpu_baseline(cfg, n_layers, dense_q4=False):
     """The C++ fp64 oracle, as it is, on a bounded sample: the first n_layers
     layers of the same chain for the bench's first input (the inputs of the
     selected experts are generated by an untimed first pass), on every host
@@ -374,7 +382,7 @@ def cpu_baseline(cfg, n_layers):
     import synth
     from oracle import cpp
     O = cpp.default()
-    inputs = [oracle.LayerInputs(cfg, l) for l in range(n_layers)]
+    inputs = [oracle.LayerInputs(cfg, l, dense_q4=dense_q4) for l in range(n_layers)]
     x0 = synth.activations(cfg)
 
     def run(layers):

@@ -336,7 +336,7 @@ int moe_chain_forward(const moe_layer_desc* desc, int32_t n_layers, void* x,
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_NO_DEVICE;
   const int nwg = chain_grid(dev);
-  if (!q4 && chain_supported(nwg, desc->n_tokens, desc->act_dtype, desc->hidden, desc->n_experts,
+  if (chain_supported(nwg, desc->n_tokens, desc->act_dtype, desc->hidden, desc->n_experts,
                       desc->top_k, desc->bits, desc->inter, shared ? desc->shared_inter : 0,
                       shared)) {
     const WsPlan P = make_ws_plan(*desc);
@@ -349,6 +349,11 @@ int moe_chain_forward(const moe_layer_desc* desc, int32_t n_layers, void* x,
     c.out = reinterpret_cast<uint16_t*>(out);
     c.router_w = router_w;
     c.router_bias = (desc->flags & MOE_FLAG_ROUTER_BIAS) ? router_bias : nullptr;
+    if (q4) {
+      c.dense = reinterpret_cast<const uint8_t*>(router_w);
+      c.dense_stride = router_step;
+      c.dense_words = make_dense_layout(*desc).words_off;
+    }
     c.slab = reinterpret_cast<const uint8_t*>(expert_slab);
     c.stride = desc->expert_stride;
     c.slot_tables = slot_tables;

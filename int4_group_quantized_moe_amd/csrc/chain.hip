@@ -249,6 +249,7 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
   uint4 dq[kMaxDownUnits];
   uint32_t dsb[kMaxDownUnits];
   float4 wr[kRR][NXP];  // router rows: the weights of the owned x elements
+  uint32_t wq[kRR], wsb[kRR];  // 4-bit dense rows: the owned elements' codes, their group's word
   float rbias = 0.0f;   // lane r: bias of router row r (when that row has one)
   int32_t slot_r[(EMAX + 255) / 256];
 
@@ -378,14 +379,29 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
   // for them.  (The shared tile: load_shared_tile.)
   auto prefetch = [&](int l) {
     const uint8_t* sblob = p.shared_blobs + (int64_t)l * p.shared_stride;
+    if (p.dense != nullptr) {
+      // dense blob: the 8 codes of the owned elements (one word) and the
+      // (scale, bias) word of their group; the shared gate is row E
+      const uint8_t* db = p.dense + (int64_t)l * p.dense_stride;
 #pragma unroll
-    for (int r = 0; r < kRR; ++r) {
-      const int row = w + NWG * r;
-      if (r < nrows) {
-        const float* rowp = row < E ? p.router_w + ((int64_t)l * E + row) * H
-                                    : reinterpret_cast<const float*>(sblob + LS.sg_off);
+      for (int r = 0; r < kRR; ++r) {
+        const int row = w + NWG * r;
+        if (r < nrows) {
+          wq[r] = *reinterpret_cast<const uint32_t*>(db + (int64_t)row * (H / 2) + 4 * tid);
+          wsb[r] = *reinterpret_cast<const uint32_t*>(db + p.dense_words +
+                                                     ((int64_t)row * (H / kGroup) + tid / 8) * 4);
+        }
+      }
+    } else {
 #pragma unroll
-        for (int m = 0; m < NXP; ++m) wr[r][m] = *reinterpret_cast<const float4*>(rowp + 8 * tid + 4 * m);
+      for (int r = 0; r < kRR; ++r) {
+        const int row = w + NWG * r;
+        if (r < nrows) {
+          const float* rowp = row < E ? p.router_w + ((int64_t)l * E + row) * H
+                                      : reinterpret_cast<const float*>(sblob + LS.sg_off);
+#pragma unroll
+          for (int m = 0; m < NXP; ++m) wr[r][m] = *reinterpret_cast<const float4*>(rowp + 8 * tid + 4 * m);
+        }
       }
     }
     // every lane loads (a clamped row): a load under a lane mask followed by
@@ -479,14 +495,23 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
     // the router logits first (their exchange gates the top-k): each
     // thread's partial dot product over its elements, summed per wave, then
     // over the 4 waves in a fixed order
+    // (4-bit dense rows: sum_i (s q_i + b) x_i = s sum_i q_i x_i + b sum_i x_i)
+    const float xsum8 = ((xv[0] + xv[1]) + (xv[2] + xv[3])) + ((xv[4] + xv[5]) + (xv[6] + xv[7]));
 #pragma unroll
     for (int r = 0; r < kRR; ++r) {
       if (r < nrows) {
         float acc = 0.f;
+        if (p.dense != nullptr) {
+          float qx = 0.f;
 #pragma unroll
-        for (int m = 0; m < NXP; ++m)
-          acc += (wr[r][m].x * xv[4 * m] + wr[r][m].y * xv[4 * m + 1]) +
-                 (wr[r][m].z * xv[4 * m + 2] + wr[r][m].w * xv[4 * m + 3]);
+          for (int i = 0; i < 8; ++i) qx += (float)((wq[r] >> (4 * i)) & 15u) * xv[i];
+          acc = bf16_bits_to_f32(wsb[r] & 0xFFFFu) * qx + bf16_bits_to_f32(wsb[r] >> 16) * xsum8;
+        } else {
+#pragma unroll
+          for (int m = 0; m < NXP; ++m)
+            acc += (wr[r][m].x * xv[4 * m] + wr[r][m].y * xv[4 * m + 1]) +
+                   (wr[r][m].z * xv[4 * m + 2] + wr[r][m].w * xv[4 * m + 3]);
+        }
         acc = wave_sum_dpp(acc);
         if (lane == 0) rred[r][wave] = acc;
       }

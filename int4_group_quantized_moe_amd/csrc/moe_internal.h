@@ -265,8 +265,10 @@ struct ChainParams {
   uint16_t* x;                   // [H] residual stream in/out
   uint16_t* x_hat;               // [H] last layer's normalised input
   uint16_t* out;                 // [H] last layer's output
-  const float* router_w;         // [L][E][H]
+  const float* router_w;         // [L][E][H] (unused with dense)
   const float* router_bias;      // [L][E] or null
+  const uint8_t* dense;          // MOE_FLAG_DENSE_Q4: layer l's dense blob at l * dense_stride
+  int64_t dense_stride, dense_words;
   const uint8_t* slab;
   int64_t stride;
   const int32_t* slot_tables;    // [L][E]
