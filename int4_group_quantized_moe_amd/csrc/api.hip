@@ -140,7 +140,8 @@ int enqueue_experts(const moe_layer_desc* d, const void* x, const int32_t* idx, 
   a.k = d->top_k;
   a.act = d->act_dtype;
   a.bits = d->bits;
-  a.mfma = a.plan.bucketed && prefill_supported(a.act, a.T, a.H, d->inter, a.Ls.inter, a.has_shared);
+  a.mfma = a.plan.bucketed &&
+           prefill_supported(a.act, a.T, a.H, a.k, d->inter, a.Ls.inter, a.has_shared);
   return to_status(launch_experts(a, s));
 }
 

@@ -202,7 +202,7 @@ struct PrefillArgs {
   int T, H, E, k, I, Is, bits;
   bool has_shared;
 };
-bool prefill_supported(int act, int64_t T, int H, int I, int Is, bool has_shared);
+bool prefill_supported(int act, int64_t T, int H, int k, int I, int Is, bool has_shared);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 // One token block (T <= 64): the same GEMMs with every weight tile requested
 // up front (batched.hip); h is written as fp32 rows of `inter` floats.
@@ -216,15 +216,16 @@ hipError_t launch_x16(const uint16_t* x, uint16_t* x16, int32_t* xe, int T, int 
 inline bool mfma_path(const moe_layer_desc& d) {
   const bool sh = (d.flags & MOE_FLAG_SHARED) != 0;
   return d.n_tokens > kDecodeMaxTokens &&
-         prefill_supported(d.act_dtype, d.n_tokens, d.hidden, d.inter, sh ? d.shared_inter : d.inter,
-                           sh);
+         prefill_supported(d.act_dtype, d.n_tokens, d.hidden, d.top_k, d.inter,
+                           sh ? d.shared_inter : d.inter, sh);
 }
 // Whether it runs the one-token-block variant: batches of 9..64 tokens.
 inline bool one_block_path(const moe_layer_desc& d) {
   const bool sh = (d.flags & MOE_FLAG_SHARED) != 0;
   const int Is = sh ? d.shared_inter : 0;
   return d.n_tokens > kDecodeMaxTokens && d.n_tokens <= kOneBlockTokens && d.n_experts < 1024 &&
-         prefill_supported(d.act_dtype, d.n_tokens, d.hidden, d.inter, sh ? Is : d.inter, sh) &&
+         prefill_supported(d.act_dtype, d.n_tokens, d.hidden, d.top_k, d.inter, sh ? Is : d.inter,
+                           sh) &&
          batched_supported(d.act_dtype, d.n_tokens, d.hidden, d.inter, Is, sh);
 }
 

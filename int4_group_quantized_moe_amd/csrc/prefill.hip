@@ -476,6 +476,12 @@ __device__ __forceinline__ constexpr int dn_slot(int p) {
 // padding (272 bytes), so that a lane's 64 values of one column sit at one
 // base address plus immediate offsets and the row reads are conflict free.
 constexpr int kHStageRow = 272;
+// down epilogue: a wave's 32 x 64 fp32 block staged with rows of 68 floats
+// (16-byte aligned rows, conflict-free column writes); the offset given to
+// rows past a tile (the partial buffer is kept below 2 GiB)
+constexpr int kEpRow = 68;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+constexpr uint32_t kDropOffset = 0x80000000u;
 
 // silu(g) * u with a hardware reciprocal (the result is rounded to fp16)
 __device__ __forceinline__ float swiglu(float g, float u) {
@@ -611,7 +617,7 @@ __device__ __forceinline__ void prefill_gateup_item(MOE_PGU_PARAMS, Stage<BITS>*
 
 template <int BITS, int MB>
 __device__ __forceinline__ void prefill_down_item(MOE_PDN_PARAMS, Stage<BITS>* st,
-                                                  int32_t* rowdst, float* roww, float* hsl,
+                                                  uint32_t* rowdst, float* roww, float* hsl,
                                                   const TileInfo& ti, int nb) {
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));  // (as in the gate/up item)
@@ -623,9 +629,12 @@ __device__ __forceinline__ void prefill_down_item(MOE_PDN_PARAMS, Stage<BITS>* s
                               : slab + (int64_t)slot_table[ti.e] * stride + d_off_r;
   const int64_t unit_b = shared ? d_unit_s : d_unit_r, tile_b = shared ? d_tile_s : d_tile_r;
   if (tid < kMT) {
-    int dst = -1;
+    // byte offset of the row's partial row (rows past the tile: an offset
+    // past the buffer, whose stores the hardware drops)
+    uint32_t off = kDropOffset;
     float wv = 0.f;
     if (tid < ti.rows) {
+      int dst;
       if (shared) {
         const int t = ti.base + tid;
         dst = t * (k + 1) + k;
@@ -635,8 +644,9 @@ __device__ __forceinline__ void prefill_down_item(MOE_PDN_PARAMS, Stage<BITS>* s
         dst = (p / k) * (k + 1) + (p % k);
         wv = topk_w[p];
       }
+      off = (uint32_t)dst * (uint32_t)H * 4u;
     }
-    rowdst[tid] = dst;
+    rowdst[tid] = off;
     roww[tid] = wv;
   }
   const int G = inter / kGroup;
@@ -673,23 +683,36 @@ __device__ __forceinline__ void prefill_down_item(MOE_PDN_PARAMS, Stage<BITS>* s
         return hs * inv_hmax;
       });
 
+  // Epilogue.  The ring is free (every wave is past the last stage's
+  // barrier).  Each wave turns its 32 x 64 blocks into rows through its own
+  // LDS region and stores each row as 16-byte pieces of 4 columns: lane
+  // (c4, r4) takes columns 4 c4 .. 4 c4 + 3 of rows r4, r4 + 4, ...  The
+  // factor roww * hmax is exact to apply in one product (hmax is a power of
+  // two).
+  float* ep = reinterpret_cast<float*>(st) + wave * (32 * kEpRow);
+  const auto rp = __builtin_amdgcn_make_buffer_rsrc(
+      partial, (short)0, (int)((uint32_t)T * (uint32_t)(k + 1) * (uint32_t)H * 4u), 0x00020000);
+  const int c4 = lane & 15, r4 = lane >> 4;
+  const uint32_t col_b = (uint32_t)(n0 + 64 * wave + 4 * c4) * 4u;
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+  for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int m0 = 32 * mb + 8 * q + 4 * half;
-      const int4 d4 = *reinterpret_cast<const int4*>(&rowdst[m0]);
-      const float4 w4 = *reinterpret_cast<const float4*>(&roww[m0]);
-      const int dv[4] = {d4.x, d4.y, d4.z, d4.w};
-      const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
+    for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (dv[i] >= 0) {
-          float* prow = partial + (int64_t)dv[i] * H + n0 + 64 * wave + l32;
-          prow[0] = wv[i] * (hmax * C[mb][0][4 * q + i]);
-          prow[32] = wv[i] * (hmax * C[mb][1][4 * q + i]);
-        }
+      for (int r = 0; r < 16; ++r)
+        ep[(8 * (r >> 2) + 4 * half + (r & 3)) * kEpRow + 32 * nb + l32] = C[mb][nb][r];
+    asm volatile("" ::: "memory");  // the wave's LDS accesses stay in order
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = r4 + 4 * j, m = 32 * mb + row;
+      const float4 v = *reinterpret_cast<const float4*>(&ep[row * kEpRow + 4 * c4]);
+      const float f = roww[m] * hmax;
+      const f32x4 o = {v.x * f, v.y * f, v.z * f, v.w * f};
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rp,
+                                             rowdst[m] + col_b, 0, 0);
     }
+    asm volatile("" ::: "memory");
+  }
 }
 
 // Persistent grids: workgroup w serves XCD w % 8 and walks that XCD's item
@@ -727,7 +750,7 @@ template <int BITS>
 __global__ __launch_bounds__(kGemmThreads, BITS == 4 ? 2 : 1) void prefill_down_kernel(
     MOE_PDN_PARAMS) {
   __shared__ __align__(256) Stage<BITS> st[kStages];
-  __shared__ __align__(16) int32_t rowdst[kMT];
+  __shared__ __align__(16) uint32_t rowdst[kMT];
   __shared__ __align__(16) float roww[kMT];
   __shared__ float hsl[MOE_MAX_INTER / kGroup];
   const int total = *ntiles * nbg;
@@ -785,11 +808,13 @@ int prefill_max_tiles(int T, int E, int k, bool has_shared) {
   return (int)(rows / kMT + E + (has_shared ? 1 : 0) + 1);
 }
 
-bool prefill_supported(int act, int64_t T, int H, int I, int Is, bool has_shared) {
+bool prefill_supported(int act, int64_t T, int H, int k, int I, int Is, bool has_shared) {
   if (act != MOE_ACT_BF16) return false;
   if (H % kTileN != 0 || I % kHCols != 0 || (has_shared && Is % kHCols != 0)) return false;
   // the gate/up kernel addresses the fp16 activation rows with 32-bit byte offsets
   if (T * H * 2 >= (int64_t)1 << 32) return false;
+  // the down kernel's partial rows: 32-bit offsets below kDropOffset
+  if (T * (k + 1) * H * 4 > (int64_t)kDropOffset - (int64_t)H * 4) return false;
   return true;
 }
 
