@@ -476,10 +476,11 @@ __device__ __forceinline__ constexpr int dn_slot(int p) {
 // padding (272 bytes), so that a lane's 64 values of one column sit at one
 // base address plus immediate offsets and the row reads are conflict free.
 constexpr int kHStageRow = 272;
-// down epilogue: a wave's 32 x 64 fp32 block staged with rows of 68 floats
-// (16-byte aligned rows, conflict-free column writes); the offset given to
-// rows past a tile (the partial buffer is kept below 2 GiB)
-constexpr int kEpRow = 68;
+// down epilogue: a wave's 32 x 64 fp32 block staged with rows of 72 floats
+// (16-byte aligned rows; a column write's two half-waves, 4 rows apart, fall
+// 32 banks apart); the offset given to rows past a tile (the partial buffer
+// is kept below 2 GiB)
+constexpr int kEpRow = 72;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr uint32_t kDropOffset = 0x80000000u;
 
