@@ -397,11 +397,12 @@ template <int ACT>
 hipError_t launch_router_act(const RouterArgs& a, hipStream_t s) {
   int nplanes = 1;
   if (router_uses_mfma(a.act, a.T, a.H)) {
-    // split K so that small batches still fill the chip (at most the planes
-    // the workspace holds)
+    // split K so that the grid fills the chip at two workgroups per CU (a
+    // workgroup's split-weight work then overlaps the other's MFMAs; at most
+    // the planes the workspace holds)
     const int tiles = ((a.E + kRouterTile - 1) / kRouterTile) * ((a.T + kRouterTile - 1) / kRouterTile);
     const int maxp = router_planes(a.T);
-    while (nplanes < maxp && tiles * nplanes < 256 && (a.H / 64) % (2 * nplanes) == 0) nplanes *= 2;
+    while (nplanes < maxp && tiles * nplanes < 512 && (a.H / 64) % (2 * nplanes) == 0) nplanes *= 2;
     // the shared-gate vector rides as row E of the GEMM when that costs no
     // extra round of workgroups (a free row in the last tile, or the grid
     // still within one workgroup per CU); else its own small kernel
