@@ -627,50 +627,61 @@ __device__ __forceinline__ float round_act1(float v) {
 
 // out[t] = sum over the token's k routed slots and the shared slot of the
 // weighted partial rows, in slot order, rounded to the act dtype.  One
-// workgroup per token; thread i holds columns 4 (i + 256 r) .. +3.  With
-// epi >= 1 it also adds the residual, x_res[t] = act(x_res[t] + out[t]), and
-// with epi == 2 writes the next layer's input act(rmsnorm(x_res[t])) (unit
-// weight), so a chain needs no separate launch between layers.
-template <int ACT>
+// workgroup per token; thread i holds columns 8 (i + 256 r) .. +7, so that
+// at hidden <= 2048 every load of a thread is in flight at once (one memory
+// round trip per token).  With epi >= 1 it also adds the residual, x_res[t] =
+// act(x_res[t] + out[t]), and with epi == 2 writes the next layer's input
+// act(rmsnorm(x_res[t])) (unit weight), so a chain needs no separate launch
+// between layers.  NJ = the most slots a call has (k + 1 <= NJ).
+template <int ACT, int NJ>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ partial,
                                                       void* __restrict__ out, int H, int k,
                                                       int has_shared, void* __restrict__ x_res,
                                                       void* __restrict__ x_hat, float eps,
                                                       int epi) {
-  constexpr int kR = MOE_MAX_HIDDEN / 1024;
+  constexpr int kR = MOE_MAX_HIDDEN / 2048;
   __shared__ float wsum[4];
   const int t = blockIdx.x;
   const int nj = k + has_shared;
   const int64_t base = (int64_t)t * H;
-  float4 v[kR];
+  float4 v[kR][2];
   float ss = 0.f;
 #pragma unroll
   for (int r = 0; r < kR; ++r) {
-    const int c = (r * 256 + (int)threadIdx.x) * 4;
+    const int c = (r * 256 + (int)threadIdx.x) * 8;
     if (c >= H) continue;
-    float4 p[MOE_MAX_TOP_K + 1];
+    float4 p[NJ][2];
 #pragma unroll
-    for (int j = 0; j < MOE_MAX_TOP_K + 1; ++j)
-      if (j < nj) p[j] = *reinterpret_cast<const float4*>(partial + ((int64_t)t * (k + 1) + j) * H + c);
-    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int j = 0; j < MOE_MAX_TOP_K + 1; ++j) {
+    for (int j = 0; j < NJ; ++j)
       if (j < nj) {
-        a.x += p[j].x;
-        a.y += p[j].y;
-        a.z += p[j].z;
-        a.w += p[j].w;
+        const float4* src =
+            reinterpret_cast<const float4*>(partial + ((int64_t)t * (k + 1) + j) * H + c);
+        p[j][0] = src[0];
+        p[j][1] = src[1];
       }
-    }
-    store_act4v<ACT>(out, base + c, a);
-    if (epi >= 1) {
-      const float4 xr = load_act4v<ACT>(x_res, base + c);
-      v[r] = make_float4(round_act1<ACT>(xr.x + round_act1<ACT>(a.x)),
-                         round_act1<ACT>(xr.y + round_act1<ACT>(a.y)),
-                         round_act1<ACT>(xr.z + round_act1<ACT>(a.z)),
-                         round_act1<ACT>(xr.w + round_act1<ACT>(a.w)));
-      store_act4v<ACT>(x_res, base + c, v[r]);
-      ss += (v[r].x * v[r].x + v[r].y * v[r].y) + (v[r].z * v[r].z + v[r].w * v[r].w);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        if (j < nj) {
+          a.x += p[j][h].x;
+          a.y += p[j][h].y;
+          a.z += p[j][h].z;
+          a.w += p[j][h].w;
+        }
+      }
+      store_act4v<ACT>(out, base + c + 4 * h, a);
+      if (epi >= 1) {
+        const float4 xr = load_act4v<ACT>(x_res, base + c + 4 * h);
+        v[r][h] = make_float4(round_act1<ACT>(xr.x + round_act1<ACT>(a.x)),
+                              round_act1<ACT>(xr.y + round_act1<ACT>(a.y)),
+                              round_act1<ACT>(xr.z + round_act1<ACT>(a.z)),
+                              round_act1<ACT>(xr.w + round_act1<ACT>(a.w)));
+        store_act4v<ACT>(x_res, base + c + 4 * h, v[r][h]);
+        ss += (v[r][h].x * v[r][h].x + v[r][h].y * v[r][h].y) +
+              (v[r][h].z * v[r][h].z + v[r][h].w * v[r][h].w);
+      }
     }
   }
   if (epi < 2) return;
@@ -681,10 +692,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const float inv = 1.0f / sqrtf(tot / (float)H + eps);
 #pragma unroll
   for (int r = 0; r < kR; ++r) {
-    const int c = (r * 256 + (int)threadIdx.x) * 4;
+    const int c = (r * 256 + (int)threadIdx.x) * 8;
     if (c < H)
-      store_act4v<ACT>(x_hat, base + c,
-                       make_float4(v[r].x * inv, v[r].y * inv, v[r].z * inv, v[r].w * inv));
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        store_act4v<ACT>(x_hat, base + c + 4 * h,
+                         make_float4(v[r][h].x * inv, v[r][h].y * inv, v[r][h].z * inv,
+                                     v[r][h].w * inv));
   }
 }
 
@@ -1178,8 +1192,12 @@ hipError_t launch_experts_t(const ExpertArgs& a, hipStream_t s) {
                        small_list, n_small, a.L.n_tiles_d);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((combine_kernel<ACT>), dim3(a.T), dim3(256), 0, s, partial, a.out, a.H, a.k,
-                     hs, a.x_res, a.x_hat_next, a.eps, a.epi);
+  if (a.k + hs <= 12)
+    hipLaunchKernelGGL((combine_kernel<ACT, 12>), dim3(a.T), dim3(256), 0, s, partial, a.out, a.H,
+                       a.k, hs, a.x_res, a.x_hat_next, a.eps, a.epi);
+  else
+    hipLaunchKernelGGL((combine_kernel<ACT, MOE_MAX_TOP_K + 1>), dim3(a.T), dim3(256), 0, s,
+                       partial, a.out, a.H, a.k, hs, a.x_res, a.x_hat_next, a.eps, a.epi);
   return hipGetLastError();
 }
 
