@@ -153,8 +153,9 @@ __device__ __forceinline__ uint32_t gload4(gbyte* a) {
 // IR, IS: intermediate size of the routed and of the shared experts; the
 // blob geometry is compile-time.
 // EPL: logits per lane of the top-k wave (E <= 64 EPL).  EC, KC: the
-// number of experts and top-k when fixed at compile time (0: from p).
-template <int BITS, int NIT, bool SHARED, int IR, int IS, int EPL, int EC, int KC>
+// number of experts and top-k when fixed at compile time (0: from p).  DQ4:
+// the router rows and shared gate come as 4-bit dense rows (p.dense).
+template <int BITS, int NIT, bool SHARED, int IR, int IS, int EPL, int EC, int KC, bool DQ4>
 __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
   static_assert(BITS == 4, "the chain runs int4 weights");
   using C = GuCfg<BITS>;
@@ -249,7 +250,8 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
   uint4 dq[kMaxDownUnits];
   uint32_t dsb[kMaxDownUnits];
   float4 wr[kRR][NXP];  // router rows: the weights of the owned x elements
-  uint32_t wq[kRR], wsb[kRR];  // 4-bit dense rows: the owned elements' codes, their group's word
+  uint32_t wq[DQ4 ? kRR : 1], wsb[DQ4 ? kRR : 1];  // 4-bit dense rows: the owned elements' codes,
+                                                   // their group's word
   float rbias = 0.0f;   // lane r: bias of router row r (when that row has one)
   int32_t slot_r[(EMAX + 255) / 256];
 
@@ -379,7 +381,7 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
   // for them.  (The shared tile: load_shared_tile.)
   auto prefetch = [&](int l) {
     const uint8_t* sblob = p.shared_blobs + (int64_t)l * p.shared_stride;
-    if (p.dense != nullptr) {
+    if constexpr (DQ4) {
       // dense blob: the 8 codes of the owned elements (one word) and the
       // (scale, bias) word of their group; the shared gate is row E
       const uint8_t* db = p.dense + (int64_t)l * p.dense_stride;
@@ -496,12 +498,13 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(ChainParams p) {
     // thread's partial dot product over its elements, summed per wave, then
     // over the 4 waves in a fixed order
     // (4-bit dense rows: sum_i (s q_i + b) x_i = s sum_i q_i x_i + b sum_i x_i)
-    const float xsum8 = ((xv[0] + xv[1]) + (xv[2] + xv[3])) + ((xv[4] + xv[5]) + (xv[6] + xv[7]));
 #pragma unroll
     for (int r = 0; r < kRR; ++r) {
       if (r < nrows) {
         float acc = 0.f;
-        if (p.dense != nullptr) {
+        if constexpr (DQ4) {
+          const float xsum8 =
+              ((xv[0] + xv[1]) + (xv[2] + xv[3])) + ((xv[4] + xv[5]) + (xv[6] + xv[7]));
           float qx = 0.f;
 #pragma unroll
           for (int i = 0; i < 8; ++i) qx += (float)((wq[r] >> (4 * i)) & 15u) * xv[i];
@@ -804,18 +807,20 @@ hipError_t launch_chain(const ChainParams& prm, int nwg, hipStream_t s) {
   void* args[] = {const_cast<ChainParams*>(&prm)};
   if (prm.bits_ != 4 || prm.H != 2048 || prm.I != 512) return hipErrorInvalidValue;
   if (prm.has_shared && prm.Is != 512) return hipErrorInvalidValue;
-  const bool small = prm.E <= 256;
+  const bool small = prm.E <= 256, dq = prm.dense != nullptr;
+#define MOE_CHAIN_FN(SH, EPL, EC, KC)                                                         \
+  (dq ? reinterpret_cast<const void*>(&chain_kernel<4, 8, SH, 512, 512, EPL, EC, KC, true>) \
+      : reinterpret_cast<const void*>(&chain_kernel<4, 8, SH, 512, 512, EPL, EC, KC, false>))
   const void* fn;
   if (prm.has_shared && prm.E == 256 && prm.k == 8)
-    fn = reinterpret_cast<const void*>(&chain_kernel<4, 8, true, 512, 512, 4, 256, 8>);
+    fn = MOE_CHAIN_FN(true, 4, 256, 8);
   else if (prm.has_shared && prm.E == 512 && prm.k == 10)
-    fn = reinterpret_cast<const void*>(&chain_kernel<4, 8, true, 512, 512, 8, 512, 10>);
+    fn = MOE_CHAIN_FN(true, 8, 512, 10);
   else if (prm.has_shared)
-    fn = small ? reinterpret_cast<const void*>(&chain_kernel<4, 8, true, 512, 512, 4, 0, 0>)
-               : reinterpret_cast<const void*>(&chain_kernel<4, 8, true, 512, 512, 8, 0, 0>);
+    fn = small ? MOE_CHAIN_FN(true, 4, 0, 0) : MOE_CHAIN_FN(true, 8, 0, 0);
   else
-    fn = small ? reinterpret_cast<const void*>(&chain_kernel<4, 8, false, 512, 512, 4, 0, 0>)
-               : reinterpret_cast<const void*>(&chain_kernel<4, 8, false, 512, 512, 8, 0, 0>);
+    fn = small ? MOE_CHAIN_FN(false, 4, 0, 0) : MOE_CHAIN_FN(false, 8, 0, 0);
+#undef MOE_CHAIN_FN
   return hipLaunchCooperativeKernel(fn, dim3(nwg), dim3(256), args, (unsigned)lds, s);
 }
 
