@@ -214,7 +214,8 @@ def main():
 
     roofline = None
     if not args.no_roofline:
-        roofline = chain_roofline(cfg, load_input, forward, bytes_per_rot, step_flops)
+        roofline = chain_roofline(cfg, load_input, forward, bytes_per_rot, step_flops,
+                                  dense_q4=args.dense_q4)
         check_chain_status(moe, d, ws, "roofline pass")
 
     # release the captured graphs (they hold the cooperative chain launch)
@@ -283,17 +284,20 @@ def describe(cfg, dense_q4=False):
             + (", router and shared gate int4 group 64" if dense_q4 else ""))
 
 
-def chain_kernel_name(cfg):
+def chain_kernel_name(cfg, dense_q4=False):
     """The instantiation of the persistent chain kernel that runs this
-    configuration (as the library dispatches it)."""
+    configuration (as the library dispatches it; the last argument selects
+    the 4-bit dense router rows)."""
     shared = "true" if cfg.shared_inter else "false"
     epl = 4 if cfg.n_experts <= 256 else 8
     spec = (cfg.n_experts, cfg.top_k) in ((256, 8), (512, 10)) and cfg.shared_inter
     ec, kc = (cfg.n_experts, cfg.top_k) if spec else (0, 0)
-    return f"chain_kernel<4, 8, {shared}, {cfg.inter}, {cfg.shared_inter or 512}, {epl}, {ec}, {kc}>"
+    dq = "true" if dense_q4 else "false"
+    return (f"chain_kernel<4, 8, {shared}, {cfg.inter}, {cfg.shared_inter or 512}, {epl}, {ec}, "
+            f"{kc}, {dq}>")
 
 
-def chain_roofline(cfg, load_input, forward, bytes_per_rot, flops, reps=64):
+def chain_roofline(cfg, load_input, forward, bytes_per_rot, flops, reps=64, dense_q4=False):
     """Average duration of one moe_chain_forward launch (for batch-1 bf16
     int4 decode this is the single persistent kernel that streams every
     layer's weights), timed with HIP events on the launch stream around the
@@ -318,7 +322,8 @@ def chain_roofline(cfg, load_input, forward, bytes_per_rot, flops, reps=64):
     avg_b = sum(bytes_per_rot[i % N_ROTATE] for i in range(reps)) / reps
     achieved = avg_b / avg_s / 1e9
     persistent = cfg.n_tokens == 1 and cfg.act == "bf16" and cfg.bits == 4
-    traffic = measured_traffic(cfg) if persistent else None
+    # (the counter summaries in profiles/ are of the fp32-router kernel)
+    traffic = measured_traffic(cfg) if persistent and not dense_q4 else None
     if flops / avg_b > MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9):
         # above the ridge point (a prefill chunk): the matrix cores bound it
         tf = flops / avg_s / 1e12
@@ -333,8 +338,8 @@ def chain_roofline(cfg, load_input, forward, bytes_per_rot, flops, reps=64):
                 "flops_per_launch": int(flops), "bytes_per_launch": int(avg_b),
                 "launches": reps}
     return {"bound": "hbm",
-            "kernel": (f"{chain_kernel_name(cfg)}: the persistent decode-chain kernel, one launch "
-                       f"per {cfg.layers}-layer step" if persistent else
+            "kernel": (f"{chain_kernel_name(cfg, dense_q4)}: the persistent decode-chain kernel, "
+                       f"one launch per {cfg.layers}-layer step" if persistent else
                        "moe_chain_forward: all kernels of one chain step"),
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
