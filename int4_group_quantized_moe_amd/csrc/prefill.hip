@@ -31,6 +31,7 @@
 // permuted within each 8-value chunk ((0,4), (1,5), (2,6), (3,7) for int4;
 // (0,2), (1,3) per word for int8); the activations and h are stored in the
 // same order, so the products pair up.
+#include "decode_common.h"
 #include "mfma_common.h"
 
 namespace moe {
@@ -550,11 +551,11 @@ __device__ __forceinline__ void prefill_gateup_item(MOE_PGU_PARAMS, Stage<BITS>*
         const float f = exp2i(ev[i]);
         const float hh = swiglu(C[mb][0][4 * q + i] * f, C[mb][1][4 * q + i] * f);
         C[mb][0][4 * q + i] = hh;
-        if (m0 + i < ti.rows) amax = max(amax, __float_as_uint(hh) & 0x7FFFFFFFu);
+        // (rows past the tile computed row 0's token: the same values)
+        amax = max(amax, __float_as_uint(hh) & 0x7FFFFFFFu);
       }
     }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, off, 64));
+  amax = dec::wave_max_dpp(amax);
   if (lane == 0) wmax[wave] = amax;
   __syncthreads();
   amax = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
