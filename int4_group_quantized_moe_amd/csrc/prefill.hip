@@ -179,25 +179,47 @@ struct LoadRoles {
 // Issue one stage: activation chunks from `abase` (+ group offset) of the MB
 // live row blocks (load j covers rows 32 j .. 32 j + 31 in every wave), codes
 // and words of group g of the weight section.
+// Buffer views of a tile's two sources: the activation (or h) rows and the
+// weight section.  A stage's loads add the lane's fixed 32-bit offset (its
+// load role) to a scalar offset that advances with the group, so they take
+// no per-lane address arithmetic; an offset past the view reads zeros.
+struct TileSrc {
+  __amdgpu_buffer_rsrc_t a, w;
+};
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t src_view(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// One buffer load of 16 (4) bytes per lane into LDS at `lds` + 16 (4) bytes
+// per lane.  (Only the device pass compiles the builtin; the host pass never
+// runs it.)
+__device__ __forceinline__ void buf_lds16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff,
+                                          int soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, MOE_L3(lds), 16, voff, soff, 0, 0);
+#endif
+}
+__device__ __forceinline__ void buf_lds4(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff,
+                                         int soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, MOE_L3(lds), 4, voff, soff, 0, 0);
+#endif
+}
+
 template <int BITS, int MB>
 __device__ __forceinline__ void issue_stage(Stage<BITS>& st, const LoadRoles<BITS>& lr,
-                                            const uint8_t* abase, const uint8_t* sec,
-                                            int64_t unit_b, int g, int wv) {
+                                            const TileSrc& src, int64_t unit_b, int g, int wv) {
   constexpr int GPK = kRowBytes * (8 / BITS) / kGroup;
   constexpr int GBYTES = kGroup * BITS / 8;
-  const uint8_t* aa = abase + (int64_t)g * kGroup * 2;
+  const int ao = g * kGroup * 2;
 #pragma unroll
-  for (int j = 0; j < MB; ++j)
-    __builtin_amdgcn_global_load_lds(MOE_G1(aa + lr.a[j]), MOE_L3(&st.A[j * 256 + wv * 64]), 16,
-                                     0, 0);
-  const uint8_t* kb = sec + (int64_t)(g / GPK) * unit_b;
-  const uint8_t* wb = kb + (g % GPK) * GBYTES;
+  for (int j = 0; j < MB; ++j) buf_lds16(src.a, &st.A[j * 256 + wv * 64], lr.a[j], ao);
+  const int ko = (int)((g / GPK) * unit_b);
 #pragma unroll
   for (int j = 0; j < cpr<BITS>(); ++j)
-    __builtin_amdgcn_global_load_lds(MOE_G1(wb + lr.b[j]), MOE_L3(&st.B[j * 256 + wv * 64]), 16,
-                                     0, 0);
-  __builtin_amdgcn_global_load_lds(MOE_G1(kb + (g % GPK) * 4 + lr.s), MOE_L3(&st.S[wv * 64]), 4,
-                                   0, 0);
+    buf_lds16(src.w, &st.B[j * 256 + wv * 64], lr.b[j], ko + (g % GPK) * GBYTES);
+  buf_lds4(src.w, &st.S[wv * 64], lr.s, ko + (g % GPK) * 4);
 }
 
 // Operand roles of a lane: LDS byte offsets (within a stage) of its A chunks
@@ -376,13 +398,12 @@ __device__ __forceinline__ void multiply(const u32x4 (&a)[2][MB], const u32x4 (&
 // group's (scale, bias) pair (the down GEMM's h scale alignment).
 template <int BITS, int MB, int DB, int DS, typename R>
 __device__ __forceinline__ void k_loop(Stage<BITS>* st, const LoadRoles<BITS>& lr,
-                                       const FragRoles& fr, const uint8_t* abase,
-                                       const uint8_t* sec, int64_t unit_b, int G, int wv,
-                                       f32x16 (&C)[MB][2], R&& ratio) {
+                                       const FragRoles& fr, const TileSrc& src, int64_t unit_b,
+                                       int G, int wv, f32x16 (&C)[MB][2], R&& ratio) {
   constexpr int L = stage_loads<BITS, MB>();
   static_assert(kStages == 3, "wait ladder below covers kStages - 1 = 2 later stages");
   const ExpandConsts ec = expand_consts<BITS>();
-  for (int g = 0; g < min(kStages, G); ++g) issue_stage<BITS, MB>(st[g], lr, abase, sec, unit_b, g, wv);
+  for (int g = 0; g < min(kStages, G); ++g) issue_stage<BITS, MB>(st[g], lr, src, unit_b, g, wv);
   for (int g = 0, slot = 0; g < G; ++g, slot = slot == kStages - 1 ? 0 : slot + 1) {
     const int later = min(kStages - 1, G - 1 - g);
     if (later >= 2) wait_vm<2 * L>();
@@ -402,7 +423,7 @@ __device__ __forceinline__ void k_loop(Stage<BITS>* st, const LoadRoles<BITS>& l
     multiply<BITS, MB>(a, q, S2, B2, 0, ec, C);
     read_a<MB>(base, fr, 2, a);
     lds_barrier();
-    if (g + kStages < G) issue_stage<BITS, MB>(st[slot], lr, abase, sec, unit_b, g + kStages, wv);
+    if (g + kStages < G) issue_stage<BITS, MB>(st[slot], lr, src, unit_b, g + kStages, wv);
     multiply<BITS, MB>(a, q, S2, B2, 2, ec, C);
   }
 }
@@ -531,9 +552,13 @@ __device__ __forceinline__ void prefill_gateup_item(MOE_PGU_PARAMS, Stage<BITS>*
   const f32x16 zero = {};
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) C[mb][0] = C[mb][1] = zero;
+  // (views: the fp16 activation rows of all tokens; the section's row tiles
+  // of gate and up rows)
+  const TileSrc src{src_view(x16, (uint32_t)T * (uint32_t)H * 2u),
+                    src_view(sec, (uint32_t)((inter / kRowTile) * tile_b))};
   k_loop<BITS, MB, 128 * cpr<BITS>() * 16, 128 * 4>(
-      st, lr, fr, reinterpret_cast<const uint8_t*>(x16), sec, unit_b, H / kGroup,
-      __builtin_amdgcn_readfirstlane(wave), C, [](int) { return 1.0f; });
+      st, lr, fr, src, unit_b, H / kGroup, __builtin_amdgcn_readfirstlane(wave), C,
+      [](int) { return 1.0f; });
 
   // epilogue: undo the rows' activation scales, h = silu(g) * u
   if (tid < kMT) te[tid] = my_e;
@@ -674,9 +699,11 @@ __device__ __forceinline__ void prefill_down_item(MOE_PDN_PARAMS, Stage<BITS>* s
   const f32x16 zero = {};
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) C[mb][0] = C[mb][1] = zero;
+  // (views: the tile's h rows; the section's row tiles of down rows)
+  const TileSrc src{src_view(h + hbase, (uint32_t)ti.rows * (uint32_t)inter * 4u),
+                    src_view(sec, (uint32_t)((H / kRowTile) * tile_b))};
   k_loop<BITS, MB, 32 * cpr<BITS>() * 16, 32 * 4>(
-      st, lr, fr, reinterpret_cast<const uint8_t*>(h + hbase), sec, unit_b, G,
-      __builtin_amdgcn_readfirstlane(wave), C, [&](int g) {
+      st, lr, fr, src, unit_b, G, __builtin_amdgcn_readfirstlane(wave), C, [&](int g) {
         float hs;
         asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)"
                      : "=v"(hs)
