@@ -289,94 +289,105 @@ __device__ __forceinline__ u32x4 expand(const u32x4 (&q)[BITS / 4], int kk, f16x
                fma_pair(c[3], S2, B2)};
 }
 
-// A operands of K steps k0, k0 + 1 for the MB live row blocks (block mb at
-// + mb * 4096 bytes)
-template <int MB>
-__device__ __forceinline__ void read_a(uint32_t base, const FragRoles& fr, int k0,
-                                       u32x4 (&a)[2][MB]) {
-  const uint32_t p = base + fr.a[k0], q = base + fr.a[k0 + 1];
+// A operands of K steps k0, k0 + 1 for the MB live row blocks: lane LDS
+// addresses p (step k0) and q (k0 + 1) of row block 0 in the stage at byte
+// offset SO past them (block mb adds mb * 4096)
+template <int MB, uint32_t SO>
+__device__ __forceinline__ void read_a_at(uint32_t p, uint32_t q, u32x4 (&a)[2][MB]) {
+  static_assert(SO + 4096 * (MB - 1) < 65536, "ds_read offset field");
   if constexpr (MB == 4) {
     asm volatile(
-        "ds_read_b128 %0, %8\n\t"
-        "ds_read_b128 %1, %8 offset:4096\n\t"
-        "ds_read_b128 %2, %8 offset:8192\n\t"
-        "ds_read_b128 %3, %8 offset:12288\n\t"
-        "ds_read_b128 %4, %9\n\t"
-        "ds_read_b128 %5, %9 offset:4096\n\t"
-        "ds_read_b128 %6, %9 offset:8192\n\t"
-        "ds_read_b128 %7, %9 offset:12288\n\t"
+        "ds_read_b128 %0, %8 offset:%10\n\t"
+        "ds_read_b128 %1, %8 offset:%11\n\t"
+        "ds_read_b128 %2, %8 offset:%12\n\t"
+        "ds_read_b128 %3, %8 offset:%13\n\t"
+        "ds_read_b128 %4, %9 offset:%10\n\t"
+        "ds_read_b128 %5, %9 offset:%11\n\t"
+        "ds_read_b128 %6, %9 offset:%12\n\t"
+        "ds_read_b128 %7, %9 offset:%13\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(a[0][0]), "=&v"(a[0][1]), "=&v"(a[0][2]), "=&v"(a[0][3]), "=&v"(a[1][0]),
           "=&v"(a[1][1]), "=&v"(a[1][2]), "=&v"(a[1][3])
-        : "v"(p), "v"(q)
+        : "v"(p), "v"(q), "i"(SO + 0), "i"(SO + 4096), "i"(SO + 8192), "i"(SO + 12288)
         : "memory");
   } else if constexpr (MB == 3) {
     asm volatile(
-        "ds_read_b128 %0, %6\n\t"
-        "ds_read_b128 %1, %6 offset:4096\n\t"
-        "ds_read_b128 %2, %6 offset:8192\n\t"
-        "ds_read_b128 %3, %7\n\t"
-        "ds_read_b128 %4, %7 offset:4096\n\t"
-        "ds_read_b128 %5, %7 offset:8192\n\t"
+        "ds_read_b128 %0, %6 offset:%8\n\t"
+        "ds_read_b128 %1, %6 offset:%9\n\t"
+        "ds_read_b128 %2, %6 offset:%10\n\t"
+        "ds_read_b128 %3, %7 offset:%8\n\t"
+        "ds_read_b128 %4, %7 offset:%9\n\t"
+        "ds_read_b128 %5, %7 offset:%10\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(a[0][0]), "=&v"(a[0][1]), "=&v"(a[0][2]), "=&v"(a[1][0]), "=&v"(a[1][1]),
           "=&v"(a[1][2])
-        : "v"(p), "v"(q)
+        : "v"(p), "v"(q), "i"(SO + 0), "i"(SO + 4096), "i"(SO + 8192)
         : "memory");
   } else if constexpr (MB == 2) {
     asm volatile(
-        "ds_read_b128 %0, %4\n\t"
-        "ds_read_b128 %1, %4 offset:4096\n\t"
-        "ds_read_b128 %2, %5\n\t"
-        "ds_read_b128 %3, %5 offset:4096\n\t"
+        "ds_read_b128 %0, %4 offset:%6\n\t"
+        "ds_read_b128 %1, %4 offset:%7\n\t"
+        "ds_read_b128 %2, %5 offset:%6\n\t"
+        "ds_read_b128 %3, %5 offset:%7\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(a[0][0]), "=&v"(a[0][1]), "=&v"(a[1][0]), "=&v"(a[1][1])
-        : "v"(p), "v"(q)
+        : "v"(p), "v"(q), "i"(SO + 0), "i"(SO + 4096)
         : "memory");
   } else {
     static_assert(MB == 1, "1..4 row blocks");
     asm volatile(
-        "ds_read_b128 %0, %2\n\t"
-        "ds_read_b128 %1, %3\n\t"
+        "ds_read_b128 %0, %2 offset:%4\n\t"
+        "ds_read_b128 %1, %3 offset:%4\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(a[0][0]), "=&v"(a[1][0])
-        : "v"(p), "v"(q)
+        : "v"(p), "v"(q), "i"(SO + 0)
         : "memory");
   }
 }
+template <int MB>
+__device__ __forceinline__ void read_a(uint32_t base, const FragRoles& fr, int k0,
+                                       u32x4 (&a)[2][MB]) {
+  read_a_at<MB, 0>(base + fr.a[k0], base + fr.a[k0 + 1], a);
+}
 
-// codes and (scale, bias) words of the lane's two weight blocks
-template <int BITS, int DB, int DS>
-__device__ __forceinline__ void read_b(uint32_t base, const FragRoles& fr,
-                                       u32x4 (&q)[2][BITS / 4], uint32_t (&sb)[2]) {
-  const uint32_t pb = base + fr.b, ps = base + fr.s;
+// codes and (scale, bias) words of the lane's two weight blocks: lane LDS
+// addresses pb (codes) and ps (words) in the stage at byte offset SO past them
+template <int BITS, int DB, int DS, uint32_t SO>
+__device__ __forceinline__ void read_b_at(uint32_t pb, uint32_t ps, u32x4 (&q)[2][BITS / 4],
+                                          uint32_t (&sb)[2]) {
+  static_assert(SO + (DB > DS ? DB : DS) < 65536, "ds_read offset field");
   if constexpr (BITS == 4) {
     asm volatile(
-        "ds_read_b128 %0, %4\n\t"
-        "ds_read_b128 %1, %4 offset:%6\n\t"
-        "ds_read_b32 %2, %5\n\t"
-        "ds_read_b32 %3, %5 offset:%7\n\t"
+        "ds_read_b128 %0, %4 offset:%6\n\t"
+        "ds_read_b128 %1, %4 offset:%7\n\t"
+        "ds_read_b32 %2, %5 offset:%6\n\t"
+        "ds_read_b32 %3, %5 offset:%8\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(q[0][0]), "=&v"(q[1][0]), "=&v"(sb[0]), "=&v"(sb[1])
-        : "v"(pb), "v"(ps), "i"(DB), "i"(DS)
+        : "v"(pb), "v"(ps), "i"(SO), "i"(SO + DB), "i"(SO + DS)
         : "memory");
   } else {
     // the lane's second chunk (2h + 1) sits in the slot whose index differs
     // from its first chunk's (2h) in bit 0 only: byte address ^ 16
     const uint32_t pb2 = pb ^ 16u;
     asm volatile(
-        "ds_read_b128 %0, %6\n\t"
-        "ds_read_b128 %1, %7\n\t"
-        "ds_read_b128 %2, %6 offset:%9\n\t"
-        "ds_read_b128 %3, %7 offset:%9\n\t"
-        "ds_read_b32 %4, %8\n\t"
-        "ds_read_b32 %5, %8 offset:%10\n\t"
+        "ds_read_b128 %0, %6 offset:%9\n\t"
+        "ds_read_b128 %1, %7 offset:%9\n\t"
+        "ds_read_b128 %2, %6 offset:%10\n\t"
+        "ds_read_b128 %3, %7 offset:%10\n\t"
+        "ds_read_b32 %4, %8 offset:%9\n\t"
+        "ds_read_b32 %5, %8 offset:%11\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(q[0][0]), "=&v"(q[0][1]), "=&v"(q[1][0]), "=&v"(q[1][1]), "=&v"(sb[0]),
           "=&v"(sb[1])
-        : "v"(pb), "v"(pb2), "v"(ps), "i"(DB), "i"(DS)
+        : "v"(pb), "v"(pb2), "v"(ps), "i"(SO), "i"(SO + DB), "i"(SO + DS)
         : "memory");
   }
+}
+template <int BITS, int DB, int DS>
+__device__ __forceinline__ void read_b(uint32_t base, const FragRoles& fr,
+                                       u32x4 (&q)[2][BITS / 4], uint32_t (&sb)[2]) {
+  read_b_at<BITS, DB, DS, 0>(base + fr.b, base + fr.s, q, sb);
 }
 
 // 2 x 2 x MB products of K steps k0, k0 + 1
@@ -396,6 +407,36 @@ __device__ __forceinline__ void multiply(const u32x4 (&a)[2][MB], const u32x4 (&
 
 // The K loop of one tile over G groups.  `ratio(g)` is the factor of the
 // group's (scale, bias) pair (the down GEMM's h scale alignment).
+// One K stage of ring slot SLOT with the lane's LDS addresses of slot 0 in fa
+// (the slot's offset goes into the reads' offset fields).
+template <int BITS, int MB, int DB, int DS, int SLOT, typename R>
+__device__ __forceinline__ void k_stage(Stage<BITS>* st, const LoadRoles<BITS>& lr,
+                                        const FragRoles& fa, const TileSrc& src, int64_t unit_b,
+                                        int G, int g, int wv, const ExpandConsts& ec,
+                                        f32x16 (&C)[MB][2], R&& ratio) {
+  constexpr int L = stage_loads<BITS, MB>();
+  constexpr uint32_t SO = SLOT * (uint32_t)sizeof(Stage<BITS>);
+  const int later = min(kStages - 1, G - 1 - g);
+  if (later >= 2) wait_vm<2 * L>();
+  else if (later == 1) wait_vm<L>();
+  else wait_vm<0>();
+  lds_barrier();
+  u32x4 q[2][BITS / 4];
+  uint32_t sb[2];
+  read_b_at<BITS, DB, DS, SO>(fa.b, fa.s, q, sb);
+  f16x2 S2[2], B2[2];
+  const float rg = ratio(g);
+  sb_f16_scaled<BITS>(sb[0], rg, S2[0], B2[0]);
+  sb_f16_scaled<BITS>(sb[1], rg, S2[1], B2[1]);
+  u32x4 a[2][MB];
+  read_a_at<MB, SO>(fa.a[0], fa.a[1], a);
+  multiply<BITS, MB>(a, q, S2, B2, 0, ec, C);
+  read_a_at<MB, SO>(fa.a[2], fa.a[3], a);
+  lds_barrier();
+  if (g + kStages < G) issue_stage<BITS, MB>(st[SLOT], lr, src, unit_b, g + kStages, wv);
+  multiply<BITS, MB>(a, q, S2, B2, 2, ec, C);
+}
+
 template <int BITS, int MB, int DB, int DS, typename R>
 __device__ __forceinline__ void k_loop(Stage<BITS>* st, const LoadRoles<BITS>& lr,
                                        const FragRoles& fr, const TileSrc& src, int64_t unit_b,
@@ -404,6 +445,25 @@ __device__ __forceinline__ void k_loop(Stage<BITS>* st, const LoadRoles<BITS>& l
   static_assert(kStages == 3, "wait ladder below covers kStages - 1 = 2 later stages");
   const ExpandConsts ec = expand_consts<BITS>();
   for (int g = 0; g < min(kStages, G); ++g) issue_stage<BITS, MB>(st[g], lr, src, unit_b, g, wv);
+  constexpr uint32_t kLastSlot = (kStages - 1) * (uint32_t)sizeof(Stage<BITS>);
+  if constexpr (kLastSlot + 4096 * (MB - 1) < 65536 && kLastSlot + (DB > DS ? DB : DS) < 65536) {
+    // the ring unrolled by its slots: every LDS read adds only an immediate
+    // offset to the lane's address in slot 0
+    const uint32_t b0 = lds_addr(st);
+    FragRoles fa = fr;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) fa.a[kk] += b0;
+    fa.b += b0;
+    fa.s += b0;
+    for (int g = 0; g < G; g += kStages) {
+      k_stage<BITS, MB, DB, DS, 0>(st, lr, fa, src, unit_b, G, g, wv, ec, C, ratio);
+      if (g + 1 < G)
+        k_stage<BITS, MB, DB, DS, 1>(st, lr, fa, src, unit_b, G, g + 1, wv, ec, C, ratio);
+      if (g + 2 < G)
+        k_stage<BITS, MB, DB, DS, 2>(st, lr, fa, src, unit_b, G, g + 2, wv, ec, C, ratio);
+    }
+    return;
+  }
   for (int g = 0, slot = 0; g < G; ++g, slot = slot == kStages - 1 ? 0 : slot + 1) {
     const int later = min(kStages - 1, G - 1 - g);
     if (later >= 2) wait_vm<2 * L>();
