@@ -261,6 +261,11 @@ __device__ __forceinline__ void split3_pair(float a, float b, uint32_t& p1, uint
 
 // blockIdx.z splits K: split z sums columns [z*kseg, (z+1)*kseg) into its
 // own logit plane (logits + z*T*(E+1)); the top-k kernel adds the planes.
+// Both operands pass through LDS: the token rows as bf16, the weight rows
+// as their three bf16 parts, split once per workgroup while staging (each
+// row read by coalesced 16-byte loads, 16 lanes per 256-byte row piece).
+// D: K stages in flight (a divisor of kseg / 64, at most kRouterDepth).
+template <int D>
 __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __restrict__ x,
                                                           const float* __restrict__ W,
                                                           const float* __restrict__ bias,
@@ -268,87 +273,102 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
                                                           float* __restrict__ logits,
                                                           int T, int H,
                                                           int E, int kseg) {
-  __shared__ __align__(16) uint16_t A[2 * kRouterTile * kRouterLdsRow];
+  constexpr int kTileElems = kRouterTile * kRouterLdsRow;
+  __shared__ __align__(16) uint16_t A[2 * kTileElems];      // token rows, two stages
+  __shared__ __align__(16) uint16_t Bp[2 * 3 * kTileElems];  // weight parts, two stages
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, half = lane >> 5;
   const int t0 = blockIdx.y * kRouterTile, e0 = blockIdx.x * kRouterTile;
   const int k0 = blockIdx.z * kseg;
   logits += (int64_t)blockIdx.z * T * (E + 1);
-  // staging: token row sr, 16 columns (2 x 16 bytes) per thread
+  // token staging: row sr, 16 columns (2 x 16 bytes) per thread
   const int sr = tid >> 2, sq = tid & 3;
   const bool srow_ok = t0 + sr < T;
   const uint16_t* xrow = x + (int64_t)(srow_ok ? t0 + sr : 0) * H + k0 + 16 * sq;
-  // B operand: expert row e, this lane's 32 K columns of each stage
-  const int e = e0 + 32 * wn + l32;
-  const bool gate_row = e == E && wsg != nullptr;  // the shared-gate vector rides as row E
-  const bool e_ok = e < E || gate_row;
-  const float* wrow = (gate_row ? wsg : W + (int64_t)(e < E ? e : 0) * H) + k0 + 32 * half;
+  // weight staging: rows 16 j + (tid >> 4) (j = 0..3), 4 columns at 4 (tid & 15);
+  // row E is the shared-gate vector when it rides in the GEMM, rows past it zeros
+  const int wc = 4 * (tid & 15);
+  const float* wrow[4];
+  bool w_ok[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = e0 + 16 * j + (tid >> 4);
+    const bool gate_row = e == E && wsg != nullptr;
+    w_ok[j] = e < E || gate_row;
+    wrow[j] = (gate_row ? wsg : W + (int64_t)(e < E ? e : 0) * H) + k0 + wc;
+  }
   const int S = kseg / 64;
 
-  auto load_stage = [&](int st, uint4 (&ra)[2], float4 (&rb)[8]) {
+  // every load unconditional (rows past the tile read row 0 and are zeroed)
+  auto load_stage = [&](int st, uint4 (&ra)[2], float4 (&rb)[4]) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) ra[q] = reinterpret_cast<const uint4*>(xrow + st * 64)[q];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) rb[j] = *reinterpret_cast<const float4*>(wrow[j] + st * 64);
+  };
+  auto store_stage = [&](int buf, const uint4 (&ra)[2], const float4 (&rb)[4]) {
+    uint16_t* dst = A + buf * kTileElems + sr * kRouterLdsRow + 16 * sq;
 #pragma unroll
     for (int q = 0; q < 2; ++q)
-      ra[q] = srow_ok ? reinterpret_cast<const uint4*>(xrow + st * 64)[q] : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(dst + 8 * q) = srow_ok ? ra[q] : make_uint4(0, 0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      rb[i] = e_ok ? reinterpret_cast<const float4*>(wrow + st * 64)[i]
-                   : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < 4; ++j) {
+      const float4 v = w_ok[j] ? rb[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+      uint32_t p1[2], p2[2], p3[2];
+      split3_pair(v.x, v.y, p1[0], p2[0], p3[0]);
+      split3_pair(v.z, v.w, p1[1], p2[1], p3[1]);
+      const int o = buf * 3 * kTileElems + (16 * j + (tid >> 4)) * kRouterLdsRow + wc;
+      *reinterpret_cast<uint2*>(Bp + o) = make_uint2(p1[0], p1[1]);
+      *reinterpret_cast<uint2*>(Bp + o + kTileElems) = make_uint2(p2[0], p2[1]);
+      *reinterpret_cast<uint2*>(Bp + o + 2 * kTileElems) = make_uint2(p3[0], p3[1]);
+    }
   };
-  auto store_stage = [&](int buf, int st, const uint4 (&ra)[2]) {
-    uint16_t* dst = A + buf * kRouterTile * kRouterLdsRow + sr * kRouterLdsRow + 16 * sq;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) *reinterpret_cast<uint4*>(dst + 8 * q) = ra[q];
-  };
-  // one stage of products: the fp32 router weights split exactly into three
-  // bf16 parts, smallest first
+  // one stage of products, the weights' three bf16 parts smallest first
   rf32x16 acc = {};
-  auto multiply = [&](const uint16_t* As, const float4 (&cb)[8]) {
+  auto multiply = [&](int buf) {
+    const uint16_t* As = A + buf * kTileElems + (32 * wm + l32) * kRouterLdsRow + 32 * half;
+    const uint16_t* Bs = Bp + buf * 3 * kTileElems + (32 * wn + l32) * kRouterLdsRow + 32 * half;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const ru32x4 a = *reinterpret_cast<const ru32x4*>(
-          As + (32 * wm + l32) * kRouterLdsRow + 32 * half + 8 * ks);
-      const float4 v0 = cb[2 * ks], v1 = cb[2 * ks + 1];
-      uint32_t p1[4], p2[4], p3[4];
-      split3_pair(v0.x, v0.y, p1[0], p2[0], p3[0]);
-      split3_pair(v0.z, v0.w, p1[1], p2[1], p3[1]);
-      split3_pair(v1.x, v1.y, p1[2], p2[2], p3[2]);
-      split3_pair(v1.z, v1.w, p1[3], p2[3], p3[3]);
-      const ru32x4 b1 = {p1[0], p1[1], p1[2], p1[3]};
-      const ru32x4 b2 = {p2[0], p2[1], p2[2], p2[3]};
-      const ru32x4 b3 = {p3[0], p3[1], p3[2], p3[3]};
-      const rbf16x8 av = __builtin_bit_cast(rbf16x8, a);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(rbf16x8, b3), acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(rbf16x8, b2), acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(rbf16x8, b1), acc, 0, 0, 0);
+      const rbf16x8 av = __builtin_bit_cast(rbf16x8, *reinterpret_cast<const ru32x4*>(As + 8 * ks));
+      const rbf16x8 b1 =
+          __builtin_bit_cast(rbf16x8, *reinterpret_cast<const ru32x4*>(Bs + 8 * ks));
+      const rbf16x8 b2 =
+          __builtin_bit_cast(rbf16x8, *reinterpret_cast<const ru32x4*>(Bs + kTileElems + 8 * ks));
+      const rbf16x8 b3 = __builtin_bit_cast(
+          rbf16x8, *reinterpret_cast<const ru32x4*>(Bs + 2 * kTileElems + 8 * ks));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b3, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b2, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b1, acc, 0, 0, 0);
     }
   };
 
-  // a ring of kRouterDepth stages in registers: stage st is multiplied
-  // while stages st + 1 .. st + kRouterDepth - 1 are in flight, and its
-  // registers then take stage st + kRouterDepth (the activations pass
-  // through a double-buffered LDS tile one stage ahead)
+  // a ring of D stages in registers: stage st is multiplied from LDS while
+  // stages st + 1 .. st + D are in flight (its registers were written to LDS
+  // one step earlier, so they take stage st + D at once), and stage st + 1 is
+  // split into the other LDS buffer.  No load or store sits under a branch, so
+  // each step waits only for the stage it stores: past the last stage the
+  // indices are clamped and the extra copies go unused.
   {
-    uint4 ra[kRouterDepth][2];
-    float4 rb[kRouterDepth][8];
+    uint4 ra[D][2];
+    float4 rb[D][4];
 #pragma unroll
-    for (int j = 0; j < kRouterDepth; ++j)
-      if (j < S) load_stage(j, ra[j], rb[j]);
-    store_stage(0, 0, ra[0]);
+    for (int j = 0; j < D; ++j) load_stage(j, ra[j], rb[j]);
+    store_stage(0, ra[0], rb[0]);
     __syncthreads();
-    for (int st0 = 0; st0 < S; st0 += kRouterDepth) {
+    for (int st0 = 0; st0 < S; st0 += D) {
 #pragma unroll
-      for (int j = 0; j < kRouterDepth; ++j) {
+      for (int j = 0; j < D; ++j) {
         const int st = st0 + j;
-        if (st < S) {
-          multiply(A + (st & 1) * kRouterTile * kRouterLdsRow, rb[j]);
-          if (st + kRouterDepth < S) load_stage(st + kRouterDepth, ra[j], rb[j]);
-          if (st + 1 < S) store_stage((st + 1) & 1, st + 1, ra[(j + 1) % kRouterDepth]);
-          __syncthreads();
-        }
+        load_stage(min(st + D, S - 1), ra[j], rb[j]);
+        multiply(st & 1);
+        store_stage((st + 1) & 1, ra[(j + 1) % D], rb[(j + 1) % D]);
+        __syncthreads();
       }
     }
   }
-  if (!e_ok) return;
+  const int e = e0 + 32 * wn + l32;
+  if (!(e < E || (e == E && wsg != nullptr))) return;
   const float b = (bias != nullptr && blockIdx.z == 0 && e < E) ? bias[e] : 0.0f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -414,8 +434,19 @@ hipError_t launch_router_act(const RouterArgs& a, hipStream_t s) {
     const dim3 grid(fold ? gtiles : etiles, ytiles, nplanes);
     const uint16_t* xb = reinterpret_cast<const uint16_t*>(a.x);
     const float* wg = fold ? a.shared_gate_w : nullptr;
-    hipLaunchKernelGGL(router_mfma_kernel, grid, dim3(256), 0, s, xb, a.router_w, a.router_bias,
-                       wg, a.logits, a.T, a.H, a.E, a.H / nplanes);
+    // K stages of each split; the stage ring is the largest of 4, 2, 1 dividing it
+    const int S = a.H / nplanes / 64;
+    static_assert(kRouterDepth == 4, "stage rings of 4, 2 and 1");
+#define MOE_ROUTER_GEMM(D)                                                                   \
+  hipLaunchKernelGGL(router_mfma_kernel<D>, grid, dim3(256), 0, s, xb, a.router_w,            \
+                     a.router_bias, wg, a.logits, a.T, a.H, a.E, a.H / nplanes)
+    if (S % 4 == 0)
+      MOE_ROUTER_GEMM(4);
+    else if (S % 2 == 0)
+      MOE_ROUTER_GEMM(2);
+    else
+      MOE_ROUTER_GEMM(1);
+#undef MOE_ROUTER_GEMM
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.shared_gate_w != nullptr && !fold) {
