@@ -725,7 +725,10 @@ __global__ __launch_bounds__(64) void bucket_mask_kernel(const int32_t* __restri
 // Per-expert counts and bucket offsets (exclusive scan over experts), the
 // per-block write offsets, and the list of buckets the GEMV kernels take:
 // experts with 1 .. min_rows-1 tokens, and the shared expert (bucket E) when
-// T < min_rows.  One workgroup of 1024 threads (E <= 1024).
+// T < min_rows.  One workgroup of 1024 threads (E <= 1024).  When the block
+// masks fit one round of loads per thread, Q = 1024 / E' threads share an
+// expert (E' = 256, 512 or 1024 expert slots), each reading a run of at most
+// 16 consecutive blocks; else one thread per expert reads them in rounds.
 __global__ __launch_bounds__(1024) void bucket_scan_kernel(const uint64_t* __restrict__ masks,
                                                            int32_t* __restrict__ counts,
                                                            int32_t* __restrict__ offsets,
@@ -735,15 +738,41 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(const uint64_t* __res
                                                            int E, int k, int nblk, int min_rows,
                                                            int has_shared) {
   __shared__ int wsum[16], wsmall[16];
+  __shared__ int cqs[1024];  // one round: count of thread (q, e)'s run, at q * EP + e
+  __shared__ int exl[1024];  // one round: expert e's bucket offset
   const int e = threadIdx.x, lane = e & 63, wave = e >> 6;
   constexpr int kU = 16;  // block masks in flight per thread and round
+  // one round: Q threads per expert, thread (q, eq) = q * EP + eq reads blocks
+  // q * BQ .. q * BQ + BQ - 1 of expert eq; the per-block counts kept a byte each
+  const int Q = E <= 256 ? 4 : (E <= 512 ? 2 : 1), EP = 1024 / Q;
+  const int q = e / EP, eq = e % EP, BQ = (nblk + Q - 1) / Q;
+  const bool one_round = BQ <= kU;
+  uint32_t pq[kU / 4] = {};
   // with at most kPackedBlocks blocks the per-block counts are kept, a byte
   // each, for the offsets below (no second read of the masks)
   constexpr int kPackedBlocks = 64;
   const bool packed = nblk <= kPackedBlocks;
   uint32_t pc[kPackedBlocks / 4] = {};
   int c = 0;
-  if (e < E && packed) {
+  if (one_round) {
+    int cv = 0;
+    if (eq < E) {
+      // every load unconditional (past the run: the last block again, not counted)
+      uint64_t m[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) m[u] = masks[(int64_t)min(q * BQ + u, nblk - 1) * E + eq];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int n = (u < BQ && q * BQ + u < nblk) ? __popcll(m[u]) : 0;
+        cv += n;
+        pq[u >> 2] |= (uint32_t)n << (8 * (u & 3));
+      }
+    }
+    cqs[e] = cv;
+    __syncthreads();
+    if (e < E)
+      for (int j = 0; j < Q; ++j) c += cqs[j * EP + e];
+  } else if (e < E && packed) {
 #pragma unroll
     for (int r = 0; r < kPackedBlocks / kU; ++r) {
       uint64_t m[kU];
@@ -794,6 +823,24 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(const uint64_t* __res
   if (e < E) {
     counts[e] = c;
     offsets[e] = excl;
+  }
+  if (one_round) {
+    // thread (q, eq): its run of blocks starts after the runs of q' < q
+    if (e < E) exl[e] = excl;
+    __syncthreads();
+    if (eq < E) {
+      int run = exl[eq];
+      for (int j = 0; j < q; ++j) run += cqs[j * EP + eq];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int b = q * BQ + u;
+        if (u < BQ && b < nblk) {
+          blkoff[(int64_t)b * E + eq] = run;
+          run += (pq[u >> 2] >> (8 * (u & 3))) & 0xFFu;
+        }
+      }
+    }
+  } else if (e < E) {
     int run = excl;
     if (packed) {
 #pragma unroll
