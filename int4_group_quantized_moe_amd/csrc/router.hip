@@ -149,23 +149,24 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ logits, int
     // shared-gate logit, too: a partial per plane, or the whole logit in
     // plane 0 and zeros in the others)
     // (every load of the token's E + 1 logits over the planes in flight
-    // together: MPL * 64 + 1 >= E + 1 entries per lane group)
+    // together: MPL * 64 + 1 >= E + 1 entries per lane group; the loads are
+    // unconditional, past the last plane or logit at a clamped index and not
+    // used, so that none waits for the one before it)
     const int64_t ps = (int64_t)T * (E + 1);
+    float p[kRouterMaxPlanes][MPL + 1];
+#pragma unroll
+    for (int z = 0; z < kRouterMaxPlanes; ++z)
+#pragma unroll
+      for (int m = 0; m <= MPL; ++m)
+        p[z][m] = lt[min(z, nplanes - 1) * ps + min(lane + 64 * m, E)];
     float v[MPL + 1];
 #pragma unroll
-    for (int m = 0; m <= MPL; ++m) v[m] = 0.f;
+    for (int m = 0; m <= MPL; ++m) {
+      const bool ok = lane + 64 * m <= E;
+      v[m] = ok ? p[0][m] : 0.f;
 #pragma unroll
-    for (int z = 0; z < kRouterMaxPlanes; ++z) {
-      if (z < nplanes) {
-        float p[MPL + 1];
-#pragma unroll
-        for (int m = 0; m <= MPL; ++m) {
-          const int e = lane + 64 * m;
-          p[m] = e <= E ? lt[z * ps + e] : 0.f;
-        }
-#pragma unroll
-        for (int m = 0; m <= MPL; ++m) v[m] = z == 0 ? p[m] : v[m] + p[m];
-      }
+      for (int z = 1; z < kRouterMaxPlanes; ++z)
+        if (z < nplanes && ok) v[m] = v[m] + p[z][m];
     }
 #pragma unroll
     for (int m = 0; m <= MPL; ++m) {
