@@ -659,6 +659,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
         p[j][0] = src[0];
         p[j][1] = src[1];
       }
+    // the residual columns requested with the partial rows (one round trip)
+    float4 xr[2];
+    if (epi >= 1)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) xr[h] = load_act4v<ACT>(x_res, base + c + 4 * h);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -673,11 +678,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       }
       store_act4v<ACT>(out, base + c + 4 * h, a);
       if (epi >= 1) {
-        const float4 xr = load_act4v<ACT>(x_res, base + c + 4 * h);
-        v[r][h] = make_float4(round_act1<ACT>(xr.x + round_act1<ACT>(a.x)),
-                              round_act1<ACT>(xr.y + round_act1<ACT>(a.y)),
-                              round_act1<ACT>(xr.z + round_act1<ACT>(a.z)),
-                              round_act1<ACT>(xr.w + round_act1<ACT>(a.w)));
+        v[r][h] = make_float4(round_act1<ACT>(xr[h].x + round_act1<ACT>(a.x)),
+                              round_act1<ACT>(xr[h].y + round_act1<ACT>(a.y)),
+                              round_act1<ACT>(xr[h].z + round_act1<ACT>(a.z)),
+                              round_act1<ACT>(xr[h].w + round_act1<ACT>(a.w)));
         store_act4v<ACT>(x_res, base + c + 4 * h, v[r][h]);
         ss += (v[r][h].x * v[r][h].x + v[r][h].y * v[r][h].y) +
               (v[r][h].z * v[r][h].z + v[r][h].w * v[r][h].w);
