@@ -632,13 +632,16 @@ __device__ __forceinline__ float round_act1(float v) {
 // round trip per token).  With epi >= 1 it also adds the residual, x_res[t] =
 // act(x_res[t] + out[t]), and with epi == 2 writes the next layer's input
 // act(rmsnorm(x_res[t])) (unit weight), so a chain needs no separate launch
-// between layers.  NJ = the most slots a call has (k + 1 <= NJ).
-template <int ACT, int NJ>
+// between layers.  NJ = the most slots a call has (k + 1 <= NJ).  F16P: the
+// partial rows are fp16 with a power-of-two scale 2^e per row and 64-column
+// block, the exponents a byte each at byte offset e_off (the grouped GEMMs'
+// down kernel); the scale is undone exactly before the same fp32 sum.
+template <int ACT, int NJ, bool F16P>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ partial,
                                                       void* __restrict__ out, int H, int k,
                                                       int has_shared, void* __restrict__ x_res,
                                                       void* __restrict__ x_hat, float eps,
-                                                      int epi) {
+                                                      int epi, int64_t e_off) {
   constexpr int kR = MOE_MAX_HIDDEN / 2048;
   __shared__ float wsum[4];
   const int t = blockIdx.x;
@@ -654,10 +657,26 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
       if (j < nj) {
-        const float4* src =
-            reinterpret_cast<const float4*>(partial + ((int64_t)t * (k + 1) + j) * H + c);
-        p[j][0] = src[0];
-        p[j][1] = src[1];
+        const int64_t row = (int64_t)t * (k + 1) + j;
+        if constexpr (F16P) {
+          const uint4 q = *reinterpret_cast<const uint4*>(
+              reinterpret_cast<const uint16_t*>(partial) + row * H + c);
+          const int e = reinterpret_cast<const int8_t*>(partial)[e_off + row * (H / 64) + c / 64];
+          const float sc = __uint_as_float((uint32_t)(127 + e) << 23);  // 2^e
+          const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+          float f[8];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            f[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] & 0xFFFFu)) * sc;
+            f[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] >> 16)) * sc;
+          }
+          p[j][0] = make_float4(f[0], f[1], f[2], f[3]);
+          p[j][1] = make_float4(f[4], f[5], f[6], f[7]);
+        } else {
+          const float4* src = reinterpret_cast<const float4*>(partial + row * H + c);
+          p[j][0] = src[0];
+          p[j][1] = src[1];
+        }
       }
     // the residual columns requested with the partial rows (one round trip)
     float4 xr[2];
@@ -1243,12 +1262,23 @@ hipError_t launch_experts_t(const ExpertArgs& a, hipStream_t s) {
                        small_list, n_small, a.L.n_tiles_d);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if (a.k + hs <= 12)
-    hipLaunchKernelGGL((combine_kernel<ACT, 12>), dim3(a.T), dim3(256), 0, s, partial, a.out, a.H,
-                       a.k, hs, a.x_res, a.x_hat_next, a.eps, a.epi);
-  else
-    hipLaunchKernelGGL((combine_kernel<ACT, MOE_MAX_TOP_K + 1>), dim3(a.T), dim3(256), 0, s,
-                       partial, a.out, a.H, a.k, hs, a.x_res, a.x_hat_next, a.eps, a.epi);
+  // the grouped GEMMs of large batches write fp16 partial rows (their down
+  // kernel's epilogue), every other path fp32
+  const bool f16p = a.mfma && !one_block;
+  const int64_t e_off = (int64_t)a.T * (a.k + 1) * a.H * 2;
+#define MOE_COMBINE(NJ, F16P)                                                                 \
+  hipLaunchKernelGGL((combine_kernel<ACT, NJ, F16P>), dim3(a.T), dim3(256), 0, s, partial, a.out, \
+                     a.H, a.k, hs, a.x_res, a.x_hat_next, a.eps, a.epi, e_off)
+  if constexpr (ACT == MOE_ACT_BF16) {
+    if (f16p) {
+      if (a.k + hs <= 12) MOE_COMBINE(12, true);
+      else MOE_COMBINE(MOE_MAX_TOP_K + 1, true);
+      return hipGetLastError();
+    }
+  }
+  if (a.k + hs <= 12) MOE_COMBINE(12, false);
+  else MOE_COMBINE(MOE_MAX_TOP_K + 1, false);
+#undef MOE_COMBINE
   return hipGetLastError();
 }
 

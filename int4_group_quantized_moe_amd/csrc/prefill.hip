@@ -561,9 +561,10 @@ constexpr int kHStageRow = 272;
 // down epilogue: a wave's 32 x 64 fp32 block staged with rows of 72 floats
 // (16-byte aligned rows; a column write's two half-waves, 4 rows apart, fall
 // 32 banks apart); the offset given to rows past a tile (the partial buffer
-// is kept below 2 GiB)
+// is kept below 2 GiB), and their row marker
 constexpr int kEpRow = 72;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr uint32_t kDropOffset = 0x80000000u;
 
 // silu(g) * u with a hardware reciprocal (the result is rounded to fp16)
@@ -686,8 +687,12 @@ __device__ __forceinline__ void prefill_gateup_item(MOE_PGU_PARAMS, Stage<BITS>*
 // n0 .. n0+255).  Each staged group of h is brought to the tile's largest h
 // scale through the group's (scale, bias) pair (a power-of-two factor of at
 // most 1); the results are multiplied by that scale once.  Writes
-// roww * (h . Wd^T) of every row to its partial row (fp32; the shared
-// expert's row is j = k).
+// roww * (h . Wd^T) of every row to its partial row (the shared expert's row
+// is j = k) in fp16 after a power-of-two scale per 32-row x 64-column block
+// of a wave: the bound max|value| x max|row factor| is brought to
+// [2^14, 2^15), so every value at or above 2^-29 of it keeps 11 significant
+// bits (relative error at most 2^-11); the scale's exponent is stored as a
+// byte per (row, 64-column block) behind the fp16 rows.
 
 #define MOE_PDN_PARAMS                                                                       \
   const uint16_t* __restrict__ h, const int32_t* __restrict__ pairs,                           \
@@ -716,8 +721,8 @@ __device__ __forceinline__ void prefill_down_item(MOE_PDN_PARAMS, Stage<BITS>* s
                               : slab + (int64_t)slot_table[ti.e] * stride + d_off_r;
   const int64_t unit_b = shared ? d_unit_s : d_unit_r, tile_b = shared ? d_tile_s : d_tile_r;
   if (tid < kMT) {
-    // byte offset of the row's partial row (rows past the tile: an offset
-    // past the buffer, whose stores the hardware drops)
+    // byte offset of the row's fp16 partial row (rows past the tile: an
+    // offset past the buffer, whose stores the hardware drops)
     uint32_t off = kDropOffset;
     float wv = 0.f;
     if (tid < ti.rows) {
@@ -731,7 +736,7 @@ __device__ __forceinline__ void prefill_down_item(MOE_PDN_PARAMS, Stage<BITS>* s
         dst = (p / k) * (k + 1) + (p % k);
         wv = topk_w[p];
       }
-      off = (uint32_t)dst * (uint32_t)H * 4u;
+      off = (uint32_t)dst * (uint32_t)H * 2u;
     }
     rowdst[tid] = off;
     roww[tid] = wv;
@@ -774,15 +779,22 @@ __device__ __forceinline__ void prefill_down_item(MOE_PDN_PARAMS, Stage<BITS>* s
 
   // Epilogue.  The ring is free (every wave is past the last stage's
   // barrier).  Each wave turns its 32 x 64 blocks into rows through its own
-  // LDS region and stores each row as 16-byte pieces of 4 columns: lane
+  // LDS region and stores each row as 8-byte fp16 pieces of 4 columns: lane
   // (c4, r4) takes columns 4 c4 .. 4 c4 + 3 of rows r4, r4 + 4, ...  The
-  // factor roww * hmax is exact to apply in one product (hmax is a power of
-  // two).
+  // row factor roww * hmax and the block's scale 2^-e are powers of two
+  // times roww, so (value x factor) x scale is one product.  The exponent
+  // byte of (row, block) sits at the row's fp16 byte offset / 128 (H fp16
+  // values, H / 64 bytes) behind the fp16 rows.
   float* ep = reinterpret_cast<float*>(st) + wave * (32 * kEpRow);
-  const auto rp = __builtin_amdgcn_make_buffer_rsrc(
-      partial, (short)0, (int)((uint32_t)T * (uint32_t)(k + 1) * (uint32_t)H * 4u), 0x00020000);
+  const uint32_t nrows = (uint32_t)T * (uint32_t)(k + 1);
+  const auto rp = __builtin_amdgcn_make_buffer_rsrc(partial, (short)0,
+                                                    (int)(nrows * (uint32_t)H * 2u), 0x00020000);
+  const auto re = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<uint8_t*>(partial) + (size_t)nrows * (size_t)H * 2u, (short)0,
+      (int)(nrows * (uint32_t)(H / 64)), 0x00020000);
   const int c4 = lane & 15, r4 = lane >> 4;
-  const uint32_t col_b = (uint32_t)(n0 + 64 * wave + 4 * c4) * 4u;
+  const uint32_t col_b = (uint32_t)(n0 + 64 * wave + 4 * c4) * 2u;
+  const uint32_t blk = (uint32_t)(n0 + 64 * wave) / 64u;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
@@ -791,14 +803,34 @@ __device__ __forceinline__ void prefill_down_item(MOE_PDN_PARAMS, Stage<BITS>* s
       for (int r = 0; r < 16; ++r)
         ep[(8 * (r >> 2) + 4 * half + (r & 3)) * kEpRow + 32 * nb + l32] = C[mb][nb][r];
     asm volatile("" ::: "memory");  // the wave's LDS accesses stay in order
+    float4 v[8];
+    float f[8];
+    float bnd = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int row = r4 + 4 * j, m = 32 * mb + row;
-      const float4 v = *reinterpret_cast<const float4*>(&ep[row * kEpRow + 4 * c4]);
-      const float f = roww[m] * hmax;
-      const f32x4 o = {v.x * f, v.y * f, v.z * f, v.w * f};
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rp,
-                                             rowdst[m] + col_b, 0, 0);
+      v[j] = *reinterpret_cast<const float4*>(&ep[row * kEpRow + 4 * c4]);
+      f[j] = roww[m] * hmax;
+      const float a = fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)), fmaxf(fabsf(v[j].z), fabsf(v[j].w)));
+      bnd = fmaxf(bnd, a * fabsf(f[j]));
+    }
+    const uint32_t mx = dec::wave_max_dpp(__float_as_uint(bnd) & 0x7FFFFFFFu);
+    int e = mx == 0 ? 0 : (int)(mx >> 23) - 127 - 14;
+    e = e < -100 ? -100 : (e > 100 ? 100 : e);
+    const float sc = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int m = 32 * mb + r4 + 4 * j;
+      const float g = f[j] * sc;
+      const uint32_t h0 = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v[j].x * g)) |
+                          ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v[j].y * g)) << 16);
+      const uint32_t h1 = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v[j].z * g)) |
+                          ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v[j].w * g)) << 16);
+      const uint32_t off = rowdst[m];
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{h0, h1}, rp, off + col_b, 0, 0);
+      // the row's exponent byte from lane c4 = 0 (the others' go past the buffer)
+      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(int8_t)e, re,
+                                           c4 == 0 ? (off >> 7) + blk : kDropOffset, 0, 0);
     }
     asm volatile("" ::: "memory");
   }
@@ -902,7 +934,8 @@ bool prefill_supported(int act, int64_t T, int H, int k, int I, int Is, bool has
   if (H % kTileN != 0 || I % kHCols != 0 || (has_shared && Is % kHCols != 0)) return false;
   // the gate/up kernel addresses the fp16 activation rows with 32-bit byte offsets
   if (T * H * 2 >= (int64_t)1 << 32) return false;
-  // the down kernel's partial rows: 32-bit offsets below kDropOffset
+  // the down kernel's partial rows (fp16, then the exponent bytes): 32-bit
+  // offsets below kDropOffset
   if (T * (k + 1) * H * 4 > (int64_t)kDropOffset - (int64_t)H * 4) return false;
   return true;
 }
