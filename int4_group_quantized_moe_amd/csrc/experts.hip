@@ -748,7 +748,10 @@ __global__ __launch_bounds__(64) void bucket_mask_kernel(const int32_t* __restri
 // Per-expert counts and bucket offsets (exclusive scan over experts), the
 // per-block write offsets, and the list of buckets the GEMV kernels take:
 // experts with 1 .. min_rows-1 tokens, and the shared expert (bucket E) when
-// T < min_rows.  One workgroup of 1024 threads (E <= 1024).  When the block
+// T < min_rows.  One workgroup of 1024 threads (E <= 1024).  With tiles !=
+// nullptr (E + has_shared <= 1024) it also builds the grouped GEMMs' tile
+// list as the tile-list kernel does (bucket E the shared expert's T rows,
+// each bucket of at least tile_min entries cut into tiles of mt rows).  When the block
 // masks fit one round of loads per thread, Q = 1024 / E' threads share an
 // expert (E' = 256, 512 or 1024 expert slots), each reading a run of at most
 // 16 consecutive blocks; else one thread per expert reads them in rounds.
@@ -759,7 +762,10 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(const uint64_t* __res
                                                            int32_t* __restrict__ small_list,
                                                            int32_t* __restrict__ n_small, int T,
                                                            int E, int k, int nblk, int min_rows,
-                                                           int has_shared) {
+                                                           int has_shared,
+                                                           int32_t* __restrict__ tiles,
+                                                           int32_t* __restrict__ ntiles,
+                                                           int max_tiles, int mt, int tile_min) {
   __shared__ int wsum[16], wsmall[16];
   __shared__ int cqs[1024];  // one round: count of thread (q, e)'s run, at q * EP + e
   __shared__ int exl[1024];  // one round: expert e's bucket offset
@@ -884,6 +890,30 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(const uint64_t* __res
           blkoff[(int64_t)(b0 + u) * E + e] = run;
           run += __popcll(m[u]);
         }
+      }
+    }
+  }
+  if (tiles != nullptr) {
+    const int nb = e < E ? c : (e == E && has_shared ? T : 0);
+    const int ct = nb >= tile_min ? (nb + mt - 1) / mt : 0;
+    int tv = ct;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(tv, off, 64);
+      if (lane >= off) tv += o;
+    }
+    __shared__ int tsum[16];
+    if (lane == 63) tsum[wave] = tv;
+    __syncthreads();
+    int tb = 0;
+    for (int w = 0; w < wave; ++w) tb += tsum[w];
+    if (e == 1023) *ntiles = min(tb + tv, max_tiles);
+    const int tbase = tb + tv - ct;
+    for (int i = 0; i < ct; ++i) {
+      const int t = tbase + i;
+      if (t < max_tiles) {
+        tiles[2 * t] = e;
+        tiles[2 * t + 1] = i * mt;
       }
     }
   }
@@ -1198,6 +1228,8 @@ hipError_t launch_experts_t(const ExpertArgs& a, hipStream_t s) {
   const bool small_batch = nblk == 1 && a.E < 1024;
   const bool one_block =
       a.mfma && small_batch && batched_supported(a.act, a.T, a.H, a.L.inter, Is, a.has_shared);
+  // larger batches: the scan builds the MFMA tile list where every bucket has a thread
+  const bool scan_tiles = a.mfma && !small_batch && a.E + hs <= 1024;
   if (small_batch) {
     hipLaunchKernelGGL(bucket_small_kernel, dim3(1), dim3(1024), 0, s, a.topk_idx, counts,
                        offsets, pairs, small_list, n_small, a.mfma ? tiles : nullptr, ntiles,
@@ -1206,7 +1238,9 @@ hipError_t launch_experts_t(const ExpertArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(bucket_mask_kernel, dim3(nblk), dim3(64), 0, s, a.topk_idx, masks, a.T,
                        a.E, a.k);
     hipLaunchKernelGGL(bucket_scan_kernel, dim3(1), dim3(1024), 0, s, masks, counts, offsets,
-                       blkoff, small_list, n_small, a.T, a.E, a.k, nblk, min_rows, hs);
+                       blkoff, small_list, n_small, a.T, a.E, a.k, nblk, min_rows, hs,
+                       scan_tiles ? tiles : nullptr, ntiles, P.max_tiles, kMfmaTileRows,
+                       kMfmaMinRows);
     hipLaunchKernelGGL(bucket_scatter_kernel, dim3(nblk), dim3(64), 0, s, a.topk_idx, masks,
                        blkoff, pairs, a.T, a.E, a.k);
   }
@@ -1228,7 +1262,7 @@ hipError_t launch_experts_t(const ExpertArgs& a, hipStream_t s) {
     pa.out = a.out;
     pa.tiles = tiles;
     pa.ntiles = ntiles;
-    pa.tiles_ready = small_batch;
+    pa.tiles_ready = small_batch || scan_tiles;
     pa.x16 = reinterpret_cast<uint16_t*>(a.ws + P.x16);
     pa.xe = reinterpret_cast<int32_t*>(a.ws + P.xe);
     pa.x16_ready = a.x16_ready;
