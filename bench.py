@@ -218,7 +218,7 @@ def main():
                                   dense_q4=args.dense_q4)
         check_chain_status(moe, d, ws, "roofline pass")
 
-    # release the captured graphs (they hold the cooperative chain launch)
+    # release the captured graphs (they hold the persistent chain launch)
     # and drain the device while the runtime is whole, not at interpreter exit
     for g in graphs:
         g.reset()

@@ -394,12 +394,15 @@ int moe_rmsnorm(const moe_layer_desc* desc, void* x, const void* out, void* x_ha
  *                 another order than moe_rmsnorm's, so x_hat may differ from
  *                 moe_rmsnorm's by one rounding of the act dtype.
  *   ws            workspace of moe_workspace_bytes(desc) bytes.  For T = 1 the
- *                 chain may run as one persistent cooperative kernel that
- *                 exchanges data between workgroups through epoch-tagged words
- *                 in ws: ws must be zero-filled before its first chain call and
- *                 then reused only by chain calls of the same desc (it keeps the
- *                 last epoch; 2^32 layers before the counter wraps).  A bounded
- *                 wait that expires sets bit 0 of the chain status word
+ *                 chain may run as one persistent kernel (one workgroup per
+ *                 compute unit, all resident at once) that exchanges data
+ *                 between workgroups through epoch-tagged words in ws: ws must
+ *                 be zero-filled before its first chain call and then reused
+ *                 only by chain calls of the same desc (it keeps the last
+ *                 epoch; 2^32 layers before the counter wraps).  A bounded wait
+ *                 that expires (for instance when other work holds compute
+ *                 units at the same time, so that not every workgroup is
+ *                 resident) sets bit 0 of the chain status word
  *                 (moe_chain_status); results of that call are then invalid.
  * Defined by: each token's decode step runs every layer's forward pass in
  * turn, the MoE block after the mixer (xix.ai page, 4th and 5th paragraphs;

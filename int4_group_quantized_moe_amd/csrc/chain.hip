@@ -1,5 +1,9 @@
-// Persistent batch-1 decode chain: every layer of the chain in ONE
-// cooperative launch, one workgroup per compute unit.
+// Persistent batch-1 decode chain: every layer of the chain in ONE launch,
+// one workgroup per compute unit.  The launch is an ordinary one after a
+// check that the device holds the whole grid at once (a cooperative launch
+// makes the same check, and costs about 10 us of idle GPU on each side of it
+// inside a graph replay); should other work hold compute units at the same
+// time, a bounded wait below expires and says so in the status word.
 //
 // A layer needs three all-to-all exchanges (the full input before the
 // router, the full logits before the top-k, every selected expert's full h
@@ -821,7 +825,13 @@ hipError_t launch_chain(const ChainParams& prm, int nwg, hipStream_t s) {
   else
     fn = small ? MOE_CHAIN_FN(false, 4, 0, 0) : MOE_CHAIN_FN(false, 8, 0, 0);
 #undef MOE_CHAIN_FN
-  return hipLaunchCooperativeKernel(fn, dim3(nwg), dim3(256), args, (unsigned)lds, s);
+  // every workgroup must be resident together: the exchanges wait on each other
+  int per_cu = 0, dev = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, lds);
+  if (e != hipSuccess) return e;
+  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+  if ((int64_t)per_cu * chain_grid(dev) < nwg) return hipErrorCooperativeLaunchTooLarge;
+  return hipLaunchKernel(fn, dim3(nwg), dim3(256), args, lds, s);
 }
 
 }  // namespace moe

@@ -261,7 +261,7 @@ bool decode_fast_supported(int T, int act, int H, int k, int E, int bits, int I,
                            bool has_shared);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 
-// Persistent decode chain (one cooperative launch for all layers).
+// Persistent decode chain (one launch for all layers, every workgroup resident).
 struct ChainParams {
   uint16_t* x;                   // [H] residual stream in/out
   uint16_t* x_hat;               // [H] last layer's normalised input
