@@ -826,12 +826,12 @@ __device__ __forceinline__ void prefill_down_item(MOE_PDN_PARAMS, Stage<BITS>* s
                           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v[j].y * g)) << 16);
       const uint32_t h1 = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v[j].z * g)) |
                           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v[j].w * g)) << 16);
-      const uint32_t off = rowdst[m];
-      __builtin_amdgcn_raw_buffer_store_b64(u32x2{h0, h1}, rp, off + col_b, 0, 0);
-      // the row's exponent byte from lane c4 = 0 (the others' go past the buffer)
-      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(int8_t)e, re,
-                                           c4 == 0 ? (off >> 7) + blk : kDropOffset, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{h0, h1}, rp, rowdst[m] + col_b, 0, 0);
     }
+    // the block's exponent byte for each of its rows: lane (c4 < 8, r4) writes
+    // row r4 + 4 c4's (the other lanes' go past the buffer)
+    const uint32_t eoff = c4 < 8 ? (rowdst[32 * mb + r4 + 4 * (c4 & 7)] >> 7) + blk : kDropOffset;
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(int8_t)e, re, eoff, 0, 0);
     asm volatile("" ::: "memory");
   }
 }
