@@ -90,9 +90,9 @@ struct WsPlan {
   bool bucketed;
 };
 
-// Logit planes of the router GEMM's K split (up to 8 for small batches, 2
-// for large ones: two workgroups per CU).
-inline int router_planes(int64_t T) { return T < 1024 ? 8 : 2; }
+// Logit planes of the router GEMM's K split (up to 16 for one token block,
+// 8 for other small batches, 2 for large ones: two workgroups per CU).
+inline int router_planes(int64_t T) { return T <= kOneBlockTokens ? 16 : (T < 1024 ? 8 : 2); }
 
 inline WsPlan make_ws_plan(const moe_layer_desc& d) {
   WsPlan p{};

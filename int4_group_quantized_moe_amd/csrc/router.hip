@@ -14,7 +14,7 @@ namespace {
 constexpr int kRouterWaves = 4;     // rows per workgroup (one per wave)
 constexpr int kRouterMaxTT = 8;     // tokens per LDS chunk
 constexpr int kRouterMaxRegIt = 8;  // row cached in registers when H <= 64*4*8
-constexpr int kRouterMaxPlanes = 8;       // K split of the router GEMM (logit planes)
+constexpr int kRouterMaxPlanes = 16;      // K split of the router GEMM (logit planes)
 constexpr int kRouterFoldMaxBlocks = 256;  // router GEMM grid that still runs in one round
 
 template <int ACT>
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const void* __restrict
 // 64 logits tie at the threshold), then the softmax over the k selected
 // logits.  The LDS arrays are the wave's own.  With x16, the wave also writes
 // the token's activation row in fp16 (x16_row).
-template <int MPL>
+template <int MPL, int NP>
 __device__ __forceinline__ void topk_token(const float* __restrict__ logits, int32_t* __restrict__ topk_idx,
                                            float* __restrict__ topk_w, float* __restrict__ gamma,
                                            int T, int E, int k, int has_gate, int nplanes, int t,
@@ -153,9 +153,9 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ logits, int
     // unconditional, past the last plane or logit at a clamped index and not
     // used, so that none waits for the one before it)
     const int64_t ps = (int64_t)T * (E + 1);
-    float p[kRouterMaxPlanes][MPL + 1];
+    float p[NP][MPL + 1];
 #pragma unroll
-    for (int z = 0; z < kRouterMaxPlanes; ++z)
+    for (int z = 0; z < NP; ++z)
 #pragma unroll
       for (int m = 0; m <= MPL; ++m)
         p[z][m] = lt[min(z, nplanes - 1) * ps + min(lane + 64 * m, E)];
@@ -165,7 +165,7 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ logits, int
       const bool ok = lane + 64 * m <= E;
       v[m] = ok ? p[0][m] : 0.f;
 #pragma unroll
-      for (int z = 1; z < kRouterMaxPlanes; ++z)
+      for (int z = 1; z < NP; ++z)
         if (z < nplanes && ok) v[m] = v[m] + p[z][m];
     }
 #pragma unroll
@@ -190,7 +190,8 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ logits, int
 }
 
 // One wave per token.
-template <int MPL>
+// NP: the most logit planes of a call (nplanes <= NP).
+template <int MPL, int NP>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits,
                                                    int32_t* __restrict__ topk_idx,
                                                    float* __restrict__ topk_w,
@@ -208,7 +209,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   const int wave = threadIdx.x >> 6;
   const int t = blockIdx.x * (int)(blockDim.x >> 6) + wave;
   if (t >= T) return;
-  topk_token<MPL>(logits, topk_idx, topk_w, gamma, T, E, k, has_gate, nplanes, t, sel_idx[wave],
+  topk_token<MPL, NP>(logits, topk_idx, topk_w, gamma, T, E, k, has_gate, nplanes, t, sel_idx[wave],
                   sel_val[wave], sel_w[wave], &gam[wave], cand_key[wave], cand_idx[wave],
                   cand_val[wave], lsum[wave], xsrc, x16, xe, H, x16_bits);
 }
@@ -220,15 +221,28 @@ hipError_t launch_topk(const RouterArgs& a, hipStream_t s, int nplanes) {
   const dim3 grid((a.T + wpb - 1) / wpb), block(64 * wpb);
   const int hg = a.shared_gate_w ? 1 : 0;
   const uint16_t* xs = reinterpret_cast<const uint16_t*>(a.x);
-  if (a.E <= 256)
-    hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, a.logits, a.topk_idx, a.topk_w,
-                       a.gamma, a.T, a.E, a.k, hg, nplanes, xs, a.x16, a.xe, a.H, a.x16_bits);
-  else if (a.E <= 512)
-    hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, s, a.logits, a.topk_idx, a.topk_w,
-                       a.gamma, a.T, a.E, a.k, hg, nplanes, xs, a.x16, a.xe, a.H, a.x16_bits);
-  else
-    hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, a.logits, a.topk_idx, a.topk_w,
-                       a.gamma, a.T, a.E, a.k, hg, nplanes, xs, a.x16, a.xe, a.H, a.x16_bits);
+  if (nplanes > kRouterMaxPlanes) return hipErrorInvalidValue;
+  // every plane load of a token is issued, so the bound follows the call's planes
+  const int np = nplanes <= 2 ? 2 : (nplanes <= 8 ? 8 : kRouterMaxPlanes);
+#define MOE_TOPK(MPL, NP)                                                                      \
+  hipLaunchKernelGGL((topk_kernel<MPL, NP>), grid, block, 0, s, a.logits, a.topk_idx, a.topk_w, \
+                     a.gamma, a.T, a.E, a.k, hg, nplanes, xs, a.x16, a.xe, a.H, a.x16_bits)
+#define MOE_TOPK_NP(MPL)      \
+  if (np == 2)                \
+    MOE_TOPK(MPL, 2);         \
+  else if (np == 8)           \
+    MOE_TOPK(MPL, 8);         \
+  else                        \
+    MOE_TOPK(MPL, kRouterMaxPlanes)
+  if (a.E <= 256) {
+    MOE_TOPK_NP(4);
+  } else if (a.E <= 512) {
+    MOE_TOPK_NP(8);
+  } else {
+    MOE_TOPK_NP(16);
+  }
+#undef MOE_TOPK_NP
+#undef MOE_TOPK
   return hipGetLastError();
 }
 
