@@ -141,9 +141,27 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ logits, int
                                            float* cand_val, float* lsum,
                                            const uint16_t* __restrict__ xsrc,
                                            uint16_t* __restrict__ x16, int32_t* __restrict__ xe,
-                                           int H, int x16_bits) {
+                                           int H, int x16_bits,
+                                           const float* __restrict__ gate_w) {
   const int lane = threadIdx.x & 63;
   const float* lt = logits + (int64_t)t * (E + 1);
+  // with gate_w (bf16 activations, logits in planes): the shared-gate logit
+  // w_sg . x[t] here, 8 consecutive columns per lane and step, instead of
+  // row E of the planes
+  float gacc = 0.f;
+  if (gate_w != nullptr) {
+    const uint16_t* xr = xsrc + (int64_t)t * H;
+#pragma unroll 4
+    for (int c = 8 * lane; c < H; c += 512) {
+      const uint4 xv = *reinterpret_cast<const uint4*>(xr + c);
+      const float4 w0 = *reinterpret_cast<const float4*>(gate_w + c);
+      const float4 w1 = *reinterpret_cast<const float4*>(gate_w + c + 4);
+      gacc += bf16_bits_to_f32(xv.x & 0xFFFFu) * w0.x + bf16_bits_to_f32(xv.x >> 16) * w0.y +
+              bf16_bits_to_f32(xv.y & 0xFFFFu) * w0.z + bf16_bits_to_f32(xv.y >> 16) * w0.w +
+              bf16_bits_to_f32(xv.z & 0xFFFFu) * w1.x + bf16_bits_to_f32(xv.z >> 16) * w1.y +
+              bf16_bits_to_f32(xv.w & 0xFFFFu) * w1.z + bf16_bits_to_f32(xv.w >> 16) * w1.w;
+    }
+  }
   if (nplanes > 1) {
     // logits split over K planes: add them in plane order (row E, the
     // shared-gate logit, too: a partial per plane, or the whole logit in
@@ -173,6 +191,10 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ logits, int
       const int e = lane + 64 * m;
       if (e <= E) lsum[e] = v[m];
     }
+    if (gate_w != nullptr) {
+      gacc = warp_sum(gacc);
+      if (lane == 0) lsum[E] = gacc;  // (after the planes' row E above)
+    }
     dec::lds_wave_sync();
     lt = lsum;
   }
@@ -199,7 +221,8 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
                                                    int k, int has_gate, int nplanes,
                                                    const uint16_t* __restrict__ xsrc,
                                                    uint16_t* __restrict__ x16,
-                                                   int32_t* __restrict__ xe, int H, int x16_bits) {
+                                                   int32_t* __restrict__ xe, int H, int x16_bits,
+                                                   const float* __restrict__ gate_w) {
   __shared__ int32_t sel_idx[4][MOE_MAX_TOP_K];
   __shared__ float sel_val[4][MOE_MAX_TOP_K], sel_w[4][MOE_MAX_TOP_K], gam[4];
   __shared__ __align__(16) uint32_t cand_key[4][64];
@@ -211,10 +234,10 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   if (t >= T) return;
   topk_token<MPL, NP>(logits, topk_idx, topk_w, gamma, T, E, k, has_gate, nplanes, t, sel_idx[wave],
                   sel_val[wave], sel_w[wave], &gam[wave], cand_key[wave], cand_idx[wave],
-                  cand_val[wave], lsum[wave], xsrc, x16, xe, H, x16_bits);
+                  cand_val[wave], lsum[wave], xsrc, x16, xe, H, x16_bits, gate_w);
 }
 
-hipError_t launch_topk(const RouterArgs& a, hipStream_t s, int nplanes) {
+hipError_t launch_topk(const RouterArgs& a, hipStream_t s, int nplanes, const float* gate_w) {
   // one wave per token; small batches one wave per workgroup, so that the
   // tokens' logit loads spread over more compute units
   const int wpb = a.T <= 1024 ? 1 : 4;
@@ -226,7 +249,7 @@ hipError_t launch_topk(const RouterArgs& a, hipStream_t s, int nplanes) {
   const int np = nplanes <= 2 ? 2 : (nplanes <= 8 ? 8 : kRouterMaxPlanes);
 #define MOE_TOPK(MPL, NP)                                                                      \
   hipLaunchKernelGGL((topk_kernel<MPL, NP>), grid, block, 0, s, a.logits, a.topk_idx, a.topk_w, \
-                     a.gamma, a.T, a.E, a.k, hg, nplanes, xs, a.x16, a.xe, a.H, a.x16_bits)
+                     a.gamma, a.T, a.E, a.k, hg, nplanes, xs, a.x16, a.xe, a.H, a.x16_bits, gate_w)
 #define MOE_TOPK_NP(MPL)      \
   if (np == 2)                \
     MOE_TOPK(MPL, 2);         \
@@ -431,6 +454,7 @@ hipError_t launch_router_gemv(const RouterArgs& a, hipStream_t s);
 template <int ACT>
 hipError_t launch_router_act(const RouterArgs& a, hipStream_t s) {
   int nplanes = 1;
+  const float* gate_in_topk = nullptr;  // the shared-gate logit taken by the top-k kernel
   if (router_uses_mfma(a.act, a.T, a.H)) {
     // split K so that the grid fills the chip at two workgroups per CU (a
     // workgroup's split-weight work then overlaps the other's MFMAs; at most
@@ -465,15 +489,21 @@ hipError_t launch_router_act(const RouterArgs& a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.shared_gate_w != nullptr && !fold) {
-      hipLaunchKernelGGL((gate_logit_kernel<ACT>), dim3((a.T + 3) / 4), dim3(256), 0, s, a.x,
-                         a.shared_gate_w, a.logits, a.T, a.H, a.E, nplanes);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
+      // bf16 rows over several planes: the top-k kernel reads each token's
+      // row anyway and writes the logit where it ranks; else its own kernel
+      if (ACT == MOE_ACT_BF16 && nplanes > 1) {
+        gate_in_topk = a.shared_gate_w;
+      } else {
+        hipLaunchKernelGGL((gate_logit_kernel<ACT>), dim3((a.T + 3) / 4), dim3(256), 0, s, a.x,
+                           a.shared_gate_w, a.logits, a.T, a.H, a.E, nplanes);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+      }
     }
   } else {
     hipError_t e = launch_router_gemv<ACT>(a, s);
     if (e != hipSuccess) return e;
   }
-  return launch_topk(a, s, nplanes);
+  return launch_topk(a, s, nplanes, gate_in_topk);
 }
 
 template <int ACT>
