@@ -603,6 +603,36 @@ def test_grouped_mfma_path_tiny(T, k, bits):
     _free()
 
 
+def test_grouped_mfma_dynamic_range():
+    """Tokens whose activation rows differ by 2^5 either way share the grouped
+    GEMMs' 128-row tiles, so h (fp16 after one power-of-two scale per tile and
+    128-column block) spans about 2^20 within a tile, and the partial rows
+    (fp16 with a scale per 32-row x 64-column block) as much; each scale's
+    rows are checked against the oracle on their own size.  (The tile's h scale
+    keeps 11 significant bits for values within 2^-29 of the tile's largest:
+    rows of one tile more than about 2^14 apart in input scale lose
+    precision.)  The oracle takes the routing the GPU chose: at scaled logits
+    the lower softmax weights are tiny and carry the logits' fp32 rounding,
+    which the routing tests check at ordinary scale."""
+    wl = _wl()
+    cfg = configs.TINY.with_(n_tokens=300, top_k=3, bits=4, act="bf16")
+    say("[mfma] tiny bf16 T=300 rows scaled by 2^-5, 1, 2^5")
+    w = wl.Workload(cfg, n_layers=1)
+    group = np.arange(cfg.n_tokens) % 3
+    x_np = synth.activations(cfg).astype(np.float64) * (2.0 ** (5 * (group - 1)))[:, None]
+    x = wl.act_tensor(cfg, x_np.astype(np.float32))
+    out, idx, wt, g = run_layer(w, cfg, x)
+    inp = oracle.LayerInputs(cfg, 0)
+    ref = oracle.oracle_layer(inp, x_np, routing=(idx.cpu().numpy(),
+                                                  wt.cpu().numpy().astype(np.float64)))
+    got = out.float().cpu().numpy()
+    for s in range(3):
+        rows = group == s
+        check_out(got[rows], ref["out"][rows], cfg.act, f"rows scaled by 2^{5 * (s - 1)}")
+    del w
+    _free()
+
+
 @pytest.mark.parametrize("cfgname,T", [("batched_80b", 320), ("batched_80b_int8", 300)])
 def test_grouped_mfma_path_80b(cfgname, T):
     """80B-shaped layer with a Zipf-skewed router (one bucket holds most tokens)
