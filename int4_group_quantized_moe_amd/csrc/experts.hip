@@ -1080,6 +1080,45 @@ __device__ __forceinline__ float round_act(float v) {
 // r < 4 (H <= 8192) in registers, so x is read once: the residual sum (x +
 // out, rounded to the act dtype and stored back), its sum of squares, and
 // the normalised row.
+// The same as rmsnorm_kernel with one wave per row, four rows per workgroup,
+// for H = 512 NC: lane l holds chunks l, l + 64, ... of 8 values, every load
+// of a row in flight together; the sum of squares in lane order, then across
+// the wave.
+template <int ACT, int NC>
+__global__ __launch_bounds__(256) void rmsnorm_row_kernel(void* __restrict__ x,
+                                                          const void* __restrict__ out,
+                                                          void* __restrict__ x_hat, int T, int H,
+                                                          float eps, int do_norm) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (t >= T) return;
+  const int64_t base = (int64_t)t * H;
+  float v[NC][8], o[NC][8];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    load_act8<ACT>(x, base + 8 * (lane + 64 * i), v[i]);
+    if (out != nullptr) load_act8<ACT>(out, base + 8 * (lane + 64 * i), o[i]);
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    if (out != nullptr) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[i][j] = round_act<ACT>(v[i][j] + o[i][j]);
+      store_act8<ACT>(x, base + 8 * (lane + 64 * i), v[i]);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ss += v[i][j] * v[i][j];
+  }
+  if (!do_norm) return;
+  const float inv = 1.0f / sqrtf(warp_sum(ss) / (float)H + eps);
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[i][j] *= inv;
+    store_act8<ACT>(x_hat, base + 8 * (lane + 64 * i), v[i]);
+  }
+}
+
 template <int ACT>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(void* __restrict__ x,
                                                       const void* __restrict__ out,
@@ -1328,6 +1367,29 @@ hipError_t launch_experts(const ExpertArgs& a, hipStream_t s) {
 
 hipError_t launch_rmsnorm(void* x, const void* out, void* x_hat, int T, int H, int act, float eps,
                           bool do_norm, hipStream_t s) {
+  // one wave per row where H is 1024, 2048 or 4096
+  const int nc = H % 512 == 0 ? H / 512 : 0;
+  if (nc == 2 || nc == 4 || nc == 8) {
+    const dim3 grid((unsigned)((T + 3) / 4));
+    const int dn = do_norm ? 1 : 0;
+#define MOE_RMS_ROW(A, NC)                                                                        \
+  hipLaunchKernelGGL((rmsnorm_row_kernel<A, NC>), grid, dim3(256), 0, s, x, out, x_hat, T, H, eps, dn)
+#define MOE_RMS_ROW_NC(A)   \
+  if (nc == 2)              \
+    MOE_RMS_ROW(A, 2);      \
+  else if (nc == 4)         \
+    MOE_RMS_ROW(A, 4);      \
+  else                      \
+    MOE_RMS_ROW(A, 8)
+    if (act == MOE_ACT_F32) {
+      MOE_RMS_ROW_NC(MOE_ACT_F32);
+    } else {
+      MOE_RMS_ROW_NC(MOE_ACT_BF16);
+    }
+#undef MOE_RMS_ROW_NC
+#undef MOE_RMS_ROW
+    return hipGetLastError();
+  }
   if (act == MOE_ACT_F32)
     hipLaunchKernelGGL(rmsnorm_kernel<MOE_ACT_F32>, dim3(T), dim3(256), 0, s, x, out, x_hat, H, eps,
                        do_norm ? 1 : 0);
