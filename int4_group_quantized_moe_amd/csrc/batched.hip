@@ -314,7 +314,10 @@ __device__ __forceinline__ void bd_down_item(MOE_BD_PARAMS, BdLds& sm, const Til
   // stage h: thread (row, group) holds the row's 64 fp32 values of the group;
   // the 8 threads of a row (consecutive lanes) agree on the row's scale 2^-e
   // (its largest magnitude to [2^14, 2^15)) and store the scaled values in
-  // fp16, in the weights' fp16 K order
+  // fp16, in the weights' fp16 K order.  Group g's 16-byte chunk c sits at
+  // chunk c ^ (g & 6) of the group: with 1040-byte rows the groups g, g + 2,
+  // g + 4, g + 6 of a row would otherwise start on the same banks, so that
+  // the staging stores of a wave hit each bank four times.
   {
     const int row = tid >> 3, g = tid & 7;
     const bool ok = row < 32 * MB && row < ti.rows && g < GD;
@@ -349,7 +352,7 @@ __device__ __forceinline__ void bd_down_item(MOE_BD_PARAMS, BdLds& sm, const Til
           o[i] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
                  ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
         }
-        *reinterpret_cast<u32x4*>(&sm.h16[row * kBdLdsRow + g * kGroup + 8 * c]) =
+        *reinterpret_cast<u32x4*>(&sm.h16[row * kBdLdsRow + g * kGroup + 8 * (c ^ (g & 6))]) =
             u32x4{o[0], o[1], o[2], o[3]};
       }
       if (g == 0) sm.he[row] = e;
@@ -371,7 +374,8 @@ __device__ __forceinline__ void bd_down_item(MOE_BD_PARAMS, BdLds& sm, const Til
         const u32x4 b = w_frag_f16<BITS>(q[g], kk, S2, B2);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-          const int o = (32 * mb + l32) * kBdLdsRow + g * kGroup + 32 * half + 8 * kk;
+          const int o =
+              (32 * mb + l32) * kBdLdsRow + g * kGroup + 8 * ((4 * half + kk) ^ (g & 6));
           acc[mb] = mfma_f16(*reinterpret_cast<const u32x4*>(&sm.h16[o]), b, acc[mb]);
         }
       }
